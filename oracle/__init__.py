@@ -1,0 +1,122 @@
+"""Python face of the plain fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product library or its binding.
+It shares no code with the GPU path; both sides only consume the seeded inputs
+of the `workloads` package.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
+WFMT = {"f32": 0, "bf16": 1}
+GCC_FLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-shared", "-fPIC"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """gcc -O2 -fopenmp (no fast-math, no contraction) `src` into shared library `out`."""
+    tmp = out + ".tmp%d" % os.getpid()
+    subprocess.run(["gcc", *GCC_FLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        compile_source(SRC, LIB)
+    return LIB
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """ctypes binding of one compiled oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        lib.oracle_windows.argtypes = [ctypes.c_int] * 3 + [P] * 5
+        lib.oracle_windows.restype = None
+        lib.oracle_mqa_logits.argtypes = ([ctypes.c_int] * 6 + [P] * 5 + [ctypes.c_int, ctypes.c_double]
+                                          + [P, P, P, ctypes.c_int64, P, P, ctypes.c_int])
+        lib.oracle_mqa_logits.restype = ctypes.c_int
+        for name, argt in (("oracle_dec_bf16", ctypes.c_uint16), ("oracle_dec_e4m3", ctypes.c_uint8),
+                           ("oracle_dec_e2m1", ctypes.c_uint8), ("oracle_dec_e8m0", ctypes.c_uint8)):
+            fn = getattr(lib, name)
+            fn.argtypes = [argt]
+            fn.restype = ctypes.c_double
+        self.lib = lib
+        self.path = path
+
+    def decode(self, fmt: str, code: int) -> float:
+        """One element code -> its exact value (fmt in bf16, e4m3, e2m1, e8m0)."""
+        return getattr(self.lib, "oracle_dec_" + fmt)(code)
+
+    def windows(self, wl) -> tuple[np.ndarray, np.ndarray]:
+        """Per-row [start, end) of a workload as int32 [B, S_q] arrays."""
+        ws = np.empty((wl.B, wl.S_q), np.int32)
+        we = np.empty((wl.B, wl.S_q), np.int32)
+        offs = None if wl.offsets is None else np.ascontiguousarray(wl.offsets, np.int32)
+        st = None if wl.starts is None else np.ascontiguousarray(wl.starts, np.int32)
+        en = None if wl.ends is None else np.ascontiguousarray(wl.ends, np.int32)
+        self.lib.oracle_windows(wl.B, wl.S_q, wl.S_k, _ptr(offs), _ptr(st), _ptr(en), _ptr(ws), _ptr(we))
+        return ws, we
+
+    def logits(self, wl, rows: Optional[Sequence[int]] = None, threads: int = 0, return_threads: bool = False):
+        """fp64 scores and per-cell error scales.
+
+        rows: global row ids b*S_q+i to evaluate (None: all rows).  Returns
+        (ref, bound) as float64 [n_rows, S_k] (and the thread count if asked)."""
+        ws, we = self.windows(wl)
+        if rows is None:
+            n_rows, rows_arr = wl.B * wl.S_q, None
+        else:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, np.int64))
+            n_rows = rows_arr.size
+        ref = np.empty((n_rows, wl.S_k), np.float64)
+        bound = np.empty((n_rows, wl.S_k), np.float64)
+        arrs = [None if a is None else np.ascontiguousarray(a) for a in (wl.q, wl.q_scale, wl.k, wl.k_scale, wl.w)]
+        used = self.lib.oracle_mqa_logits(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, FMT[wl.fmt], *[_ptr(a) for a in arrs],
+                                          WFMT[wl.w_dtype], float(wl.sm_scale), _ptr(ws), _ptr(we),
+                                          _ptr(rows_arr), n_rows, _ptr(ref), _ptr(bound), int(threads))
+        if used < 0:
+            raise RuntimeError("oracle_mqa_logits rejected its arguments")
+        return (ref, bound, used) if return_threads else (ref, bound)
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        _default = Oracle(LIB)
+    return _default
+
+
+def decode(fmt: str, code: int) -> float:
+    return default().decode(fmt, code)
+
+
+def windows(wl):
+    return default().windows(wl)
+
+
+def logits(wl, rows=None, threads: int = 0, return_threads: bool = False):
+    return default().logits(wl, rows=rows, threads=threads, return_threads=return_threads)
