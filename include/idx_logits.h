@@ -1,0 +1,173 @@
+/*
+ * idx_logits.h -- C ABI of the MI355X lightning-indexer scoring library
+ * ("MQA logits", DSA indexer forward).
+ *
+ * For every query row i of batch b and every key column j inside the row's
+ * visibility window [start, end):
+ *
+ *     out[b,i,j] = sm_scale * sum_{h<64} w[b,i,h] * max(0, q[b,i,h,:] . k[b,j,:])
+ *
+ * 64 query heads share one 128-wide key head.  With clean_logits set, every
+ * other column of the row is -inf.
+ *
+ * Where this is defined: DeepGEMM pull request 435, "Improve SM100 MX MQA
+ * logits clean-output performance" (Performance section and standalone
+ * reproducer: q[m,64,D], k[n,D], w[m,64], per-row windows, clean_logits,
+ * logits_dtype, optional precomputed schedule metadata); cudnn-frontend pull
+ * request 416, "DSA indexer forward: add a lean SM100 fast path" (What,
+ * Precision / determinism and Support surface sections: one KV head for 64
+ * query heads, D=128, BF16 Q/K, BF16 or FP32 W, FP32 scores, sm_scale per call,
+ * q_causal_offsets folded into per-row windows, 16-byte-aligned bases, -inf
+ * outside the causal window).  The ReLU on each head's dot before the
+ * weighting is the plainest reading of the "head-sum" those pages describe.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call is asynchronous on that stream: no host synchronisation and
+ *    no host read of device data, so calls can be captured in a HIP graph.
+ *  - All argument checks run on the host before anything is launched; a
+ *    non-OK status means nothing was enqueued.  Device-resident values
+ *    (windows, scales) are not inspected.
+ *  - idx_last_error() returns a thread-local description of the last non-OK
+ *    status.
+ */
+#ifndef IDX_LOGITS_H
+#define IDX_LOGITS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IDX_ABI_VERSION 1
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_E_INVALID = 1,     /* bad pointer, size, alignment, stride or scalar      */
+  IDX_E_UNSUPPORTED = 2, /* valid request outside the supported set (H!=64...)  */
+  IDX_E_WORKSPACE = 3,   /* plan / workspace buffer missing or too small         */
+  IDX_E_HIP = 4          /* a HIP launch failed                                  */
+} idx_status_t;
+
+/* Element format of Q and K (the same for both). */
+typedef enum {
+  IDX_IN_BF16 = 0,       /* bfloat16                                             */
+  IDX_IN_FP8_E4M3 = 1,   /* e4m3fn codes with one fp32 scale per K row           */
+  IDX_IN_MXFP8_E4M3 = 2, /* e4m3fn codes, one E8M0 scale per 32 elements of D   */
+  IDX_IN_MXFP4_E2M1 = 3  /* e2m1 codes two per byte, E8M0 per 32 elements of D  */
+} idx_in_t;
+
+/* Floating type of the weights and of the output. */
+typedef enum { IDX_F32 = 0, IDX_BF16 = 1 } idx_fp_t;
+
+/*
+ * One scoring call.  Layouts are dense row-major with the last index fastest.
+ *
+ *  q        [B, S_q, H, D] elements; MXFP4: [B, S_q, H, D/2] bytes, the low
+ *           nibble of each byte holding the even element.
+ *  q_scale  MX formats: int32 [B, S_q, H]; byte b (bits 8b..8b+7) is the E8M0
+ *           exponent (value 2^(e-127)) of elements [32b, 32b+32).  Otherwise NULL.
+ *  k        [B, S_k, D] elements (MXFP4: [B, S_k, D/2] bytes).
+ *  k_scale  FP8: fp32 [B, S_k], finite and >= 0, multiplying row j of K.
+ *           MX formats: int32 [B, S_k] packed like q_scale.  BF16: NULL.
+ *  w        [B, S_q, H] in w_dtype.
+ *  out      [B, S_q, out_row_stride] in out_dtype (batch stride
+ *           S_q * out_row_stride elements).  Only columns [0, S_k) of each row
+ *           are written; columns [S_k, out_row_stride) are never touched.
+ *  clean_logits  1: every column outside the row's window is written -inf.
+ *                0: those columns are left untouched; in-window values are
+ *                bitwise identical to the clean_logits=1 call.
+ *
+ * H must be 64 and D 128 (else IDX_E_UNSUPPORTED).  q, k, w, out and the
+ * scale pointers must be 16-byte aligned; out_row_stride >= S_k.
+ * sm_scale must be finite.  Results are deterministic: the same inputs give
+ * bitwise identical outputs, with or without a precomputed plan, for any B.
+ */
+typedef struct {
+  int32_t B, S_q, S_k, H, D;
+  idx_in_t in_dtype;
+  const void* q;
+  const void* q_scale;
+  const void* k;
+  const void* k_scale;
+  const void* w;
+  idx_fp_t w_dtype;
+  float sm_scale;
+  void* out;
+  idx_fp_t out_dtype;
+  int64_t out_row_stride;
+  int32_t clean_logits;
+} idx_logits_args_t;
+
+/* ABI version of the loaded library (IDX_ABI_VERSION of its build). */
+int32_t idx_abi_version(void);
+
+/*
+ * Size in bytes of the plan (windows + schedule metadata) for these
+ * dimensions; 0 when a dimension is <= 0 or the size would overflow.
+ * The plan plays the role of the schedule metadata that the DeepGEMM
+ * pull request 435 reproducer precomputes outside timing.
+ */
+size_t idx_logits_plan_bytes(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D);
+
+/*
+ * Build a plan on `stream`: the per-row windows and the work schedule.
+ *
+ * Windows (each row of batch b, query index i):
+ *  - row_starts and row_ends both given ([B, S_q] int32 device arrays):
+ *      start = clamp(row_starts, 0, S_k), end = clamp(row_ends, start, S_k);
+ *  - otherwise, from q_causal_offsets ([B] int32 device array, or NULL for
+ *    all zero): start = 0, end = clamp(S_k - S_q + off[b] + i + 1, 0, S_k),
+ *    computed in 64-bit integers so no offset can overflow.
+ *  An empty window (start == end) makes the whole row -inf.
+ * `plan` is a device buffer of at least idx_logits_plan_bytes(...) bytes,
+ * 256-byte aligned.  Once the stream reaches the end of this call the plan is
+ * immutable and may serve any number of idx_logits_run calls with the same
+ * dimensions and windows, whatever their Q, K, W, formats or flags.  It
+ * holds no pointer to caller data.
+ */
+idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                             const int32_t* q_causal_offsets, const int32_t* row_starts,
+                             const int32_t* row_ends, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * Device workspace a call to idx_logits_run with plan == NULL needs (the plan
+ * is then built inside the call); 0 for invalid arguments.
+ */
+size_t idx_logits_workspace_bytes(const idx_logits_args_t* a);
+
+/*
+ * Score one batch of queries on `stream`.
+ *
+ * plan != NULL: a plan built by idx_logits_plan for the same (B, S_q, S_k,
+ *   H, D); the window arguments are then ignored and workspace may be NULL.
+ *   A plan whose recorded dimensions differ from `a` is detected on the
+ *   device: the call then writes quiet NaN to columns [0, S_k) of every row.
+ * plan == NULL: the plan is first built into `workspace` (at least
+ *   idx_logits_workspace_bytes(a) bytes, 256-byte aligned) from
+ *   q_causal_offsets / row_starts / row_ends exactly as idx_logits_plan
+ *   would, then used; the result is bitwise identical to the planned call.
+ */
+idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                            const int32_t* row_starts, const int32_t* row_ends, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * Copy the windows stored in a plan into caller device arrays
+ * win_start / win_end ([B, S_q] int32) on `stream` (for inspection and tests).
+ */
+idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H,
+                                     int32_t D, int32_t* win_start, int32_t* win_end, void* stream);
+
+/* Thread-local text of the last non-OK status returned on this thread. */
+const char* idx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IDX_LOGITS_H */

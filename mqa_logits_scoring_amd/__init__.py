@@ -1,0 +1,203 @@
+"""Thin Python binding of libidx_logits.so, the MI355X lightning-indexer
+scoring library ("MQA logits").  The C ABI is declared in include/idx_logits.h;
+the functions here carry the same names and only marshal arguments: every step
+of the computation runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.
+
+If the library is missing the import still succeeds but every call raises, so
+nothing can silently fall back to another implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libidx_logits.so")
+
+IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
+IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
+FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
+EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_workspace_bytes",
+            "idx_logits_run", "idx_logits_plan_windows", "idx_last_error")
+
+
+class IdxLogitsArgs(ctypes.Structure):
+    """Mirror of idx_logits_args_t."""
+    _fields_ = [("B", ctypes.c_int32), ("S_q", ctypes.c_int32), ("S_k", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("in_dtype", ctypes.c_int), ("q", ctypes.c_void_p),
+                ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("w", ctypes.c_void_p), ("w_dtype", ctypes.c_int), ("sm_scale", ctypes.c_float),
+                ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int), ("out_row_stride", ctypes.c_int64),
+                ("clean_logits", ctypes.c_int32)]
+
+
+class IdxError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mqa_logits_scoring_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.idx_abi_version.restype = I32
+        L.idx_abi_version.argtypes = []
+        L.idx_last_error.restype = ctypes.c_char_p
+        L.idx_last_error.argtypes = []
+        L.idx_logits_plan_bytes.restype = SZ
+        L.idx_logits_plan_bytes.argtypes = [I32] * 5
+        L.idx_logits_plan.restype = ctypes.c_int
+        L.idx_logits_plan.argtypes = [I32] * 5 + [P, P, P, P, SZ, P]
+        L.idx_logits_workspace_bytes.restype = SZ
+        L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
+        L.idx_logits_run.restype = ctypes.c_int
+        L.idx_logits_run.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, P, SZ, P]
+        L.idx_logits_plan_windows.restype = ctypes.c_int
+        L.idx_logits_plan_windows.argtypes = [P] + [I32] * 5 + [P, P, P]
+        _lib = L
+    return _lib
+
+
+def idx_last_error() -> str:
+    return lib().idx_last_error().decode()
+
+
+def idx_abi_version() -> int:
+    return int(lib().idx_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != IDX_OK:
+        raise IdxError(fn, status, idx_last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev_i32(x, device) -> Optional[torch.Tensor]:
+    if x is None:
+        return None
+    t = torch.as_tensor(x, dtype=torch.int32, device=device)
+    return t.contiguous()
+
+
+def idx_logits_plan_bytes(B: int, S_q: int, S_k: int, H: int = 64, D: int = 128) -> int:
+    return int(lib().idx_logits_plan_bytes(B, S_q, S_k, H, D))
+
+
+def idx_logits_plan(B: int, S_q: int, S_k: int, H: int = 64, D: int = 128, *, q_causal_offsets=None,
+                    row_starts=None, row_ends=None, plan: Optional[torch.Tensor] = None, device=None,
+                    stream=None) -> torch.Tensor:
+    """Build a plan (windows + schedule) on the stream; returns the uint8 plan tensor."""
+    device = torch.device(device if device is not None else (plan.device if plan is not None else "cuda"))
+    nbytes = idx_logits_plan_bytes(B, S_q, S_k, H, D)
+    if plan is None:
+        plan = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    offs = _dev_i32(q_causal_offsets, device)
+    st = _dev_i32(row_starts, device)
+    en = _dev_i32(row_ends, device)
+    _check("idx_logits_plan", lib().idx_logits_plan(B, S_q, S_k, H, D, _ptr(offs), _ptr(st), _ptr(en), _ptr(plan),
+                                                      plan.numel() * plan.element_size(), _stream(stream, device)))
+    plan._idx_keep = (offs, st, en)  # keep the window inputs alive until the stream has used them
+    return plan
+
+
+def idx_logits_plan_windows(plan: torch.Tensor, B: int, S_q: int, S_k: int, H: int = 64, D: int = 128,
+                            stream=None):
+    """The per-row windows stored in a plan, as int32 [B, S_q] device tensors (start, end)."""
+    ws = torch.empty((B, S_q), dtype=torch.int32, device=plan.device)
+    we = torch.empty((B, S_q), dtype=torch.int32, device=plan.device)
+    _check("idx_logits_plan_windows", lib().idx_logits_plan_windows(_ptr(plan), B, S_q, S_k, H, D, _ptr(ws),
+                                                                      _ptr(we), _stream(stream, plan.device)))
+    return ws, we
+
+
+def _shape_info(q: torch.Tensor, k: torch.Tensor, in_dtype: str):
+    if q.dim() == 3:
+        q = q.unsqueeze(0)
+    if k.dim() == 2:
+        k = k.unsqueeze(0)
+    if q.dim() != 4 or k.dim() != 3:
+        raise ValueError("q must be [B,S_q,H,D'] or [S_q,H,D']; k [B,S_k,D'] or [S_k,D']")
+    B, S_q, H, Dq = q.shape
+    D = Dq * 2 if in_dtype == "mxfp4" else Dq
+    return q, k, B, S_q, k.shape[1], H, D
+
+
+def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, in_dtype: str,
+              q_scale=None, k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True) -> IdxLogitsArgs:
+    """Fill an idx_logits_args_t from tensors (no copies, no checks beyond shapes)."""
+    q4, k3, B, S_q, S_k, H, D = _shape_info(q, k, in_dtype)
+    if out.dtype not in FP_DTYPES or w.dtype not in FP_DTYPES:
+        raise ValueError("w and out must be float32 or bfloat16")
+    a = IdxLogitsArgs()
+    a.B, a.S_q, a.S_k, a.H, a.D = B, S_q, S_k, H, D
+    a.in_dtype = IN_DTYPES[in_dtype]
+    a.q, a.k, a.w, a.out = _ptr(q), _ptr(k), _ptr(w), _ptr(out)
+    a.q_scale, a.k_scale = _ptr(q_scale), _ptr(k_scale)
+    a.w_dtype = FP_DTYPES[w.dtype]
+    a.out_dtype = FP_DTYPES[out.dtype]
+    a.sm_scale = float(sm_scale)
+    a.out_row_stride = out.stride(-2) if out.dim() >= 2 else S_k
+    a.clean_logits = 1 if clean_logits else 0
+    return a
+
+
+def idx_logits_workspace_bytes(args: IdxLogitsArgs) -> int:
+    return int(lib().idx_logits_workspace_bytes(ctypes.byref(args)))
+
+
+def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtype: str, q_scale=None,
+                   k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
+                   out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+                   plan: Optional[torch.Tensor] = None, q_causal_offsets=None, row_starts=None, row_ends=None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Score q against k on the stream; returns `out` ([B,S_q,S_k] or the caller's buffer).
+
+    Tensors are passed as raw device buffers: q/k of any 1- or 2-byte dtype
+    holding the codes (bf16 bits, e4m3 bytes, packed e2m1 bytes), scales as
+    int32 (MX) or float32 (FP8 rows), w as float32 or bfloat16.  All must be
+    contiguous; `out` may have a row stride larger than S_k."""
+    for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    q4, k3, B, S_q, S_k, H, D = _shape_info(q, k, in_dtype)
+    device = q.device
+    if out is None:
+        shape = (B, S_q, S_k) if q.dim() == 4 else (S_q, S_k)
+        out = torch.empty(shape, dtype=out_dtype, device=device)
+    args = make_args(q, k, w, out, in_dtype=in_dtype, q_scale=q_scale, k_scale=k_scale, sm_scale=sm_scale,
+                     clean_logits=clean_logits)
+    offs = st = en = None
+    ws_bytes = 0
+    if plan is None:
+        offs = _dev_i32(q_causal_offsets, device)
+        st = _dev_i32(row_starts, device)
+        en = _dev_i32(row_ends, device)
+        ws_bytes = idx_logits_workspace_bytes(args)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check("idx_logits_run", lib().idx_logits_run(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en),
+                                                    _ptr(workspace), ws_bytes, _stream(stream, device)))
+    return out

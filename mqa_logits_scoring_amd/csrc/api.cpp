@@ -1,0 +1,189 @@
+// Host side of the C ABI: argument validation (all of it before any launch),
+// plan construction, work decomposition and kernel dispatch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+idx_status_t fail(idx_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D) {
+  if (B <= 0 || S_q <= 0 || S_k <= 0 || H <= 0 || D <= 0)
+    return fail(IDX_E_INVALID, "dimensions must be positive (B=%d S_q=%d S_k=%d H=%d D=%d)", B, S_q, S_k, H, D);
+  if (H != 64 || D != 128)
+    return fail(IDX_E_UNSUPPORTED, "only H=64 query heads and D=128 are supported (got H=%d D=%d)", H, D);
+  const idx::PlanLayout L = idx::plan_layout(B, S_q);
+  if (L.total == 0) return fail(IDX_E_INVALID, "B*S_q=%lld rows is too large", (long long)B * S_q);
+  return IDX_OK;
+}
+
+int row_bytes(idx_in_t f) {
+  switch (f) {
+    case IDX_IN_BF16: return 256;
+    case IDX_IN_FP8_E4M3:
+    case IDX_IN_MXFP8_E4M3: return 128;
+    case IDX_IN_MXFP4_E2M1: return 64;
+  }
+  return 0;
+}
+
+// Key columns per compute unit: enough units to spread a few per CU slot over
+// 256 CUs, few enough that each unit amortises loading its rows' Q.
+int32_t pick_chunk_cols(int64_t S_k, int64_t n_tiles) {
+  const int64_t cols = (S_k + 63) / 64 * 64;
+  int64_t ch = (cols * n_tiles + 4095) / 4096;
+  ch = (ch + 63) / 64 * 64;
+  if (ch < 256) ch = 256;
+  if (ch > 8192) ch = 8192;
+  return int32_t(ch);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t idx_abi_version(void) { return IDX_ABI_VERSION; }
+
+const char* idx_last_error(void) { return g_err; }
+
+size_t idx_logits_plan_bytes(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D) {
+  if (B <= 0 || S_q <= 0 || S_k <= 0 || H <= 0 || D <= 0) return 0;
+  return idx::plan_layout(B, S_q).total;
+}
+
+idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                             const int32_t* q_causal_offsets, const int32_t* row_starts, const int32_t* row_ends,
+                             void* plan, size_t plan_bytes, void* stream) {
+  idx_status_t st = check_dims(B, S_q, S_k, H, D);
+  if (st != IDX_OK) return st;
+  if ((row_starts == nullptr) != (row_ends == nullptr))
+    return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
+  const size_t need = idx::plan_layout(B, S_q).total;
+  if (plan_bytes < need)
+    return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
+  hipError_t e = idx::launch_plan(B, S_q, S_k, H, D, q_causal_offsets, row_starts, row_ends, plan,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
+size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) {
+  if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return 0;
+  return idx::plan_layout(a->B, a->S_q).total;
+}
+
+idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                                     int32_t* win_start, int32_t* win_end, void* stream) {
+  idx_status_t st = check_dims(B, S_q, S_k, H, D);
+  if (st != IDX_OK) return st;
+  if (plan == nullptr || win_start == nullptr || win_end == nullptr)
+    return fail(IDX_E_INVALID, "plan, win_start and win_end must be non-NULL");
+  hipError_t e = idx::launch_copy_windows(plan, int64_t(B) * S_q, win_start, win_end,
+                                          static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(IDX_E_HIP, "window copy launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
+idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                            const int32_t* row_starts, const int32_t* row_ends, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (a == nullptr) return fail(IDX_E_INVALID, "args is NULL");
+  idx_status_t st = check_dims(a->B, a->S_q, a->S_k, a->H, a->D);
+  if (st != IDX_OK) return st;
+  const idx_in_t f = a->in_dtype;
+  if (f != IDX_IN_BF16 && f != IDX_IN_FP8_E4M3 && f != IDX_IN_MXFP8_E4M3 && f != IDX_IN_MXFP4_E2M1)
+    return fail(IDX_E_INVALID, "unknown in_dtype %d", int(f));
+  if ((a->w_dtype != IDX_F32 && a->w_dtype != IDX_BF16) || (a->out_dtype != IDX_F32 && a->out_dtype != IDX_BF16))
+    return fail(IDX_E_INVALID, "w_dtype and out_dtype must be IDX_F32 or IDX_BF16");
+  const bool mx = f == IDX_IN_MXFP8_E4M3 || f == IDX_IN_MXFP4_E2M1;
+  if (a->q == nullptr || a->k == nullptr || a->w == nullptr || a->out == nullptr)
+    return fail(IDX_E_INVALID, "q, k, w and out must be non-NULL");
+  if (mx && a->q_scale == nullptr) return fail(IDX_E_INVALID, "MX formats need q_scale");
+  if ((mx || f == IDX_IN_FP8_E4M3) && a->k_scale == nullptr)
+    return fail(IDX_E_INVALID, "FP8 and MX formats need k_scale");
+  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->w) || !aligned16(a->out) ||
+      (mx && !aligned16(a->q_scale)) || ((mx || f == IDX_IN_FP8_E4M3) && !aligned16(a->k_scale)))
+    return fail(IDX_E_INVALID, "q, k, w, out and scale pointers must be 16-byte aligned");
+  if (a->out_row_stride < a->S_k)
+    return fail(IDX_E_INVALID, "out_row_stride %lld < S_k %d", (long long)a->out_row_stride, a->S_k);
+  const int64_t rows = int64_t(a->B) * a->S_q;
+  if (a->out_row_stride > (int64_t(1) << 40) || rows * a->out_row_stride > (int64_t(1) << 40))
+    return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
+                (long long)a->out_row_stride);
+  if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
+  (void)row_bytes;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
+  const unsigned char* p = static_cast<const unsigned char*>(plan);
+  if (p == nullptr) {
+    if ((row_starts == nullptr) != (row_ends == nullptr))
+      return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
+    if (workspace == nullptr) return fail(IDX_E_WORKSPACE, "no plan and no workspace");
+    if (!aligned256(workspace)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
+    if (workspace_bytes < L.total)
+      return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+    hipError_t e = idx::launch_plan(a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends,
+                                    workspace, s);
+    if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
+    p = static_cast<const unsigned char*>(workspace);
+  } else if (!aligned256(p)) {
+    return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  }
+
+  idx::ScoreArgs k{};
+  k.q = a->q;
+  k.q_scale = a->q_scale;
+  k.k = a->k;
+  k.k_scale = a->k_scale;
+  k.w = a->w;
+  k.out = a->out;
+  k.plan = p;
+  k.ld = a->out_row_stride;
+  k.sm_scale = a->sm_scale;
+  k.B = a->B;
+  k.S_q = a->S_q;
+  k.S_k = a->S_k;
+  k.n_tiles = int32_t(L.n_tiles);
+  k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q));
+  k.chunk_cols = pick_chunk_cols(a->S_k, L.n_tiles);
+  k.n_chunks = int32_t((int64_t(a->S_k) + idx::kColAlign - 1 + k.chunk_cols - 1) / k.chunk_cols);
+  const int64_t n_compute = int64_t(k.n_chunks) * L.n_tiles;
+  if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
+  k.n_compute = int32_t(n_compute);
+  k.off_start = uint32_t(L.off_start);
+  k.off_end = uint32_t(L.off_end);
+  k.off_slot = uint32_t(L.off_slot);
+  k.off_lo = uint32_t(L.off_lo);
+  k.off_hi = uint32_t(L.off_hi);
+  if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
+
+  const bool clean = a->clean_logits != 0;
+  hipError_t e = hipSuccess;
+  switch (f) {
+    case IDX_IN_BF16: e = idx::launch_score_bf16(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_FP8_E4M3: e = idx::launch_score_fp8(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_MXFP8_E4M3: e = idx::launch_score_mxfp8(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_MXFP4_E2M1: e = idx::launch_score_mxfp4(a->w_dtype, a->out_dtype, clean, k, s); break;
+  }
+  if (e != hipSuccess) return fail(IDX_E_HIP, "scoring launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
+}  // extern "C"

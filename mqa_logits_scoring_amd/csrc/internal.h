@@ -1,0 +1,103 @@
+// Internal declarations shared by the host API and the HIP kernels of the
+// lightning-indexer scoring library.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/idx_logits.h"
+
+namespace idx {
+
+// ---------------------------------------------------------------------------
+// Plan layout (device memory, 256-byte aligned sections)
+//
+//   PlanHeader                      (256 B)
+//   int32 win_start[B*S_q]          window start per row
+//   int32 win_end[B*S_q]            window end per row
+//   int32 slot_row[n_tiles*kTileRows]  global row (b*S_q+i) of every tile slot,
+//                                   -1 for the padding slots of a ragged tail
+//   int32 tile_lo[n_tiles]          first column computed for the tile
+//   int32 tile_hi[n_tiles]          one past the last column computed
+//
+// A tile is kTileRows consecutive query rows of one batch.  [tile_lo,
+// tile_hi) is the union of its rows' windows widened to kColAlign columns
+// and clipped to [0, S_k); cells of a row outside it are cleanup work.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPlanMagic = 0x50584449u;  // "IDXP"
+constexpr int kTileRows = 8;                   // query rows per tile
+constexpr int kColAlign = 32;                  // coverage granularity in columns
+
+struct PlanHeader {
+  uint32_t magic;
+  int32_t B, S_q, S_k, H, D;
+  int32_t n_tiles, tile_rows;
+  int32_t reserved[56];
+};
+static_assert(sizeof(PlanHeader) == 256, "plan header is one 256-byte section");
+
+struct PlanLayout {
+  size_t off_start, off_end, off_slot, off_lo, off_hi, total;
+  int64_t n_rows, n_tiles;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+__host__ __device__ inline int64_t tiles_per_batch(int64_t S_q) { return (S_q + kTileRows - 1) / kTileRows; }
+
+// Layout of a plan; total == 0 when the sizes overflow.
+inline PlanLayout plan_layout(int64_t B, int64_t S_q) {
+  PlanLayout L{};
+  L.n_rows = B * S_q;
+  L.n_tiles = B * tiles_per_batch(S_q);
+  if (B <= 0 || S_q <= 0 || L.n_rows > (int64_t(1) << 31) - 1 || L.n_tiles * kTileRows > (int64_t(1) << 31) - 1)
+    return L;
+  size_t off = align256(sizeof(PlanHeader));
+  L.off_start = off;
+  off += align256(size_t(L.n_rows) * 4);
+  L.off_end = off;
+  off += align256(size_t(L.n_rows) * 4);
+  L.off_slot = off;
+  off += align256(size_t(L.n_tiles) * kTileRows * 4);
+  L.off_lo = off;
+  off += align256(size_t(L.n_tiles) * 4);
+  L.off_hi = off;
+  off += align256(size_t(L.n_tiles) * 4);
+  L.total = off;
+  return L;
+}
+
+// Everything a scoring kernel needs, passed by value.
+struct ScoreArgs {
+  const void* q;
+  const void* q_scale;
+  const void* k;
+  const void* k_scale;
+  const void* w;
+  void* out;
+  const unsigned char* plan;
+  int64_t ld;  // output row stride in elements
+  float sm_scale;
+  int32_t B, S_q, S_k;
+  int32_t n_tiles, tiles_per_batch;
+  int32_t chunk_cols;    // columns per compute unit (multiple of 64)
+  int32_t n_chunks;      // compute units per tile (upper bound)
+  int32_t n_compute;     // n_tiles * n_chunks
+  uint32_t off_start, off_end, off_slot, off_lo, off_hi;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
+                       const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream);
+hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
+hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
+                             hipStream_t stream);
+hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
+                            hipStream_t stream);
+hipError_t launch_score_mxfp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
+                              hipStream_t stream);
+hipError_t launch_score_mxfp4(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
+                              hipStream_t stream);
+
+}  // namespace idx

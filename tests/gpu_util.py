@@ -1,0 +1,119 @@
+"""Helpers for the GPU tests: move a workload to the device, run the library
+through its binding (which calls the C ABI), and compare with the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mqa_logits_scoring_amd as lib
+import oracle
+
+DEV = "cuda"
+
+
+def dev_inputs(wl, device=DEV) -> dict:
+    """Raw code buffers of a workload as device tensors."""
+    d = {}
+    d["q"] = torch.from_numpy(np.ascontiguousarray(wl.q).view(np.int16 if wl.q.dtype == np.uint16 else np.uint8)).to(device)
+    d["k"] = torch.from_numpy(np.ascontiguousarray(wl.k).view(np.int16 if wl.k.dtype == np.uint16 else np.uint8)).to(device)
+    d["q_scale"] = None if wl.q_scale is None else torch.from_numpy(wl.q_scale.view(np.int32)).to(device)
+    if wl.k_scale is None:
+        d["k_scale"] = None
+    elif wl.k_scale.dtype == np.float32:
+        d["k_scale"] = torch.from_numpy(wl.k_scale).to(device)
+    else:
+        d["k_scale"] = torch.from_numpy(wl.k_scale.view(np.int32)).to(device)
+    if wl.w_dtype == "bf16":
+        d["w"] = torch.from_numpy(wl.w.view(np.int16)).view(torch.bfloat16).to(device)
+    else:
+        d["w"] = torch.from_numpy(wl.w).to(device)
+    d["offsets"] = None if wl.offsets is None else torch.from_numpy(np.asarray(wl.offsets, np.int32)).to(device)
+    d["starts"] = None if wl.starts is None else torch.from_numpy(np.asarray(wl.starts, np.int32)).to(device)
+    d["ends"] = None if wl.ends is None else torch.from_numpy(np.asarray(wl.ends, np.int32)).to(device)
+    return d
+
+
+def out_dtype(wl):
+    return torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+
+
+def make_plan(wl, d):
+    return lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
+                               row_starts=d["starts"], row_ends=d["ends"], device=d["q"].device)
+
+
+def run(wl, d, plan=None, out=None, clean=None):
+    """One library call; plan None builds the plan inside the call."""
+    return lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                              sm_scale=wl.sm_scale, clean_logits=wl.clean if clean is None else clean, out=out,
+                              out_dtype=out_dtype(wl), plan=plan, q_causal_offsets=d["offsets"],
+                              row_starts=d["starts"], row_ends=d["ends"])
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 7), 0.0)
+
+
+def compare_rows(wl, got: np.ndarray, ref: np.ndarray, bound: np.ndarray, clean: bool = True, what: str = ""):
+    """got/ref/bound: [n_rows, S_k].  -inf placement bit-exact, values within
+    1e-4 * bound (+ one bf16 ulp of the reference for bf16 output).  Returns
+    (max err / bound, rel-L2)."""
+    inside = ~np.isneginf(ref)
+    assert not np.any(np.isnan(got[inside])), f"{what}: NaN inside windows"
+    if clean:
+        bad = np.isneginf(got) != ~inside
+        assert not np.any(bad), f"{what}: -inf placement differs at {np.argwhere(bad)[:5].tolist()}"
+    tol = 1e-4 * bound[inside]
+    if wl.out_dtype == "bf16":
+        tol = tol + bf16_ulp(ref[inside])
+    err = np.abs(got[inside] - ref[inside])
+    worst = np.argmax(err - tol) if err.size else 0
+    assert np.all(err <= tol), (f"{what}: |err| {err[worst]:.3e} > tol {tol[worst]:.3e} "
+                                f"(ref {ref[inside][worst]:.6e} got {got[inside][worst]:.6e})")
+    ratio = float(np.max(err / np.maximum(bound[inside], 1e-300))) if err.size else 0.0
+    den = float(np.sqrt(np.sum(ref[inside] ** 2)))
+    rel_l2 = float(np.sqrt(np.sum(err ** 2)) / den) if den > 0 else 0.0
+    return ratio, rel_l2
+
+
+def mask_check_all_rows(wl, out: torch.Tensor, plan_ws=None):
+    """-inf placement over every row, on the device: cell is -inf <=> outside the oracle's window."""
+    ws, we = oracle.windows(wl)
+    ws_t = torch.from_numpy(ws.reshape(-1)).to(out.device)
+    we_t = torch.from_numpy(we.reshape(-1)).to(out.device)
+    o = out.reshape(wl.B * wl.S_q, -1)[:, : wl.S_k]
+    cols = torch.arange(wl.S_k, device=out.device)
+    step = max(1, (1 << 26) // wl.S_k)
+    for r0 in range(0, wl.B * wl.S_q, step):
+        r1 = min(r0 + step, wl.B * wl.S_q)
+        inside = (cols[None, :] >= ws_t[r0:r1, None]) & (cols[None, :] < we_t[r0:r1, None])
+        ninf = torch.isneginf(o[r0:r1])
+        bad = ninf == inside
+        if bool(bad.any()):
+            idx = torch.nonzero(bad)[:5].cpu().tolist()
+            raise AssertionError(f"-inf placement wrong at rows/cols {[(r0 + a, b) for a, b in idx]}")
+        assert not bool(torch.isnan(o[r0:r1]).any()), "NaN in output"
+
+
+def sample_rows(wl, n_random: int = 12, seed: int = 0) -> np.ndarray:
+    """Rows for value checks: ends and tile edges of every batch, empty rows, a few random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(wl.B):
+        base = b * wl.S_q
+        for i in (0, 1, 7, 8, 9, wl.S_q // 2, wl.S_q - 9, wl.S_q - 8, wl.S_q - 2, wl.S_q - 1):
+            if 0 <= i < wl.S_q:
+                rows.add(base + i)
+    ws, we = oracle.windows(wl)
+    empt = np.argwhere((we <= ws).reshape(-1)).ravel()
+    rows.update(int(x) for x in empt[:8])
+    rows.update(int(x) for x in rng.integers(0, wl.B * wl.S_q, size=n_random))
+    return np.array(sorted(rows), np.int64)

@@ -1,0 +1,95 @@
+"""The C ABI on the CPU: the library loads, exports every entry point its
+header declares, and rejects bad arguments on the host before launching
+anything (only cases that fail validation are called here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mqa_logits_scoring_amd as lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "idx_logits.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(lib.EXPORTED), names
+    L = lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert lib.idx_abi_version() == 1
+
+
+def test_plan_bytes():
+    assert lib.idx_logits_plan_bytes(1, 128, 512) > 0
+    assert lib.idx_logits_plan_bytes(0, 128, 512) == 0
+    assert lib.idx_logits_plan_bytes(1, -1, 512) == 0
+    a = lib.idx_logits_plan_bytes(1, 2048, 32768)
+    b = lib.idx_logits_plan_bytes(1, 2048, 64)
+    assert a == b  # the plan does not grow with S_k
+
+
+FAKE = 1 << 20  # never dereferenced: every call below fails validation first
+
+
+def _args(**kw):
+    a = lib.IdxLogitsArgs()
+    a.B, a.S_q, a.S_k, a.H, a.D = 1, 16, 64, 64, 128
+    a.in_dtype = 2
+    a.q = a.k = a.w = a.out = a.q_scale = a.k_scale = FAKE
+    a.w_dtype = a.out_dtype = 0
+    a.sm_scale = 1.0
+    a.out_row_stride = 64
+    a.clean_logits = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _run(a, plan=None, ws=None, ws_bytes=0):
+    return lib.lib().idx_logits_run(ctypes.byref(a), plan, None, None, None, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=32), lib.IDX_E_UNSUPPORTED),
+    (dict(D=64), lib.IDX_E_UNSUPPORTED),
+    (dict(B=0), lib.IDX_E_INVALID),
+    (dict(S_k=-3), lib.IDX_E_INVALID),
+    (dict(in_dtype=9), lib.IDX_E_INVALID),
+    (dict(w_dtype=5), lib.IDX_E_INVALID),
+    (dict(q=None), lib.IDX_E_INVALID),
+    (dict(q_scale=None), lib.IDX_E_INVALID),
+    (dict(k_scale=None), lib.IDX_E_INVALID),
+    (dict(out=FAKE + 4), lib.IDX_E_INVALID),
+    (dict(out_row_stride=63), lib.IDX_E_INVALID),
+    (dict(sm_scale=float("inf")), lib.IDX_E_INVALID),
+    (dict(sm_scale=float("nan")), lib.IDX_E_INVALID),
+])
+def test_run_rejects(kw, status):
+    assert _run(_args(**kw)) == status
+    assert lib.idx_last_error() != ""
+
+
+def test_run_needs_plan_or_workspace():
+    assert _run(_args()) == lib.IDX_E_WORKSPACE
+    assert _run(_args(), ws=FAKE, ws_bytes=16) == lib.IDX_E_WORKSPACE
+    assert "workspace" in lib.idx_last_error()
+    assert _run(_args(), ws=FAKE + 16, ws_bytes=1 << 20) == lib.IDX_E_INVALID  # misaligned
+    assert _run(_args(), plan=FAKE + 8) == lib.IDX_E_INVALID
+
+
+def test_plan_rejects():
+    L = lib.lib()
+    assert L.idx_logits_plan(1, 16, 64, 32, 128, None, None, None, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan(1, 16, 64, 64, 128, None, FAKE, None, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, FAKE, 8, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID

@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, and
+the exact relations the method fixes between GPU runs."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mqa_logits_scoring_amd as lib
+import oracle
+import workloads as W
+from gpu_util import (compare_rows, dev_inputs, make_plan, mask_check_all_rows, run, sample_rows, to_f64)
+import oracle_pins as P
+
+pytestmark = pytest.mark.gpu
+
+
+def _full_compare(wl, out, clean=True, what=""):
+    ref, bound = oracle.logits(wl)
+    got = to_f64(out).reshape(wl.B * wl.S_q, -1)[:, : wl.S_k]
+    return compare_rows(wl, got, ref, bound, clean=clean, what=what or wl.name)
+
+
+# ---------------------------------------------------------------------------
+# plan: windows bit-exact against the oracle's window rules
+# ---------------------------------------------------------------------------
+
+WINDOW_CASES = [
+    dict(B=1, S_q=128, S_k=512, offsets=[0]),
+    dict(B=4, S_q=37, S_k=100, offsets=[0, -1, 5, -200]),
+    dict(B=3, S_q=9, S_k=50, offsets=[2 ** 31 - 1, -2 ** 31, -49]),
+    dict(B=2, S_q=21, S_k=300, windows="irregular"),
+    dict(B=1, S_q=6, S_k=50, windows="explicit", starts=[[-5, 10, 60, 30, 7, 0]], ends=[[20, 70, 80, 10, 7, 50]]),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[str(i) for i in range(len(WINDOW_CASES))])
+def test_plan_windows_match_oracle(case):
+    case = dict(case)
+    wl = W.make_random("bf16", case.pop("B"), case.pop("S_q"), case.pop("S_k"), H=64, D=128, seed=3, **case)
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    ws, we = lib.idx_logits_plan_windows(plan, wl.B, wl.S_q, wl.S_k)
+    ows, owe = oracle.windows(wl)
+    assert np.array_equal(ws.cpu().numpy(), ows) and np.array_equal(we.cpu().numpy(), owe)
+
+
+# ---------------------------------------------------------------------------
+# small shapes, every format x weight type x output type x clean flag
+# (3 tiles with a ragged tail, ragged key tails, irregular windows)
+# ---------------------------------------------------------------------------
+
+MATRIX = [(f, wd, od, cl) for f in W.FORMATS for wd in ("f32", "bf16") for od in ("f32", "bf16") for cl in (True, False)]
+
+
+@pytest.mark.parametrize("fmt,w_dtype,o_dtype,clean", MATRIX, ids=["-".join(map(str, m)) for m in MATRIX])
+def test_small_matrix(fmt, w_dtype, o_dtype, clean):
+    wl = W.make_random(fmt, 2, 21, 300, w_dtype=w_dtype, out_dtype=o_dtype, sm_scale=0.3, clean=clean, seed=17,
+                       windows="irregular")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    torch.cuda.synchronize()
+    _full_compare(wl, out, clean=clean)
+
+
+@pytest.mark.parametrize("S_k", [1, 31, 32, 33, 63, 64, 65, 127, 129, 999, 4100])
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_ragged_key_tails(fmt, S_k):
+    """Windows reaching the last key column for S_k around the 32/64-column block edges."""
+    wl = W.make_random(fmt, 1, 13, S_k, sm_scale=0.5, seed=S_k, offsets=[0])
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    torch.cuda.synchronize()
+    _full_compare(wl, out)
+
+
+def test_c1_full():
+    wl = W.make("c1")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    torch.cuda.synchronize()
+    ratio, rel = _full_compare(wl, out)
+    print(f"c1: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+
+
+def test_c5_nonaligned_full():
+    wl = W.make("c5_nonaligned")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    torch.cuda.synchronize()
+    ratio, rel = _full_compare(wl, out)
+    print(f"c5 non-aligned: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+
+
+# ---------------------------------------------------------------------------
+# exact cases: small-integer codes and power-of-two weights make every
+# intermediate exact in fp32, so the GPU must equal the oracle bitwise
+# ---------------------------------------------------------------------------
+
+class _Capture:
+    """Stand-in oracle that records the workloads a pin builds and returns its real answers."""
+
+    def __init__(self):
+        self.real = oracle.default()
+        self.seen = []
+
+    def logits(self, wl, **kw):
+        self.seen.append(wl)
+        return self.real.logits(wl, **kw)
+
+    def windows(self, wl):
+        return self.real.windows(wl)
+
+    def decode(self, f, c):
+        return self.real.decode(f, c)
+
+
+@pytest.mark.parametrize("pin", [P.pin_one_hot, P.pin_rank_one, P.pin_zero_workload], ids=lambda p: p.__name__)
+def test_exact_cases_bitwise(pin):
+    cap = _Capture()
+    pin(cap)
+    assert cap.seen
+    for wl in cap.seen:
+        ref, _ = oracle.logits(wl)
+        d = dev_inputs(wl)
+        out = run(wl, d)
+        got = to_f64(out).reshape(wl.B * wl.S_q, -1)
+        exact = ref.astype(np.float32).astype(np.float64) if wl.out_dtype == "f32" else None
+        assert exact is not None
+        same = (got == exact) | (np.isneginf(got) & np.isneginf(exact))
+        assert np.all(same), f"{pin.__name__} {wl.fmt}: {np.argwhere(~same)[:5].tolist()} " \
+                             f"got {got[~same][:5]} want {exact[~same][:5]}"
+
+
+# ---------------------------------------------------------------------------
+# exact relations between GPU runs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_determinism_and_plan_equivalence(fmt):
+    wl = W.make_random(fmt, 2, 40, 700, seed=5, windows="irregular", w_dtype="bf16")
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    first = run(wl, d, plan=plan)
+    for i in range(20):
+        o = run(wl, d, plan=plan if i % 2 else None)
+        assert torch.equal(o.view(torch.int32), first.view(torch.int32)), f"run {i} differs"
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_batch_invariance(fmt):
+    wl = W.make_random(fmt, 3, 19, 260, seed=8, offsets=[0, -5, 3])
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    for b in range(3):
+        sl = lambda a: None if a is None else a[b:b + 1]
+        one = wl.replace(B=1, q=sl(wl.q), q_scale=sl(wl.q_scale), k=sl(wl.k), k_scale=sl(wl.k_scale), w=sl(wl.w),
+                         offsets=wl.offsets[b:b + 1])
+        o1 = run(one, dev_inputs(one))
+        assert torch.equal(o1[0].view(torch.int32), out[b].view(torch.int32)), b
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_w_bf16_equals_f32_holding_bf16(fmt):
+    wl = W.make_random(fmt, 1, 16, 200, seed=9, w_dtype="bf16", offsets=[0])
+    d = dev_inputs(wl)
+    a = run(wl, d)
+    d2 = dict(d, w=d["w"].float())
+    b = run(wl.replace(w_dtype="f32"), d2)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_clean_and_unclean_agree_inside(fmt):
+    wl = W.make_random(fmt, 1, 24, 500, seed=10, windows="irregular")
+    d = dev_inputs(wl)
+    a = run(wl, d, clean=True)
+    sentinel = torch.full_like(a, 12345.0)
+    b = run(wl, d, clean=False, out=sentinel)
+    inside = ~torch.isneginf(a)
+    assert torch.equal(a[inside], b[inside])
+    assert bool((b[~inside] == 12345.0).all()), "clean_logits=0 touched cells outside the windows"
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_weight_and_scale_doubling(fmt):
+    wl = W.make_random(fmt, 1, 16, 300, seed=12, offsets=[0])
+    d = dev_inputs(wl)
+    base = run(wl, d)
+    x4 = run(wl, dict(d, w=d["w"] * 4))
+    fin = ~torch.isneginf(base)
+    assert torch.equal(x4[fin], base[fin] * 4)
+    if fmt in ("mxfp8", "mxfp4"):
+        k2 = run(wl, dict(d, k_scale=d["k_scale"] + 0x01010101))
+        assert torch.equal(k2[fin], base[fin] * 2)
+
+
+def test_row_stride_guard_band():
+    wl = W.make_random("mxfp8", 2, 11, 77, seed=13, offsets=[0, 4])
+    d = dev_inputs(wl)
+    buf = torch.full((wl.B, wl.S_q, 96), 777.0, device="cuda")
+    run(wl, d, out=buf)
+    assert bool((buf[..., 77:] == 777.0).all())
+    ref = run(wl, d)
+    assert torch.equal(buf[..., :77], ref)
+
+
+def test_plan_dimension_mismatch_is_loud():
+    wl = W.make_random("fp8", 1, 16, 128, seed=14, offsets=[0])
+    d = dev_inputs(wl)
+    other = W.make_random("fp8", 1, 16, 256, seed=14, offsets=[0])
+    plan = make_plan(other, dev_inputs(other))
+    out = run(wl, d, plan=plan)
+    assert bool(torch.isnan(out).all())
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size: sampled rows against the oracle, the
+# -inf placement of every row, and plan / no-plan equality
+# ---------------------------------------------------------------------------
+
+NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5"]
+
+
+@pytest.mark.parametrize("name", NAMED)
+def test_named_full_size(name):
+    wl = W.make(name)
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    out = run(wl, d, plan=plan)
+    out2 = run(wl, d)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
+                       out2.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
+    if wl.clean:
+        mask_check_all_rows(wl, out)
+    rows = sample_rows(wl)
+    ref, bound = oracle.logits(wl, rows=rows)
+    got = to_f64(out.reshape(wl.B * wl.S_q, -1)[torch.from_numpy(rows).cuda()])
+    ratio, rel = compare_rows(wl, got, ref, bound, clean=wl.clean, what=name)
+    print(f"{name}: {len(rows)} rows, max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+
+
+def test_mx_block_layout_probes():
+    """The oracle's MX layout probes (one d-block populated, one scale byte raised,
+    nibble order) run on the GPU: within tolerance of the oracle for every variant."""
+    cap = _Capture()
+    P.pin_mx_block_layout(cap)
+    for wl in cap.seen:
+        out = run(wl, dev_inputs(wl))
+        torch.cuda.synchronize()
+        _full_compare(wl, out, what=f"layout probe {wl.fmt}")

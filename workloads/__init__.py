@@ -99,18 +99,18 @@ def e4m3_codes(x: torch.Tensor) -> np.ndarray:
 _E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 
 
+# midpoints between consecutive magnitudes
+_E2M1_MID = (_E2M1_MAG[1:] + _E2M1_MAG[:-1]) / 2
+
+
 def e2m1_codes(x: np.ndarray) -> np.ndarray:
     """float array -> 4-bit e2m1 codes (uint8 0..15), RNE with saturation at 6."""
-    x = np.asarray(x, dtype=np.float64)
+    x = np.asarray(x)
     mag = np.minimum(np.abs(x), 6.0)
-    # distance to every code magnitude; ties go to the even code index
-    d = np.abs(mag[..., None] - _E2M1_MAG)
-    best = np.argmin(d, axis=-1)
-    dmin = np.take_along_axis(d, best[..., None], axis=-1)[..., 0]
-    nxt = np.minimum(best + 1, 7)
-    dnext = np.abs(mag - _E2M1_MAG[nxt])
-    tie_up = (dnext == dmin) & (nxt != best) & (best % 2 == 1)
-    code = np.where(tie_up, nxt, best).astype(np.uint8)
+    code = np.searchsorted(_E2M1_MID, mag, side="left")  # number of midpoints strictly below mag
+    # a magnitude exactly on a midpoint goes to the even code of the two
+    on_mid = (code < 7) & (mag == _E2M1_MID[np.minimum(code, 6)])
+    code = np.where(on_mid & (code % 2 == 1), code + 1, code).astype(np.uint8)
     sign = np.signbit(x).astype(np.uint8) << 3
     return code | sign
 
