@@ -135,8 +135,13 @@ idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
                              const int32_t* row_ends, void* plan, size_t plan_bytes, void* stream);
 
 /*
- * Device workspace a call to idx_logits_run with plan == NULL needs (the plan
- * is then built inside the call); 0 for invalid arguments.
+ * Device workspace bytes a call to idx_logits_run needs; 0 for invalid
+ * arguments.  It covers the plan when the call builds it (plan == NULL) and,
+ * for FP8, MXFP8 and MXFP4 inputs, the per-call weighted-query pieces: those
+ * formats use ReLU(x) = (x + |x|) / 2, so sum_h w_h ReLU(S_h) is half of
+ * sum_h w_h |S_h| (one FMA per head in the epilogue) plus qt . k with
+ * qt = sum_h w_h q_h, taken by one extra MFMA block from qt written exactly
+ * as six e4m3 pieces with E8M0 block scales.
  */
 size_t idx_logits_workspace_bytes(const idx_logits_args_t* a);
 
@@ -144,11 +149,13 @@ size_t idx_logits_workspace_bytes(const idx_logits_args_t* a);
  * Score one batch of queries on `stream`.
  *
  * plan != NULL: a plan built by idx_logits_plan for the same (B, S_q, S_k,
- *   H, D); the window arguments are then ignored and workspace may be NULL.
+ *   H, D); the window arguments are then ignored.  BF16 calls need no
+ *   workspace; FP8 and MX calls still need idx_logits_workspace_bytes(a).
  *   A plan whose recorded dimensions differ from `a` is detected on the
  *   device: the call then writes quiet NaN to columns [0, S_k) of every row.
  * plan == NULL: the plan is first built into `workspace` (at least
- *   idx_logits_workspace_bytes(a) bytes, 256-byte aligned) from
+ *   idx_logits_workspace_bytes(a) bytes, 256-byte aligned, owned by the
+ *   caller and not read after the stream passes the call) from
  *   q_causal_offsets / row_starts / row_ends exactly as idx_logits_plan
  *   would, then used; the result is bitwise identical to the planned call.
  */

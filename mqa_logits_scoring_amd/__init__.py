@@ -189,15 +189,15 @@ def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtyp
     args = make_args(q, k, w, out, in_dtype=in_dtype, q_scale=q_scale, k_scale=k_scale, sm_scale=sm_scale,
                      clean_logits=clean_logits)
     offs = st = en = None
-    ws_bytes = 0
     if plan is None:
         offs = _dev_i32(q_causal_offsets, device)
         st = _dev_i32(row_starts, device)
         en = _dev_i32(row_ends, device)
-        ws_bytes = idx_logits_workspace_bytes(args)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    # the workspace holds the in-call plan and, for FP8 / MX inputs, the
+    # weighted-query pieces; idx_logits_workspace_bytes gives its size
+    if workspace is None:
+        workspace = torch.empty(max(idx_logits_workspace_bytes(args), 1), dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check("idx_logits_run", lib().idx_logits_run(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en),
                                                     _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out

@@ -41,15 +41,30 @@ int row_bytes(idx_in_t f) {
   return 0;
 }
 
-// Key columns per compute unit: enough units to spread a few per CU slot over
-// 256 CUs, few enough that each unit amortises loading its rows' Q.
-int32_t pick_chunk_cols(int64_t S_k, int64_t n_tiles) {
-  const int64_t cols = (S_k + 63) / 64 * 64;
-  int64_t ch = (cols * n_tiles + 4095) / 4096;
-  ch = (ch + 63) / 64 * 64;
-  if (ch < 256) ch = 256;
-  if (ch > 8192) ch = 8192;
-  return int32_t(ch);
+// Work split of a tile's key columns into chunks (one compute unit each).
+// Long key ranges are cut into a multiple of 8 chunks so that each of the 8
+// XCDs owns a fixed slice of K (kept in its L2); chunks hold 2048 key columns
+// or so, enough work per unit to amortise loading its rows' Q.  Short key
+// ranges use 256-column chunks without XCD ownership (K fits in every L2).
+struct Split {
+  int32_t chunk_cols, n_chunks, xcd;
+};
+Split pick_split(int64_t S_k) {
+  const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
+  Split sp{};
+  if (span >= 8 * 1024) {
+    int64_t cpx = (span + 8 * 2048 - 1) / (8 * 2048);  // chunks per XCD
+    int64_t ch = (span + 8 * cpx - 1) / (8 * cpx);
+    ch = (ch + 63) / 64 * 64;
+    sp.chunk_cols = int32_t(ch);
+    sp.n_chunks = int32_t(8 * cpx);
+    sp.xcd = 1;
+  } else {
+    sp.chunk_cols = 256;
+    sp.n_chunks = int32_t((span + 255) / 256);
+    sp.xcd = 0;
+  }
+  return sp;
 }
 
 }  // namespace
@@ -85,7 +100,9 @@ idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
 
 size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) {
   if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return 0;
-  return idx::plan_layout(a->B, a->S_q).total;
+  const idx_in_t f = a->in_dtype;
+  if (f != IDX_IN_BF16 && f != IDX_IN_FP8_E4M3 && f != IDX_IN_MXFP8_E4M3 && f != IDX_IN_MXFP4_E2M1) return 0;
+  return idx::workspace_layout(f, a->B, a->S_q, a->S_k).total;
 }
 
 idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
@@ -131,20 +148,32 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(f, a->B, a->S_q, a->S_k);
   const unsigned char* p = static_cast<const unsigned char*>(plan);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
+    return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
+  if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  if (WL.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
+  if (ws == nullptr)
+    return fail(IDX_E_WORKSPACE, "this call needs a workspace of %zu bytes (idx_logits_workspace_bytes)", WL.total);
+  if (!aligned256(ws)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < WL.total)
+    return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, WL.total);
   if (p == nullptr) {
-    if ((row_starts == nullptr) != (row_ends == nullptr))
-      return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
-    if (workspace == nullptr) return fail(IDX_E_WORKSPACE, "no plan and no workspace");
-    if (!aligned256(workspace)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
-    if (workspace_bytes < L.total)
-      return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
     hipError_t e = idx::launch_plan(a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends,
-                                    workspace, s);
+                                    ws + WL.off_plan, s);
     if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
-    p = static_cast<const unsigned char*>(workspace);
-  } else if (!aligned256(p)) {
-    return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+    p = ws + WL.off_plan;
+  }
+  {
+    hipError_t e = idx::launch_kfrag(f, a->k, a->B, a->S_k, ws + WL.off_kfrag, s);
+    if (e != hipSuccess) return fail(IDX_E_HIP, "K reorder launch failed: %s", hipGetErrorString(e));
+  }
+  if (idx::uses_pieces(f)) {
+    hipError_t e = idx::launch_pieces(f, a->w_dtype, a->q, a->q_scale, a->w, rows, ws + WL.off_pieces,
+                                      reinterpret_cast<uint32_t*>(ws + WL.off_pscales), s);
+    if (e != hipSuccess) return fail(IDX_E_HIP, "weighted-query launch failed: %s", hipGetErrorString(e));
   }
 
   idx::ScoreArgs k{};
@@ -162,8 +191,10 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   k.S_k = a->S_k;
   k.n_tiles = int32_t(L.n_tiles);
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q));
-  k.chunk_cols = pick_chunk_cols(a->S_k, L.n_tiles);
-  k.n_chunks = int32_t((int64_t(a->S_k) + idx::kColAlign - 1 + k.chunk_cols - 1) / k.chunk_cols);
+  const Split sp = pick_split(a->S_k);
+  k.chunk_cols = sp.chunk_cols;
+  k.n_chunks = sp.n_chunks;
+  k.xcd_chunks = sp.xcd;
   const int64_t n_compute = int64_t(k.n_chunks) * L.n_tiles;
   if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
   k.n_compute = int32_t(n_compute);
@@ -173,6 +204,9 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   k.off_lo = uint32_t(L.off_lo);
   k.off_hi = uint32_t(L.off_hi);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
+  k.pieces = idx::uses_pieces(f) ? ws + WL.off_pieces : nullptr;
+  k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
+  k.kfrag = ws + WL.off_kfrag;
 
   const bool clean = a->clean_logits != 0;
   hipError_t e = hipSuccess;

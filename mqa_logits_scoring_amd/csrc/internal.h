@@ -68,6 +68,63 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q) {
   return L;
 }
 
+// ---------------------------------------------------------------------------
+// Weighted-query pieces (FP8, MXFP8 and MXFP4 inputs)
+//
+// Those formats score with ReLU(x) = (x + |x|) / 2:
+//   sum_h w_h ReLU(S_h) = ( sum_h w_h |S_h| + qt . k ) / 2,  qt = sum_h w_h q_h,
+// so the epilogue needs one FMA (with |.| as a free source modifier) per head
+// instead of a max and an FMA, and the linear term qt . k comes from one more
+// MFMA block.  qt (fp32) is written as kPieces e4m3 rows with one E8M0 scale
+// per 32 elements, each piece encoding the exact fp32 residual of the ones
+// before it, so the pieces sum to qt within 2^-(4 kPieces) of its block maxima.
+//
+// Workspace layout (256-byte aligned sections):
+//   [plan, when the call builds it]  [pieces: n_rows x kPieces x 128 B]
+//   [piece scales: n_rows x kPieces x uint32]
+// ---------------------------------------------------------------------------
+constexpr int kPieces = 6;
+
+inline bool uses_pieces(idx_in_t f) { return f != IDX_IN_BF16; }
+
+// ---------------------------------------------------------------------------
+// K in fragment order
+//
+// The scoring kernel feeds K to the MFMAs as B operands, 32 key rows at a
+// time; lane (c, g) needs 16-byte chunks of row c at format-specific offsets.
+// Read straight from [S_k, D] rows, every such load touches 32 cache lines.
+// Each call therefore first copies K into fragment order: block u (rows
+// 32u..32u+31) is ROWB*32 contiguous bytes, chunk v of lane l = c + 32g at
+// u*32*ROWB + v*1024 + l*16, so each fragment load is 1 KB contiguous.  The
+// last block is zero-padded.
+// ---------------------------------------------------------------------------
+inline int row_bytes_of(idx_in_t f) {
+  return f == IDX_IN_BF16 ? 256 : (f == IDX_IN_MXFP4_E2M1 ? 64 : 128);
+}
+
+struct WorkspaceLayout {
+  size_t off_plan, off_pieces, off_pscales, off_kfrag, total;
+};
+
+inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k) {
+  WorkspaceLayout W{};
+  const PlanLayout L = plan_layout(B, S_q);
+  if (L.total == 0 || S_k <= 0) return W;
+  size_t off = 0;
+  W.off_plan = off;
+  off += L.total;
+  if (uses_pieces(f)) {
+    W.off_pieces = off;
+    off += align256(size_t(L.n_rows) * kPieces * 128);
+    W.off_pscales = off;
+    off += align256(size_t(L.n_rows) * kPieces * 4);
+  }
+  W.off_kfrag = off;
+  off += align256(size_t(B) * size_t((S_k + 31) / 32) * 32 * row_bytes_of(f));
+  W.total = off;
+  return W;
+}
+
 // Everything a scoring kernel needs, passed by value.
 struct ScoreArgs {
   const void* q;
@@ -84,13 +141,20 @@ struct ScoreArgs {
   int32_t chunk_cols;    // columns per compute unit (multiple of 64)
   int32_t n_chunks;      // compute units per tile (upper bound)
   int32_t n_compute;     // n_tiles * n_chunks
+  int32_t xcd_chunks;    // 1: n_chunks % 8 == 0 and chunk c runs on XCD c % 8
   uint32_t off_start, off_end, off_slot, off_lo, off_hi;
+  const unsigned char* pieces;   // [n_rows][kPieces][128] e4m3 codes (formats with pieces)
+  const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
+  const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
 };
 
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream);
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
+hipError_t launch_pieces(idx_in_t fmt, idx_fp_t w_dtype, const void* q, const void* q_scale, const void* w,
+                         int64_t n_rows, unsigned char* pieces, uint32_t* pscales, hipStream_t stream);
+hipError_t launch_kfrag(idx_in_t fmt, const void* k, int64_t B, int64_t S_k, unsigned char* kfrag, hipStream_t stream);
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);
 hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,

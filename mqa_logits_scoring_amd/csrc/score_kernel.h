@@ -2,7 +2,7 @@
 //
 // Computes, for the rows of one tile and one chunk of key columns,
 //   out[i, j] = sm_scale * sum_h w[i,h] * max(0, q[i,h,:] . k[j,:])
-// (the lightning-indexer score; see include/idx_logits.h for where the pages
+// (the lightning-indexer score; include/idx_logits.h says where the pages
 // define it) and writes -inf to the tile's in-coverage cells outside a row's
 // window when cleaning.  Cells outside the tile's coverage are written by
 // cleanup units that run after the compute units in the same grid, so cleanup
@@ -11,21 +11,31 @@
 //
 // Work decomposition
 //   workgroup = 4 waves = one tile of kTileRows query rows x one key chunk
-//   wave      = TW query rows; for each row its Q (64 heads x 128 d) sits in
-//               registers for the whole chunk, as A operands of 32x32 MFMAs
+//   wave      = 2 query rows; each row's Q (64 heads x 128 d) sits in
+//               registers for the whole chunk as A operands of 32x32 MFMAs
 //               (heads on the M dimension)
-//   key chunk = stages of 64 columns, staged through LDS (double buffered) and
-//               shared by the four waves; each stage is two 32-column blocks
-//               that are the B operands (key columns on N)
+//   32-column block u of the chunk = the B operand (key columns on N).  Every
+//               wave loads its own B fragments straight from global memory
+//               one block ahead; the four waves of a workgroup walk the same
+//               columns, so the key rows come from L1/L2 and no LDS staging,
+//               barrier or bank traffic sits on the critical path.
 //   epilogue  = in registers: lane l of the 32x32 accumulator holds column
-//               l%32 and 16 heads per M block; ReLU, weight and sum its 32
-//               heads, then one permlane32 swap joins the two lane halves
-//               (heads differ between halves, the column does not) and leaves
-//               one row's 32 consecutive columns per half-wave, stored
-//               coalesced.  The epilogue of one 32-column block is issued
-//               between the MFMAs of the next, so vector ALU and matrix
-//               pipes overlap (cudnn-frontend pull request 416 keeps its
-//               head-sum register-resident for the same reason, Why section).
+//               l%32 and 16 heads per M block; weight and sum its heads, then
+//               one permlane32 swap joins the two lane halves (heads differ
+//               between halves, the column does not) and leaves one row's 32
+//               consecutive columns per half-wave, stored coalesced.  The
+//               epilogue of one MFMA block is issued between the MFMAs of the
+//               next, so the vector ALU and matrix pipes overlap (cudnn-frontend
+//               pull request 416 keeps its head-sum register-resident for the
+//               same reason, Why section).
+//
+// FP8, MXFP8 and MXFP4 inputs use ReLU(x) = (x + |x|) / 2: the epilogue is one
+// FMA per head with |.| as a free source modifier, and the linear half
+// qt . k (qt = sum_h w_h q_h) comes from one more MFMA block fed by the
+// weighted-query pieces (internal.h).  On gfx950 two waves per SIMD can hide
+// about 12 vector instructions under each 64-cycle e4m3 MFMA; the plain
+// max + FMA epilogue needs about 19, the split form about 8.  BF16 inputs are
+// MFMA-bound with either form and keep max + FMA.
 //
 // Operand layout inside a lane: any permutation of d applied alike to Q and K
 // leaves every dot product unchanged, so each format places d where loads are
@@ -33,8 +43,8 @@
 // (c = l%32, g = l/32) holds LB bytes of its Q row (head c) and K row (column
 // c) as 16-byte chunks; Fmt<> gives their offsets, the k-steps that use them,
 // and how the scale word is shifted per lane half so that op_sel picks the
-// right E8M0 byte (the placement of the scaled f8f6f4 MFMA differs between
-// e4m3 and e2m1 operands, see Fmt<>).
+// right E8M0 byte (the scaled f8f6f4 MFMA places e4m3 and e2m1 operands
+// differently, see Fmt<> and Lin<>).
 #pragma once
 
 #include "internal.h"
@@ -87,7 +97,26 @@ struct Fmt<IDX_IN_MXFP4_E2M1> {
   static constexpr int SCALE_SHIFT = 16, OPSEL_STEP = 1;
 };
 
-constexpr int kStageCols = 64;
+// The weighted-query pieces are e4m3 rows (A operand) multiplied with K in
+// its own format (B operand) in the same 32x32x64 MFMA.  Both operands live
+// in one logical k space: an e4m3 lane half g holds k = 16g + [0,16) in bytes
+// 0-15 and k = 32 + 16g + [0,16) in bytes 16-31 (scale block kb from lane half
+// kb); an e2m1 lane half g holds k = 32g + [0,32) (its own scale).  So pieces
+// are loaded with the Q chunk offsets for e4m3 K, and for e2m1 K with chunks
+// at 16g + {0, 64, 32, 96} (k-step s pairs elements 32s+16g.. with
+// 64+32s+16g..), lane half g scaling piece block s+2g (op_sel s on the word
+// shifted right by 16g).
+template <int F>
+struct Lin {
+  static constexpr int OFF[4] = {0, 32, 64, 96};  // + 16 g
+  static constexpr int SCALE_SHIFT = 8, OPSEL_STEP = 2;
+};
+template <>
+struct Lin<IDX_IN_MXFP4_E2M1> {
+  static constexpr int OFF[4] = {0, 64, 32, 96};
+  static constexpr int SCALE_SHIFT = 16, OPSEL_STEP = 1;
+};
+
 constexpr int kThreads = 256;
 
 template <bool OBF>
@@ -97,9 +126,9 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
     uint32_t u = __float_as_uint(v);
     uint32_t r = ((u >> 16) & 1u) + 0x7FFFu;
     uint16_t h = (u & 0x7FFFFFFFu) > 0x7F800000u ? uint16_t((u >> 16) | 0x40u) : uint16_t((u + r) >> 16);
-    static_cast<uint16_t*>(out)[idx] = h;
+    __builtin_nontemporal_store(h, static_cast<uint16_t*>(out) + idx);
   } else {
-    static_cast<float*>(out)[idx] = v;
+    __builtin_nontemporal_store(v, static_cast<float*>(out) + idx);
   }
 }
 
@@ -134,19 +163,30 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
   }
 }
 
-template <int F, bool WBF, bool OBF, bool CLEAN, int TW>
-__global__ void __launch_bounds__(kThreads, 1) score_kernel(const ScoreArgs a) {
+// Waves per SIMD the kernel is built for: the FP8-family and FP4 kernels fit in
+// 256 registers and run two workgroups per CU so one wave's epilogue overlaps
+// the other's MFMAs; the BF16 kernel holds twice the Q bytes and runs one.
+template <int F>
+constexpr int waves_per_eu() {
+  return F == IDX_IN_BF16 ? 1 : 2;
+}
+
+// K fragment buffers per wave (even): the load of a block is issued
+// kfrag_ring - 1 blocks before its MFMAs.
+template <int F>
+constexpr int kfrag_ring() {
+  return F == IDX_IN_MXFP4_E2M1 ? 4 : 2;
+}
+
+template <int F, bool WBF, bool OBF, bool CLEAN>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(waves_per_eu<F>(), waves_per_eu<F>()))) score_kernel(const ScoreArgs a) {
   using T = Fmt<F>;
-  static_assert(TW == 1 || TW == 2, "one or two query rows per wave");
+  constexpr int TW = 2;  // query rows per wave
   static_assert(4 * TW == kTileRows, "four waves cover one tile");
-  constexpr int STRIDE = T::ROWB + 16;  // padded LDS row: conflict-free 16-byte lane reads
   constexpr bool HAS_KS = T::MX || T::ROWSCALE;
-  constexpr int STAGE_BYTES = kStageCols * STRIDE + kStageCols * 4;
-  constexpr int CPR = T::ROWB / 16;                  // 16-byte chunks per K row
-  constexpr int NCH = kStageCols * CPR / kThreads;   // chunks per thread per stage
-  constexpr int QD = T::LB / 4;                      // dwords per lane per row
-  constexpr int KD = T::KB / 4;                      // dwords per lane per k-step
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE_BYTES];
+  constexpr int QD = T::LB / 4;  // dwords per lane per row
+  constexpr int KD = T::KB / 4;  // dwords per lane per k-step
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
@@ -161,15 +201,26 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(const ScoreArgs a) {
   }
   if (!plan_ok) return;
 
-  // longest tiles first for causal windows: the last rows see the most keys
-  const int tile = a.n_tiles - 1 - bid / a.n_chunks;
-  const int chunk = bid % a.n_chunks;
+  // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  When the chunk
+  // count is a multiple of 8, XCD x only ever gets chunks x, x+8, ... so its
+  // slice of K stays in its own L2; consecutive units of one XCD share a tile
+  // so that tile's Q is fetched once per XCD.  Longest tiles go first: under
+  // causal windows the last rows see the most keys.
+  int tile, chunk;
+  if (a.xcd_chunks) {
+    const int x = bid & 7, i = bid >> 3, cpx = a.n_chunks >> 3;
+    tile = a.n_tiles - 1 - i / cpx;
+    chunk = x + 8 * (i % cpx);
+  } else {
+    tile = a.n_tiles - 1 - bid / a.n_chunks;
+    chunk = bid % a.n_chunks;
+  }
   const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
   const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
   const int c0 = lo + chunk * a.chunk_cols;
   if (c0 >= hi) return;
-  const int c1 = min(hi, c0 + a.chunk_cols);
-  const int n_stages = (c1 - c0 + kStageCols - 1) / kStageCols;
+  const int c1 = min(hi, c0 + a.chunk_cols);  // columns [c0, c1) are this unit's
+  const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
 
   // ---- the wave's query rows ----------------------------------------------
@@ -184,7 +235,7 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(const ScoreArgs a) {
     rows[t] = r >= 0 ? r : first_row;
   }
 
-  // Q fragments: qf[t][mb] = lane's LB bytes of head 32*mb + c, from byte g*LB
+  // Q fragments of head 32*mb + c for both rows, and their MX scale words
   uint32_t qf[TW][2][QD];
   uint32_t sa[TW][2];
 #pragma unroll
@@ -236,165 +287,299 @@ __global__ void __launch_bounds__(kThreads, 1) score_kernel(const ScoreArgs a) {
     }
   }
 
-  // the row this lane stores: half-wave g stores row t = g (TW = 2); with one
-  // row per wave only the low half stores
-  const int my_t = (TW == 2) ? g : 0;
-  const bool my_valid = (TW == 2) ? (g ? rvalid[TW - 1] : rvalid[0]) : (rvalid[0] && g == 0);
-  const int my_row = (TW == 2) ? (g ? rows[TW - 1] : rows[0]) : rows[0];
-  (void)my_t;
+  // half-wave g stores row g of the wave; a padding row stores nothing
+  // (its column bound is c0)
+  const bool my_valid = g ? rvalid[1] : rvalid[0];
+  const int my_row = g ? rows[1] : rows[0];
   const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
   const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
-  const int64_t obase = int64_t(my_row) * a.ld;
 
-  const unsigned char* kb = static_cast<const unsigned char*>(a.k) + int64_t(b) * a.S_k * T::ROWB;
+  // K in fragment order (internal.h): block kb0 + u holds columns c0 + 32u..
+  const int nblk = (a.S_k + 31) >> 5;
+  const unsigned char* kfb = a.kfrag + int64_t(b) * nblk * (32 * T::ROWB) + lane * 16;
+  const int kb0 = c0 >> 5;  // c0 is a multiple of 32
   const uint32_t* ksb = HAS_KS ? static_cast<const uint32_t*>(a.k_scale) + int64_t(b) * a.S_k : nullptr;
+  const int last_row = a.S_k - 1;
 
-  // ---- stage staging: global -> registers -> LDS -----------------------------
-  uint4 stg[NCH];
-  uint32_t stg_s = 0;
-  auto gload = [&](int s) {
-    const int jb = c0 + s * kStageCols;
-#pragma unroll
-    for (int v = 0; v < NCH; ++v) {
-      const int qq = tid + kThreads * v;
-      const int j = jb + qq / CPR;
-      stg[v] = j < a.S_k ? reinterpret_cast<const uint4*>(kb + int64_t(j) * T::ROWB)[qq % CPR]
-                         : make_uint4(0, 0, 0, 0);
-    }
-    if constexpr (HAS_KS) {
-      if (tid < kStageCols) {
-        const int j = jb + tid;
-        stg_s = j < a.S_k ? ksb[j] : 0u;
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    unsigned char* base = lds + buf * STAGE_BYTES;
-#pragma unroll
-    for (int v = 0; v < NCH; ++v) {
-      const int qq = tid + kThreads * v;
-      *reinterpret_cast<uint4*>(base + (qq / CPR) * STRIDE + (qq % CPR) * 16) = stg[v];
-    }
-    if constexpr (HAS_KS) {
-      if (tid < kStageCols) *reinterpret_cast<uint32_t*>(base + kStageCols * STRIDE + tid * 4) = stg_s;
-    }
-  };
-
-  // B operand of 32-column block u of a stage, plus the column's scale word
-  auto bread = [&](int buf, int u, uint32_t (&bf)[QD], uint32_t& sb, float& kscl) {
-    const unsigned char* base = lds + buf * STAGE_BYTES;
-    const unsigned char* p = base + (32 * u + c) * STRIDE + g * T::CBASE;
+  // B operand of 32-column block u: 1 KB contiguous per chunk, plus the
+  // column's raw scale word (interpreted where it is used, so that nothing
+  // waits for the load before then).  Blocks and rows past the end of K are
+  // clamped to the last ones: always in bounds, and the columns they feed are
+  // never stored.
+  auto kload = [&](int u, uint32_t (&bf)[QD], uint32_t& kword) {
+    const unsigned char* p = kfb + int64_t(min(kb0 + u, nblk - 1)) * (32 * T::ROWB);
 #pragma unroll
     for (int v = 0; v < QD / 4; ++v) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p + v * T::CSTRIDE);
+      const uint4 x = *reinterpret_cast<const uint4*>(p + v * 1024);
       bf[4 * v + 0] = x.x;
       bf[4 * v + 1] = x.y;
       bf[4 * v + 2] = x.z;
       bf[4 * v + 3] = x.w;
     }
-    if constexpr (HAS_KS) {
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(base + kStageCols * STRIDE + (32 * u + c) * 4);
-      if constexpr (T::MX) sb = g ? (word >> T::SCALE_SHIFT) : word;
-      if constexpr (T::ROWSCALE) kscl = __uint_as_float(word);
-    }
+    if constexpr (HAS_KS) kword = ksb[min(c0 + 32 * u + c, last_row)];
+  };
+  // MX: the lane half's E8M0 bytes of the column's scale word
+  auto kscale_mx = [&](uint32_t kword) {
+    if constexpr (T::MX)
+      return g ? (kword >> T::SCALE_SHIFT) : kword;
+    else
+      return kword;
   };
 
-  auto mma = [&](f32x16 (&acc)[TW][2], const uint32_t (&bf)[QD], uint32_t sb) {
+  // all k-steps of one 32x32 block: acc = Q(row t, heads 32*mb..) x K(32 columns)^T
+  auto mfma_block = [&](f32x16& acc, const uint32_t (&q)[QD], uint32_t sA, const uint32_t (&bf)[QD],
+                        uint32_t sB) {
+    f32x16 d = {};
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        f32x16 d = {};
-#pragma unroll
-        for (int s = 0; s < T::KSTEPS; ++s) {
-          if constexpr (F == IDX_IN_BF16) {
-            bf16x8 av, bv;
-            __builtin_memcpy(&av, &qf[t][mb][s * KD], 16);
-            __builtin_memcpy(&bv, &bf[s * KD], 16);
-            d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, d, 0, 0, 0);
-          } else {
-            i32x8 av = {}, bv = {};
-#pragma unroll
-            for (int e = 0; e < KD; ++e) {
-              av[e] = int(qf[t][mb][s * KD + e]);
-              bv[e] = int(bf[s * KD + e]);
-            }
-            if constexpr (T::MX) {
-              constexpr int OS = T::OPSEL_STEP;
-              if (s == 0)
-                d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, 0, sa[t][mb], 0, sb);
-              else
-                d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, OS, sa[t][mb], OS,
-                                                                    sb);
-            } else {
-              d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, 0, 127, 0, 127);
-            }
-          }
-        }
-        acc[t][mb] = d;
-      }
-    }
-  };
-
-  auto epi = [&](const f32x16 (&acc)[TW][2], int jbase, float kscl) {
-    float p[TW];
-#pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      float s = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s = __builtin_fmaf(wv[t][mb][r], __builtin_fmaxf(acc[t][mb][r], 0.f), s);
-      }
-      p[t] = s;
-    }
-    // lanes c and c+32 hold the same column for different heads: swap the
-    // upper half of row 0's partial with the lower half of row 1's
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[TW - 1]), false, false);
-    const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    float scale = a.sm_scale;
-    if constexpr (T::ROWSCALE) scale = a.sm_scale * kscl;
-    const float v = tot * scale;
-    const int j = jbase + c;
-    if (my_valid && j < c1) {
-      const bool inwin = j >= my_s && j < my_e;
-      if constexpr (CLEAN) {
-        store_out<OBF>(a.out, obase + j, inwin ? v : -__builtin_inff());
+    for (int s = 0; s < T::KSTEPS; ++s) {
+      if constexpr (F == IDX_IN_BF16) {
+        bf16x8 av, bv;
+        __builtin_memcpy(&av, &q[s * KD], 16);
+        __builtin_memcpy(&bv, &bf[s * KD], 16);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, d, 0, 0, 0);
       } else {
-        if (inwin) store_out<OBF>(a.out, obase + j, v);
+        i32x8 av = {}, bv = {};
+#pragma unroll
+        for (int e = 0; e < KD; ++e) {
+          av[e] = int(q[s * KD + e]);
+          bv[e] = int(bf[s * KD + e]);
+        }
+        if constexpr (T::MX) {
+          constexpr int OS = T::OPSEL_STEP;
+          if (s == 0)
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, 0, sA, 0, sB);
+          else
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, OS, sA, OS, sB);
+        } else {
+          d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, T::CODE, T::CODE, 0, 127, 0, 127);
+        }
+      }
+    }
+    acc = d;
+  };
+
+  const int my_c1 = my_valid ? c1 : c0;
+  // One pipeline stage: MFMA, 8 VALU, MFMA, 8 VALU, then a full scheduling
+  // barrier so the next stage's instructions stay after this one's.
+  auto interleave_stage = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto store = [&](float v, int u) {
+    const int j = c0 + 32 * u + c;
+    if (j >= c0 && j < my_c1) {
+      const bool inwin = j >= my_s && j < my_e;
+      const int64_t idx = int64_t(my_row) * a.ld + j;
+      if constexpr (CLEAN) {
+        store_out<OBF>(a.out, idx, inwin ? v : -__builtin_inff());
+      } else {
+        if (inwin) store_out<OBF>(a.out, idx, v);
       }
     }
   };
 
-  // ---- main loop: stage s holds columns [c0 + 64 s, c0 + 64 s + 64) --------
-  f32x16 acc0[TW][2], acc1[TW][2];
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  float kprev = 1.f;
-  for (int s = 0; s < n_stages; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < n_stages) gload(s + 1);
-    uint32_t bf[QD];
-    uint32_t sb = 0;
-    float k0 = 1.f, k1 = 1.f;
-    bread(buf, 0, bf, sb, k0);
-    mma(acc0, bf, sb);
-    if (s > 0) epi(acc1, c0 + kStageCols * (s - 1) + 32, kprev);
-    bread(buf, 1, bf, sb, k1);
-    mma(acc1, bf, sb);
-    epi(acc0, c0 + kStageCols * s, k0);
-    kprev = k1;
-    if (s + 1 < n_stages) swrite(buf ^ 1);
-    __syncthreads();
+  // Blocks u = 2s and 2s+1 form iteration s; the fragments of the next block
+  // are loaded while the current one is computed.  Work is pipelined over
+  // 32x32 MFMA blocks: the MFMAs of one block run while the epilogue of the
+  // previous block executes, with two accumulators alternating.
+  f32x16 accA = {}, accB = {};
+  float p0 = 0.f, p1 = 0.f, kprev = 1.f;
+
+  if constexpr (F != IDX_IN_BF16) {
+    // Blocks per 32-column block u: L (linear term of both rows from the
+    // weighted-query pieces), then (row 0 | row 1) x (heads 0-31 | 32-63).
+    // Pieces of row t sit on A rows {0-3, 8, 9} + 4t, which the 32x32 output
+    // puts in lane half t, registers 0-5: after the head-sum swap, lane half t
+    // holds row t's columns, so the linear term adds in place.
+    using LN = Lin<F>;
+    uint32_t lf[16];
+    uint32_t sl;
+    {
+      const int tt = (c >> 2) & 1, pc = (c & 3) + 4 * (c >> 3);
+      const bool has = c < 16 && pc < kPieces;
+      const int64_t prow = int64_t(rows[tt]) * kPieces + (has ? pc : 0);
+      const unsigned char* src = a.pieces + prow * 128 + 16 * g;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint4 x = has ? *reinterpret_cast<const uint4*>(src + LN::OFF[v]) : make_uint4(0, 0, 0, 0);
+        lf[4 * v + 0] = x.x;
+        lf[4 * v + 1] = x.y;
+        lf[4 * v + 2] = x.z;
+        lf[4 * v + 3] = x.w;
+      }
+      const uint32_t word = has ? a.pscales[prow] : 0x7F7F7F7Fu;
+      sl = g ? (word >> LN::SCALE_SHIFT) : word;
+    }
+    const float half_scale = 0.5f * a.sm_scale;
+
+    auto mfma_lin = [&](f32x16& acc, const uint32_t (&bf)[QD], uint32_t sb) {
+      f32x16 d = {};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        i32x8 av, bv = {};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) av[e] = int(lf[8 * s + e]);
+#pragma unroll
+        for (int e = 0; e < KD; ++e) bv[e] = int(bf[s * KD + e]);
+        constexpr int OA = LN::OPSEL_STEP;
+        if constexpr (T::MX) {
+          constexpr int OB = T::OPSEL_STEP;
+          if (s == 0)
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, 0, sl, 0, sb);
+          else
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, OA, sl, OB, sb);
+        } else {
+          if (s == 0)
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, 0, sl, 0, 127);
+          else
+            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, OA, sl, 0, 127);
+        }
+      }
+      acc = d;
+    };
+    auto epi_lin = [&](const f32x16& acc) {
+      float v = acc[0];
+#pragma unroll
+      for (int r = 1; r < kPieces; ++r) v += acc[r];
+      return v;
+    };
+    // weight and sum |S| of the lane's 16 heads of one block (fixed order)
+    auto epi_abs = [&](const f32x16& acc, const float (&w)[16], float p) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[r], __builtin_fabsf(acc[r]), p);
+      return p;
+    };
+    auto combine_abs = [&](float q0, float q1, float lin, float kscl) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
+      const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + lin;
+      float scale = half_scale;
+      if constexpr (T::ROWSCALE) scale = half_scale * kscl;
+      return tot * scale;
+    };
+
+    float linv = 0.f;
+    // X receives this block's first and last MFMA blocks; Y the other ones.
+    // Each stage issues one MFMA block and the epilogue of the previous one;
+    // the scheduling barriers keep that order and interleave each stage as
+    // MFMA, 8 VALU, MFMA, 8 VALU so the vector work runs under the matrix
+    // work.  The empty asm statements pin the epilogue results where they
+    // are computed (otherwise the compiler may sink a whole MFMA block into
+    // the conditional store that is its only user, exposing its latency).
+    auto block_abs = [&](const uint32_t (&bf)[QD], uint32_t kword, int u, f32x16& X, f32x16& Y) {
+      const uint32_t sb = kscale_mx(kword);
+      const float ks = __uint_as_float(kword);
+      mfma_lin(X, bf, sb);                        // L of u                       ||
+      p1 = epi_abs(Y, wv[1][1], p1);              //   (row 1, heads 32-63) of u-1, completing u-1
+      float v = combine_abs(p0, p1, linv, kprev);
+      asm volatile("" : "+v"(v));
+      interleave_stage();
+      mfma_block(Y, qf[0][0], sa[0][0], bf, sb);  // (row 0, heads 0-31) of u    ||
+      linv = epi_lin(X);                          //   L of u
+      asm volatile("" : "+v"(linv));
+      interleave_stage();
+      mfma_block(X, qf[0][1], sa[0][1], bf, sb);  // (row 0, heads 32-63)        ||
+      p0 = epi_abs(Y, wv[0][0], 0.f);             //   (row 0, heads 0-31)
+      interleave_stage();
+      mfma_block(Y, qf[1][0], sa[1][0], bf, sb);  // (row 1, heads 0-31)         ||
+      p0 = epi_abs(X, wv[0][1], p0);              //   (row 0, heads 32-63)
+      asm volatile("" : "+v"(p0));
+      interleave_stage();
+      mfma_block(X, qf[1][1], sa[1][1], bf, sb);  // (row 1, heads 32-63)        ||
+      p1 = epi_abs(Y, wv[1][0], 0.f);             //   (row 1, heads 0-31)
+      asm volatile("" : "+v"(p1));
+      interleave_stage();
+      kprev = ks;
+      store(v, u - 1);
+    };
+
+    // A ring of NB fragment buffers: block u reads buffer u % NB, and the
+    // load of block u + NB - 1 goes into the buffer block u - 1 used, right
+    // after that block's MFMAs were issued.  The scheduling barriers keep
+    // each load there: hoisting it would force a register copy (and a wait
+    // for the load) inside the loop.
+    constexpr int NB = kfrag_ring<F>();
+    uint32_t bfs[NB][QD];
+    uint32_t kws[NB];
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) kload(i, bfs[i], kws[i]);
+    const int n_iter = (2 * n_pairs + NB - 1) / NB;
+    for (int s = 0; s < n_iter; ++s) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int u = NB * s + i;
+        kload(u + NB - 1, bfs[(i + NB - 1) % NB], kws[(i + NB - 1) % NB]);
+        if (i % 2 == 0)
+          block_abs(bfs[i], kws[i], u, accA, accB);
+        else
+          block_abs(bfs[i], kws[i], u, accB, accA);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    p1 = epi_abs(accB, wv[1][1], p1);
+    store(combine_abs(p0, p1, linv, kprev), NB * n_iter - 1);
+  } else {
+    // ReLU as a signed-integer max of the float's bits: for every non-NaN x,
+    // x > 0 exactly when its bits are a positive int32, so max(bits, 0) is
+    // max(x, 0) (with -0 giving +0) in one instruction and without the NaN
+    // quieting a float max needs.  Weighted and summed over the lane's 16
+    // heads of one block in a fixed order.
+    auto epi_relu = [&](const f32x16& acc, const float (&w)[16], float p) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[r], __int_as_float(max(__float_as_int(acc[r]), 0)), p);
+      return p;
+    };
+    auto combine = [&](float q0, float q1) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
+      return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * a.sm_scale;
+    };
+    // (row, heads) blocks (0,0) (0,1) (1,0) (1,1), alternating accA / accB
+    auto block_relu = [&](const uint32_t (&bf)[QD], int u) {
+      mfma_block(accA, qf[0][0], 0, bf, 0);  // (row 0, heads 0-31) of u  ||
+      p1 = epi_relu(accB, wv[1][1], p1);     //   (row 1, heads 32-63) of u-1, completing u-1
+      float v = combine(p0, p1);
+      asm volatile("" : "+v"(v));
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(accB, qf[0][1], 0, bf, 0);  // (row 0, heads 32-63)      ||
+      p0 = epi_relu(accA, wv[0][0], 0.f);    //   (row 0, heads 0-31)
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(accA, qf[1][0], 0, bf, 0);  // (row 1, heads 0-31)       ||
+      p0 = epi_relu(accB, wv[0][1], p0);     //   (row 0, heads 32-63)
+      asm volatile("" : "+v"(p0));
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(accB, qf[1][1], 0, bf, 0);  // (row 1, heads 32-63)      ||
+      p1 = epi_relu(accA, wv[1][0], 0.f);    //   (row 1, heads 0-31)
+      asm volatile("" : "+v"(p1));
+      __builtin_amdgcn_sched_barrier(0);
+      store(v, u - 1);
+    };
+    constexpr int NB = kfrag_ring<F>();
+    uint32_t bfs[NB][QD];
+    uint32_t kws[NB];
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) kload(i, bfs[i], kws[i]);
+    const int n_iter = (2 * n_pairs + NB - 1) / NB;
+    for (int s = 0; s < n_iter; ++s) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int u = NB * s + i;
+        kload(u + NB - 1, bfs[(i + NB - 1) % NB], kws[(i + NB - 1) % NB]);
+        block_relu(bfs[i], u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    p1 = epi_relu(accB, wv[1][1], p1);
+    store(combine(p0, p1), NB * n_iter - 1);
   }
-  epi(acc1, c0 + kStageCols * (n_stages - 1) + 32, kprev);
 }
 
 template <int F, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   const int64_t grid = int64_t(a.n_compute) + a.n_tiles;
-  hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, 2>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
