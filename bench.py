@@ -84,27 +84,21 @@ def out_bytes(wl, V: int) -> int:
 
 
 def cpu_baseline(wl, V: int, target_s: float = 12.0) -> dict:
-    """Time the oracle on whole rows of the workload, about target_s seconds,
-    and scale to one full call by visible cells."""
+    """Time the fp64 oracle on whole rows of the workload for about target_s
+    seconds and scale to one full call by visible cells."""
     import oracle
     ws, we = oracle.windows(wl)
     vis = np.maximum(we.astype(np.int64) - ws, 0).reshape(-1)
-    rng = np.random.default_rng(0)
-    order = rng.permutation(vis.size)
-    # calibrate on two rows, then take enough rows for about target_s seconds
-    t0 = time.perf_counter()
-    oracle.logits(wl, rows=order[:2])
-    t_cal = max(time.perf_counter() - t0, 1e-3)
-    per_cell = t_cal / max(int(vis[order[:2]].sum()), 1)
-    n = 2
-    acc = 0
-    while n < vis.size and acc + vis[order[n]] < target_s / per_cell:
-        acc += int(vis[order[n]])
-        n += 1
-    rows = order[:max(n, 2)]
-    t0 = time.perf_counter()
-    _, _, threads = oracle.logits(wl, rows=rows, return_threads=True)
-    dt = time.perf_counter() - t0
+    order = np.random.default_rng(0).permutation(vis.size)
+    n, dt = 8, 0.0
+    while True:
+        rows = order[:n]
+        t0 = time.perf_counter()
+        _, _, threads = oracle.logits(wl, rows=rows, return_threads=True)
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * target_s or n >= vis.size:
+            break
+        n = min(vis.size, max(n + 1, int(n * target_s / max(dt, 1e-3))))
     v_sample = int(vis[rows].sum())
     us_per_call = dt * (V / max(v_sample, 1)) * 1e6
     return {"value": round(us_per_call, 1), "unit": "µs/call", "cores": int(threads), "kind": "oracle",
@@ -131,6 +125,8 @@ def main():
                     help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-variant", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes `steps` times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode (asked for --gpus {args.gpus})",
@@ -143,6 +139,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}), flush=True)
+        return
 
     def measure(name: str):
         wl = W.make(name)

@@ -207,6 +207,7 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   k.pieces = idx::uses_pieces(f) ? ws + WL.off_pieces : nullptr;
   k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
+  k.sink = ws + WL.off_sink;
 
   const bool clean = a->clean_logits != 0;
   hipError_t e = hipSuccess;

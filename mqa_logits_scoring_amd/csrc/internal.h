@@ -103,7 +103,7 @@ inline int row_bytes_of(idx_in_t f) {
 }
 
 struct WorkspaceLayout {
-  size_t off_plan, off_pieces, off_pscales, off_kfrag, total;
+  size_t off_plan, off_pieces, off_pscales, off_kfrag, off_sink, total;
 };
 
 inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k) {
@@ -121,6 +121,9 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
   }
   W.off_kfrag = off;
   off += align256(size_t(B) * size_t((S_k + 31) / 32) * 32 * row_bytes_of(f));
+  // store sink: lanes with nothing to write store here instead of branching
+  W.off_sink = off;
+  off += 256;
   W.total = off;
   return W;
 }
@@ -146,6 +149,7 @@ struct ScoreArgs {
   const unsigned char* pieces;   // [n_rows][kPieces][128] e4m3 codes (formats with pieces)
   const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
+  void* sink;                    // 256 bytes of workspace, written by lanes with nothing to store
 };
 
 // Launchers (return the hipError_t of the launch).

@@ -48,6 +48,7 @@ __global__ void __launch_bounds__(256) pieces_kernel(const void* q, const void* 
   if (row >= n_rows) return;
   const int blk = lane >> 4;
   float a0 = 0.f, a1 = 0.f;
+#pragma unroll 16
   for (int h = 0; h < 64; ++h) {
     const int64_t qh = row * 64 + h;
     const float wh = WBF ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(w)[qh]) << 16)

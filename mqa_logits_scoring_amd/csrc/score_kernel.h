@@ -47,6 +47,8 @@
 // differently, see Fmt<> and Lin<>).
 #pragma once
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace idx {
@@ -358,7 +360,31 @@ __global__ void __launch_bounds__(kThreads)
     acc = d;
   };
 
+  // Every lane stores unconditionally: lanes with nothing to write (columns
+  // outside the unit, padding rows, and out-of-window cells when not
+  // cleaning) are pointed at a private slot of the workspace sink.  No branch
+  // means nothing can be sunk into one, and no memory wait is forced there.
   const int my_c1 = my_valid ? c1 : c0;
+  using OutT = typename std::conditional<OBF, uint16_t, float>::type;
+  OutT* const obase = static_cast<OutT*>(a.out) + int64_t(my_row) * a.ld;
+  OutT* const sink = static_cast<OutT*>(a.sink) + lane;
+  // The -inf of a cleaned cell is picked byte-wise by v_perm_b32 rather than
+  // by a select: a select on a divergent condition may be turned into a
+  // branch with the value's computation (MFMA blocks included) sunk into it,
+  // and a matrix instruction under a partial exec mask still writes every
+  // lane of its result, clobbering what the masked-off lanes held.
+  auto store = [&](float v, int u) {
+    const int j = c0 + 32 * u + c;
+    const bool inwin = (j >= my_s) & (j < my_e);
+    const bool ok = (j >= c0) & (j < my_c1) & (CLEAN | inwin);
+    OutT* const dst = ok ? obase + j : sink;
+    float val = v;
+    if constexpr (CLEAN)
+      val = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(v), 0xFF800000u,
+                                                  inwin ? 0x07060504u : 0x03020100u));
+    store_out<OBF>(dst, 0, val);
+  };
+
   // One pipeline stage: MFMA, 8 VALU, MFMA, 8 VALU, then a full scheduling
   // barrier so the next stage's instructions stay after this one's.
   auto interleave_stage = [&]() {
@@ -369,23 +395,10 @@ __global__ void __launch_bounds__(kThreads)
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto store = [&](float v, int u) {
-    const int j = c0 + 32 * u + c;
-    if (j >= c0 && j < my_c1) {
-      const bool inwin = j >= my_s && j < my_e;
-      const int64_t idx = int64_t(my_row) * a.ld + j;
-      if constexpr (CLEAN) {
-        store_out<OBF>(a.out, idx, inwin ? v : -__builtin_inff());
-      } else {
-        if (inwin) store_out<OBF>(a.out, idx, v);
-      }
-    }
-  };
-
-  // Blocks u = 2s and 2s+1 form iteration s; the fragments of the next block
-  // are loaded while the current one is computed.  Work is pipelined over
-  // 32x32 MFMA blocks: the MFMAs of one block run while the epilogue of the
-  // previous block executes, with two accumulators alternating.
+  // Work is pipelined over 32x32 MFMA blocks: the MFMAs of one block run
+  // while the epilogue of the previous block executes, with two accumulators
+  // alternating; the fragments of later 32-column blocks are loaded while the
+  // current one is computed.
   f32x16 accA = {}, accB = {};
   float p0 = 0.f, p1 = 0.f, kprev = 1.f;
 
@@ -466,31 +479,25 @@ __global__ void __launch_bounds__(kThreads)
     // Each stage issues one MFMA block and the epilogue of the previous one;
     // the scheduling barriers keep that order and interleave each stage as
     // MFMA, 8 VALU, MFMA, 8 VALU so the vector work runs under the matrix
-    // work.  The empty asm statements pin the epilogue results where they
-    // are computed (otherwise the compiler may sink a whole MFMA block into
-    // the conditional store that is its only user, exposing its latency).
+    // work.
     auto block_abs = [&](const uint32_t (&bf)[QD], uint32_t kword, int u, f32x16& X, f32x16& Y) {
       const uint32_t sb = kscale_mx(kword);
       const float ks = __uint_as_float(kword);
       mfma_lin(X, bf, sb);                        // L of u                       ||
       p1 = epi_abs(Y, wv[1][1], p1);              //   (row 1, heads 32-63) of u-1, completing u-1
-      float v = combine_abs(p0, p1, linv, kprev);
-      asm volatile("" : "+v"(v));
+      const float v = combine_abs(p0, p1, linv, kprev);
       interleave_stage();
       mfma_block(Y, qf[0][0], sa[0][0], bf, sb);  // (row 0, heads 0-31) of u    ||
       linv = epi_lin(X);                          //   L of u
-      asm volatile("" : "+v"(linv));
       interleave_stage();
       mfma_block(X, qf[0][1], sa[0][1], bf, sb);  // (row 0, heads 32-63)        ||
       p0 = epi_abs(Y, wv[0][0], 0.f);             //   (row 0, heads 0-31)
       interleave_stage();
       mfma_block(Y, qf[1][0], sa[1][0], bf, sb);  // (row 1, heads 0-31)         ||
       p0 = epi_abs(X, wv[0][1], p0);              //   (row 0, heads 32-63)
-      asm volatile("" : "+v"(p0));
       interleave_stage();
       mfma_block(X, qf[1][1], sa[1][1], bf, sb);  // (row 1, heads 32-63)        ||
       p1 = epi_abs(Y, wv[1][0], 0.f);             //   (row 1, heads 0-31)
-      asm volatile("" : "+v"(p1));
       interleave_stage();
       kprev = ks;
       store(v, u - 1);
@@ -540,19 +547,16 @@ __global__ void __launch_bounds__(kThreads)
     auto block_relu = [&](const uint32_t (&bf)[QD], int u) {
       mfma_block(accA, qf[0][0], 0, bf, 0);  // (row 0, heads 0-31) of u  ||
       p1 = epi_relu(accB, wv[1][1], p1);     //   (row 1, heads 32-63) of u-1, completing u-1
-      float v = combine(p0, p1);
-      asm volatile("" : "+v"(v));
+      const float v = combine(p0, p1);
       __builtin_amdgcn_sched_barrier(0);
       mfma_block(accB, qf[0][1], 0, bf, 0);  // (row 0, heads 32-63)      ||
       p0 = epi_relu(accA, wv[0][0], 0.f);    //   (row 0, heads 0-31)
       __builtin_amdgcn_sched_barrier(0);
       mfma_block(accA, qf[1][0], 0, bf, 0);  // (row 1, heads 0-31)       ||
       p0 = epi_relu(accB, wv[0][1], p0);     //   (row 0, heads 32-63)
-      asm volatile("" : "+v"(p0));
       __builtin_amdgcn_sched_barrier(0);
       mfma_block(accB, qf[1][1], 0, bf, 0);  // (row 1, heads 32-63)      ||
       p1 = epi_relu(accA, wv[1][0], 0.f);    //   (row 1, heads 0-31)
-      asm volatile("" : "+v"(p1));
       __builtin_amdgcn_sched_barrier(0);
       store(v, u - 1);
     };
