@@ -1,17 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the lightning-indexer scoring path on one MI355X.
 
-A step is one complete call of the path: the plan (windows + schedule) built
-inside the call, then the scoring kernel with its -inf cleanup, on inputs
-already resident in device memory.  The default workload is the MXFP8
-Q2048 / KV32768, H64 / D128, clean_logits=True call with FP32 weights and
-output and rows seeing [0, KV-Q+row) -- the configuration DeepGEMM pull
-request 435 times (Performance section) -- on seeded random inputs.
+A step is one complete call of the path on inputs already resident in device
+memory, made through the library's three phases: the plan (windows +
+schedule), the per-call preparation (K in fragment order, weighted-query
+pieces), then the scoring kernel with its -inf cleanup.  That is exactly what
+idx_logits_run does (checked bitwise after timing).  The default workload is
+the MXFP8 Q2048 / KV32768, H64 / D128, clean_logits=True call with FP32
+weights and output and rows seeing [0, KV-Q+row) -- the configuration
+DeepGEMM pull request 435 times (Performance section) -- on seeded random
+inputs.
 
 Prints one JSON line.  Alongside the whole-call time it reports the roofline
-of the scoring kernel alone (timed with events on the stream it runs on, plan
-precomputed) and the fp64 CPU oracle timed on a bounded sample of the same
+of the scoring kernel alone: its launches inside the timed steps are
+bracketed by events on the stream they run on.  HBM traffic comes from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE counts kept under profiles/ (calibrated
+against a plain copy), and only while the kernel sources are the ones they
+were taken on.  The fp64 CPU oracle is timed on a bounded sample of the same
 workload.
+
+    python bench.py --write-traffic WORKLOAD FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES [COPY_RE]
+turns rocprofv3 --pmc counter files into that traffic record (the copy runs
+are of `bench.py --copy-bytes COPY_BYTES`; COPY_RE picks its kernel).
 """
 
 from __future__ import annotations
@@ -32,6 +42,74 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 HBM_GBS = 8000.0
 METRIC = "µs/call + effective TFLOP/s (visible cells) at H64/D128, MXFP8 Q2048/KV32768"
 PAGES_US = {"c4_mxfp8_zero": 412.0, "c4_mxfp4_zero": 407.9}  # GB200, no metadata, all-zero inputs
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+CSRC = os.path.join(ROOT, "mqa_logits_scoring_amd", "csrc")
+
+
+def kernel_source_hash(fmt: str) -> str:
+    """sha256 over the sources of the scoring kernel of one input format."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("score_kernel.h", "internal.h", f"score_{fmt}.hip"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: str, fmt: str):
+    """HBM bytes per launch of the scoring kernel from the stored counter
+    record, or None when there is none or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != kernel_source_hash(fmt):
+        return None
+    return rec
+
+
+def _counter_per_dispatch(path: str, counter: str, kernel_re: str) -> float:
+    """Mean over matching dispatches of a counter (summed over its instances)
+    in a rocprofv3 counter_collection.csv."""
+    import csv
+    import re
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter or not re.search(kernel_re, r["Kernel_Name"]):
+                continue
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{path}: no {counter} rows for kernels matching {kernel_re!r}")
+    return sum(per.values()) / len(per)
+
+
+def write_traffic(argv) -> None:
+    workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes = argv[:6]
+    copy_re = argv[6] if len(argv) > 6 else "copy"
+    import workloads as W
+    fmt = W.make(workload).fmt
+    copy_bytes = int(copy_bytes)
+    kib = 1024.0
+    # the copy kernel reads and writes copy_bytes per dispatch
+    f_cal = copy_bytes / (_counter_per_dispatch(cfetch_csv, "FETCH_SIZE", copy_re) * kib)
+    w_cal = copy_bytes / (_counter_per_dispatch(cwrite_csv, "WRITE_SIZE", copy_re) * kib)
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "score_kernel") * kib * f_cal
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", "score_kernel") * kib * w_cal
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = {"fetch_bytes": round(fetch), "write_bytes": round(write), "fetch_calibration": round(f_cal, 4),
+                      "write_calibration": round(w_cal, 4), "copy_bytes": copy_bytes,
+                      "source_sha256": kernel_source_hash(fmt)}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps({workload: data[workload]}))
 
 
 def device_inputs(wl, dev) -> dict:
@@ -117,6 +195,9 @@ def _cpu_model() -> str:
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
+        write_traffic(sys.argv[2:])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -155,39 +236,53 @@ def main():
         stream = torch.cuda.current_stream(dev)
         odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((wl.B, wl.S_q, wl.S_k), dtype=odt, device=dev) for _ in range(2)]
-        plan = lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
-                                   row_starts=d["starts"], row_ends=d["ends"], device=dev)
-        cargs = lib.make_args(d["q"], d["k"], d["w"], outs[0], in_dtype=wl.fmt, q_scale=d["q_scale"],
-                             k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean)
-        d["workspace"] = torch.empty(lib.idx_logits_workspace_bytes(cargs), dtype=torch.uint8, device=dev)
-        V = visible_cells(lib, wl, plan)
+        cargs = [lib.make_args(d["q"], d["k"], d["w"], o, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                               k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
+        ws = torch.empty(lib.idx_logits_workspace_bytes(cargs[0]), dtype=torch.uint8, device=dev)
+        plan = torch.empty(lib.idx_logits_plan_bytes(wl.B, wl.S_q, wl.S_k), dtype=torch.uint8, device=dev)
+
+        def step(i, ev=None):
+            # one whole call: windows + schedule, K reorder and weighted-query
+            # pieces, then the scoring kernel (bracketed by events when timed)
+            lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
+                                row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
+            lib.idx_logits_prepare(cargs[i % 2], ws, stream=stream)
+            if ev is not None:
+                ev[0].record(stream)
+            lib.idx_logits_score(cargs[i % 2], plan, ws, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+
         for i in range(args.warmup):
-            call(lib, wl, d, outs[i % 2])
+            step(i)
         torch.cuda.synchronize()
-        # the whole call, plan built inside: exactly `steps` steps
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
         t0 = time.perf_counter()
         for i in range(args.steps):
-            call(lib, wl, d, outs[i % 2])
+            step(i, evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         us_call = wall / args.steps * 1e6
-        # the scoring kernel alone (plan precomputed), events on its stream
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        samples = []
-        for rep in range(5):
-            ev0.record(stream)
-            for i in range(args.steps):
-                call(lib, wl, d, outs[i % 2], plan=plan)
-            ev1.record(stream)
-            ev1.synchronize()
-            samples.append(ev0.elapsed_time(ev1) * 1000 / args.steps)
-        kern_us = statistics.median(samples)
-        return wl, V, us_call, kern_us
+        kern = [e0.elapsed_time(e1) * 1000 for e0, e1 in evs]
+        kern_us = statistics.mean(kern)
+        V = visible_cells(lib, wl, plan)
+        # the same call through idx_logits_run gives the same output
+        ref = torch.empty_like(outs[0])
+        lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                           sm_scale=wl.sm_scale, clean_logits=wl.clean, out=ref, q_causal_offsets=d["offsets"],
+                           row_starts=d["starts"], row_ends=d["ends"])
+        same = bool(torch.equal(ref.view(torch.int16 if odt == torch.bfloat16 else torch.int32),
+                                outs[(args.steps - 1) % 2].view(torch.int16 if odt == torch.bfloat16 else torch.int32)))
+        if not same:
+            raise RuntimeError("the phased call and idx_logits_run disagree")
+        return wl, V, us_call, kern_us, statistics.median(kern)
 
-    wl, V, us_call, kern_us = measure(args.workload)
+    wl, V, us_call, kern_us, kern_med = measure(args.workload)
     flops = 16384.0 * V
     peak = PEAK_TFLOPS[wl.fmt]
+    rec = counted_traffic(wl.name, wl.fmt)
+    traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
     achieved = flops / (kern_us * 1e-6) / 1e12
     res = {
         "metric": METRIC,
@@ -204,18 +299,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "H": wl.H, "D": wl.D,
                    "in_dtype": wl.fmt, "w_dtype": wl.w_dtype, "out_dtype": wl.out_dtype,
-                   "clean_logits": wl.clean, "visible_cells": V, "plan": "built inside each call",
+                   "clean_logits": wl.clean, "visible_cells": V, "plan": "built in every step",
                    "inputs": f"seeded random (seed {wl.seed})"},
         "eff_tflops": round(flops / (us_call * 1e-6) / 1e12, 1),
         "out_gbs": round(out_bytes(wl, V) / (us_call * 1e-6) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "score_kernel (plan precomputed)", "kernel_us": round(kern_us, 2),
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "score_kernel", "kernel_us": round(kern_us, 2), "kernel_us_median": round(kern_med, 2),
                      "flop_per_launch": flops, "algorithmic_bytes_per_launch": input_bytes(wl) + out_bytes(wl, V)},
     }
     zero_name = args.workload + "_zero"
     if not args.no_zero_variant and zero_name in W.NAMED:
-        zwl, zV, zus, zk = measure(zero_name)
+        zwl, zV, zus, zk, _ = measure(zero_name)
         res["zero_inputs"] = {"workload": zwl.name, "us_per_call": round(zus, 2), "kernel_us": round(zk, 2),
                               "pages_us_gb200": PAGES_US.get(zero_name),
                               "ratio_to_pages": round(zus / PAGES_US[zero_name], 3) if zero_name in PAGES_US else None}

@@ -164,6 +164,31 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
                             size_t workspace_bytes, void* stream);
 
 /*
+ * The two phases of idx_logits_run, for callers that reuse a prepared
+ * workspace or time the scoring alone.  idx_logits_run(a, plan, ...) with a
+ * plan is exactly idx_logits_prepare(a, ws) followed by
+ * idx_logits_score(a, plan, ws), and gives bitwise the same output.
+ *
+ * idx_logits_prepare writes into `workspace` (idx_logits_workspace_bytes(a)
+ * bytes, 256-byte aligned) what the scoring reads besides the inputs: K
+ * reordered into matrix-core fragment order and, for FP8 / MX inputs, the
+ * weighted-query pieces.  It reads k (and q, q_scale, w for FP8 / MX) and
+ * nothing else of `a`.
+ *
+ * idx_logits_score scores with a plan (required, as in idx_logits_run) and a
+ * workspace that idx_logits_prepare filled from the same k (and q, q_scale,
+ * w) contents and dimensions; nothing checks that the workspace matches, so
+ * a stale one gives wrong scores.  It may be called any number of times on
+ * one prepared workspace (another out, sm_scale, clean_logits or out_dtype).
+ * Every argument check of idx_logits_run applies to both; a non-OK status
+ * means nothing was enqueued.
+ */
+idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream);
+
+idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Copy the windows stored in a plan into caller device arrays
  * win_start / win_end ([B, S_q] int32) on `stream` (for inspection and tests).
  */

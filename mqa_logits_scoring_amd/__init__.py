@@ -23,7 +23,7 @@ IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_workspace_bytes",
-            "idx_logits_run", "idx_logits_plan_windows", "idx_last_error")
+            "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
 class IdxLogitsArgs(ctypes.Structure):
@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
         L.idx_logits_run.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, P, SZ, P]
+        L.idx_logits_prepare.restype = ctypes.c_int
+        L.idx_logits_prepare.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, SZ, P]
+        L.idx_logits_score.restype = ctypes.c_int
+        L.idx_logits_score.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, SZ, P]
         L.idx_logits_plan_windows.restype = ctypes.c_int
         L.idx_logits_plan_windows.argtypes = [P] + [I32] * 5 + [P, P, P]
         _lib = L
@@ -201,3 +205,29 @@ def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtyp
     _check("idx_logits_run", lib().idx_logits_run(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en),
                                                     _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out
+
+
+def _workspace_for(args: IdxLogitsArgs, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(idx_logits_workspace_bytes(args), 1), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def idx_logits_prepare(args: IdxLogitsArgs, workspace: Optional[torch.Tensor] = None, *, device=None,
+                       stream=None) -> torch.Tensor:
+    """First phase of idx_logits_run: fill a workspace for `args` (made by
+    make_args, whose tensors must stay alive); returns the workspace."""
+    device = torch.device(device if device is not None else (workspace.device if workspace is not None else "cuda"))
+    workspace = _workspace_for(args, workspace, device)
+    _check("idx_logits_prepare", lib().idx_logits_prepare(ctypes.byref(args), _ptr(workspace),
+                                                            workspace.numel() * workspace.element_size(),
+                                                            _stream(stream, device)))
+    return workspace
+
+
+def idx_logits_score(args: IdxLogitsArgs, plan: torch.Tensor, workspace: torch.Tensor, *, stream=None) -> None:
+    """Second phase of idx_logits_run: score into args.out from a workspace
+    that idx_logits_prepare filled for the same inputs."""
+    _check("idx_logits_score", lib().idx_logits_score(ctypes.byref(args), _ptr(plan), _ptr(workspace),
+                                                        workspace.numel() * workspace.element_size(),
+                                                        _stream(stream, workspace.device)))

@@ -31,16 +31,6 @@ idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t 
   return IDX_OK;
 }
 
-int row_bytes(idx_in_t f) {
-  switch (f) {
-    case IDX_IN_BF16: return 256;
-    case IDX_IN_FP8_E4M3:
-    case IDX_IN_MXFP8_E4M3: return 128;
-    case IDX_IN_MXFP4_E2M1: return 64;
-  }
-  return 0;
-}
-
 // Work split of a tile's key columns into chunks (one compute unit each).
 // Long key ranges are cut into a multiple of 8 chunks so that each of the 8
 // XCDs owns a fixed slice of K (kept in its L2); chunks hold 2048 key columns
@@ -117,9 +107,12 @@ idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, i
   return IDX_OK;
 }
 
-idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
-                            const int32_t* row_starts, const int32_t* row_ends, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check on the call's arguments; nothing is launched before they pass.
+idx_status_t check_args(const idx_logits_args_t* a) {
   if (a == nullptr) return fail(IDX_E_INVALID, "args is NULL");
   idx_status_t st = check_dims(a->B, a->S_q, a->S_k, a->H, a->D);
   if (st != IDX_OK) return st;
@@ -144,38 +137,40 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
     return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
                 (long long)a->out_row_stride);
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
-  (void)row_bytes;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
-  const idx::WorkspaceLayout WL = idx::workspace_layout(f, a->B, a->S_q, a->S_k);
-  const unsigned char* p = static_cast<const unsigned char*>(plan);
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
-    return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
-  if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
+  const int64_t n_compute = int64_t(pick_split(a->S_k).n_chunks) * L.n_tiles;
+  if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
+  return IDX_OK;
+}
+
+idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, size_t ws_bytes) {
   if (WL.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
   if (ws == nullptr)
     return fail(IDX_E_WORKSPACE, "this call needs a workspace of %zu bytes (idx_logits_workspace_bytes)", WL.total);
   if (!aligned256(ws)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
-  if (workspace_bytes < WL.total)
-    return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, WL.total);
-  if (p == nullptr) {
-    hipError_t e = idx::launch_plan(a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends,
-                                    ws + WL.off_plan, s);
-    if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
-    p = ws + WL.off_plan;
-  }
-  {
-    hipError_t e = idx::launch_kfrag(f, a->k, a->B, a->S_k, ws + WL.off_kfrag, s);
-    if (e != hipSuccess) return fail(IDX_E_HIP, "K reorder launch failed: %s", hipGetErrorString(e));
-  }
+  if (ws_bytes < WL.total) return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, WL.total);
+  return IDX_OK;
+}
+
+// Per-call preparation: K in MFMA fragment order and, for FP8 / MX inputs,
+// the weighted-query pieces.
+idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws, hipStream_t s) {
+  const idx_in_t f = a->in_dtype;
+  hipError_t e = idx::launch_kfrag(f, a->k, a->B, a->S_k, ws + WL.off_kfrag, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "K reorder launch failed: %s", hipGetErrorString(e));
   if (idx::uses_pieces(f)) {
-    hipError_t e = idx::launch_pieces(f, a->w_dtype, a->q, a->q_scale, a->w, rows, ws + WL.off_pieces,
-                                      reinterpret_cast<uint32_t*>(ws + WL.off_pscales), s);
+    e = idx::launch_pieces(f, a->w_dtype, a->q, a->q_scale, a->w, int64_t(a->B) * a->S_q, ws + WL.off_pieces,
+                           reinterpret_cast<uint32_t*>(ws + WL.off_pscales), s);
     if (e != hipSuccess) return fail(IDX_E_HIP, "weighted-query launch failed: %s", hipGetErrorString(e));
   }
+  return IDX_OK;
+}
 
+idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
+                   unsigned char* ws, hipStream_t s) {
+  const idx_in_t f = a->in_dtype;
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
   idx::ScoreArgs k{};
   k.q = a->q;
   k.q_scale = a->q_scale;
@@ -195,15 +190,12 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   k.chunk_cols = sp.chunk_cols;
   k.n_chunks = sp.n_chunks;
   k.xcd_chunks = sp.xcd;
-  const int64_t n_compute = int64_t(k.n_chunks) * L.n_tiles;
-  if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
-  k.n_compute = int32_t(n_compute);
+  k.n_compute = int32_t(int64_t(k.n_chunks) * L.n_tiles);  // bounded by check_args
   k.off_start = uint32_t(L.off_start);
   k.off_end = uint32_t(L.off_end);
   k.off_slot = uint32_t(L.off_slot);
   k.off_lo = uint32_t(L.off_lo);
   k.off_hi = uint32_t(L.off_hi);
-  if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
   k.pieces = idx::uses_pieces(f) ? ws + WL.off_pieces : nullptr;
   k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
@@ -219,6 +211,54 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   }
   if (e != hipSuccess) return fail(IDX_E_HIP, "scoring launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                            const int32_t* row_starts, const int32_t* row_ends, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a);
+  if (st != IDX_OK) return st;
+  const unsigned char* p = static_cast<const unsigned char*>(plan);
+  if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
+    return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
+  if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p == nullptr) {
+    hipError_t e = idx::launch_plan(a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends,
+                                    ws + WL.off_plan, s);
+    if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
+    p = ws + WL.off_plan;
+  }
+  if ((st = prepare(a, WL, ws, s)) != IDX_OK) return st;
+  return score(a, p, WL, ws, s);
+}
+
+idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a);
+  if (st != IDX_OK) return st;
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  return prepare(a, WL, ws, static_cast<hipStream_t>(stream));
+}
+
+idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  idx_status_t st = check_args(a);
+  if (st != IDX_OK) return st;
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score needs a plan");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -1,7 +1,7 @@
 // Weighted-query pieces: qt = sum_h w_h q_h for every query row, written as
 // kPieces e4m3 rows with E8M0 block scales (see internal.h).  One wave per
-// row; lane l owns elements 2l and 2l+1, so lanes 16b..16b+15 hold the
-// 32-element block b.  Element decoding follows the OCP 8-bit float and OCP
+// row; in the encoder lane l owns elements 2l and 2l+1, so lanes 16b..16b+15
+// hold the 32-element block b.  Element decoding follows the OCP 8-bit float and OCP
 // Microscaling v1.0 definitions; the e4m3 encoder rounds to nearest even.
 #include "internal.h"
 
@@ -40,37 +40,68 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | code;
 }
 
+// Q rows are read in 16-byte loads, a whole wave covering 1 KB per load: in
+// load i lane l holds EPL consecutive elements d0 = (l % LPH) * EPL.. of head
+// HPL * i + l / LPH.  Each lane accumulates w_h q_h over its heads; lanes that
+// share d0 are then summed with xor shuffles (a fixed order), and the row's
+// qt goes through LDS to the lane-owns-two-elements layout of the encoder.
+template <int F>
+struct PieceLoad {
+  static constexpr int EPL = F == IDX_IN_MXFP4_E2M1 ? 32 : 16;  // elements per lane per load
+  static constexpr int LPH = 128 / EPL;                         // lanes per head
+  static constexpr int HPL = 64 / LPH;                          // heads per load
+  static constexpr int NL = 64 / HPL;                           // loads per row
+  static constexpr int ROWB = F == IDX_IN_MXFP4_E2M1 ? 64 * 64 : 64 * 128;  // Q bytes per row
+};
+
 template <int F, bool WBF>
 __global__ void __launch_bounds__(256) pieces_kernel(const void* q, const void* q_scale, const void* w, int64_t n_rows,
                                                      unsigned char* pieces, uint32_t* pscales) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= n_rows) return;
-  const int blk = lane >> 4;
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll 16
-  for (int h = 0; h < 64; ++h) {
-    const int64_t qh = row * 64 + h;
+  using P = PieceLoad<F>;
+  __shared__ float qt_lds[4][128];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t row_raw = int64_t(blockIdx.x) * 4 + wid;
+  const bool live = row_raw < n_rows;
+  const int64_t row = live ? row_raw : n_rows - 1;  // every wave reaches the barrier
+  const int sub = lane % P::LPH, hl = lane / P::LPH;
+  const unsigned char* qrow = static_cast<const unsigned char*>(q) + row * P::ROWB + lane * 16;
+  float acc[P::EPL];
+#pragma unroll
+  for (int e = 0; e < P::EPL; ++e) acc[e] = 0.f;
+  uint4 raw[P::NL];
+#pragma unroll
+  for (int i = 0; i < P::NL; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + i * 1024);
+#pragma unroll
+  for (int i = 0; i < P::NL; ++i) {
+    const int64_t qh = row * 64 + P::HPL * i + hl;
     const float wh = WBF ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(w)[qh]) << 16)
                          : static_cast<const float*>(w)[qh];
-    float v0, v1;
-    if constexpr (F == IDX_IN_MXFP4_E2M1) {
-      const uint32_t byte = static_cast<const unsigned char*>(q)[qh * 64 + lane];
-      v0 = e2m1_value(byte & 15u);
-      v1 = e2m1_value(byte >> 4);
-    } else {
-      const uint32_t two = static_cast<const uint16_t*>(q)[qh * 64 + lane];
-      v0 = e4m3_value(two & 0xFFu);
-      v1 = e4m3_value(two >> 8);
+    float sc = 1.f;
+    if constexpr (F != IDX_IN_FP8_E4M3)
+      sc = e8m0_value((static_cast<const uint32_t*>(q_scale)[qh] >> (8 * (sub * P::EPL / 32))) & 0xFFu);
+    const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int e = 0; e < P::EPL; ++e) {
+      float v;
+      if constexpr (F == IDX_IN_MXFP4_E2M1)
+        v = e2m1_value((wd[e / 8] >> (4 * (e % 8))) & 15u);
+      else
+        v = e4m3_value((wd[e / 4] >> (8 * (e % 4))) & 0xFFu);
+      acc[e] = __builtin_fmaf(wh, v * sc, acc[e]);
     }
-    if constexpr (F != IDX_IN_FP8_E4M3) {
-      const float sc = e8m0_value((static_cast<const uint32_t*>(q_scale)[qh] >> (8 * blk)) & 0xFFu);
-      v0 *= sc;
-      v1 *= sc;
-    }
-    a0 = __builtin_fmaf(wh, v0, a0);
-    a1 = __builtin_fmaf(wh, v1, a1);
   }
+#pragma unroll
+  for (int o = P::LPH; o < 64; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < P::EPL; ++e) acc[e] += __shfl_xor(acc[e], o);
+  }
+  if (hl == 0) {
+#pragma unroll
+    for (int e = 0; e < P::EPL; ++e) qt_lds[wid][sub * P::EPL + e] = acc[e];
+  }
+  __syncthreads();
+  if (!live) return;
+  const float a0 = qt_lds[wid][2 * lane], a1 = qt_lds[wid][2 * lane + 1];
   // pieces: each encodes the exact residual left by the ones before it
   float r0 = a0, r1 = a1;
   for (int p = 0; p < kPieces; ++p) {

@@ -93,3 +93,28 @@ def test_plan_rejects():
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, FAKE, 8, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=32), lib.IDX_E_UNSUPPORTED),
+    (dict(in_dtype=9), lib.IDX_E_INVALID),
+    (dict(k=None), lib.IDX_E_INVALID),
+    (dict(out_row_stride=63), lib.IDX_E_INVALID),
+])
+def test_prepare_and_score_share_the_checks(kw, status):
+    L = lib.lib()
+    a = _args(**kw)
+    assert L.idx_logits_prepare(ctypes.byref(a), FAKE, 1 << 30, None) == status
+    assert L.idx_logits_score(ctypes.byref(a), FAKE, FAKE, 1 << 30, None) == status
+
+
+def test_prepare_and_score_need_buffers():
+    L = lib.lib()
+    a = _args()
+    assert L.idx_logits_prepare(ctypes.byref(a), None, 0, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_prepare(ctypes.byref(a), FAKE, 16, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_prepare(ctypes.byref(a), FAKE + 16, 1 << 30, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_score(ctypes.byref(a), None, FAKE, 1 << 30, None) == lib.IDX_E_WORKSPACE
+    assert "plan" in lib.idx_last_error()
+    assert L.idx_logits_score(ctypes.byref(a), FAKE + 8, FAKE, 1 << 30, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_score(ctypes.byref(a), FAKE, None, 0, None) == lib.IDX_E_WORKSPACE

@@ -149,6 +149,36 @@ def test_determinism_and_plan_equivalence(fmt):
 
 
 @pytest.mark.parametrize("fmt", W.FORMATS)
+def test_prepare_then_score_equals_run(fmt):
+    """The two-phase entry points give bitwise the output of idx_logits_run,
+    and one prepared workspace serves several scoring calls (other output
+    type, clean flag and sm_scale)."""
+    wl = W.make_random(fmt, 2, 37, 650, seed=6, windows="irregular")
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    ref_f32 = run(wl.replace(out_dtype="f32"), d, plan=plan)
+    ref_bf16 = run(wl.replace(out_dtype="bf16"), d, plan=plan)
+    out_f32 = torch.full_like(ref_f32, 7.0)
+    out_bf16 = torch.full_like(ref_bf16, 7.0)
+    a32 = lib.make_args(d["q"], d["k"], d["w"], out_f32, in_dtype=fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                        sm_scale=wl.sm_scale, clean_logits=True)
+    ws = lib.idx_logits_prepare(a32, device=d["q"].device)
+    lib.idx_logits_score(a32, plan, ws)
+    a16 = lib.make_args(d["q"], d["k"], d["w"], out_bf16, in_dtype=fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                        sm_scale=wl.sm_scale, clean_logits=True)
+    lib.idx_logits_score(a16, plan, ws)
+    assert torch.equal(out_f32.view(torch.int32), ref_f32.view(torch.int32))
+    assert torch.equal(out_bf16.view(torch.int16), ref_bf16.view(torch.int16))
+    # sm_scale is applied once at the end, so a power of two scales exactly
+    a2 = lib.make_args(d["q"], d["k"], d["w"], out_f32, in_dtype=fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                       sm_scale=wl.sm_scale * 2, clean_logits=False)
+    lib.idx_logits_score(a2, plan, ws)
+    fin = ~torch.isneginf(ref_f32)
+    assert torch.equal(out_f32[fin], ref_f32[fin] * 2)
+    assert bool(torch.isneginf(out_f32[~fin]).all()), "clean_logits=0 touched cells outside the windows"
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
 def test_batch_invariance(fmt):
     wl = W.make_random(fmt, 3, 19, 260, seed=8, offsets=[0, -5, 3])
     d = dev_inputs(wl)
