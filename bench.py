@@ -89,7 +89,8 @@ def write_traffic(argv) -> None:
     workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes = argv[:6]
     copy_re = argv[6] if len(argv) > 6 else "copy"
     import workloads as W
-    fmt = W.make(workload).fmt
+    wl = W.make(workload)
+    fmt, workload = wl.fmt, wl.name
     copy_bytes = int(copy_bytes)
     kib = 1024.0
     # the copy kernel reads and writes copy_bytes per dispatch
