@@ -31,29 +31,34 @@ idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t 
   return IDX_OK;
 }
 
-// Work split of a tile's key columns into chunks (one compute unit each).
-// Long key ranges are cut into a multiple of 8 chunks so that each of the 8
-// XCDs owns a fixed slice of K (kept in its L2); chunks hold 2048 key columns
-// or so, enough work per unit to amortise loading its rows' Q.  Short key
-// ranges use 256-column chunks without XCD ownership (K fits in every L2).
+// Work split: every tile's coverage is cut on the device into n_chunks equal
+// chunks of at least kMinChunk columns, one compute unit each.  Each unit
+// loads its rows' whole Q before its first MFMA, so units should be long; but
+// the chip needs enough of them (kTargetUnits) to stay fed, and tiles of very
+// different coverage (irregular windows) balance only when no unit is much
+// longer than kChunkCols.  When a tile has 8 or more chunks of a long key
+// range, their count is a multiple of 8 and chunk c of every tile runs on XCD
+// c % 8, so each XCD keeps its slice of K in its own L2.
 struct Split {
-  int32_t chunk_cols, n_chunks, xcd;
+  int32_t min_chunk, n_chunks, xcd;
 };
-Split pick_split(int64_t S_k) {
+constexpr int64_t kTargetUnits = 2048;  // 8 per CU
+constexpr int64_t kChunkCols = 8192;
+constexpr int64_t kMinChunk = 256;
+Split pick_split(int64_t S_k, int64_t n_tiles) {
   const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
   Split sp{};
-  if (span >= 8 * 1024) {
-    int64_t cpx = (span + 8 * 2048 - 1) / (8 * 2048);  // chunks per XCD
-    int64_t ch = (span + 8 * cpx - 1) / (8 * cpx);
-    ch = (ch + 63) / 64 * 64;
-    sp.chunk_cols = int32_t(ch);
-    sp.n_chunks = int32_t(8 * cpx);
+  int64_t want = (kTargetUnits + n_tiles - 1) / n_tiles;  // chunks per tile
+  const int64_t by_len = (span + kChunkCols - 1) / kChunkCols;
+  want = want > by_len ? want : by_len;
+  const int64_t most = (span + kMinChunk - 1) / kMinChunk;
+  want = want > most ? most : want;
+  if (span >= 8 * 1024 && want >= 4) {
+    want = (want + 7) / 8 * 8;
     sp.xcd = 1;
-  } else {
-    sp.chunk_cols = 256;
-    sp.n_chunks = int32_t((span + 255) / 256);
-    sp.xcd = 0;
   }
+  sp.n_chunks = int32_t(want);
+  sp.min_chunk = int32_t(kMinChunk);
   return sp;
 }
 
@@ -139,7 +144,7 @@ idx_status_t check_args(const idx_logits_args_t* a) {
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
-  const int64_t n_compute = int64_t(pick_split(a->S_k).n_chunks) * L.n_tiles;
+  const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles).n_chunks) * L.n_tiles;
   if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
   return IDX_OK;
 }
@@ -186,8 +191,8 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.S_k = a->S_k;
   k.n_tiles = int32_t(L.n_tiles);
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q));
-  const Split sp = pick_split(a->S_k);
-  k.chunk_cols = sp.chunk_cols;
+  const Split sp = pick_split(a->S_k, L.n_tiles);
+  k.min_chunk = sp.min_chunk;
   k.n_chunks = sp.n_chunks;
   k.xcd_chunks = sp.xcd;
   k.n_compute = int32_t(int64_t(k.n_chunks) * L.n_tiles);  // bounded by check_args

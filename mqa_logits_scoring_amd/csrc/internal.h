@@ -17,17 +17,23 @@ namespace idx {
 //   int32 win_start[B*S_q]          window start per row
 //   int32 win_end[B*S_q]            window end per row
 //   int32 slot_row[n_tiles*kTileRows]  global row (b*S_q+i) of every tile slot,
-//                                   -1 for the padding slots of a ragged tail
+//                                   -1 for the padding slots of a ragged tail;
+//                                   with explicit windows the rows of every
+//                                   kSortRows-row segment are reordered so that
+//                                   rows with alike windows share tiles
 //   int32 tile_lo[n_tiles]          first column computed for the tile
 //   int32 tile_hi[n_tiles]          one past the last column computed
 //
-// A tile is kTileRows consecutive query rows of one batch.  [tile_lo,
+// A tile is kTileRows consecutive slots of one batch.  [tile_lo,
 // tile_hi) is the union of its rows' windows widened to kColAlign columns
 // and clipped to [0, S_k); cells of a row outside it are cleanup work.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kPlanMagic = 0x50584449u;  // "IDXP"
 constexpr int kTileRows = 8;                   // query rows per tile
 constexpr int kColAlign = 32;                  // coverage granularity in columns
+constexpr int kSortRows = 1024;                // rows ordered together when building a plan
+constexpr int kSortThreads = kSortRows / 2;  // one compare-exchange per thread and pass
+static_assert(kSortRows % kTileRows == 0, "sort segments hold whole tiles");
 
 struct PlanHeader {
   uint32_t magic;
@@ -141,8 +147,9 @@ struct ScoreArgs {
   float sm_scale;
   int32_t B, S_q, S_k;
   int32_t n_tiles, tiles_per_batch;
-  int32_t chunk_cols;    // columns per compute unit (multiple of 64)
-  int32_t n_chunks;      // compute units per tile (upper bound)
+  int32_t min_chunk;     // fewest columns per compute unit (multiple of 64)
+  int32_t n_chunks;      // compute units per tile: its coverage in n_chunks equal
+                         // parts of at least min_chunk columns (upper bound)
   int32_t n_compute;     // n_tiles * n_chunks
   int32_t xcd_chunks;    // 1: n_chunks % 8 == 0 and chunk c runs on XCD c % 8
   uint32_t off_start, off_end, off_slot, off_lo, off_hi;

@@ -12,8 +12,99 @@ namespace idx {
 
 namespace {
 
-__global__ void plan_kernel(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
-                            const int32_t* starts, const int32_t* ends, unsigned char* plan, PlanLayout L) {
+// Order of a row inside its sort segment: rows with empty windows last, then
+// by which sixteenth of [0, S_k] the window ends in, then by start.  Tiles of
+// consecutive slots then hold rows whose windows nearly coincide, so a tile's
+// coverage (the union of its rows' windows) adds little masked work.  Windows
+// from causal offsets are already in this order.
+__device__ __forceinline__ uint32_t order_key(int64_t s, int64_t e, int64_t S_k, int shift) {
+  if (e <= s) return 0x80000000u;
+  const uint32_t eb = uint32_t((e * 16) / (S_k + 1));  // 0..15
+  return (eb << 27) | uint32_t(s >> shift);
+}
+
+// Windows of every row and the row order of every tile slot.  One workgroup
+// per kSortRows consecutive rows of a batch; with explicit windows the
+// segment's rows are sorted by (order_key, row) with a bitonic network in LDS.
+__global__ void __launch_bounds__(kSortThreads) window_order_kernel(int32_t S_q, int32_t S_k, const int32_t* offsets,
+                                                                    const int32_t* starts, const int32_t* ends,
+                                                                    unsigned char* plan, PlanLayout L) {
+  __shared__ uint64_t key[kSortRows];
+  int32_t* win_start = reinterpret_cast<int32_t*>(plan + L.off_start);
+  int32_t* win_end = reinterpret_cast<int32_t*>(plan + L.off_end);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(plan + L.off_slot);
+  const int64_t spb = (int64_t(S_q) + kSortRows - 1) / kSortRows;
+  const int64_t b = blockIdx.x / spb, seg = blockIdx.x % spb;
+  const int64_t i0 = seg * kSortRows;
+  const int n = int(min(int64_t(kSortRows), int64_t(S_q) - i0));
+  const bool explicit_windows = starts != nullptr && ends != nullptr;
+  int shift = 0;
+  while ((int64_t(S_k) >> shift) >= (int64_t(1) << 27)) ++shift;
+  const int64_t slot0 = b * tiles_per_batch(S_q) * kTileRows;
+  for (int r = threadIdx.x; r < kSortRows; r += kSortThreads) {
+    uint64_t k = ~uint64_t(0);
+    if (r < n) {
+      const int64_t i = i0 + r, row = b * S_q + i;
+      int64_t s, e;
+      if (explicit_windows) {
+        s = starts[row];
+        e = ends[row];
+        s = s < 0 ? 0 : (s > S_k ? S_k : s);
+        e = e < s ? s : (e > S_k ? S_k : e);
+      } else {
+        const int64_t off = offsets != nullptr ? int64_t(offsets[b]) : 0;
+        s = 0;
+        e = int64_t(S_k) - int64_t(S_q) + off + i + 1;
+        e = e < 0 ? 0 : (e > S_k ? S_k : e);
+      }
+      win_start[row] = int32_t(s);
+      win_end[row] = int32_t(e);
+      k = (uint64_t(order_key(s, e, S_k, shift)) << 32) | uint32_t(r);
+    }
+    key[r] = k;
+  }
+  if (explicit_windows) {
+    // sort only the smallest power of two holding the segment's rows, and
+    // not at all when they are in order already
+    int np2 = 2;
+    while (np2 < n) np2 <<= 1;
+    __shared__ int unsorted;
+    if (threadIdx.x == 0) unsorted = 0;
+    __syncthreads();
+    for (int r = threadIdx.x + 1; r < n; r += kSortThreads)
+      if (key[r - 1] > key[r]) unsorted = 1;
+    __syncthreads();
+    if (unsorted) {
+      for (int size = 2; size <= np2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int t = threadIdx.x; t < np2 / 2; t += kSortThreads) {
+            const int lo = 2 * stride * (t / stride) + (t % stride);  // bit `stride` of lo is clear
+            const int hi = lo + stride;
+            const bool ascending = (lo & size) == 0;
+            const uint64_t x = key[lo], y = key[hi];
+            if ((x > y) == ascending) {
+              key[lo] = y;
+              key[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+  for (int r = threadIdx.x; r < n; r += kSortThreads) {
+    const int64_t local = explicit_windows ? int64_t(uint32_t(key[r])) : int64_t(r);
+    slot_row[slot0 + i0 + r] = int32_t(b * S_q + i0 + local);
+  }
+  if (seg == spb - 1) {  // padding slots of the batch's last tile
+    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tiles_per_batch(S_q) * kTileRows; i += kSortThreads)
+      slot_row[slot0 + i] = -1;
+  }
+}
+
+// Per tile: the union of its rows' windows widened to kColAlign columns.
+__global__ void coverage_kernel(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, unsigned char* plan,
+                                PlanLayout L) {
   const int64_t tile = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (tile == 0) {
     PlanHeader* h = reinterpret_cast<PlanHeader*>(plan);
@@ -27,36 +118,14 @@ __global__ void plan_kernel(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int3
     h->tile_rows = kTileRows;
   }
   if (tile >= L.n_tiles) return;
-  int32_t* win_start = reinterpret_cast<int32_t*>(plan + L.off_start);
-  int32_t* win_end = reinterpret_cast<int32_t*>(plan + L.off_end);
-  int32_t* slot_row = reinterpret_cast<int32_t*>(plan + L.off_slot);
-  const int64_t tpb = tiles_per_batch(S_q);
-  const int64_t b = tile / tpb;
-  const int64_t i0 = (tile % tpb) * kTileRows;
+  const int32_t* win_start = reinterpret_cast<const int32_t*>(plan + L.off_start);
+  const int32_t* win_end = reinterpret_cast<const int32_t*>(plan + L.off_end);
+  const int32_t* slot_row = reinterpret_cast<const int32_t*>(plan + L.off_slot);
   int64_t lo = S_k, hi = 0;
   for (int r = 0; r < kTileRows; ++r) {
-    const int64_t i = i0 + r;
-    const int64_t slot = tile * kTileRows + r;
-    if (i >= S_q) {
-      slot_row[slot] = -1;
-      continue;
-    }
-    const int64_t row = b * S_q + i;
-    int64_t s, e;
-    if (starts != nullptr && ends != nullptr) {
-      s = starts[row];
-      e = ends[row];
-      s = s < 0 ? 0 : (s > S_k ? S_k : s);
-      e = e < s ? s : (e > S_k ? S_k : e);
-    } else {
-      const int64_t off = offsets != nullptr ? int64_t(offsets[b]) : 0;
-      s = 0;
-      e = int64_t(S_k) - int64_t(S_q) + off + i + 1;
-      e = e < 0 ? 0 : (e > S_k ? S_k : e);
-    }
-    win_start[row] = int32_t(s);
-    win_end[row] = int32_t(e);
-    slot_row[slot] = int32_t(row);
+    const int32_t row = slot_row[tile * kTileRows + r];
+    if (row < 0) continue;
+    const int64_t s = win_start[row], e = win_end[row];
     if (e > s) {
       lo = s < lo ? s : lo;
       hi = e > hi ? e : hi;
@@ -89,10 +158,15 @@ __global__ void copy_windows_kernel(const unsigned char* plan, int64_t n_rows, s
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream) {
   const PlanLayout L = plan_layout(B, S_q);
+  unsigned char* p = static_cast<unsigned char*>(plan);
+  const int64_t segs = int64_t(B) * ((int64_t(S_q) + kSortRows - 1) / kSortRows);
+  hipLaunchKernelGGL(window_order_kernel, dim3(unsigned(segs)), dim3(kSortThreads), 0, stream, S_q, S_k, offsets,
+                     starts, ends, p, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int threads = 128;
   const int64_t blocks = (L.n_tiles + threads - 1) / threads;
-  hipLaunchKernelGGL(plan_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream, B, S_q, S_k, H, D, offsets,
-                     starts, ends, static_cast<unsigned char*>(plan), L);
+  hipLaunchKernelGGL(coverage_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream, B, S_q, S_k, H, D, p, L);
   return hipGetLastError();
 }
 

@@ -219,9 +219,12 @@ __global__ void __launch_bounds__(kThreads)
   }
   const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
   const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
-  const int c0 = lo + chunk * a.chunk_cols;
+  // the tile's coverage in n_chunks equal parts (multiples of 64 columns, at
+  // least min_chunk): every unit of a tile gets the same amount of work
+  const int ccols = max(a.min_chunk, ((hi - lo + a.n_chunks - 1) / a.n_chunks + 63) & ~63);
+  const int c0 = lo + chunk * ccols;
   if (c0 >= hi) return;
-  const int c1 = min(hi, c0 + a.chunk_cols);  // columns [c0, c1) are this unit's
+  const int c1 = min(hi, c0 + ccols);  // columns [c0, c1) are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
 

@@ -272,6 +272,25 @@ def test_named_full_size(name):
     print(f"{name}: {len(rows)} rows, max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "bf16"])
+def test_reordered_plan_several_segments(fmt):
+    """Explicit irregular windows make the plan reorder the rows of every
+    1024-row segment; with several segments per batch, a partial last segment
+    and a ragged last tile, every row still gets its own scores (all rows
+    compared: values within tolerance, -inf placement exact), and the result
+    is bitwise that of the call that builds its plan in place."""
+    wl = W.make_random(fmt, 2, 2100, 2400, seed=21, windows="irregular", w_dtype="bf16", out_dtype="bf16")
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    out = run(wl, d, plan=plan)
+    out2 = run(wl, d)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    ref, bound = oracle.logits(wl)
+    got = to_f64(out).reshape(wl.B * wl.S_q, wl.S_k)
+    compare_rows(wl, got, ref.reshape(wl.B * wl.S_q, wl.S_k), bound.reshape(wl.B * wl.S_q, wl.S_k),
+                 what=f"reordered {fmt}")
+
+
 def test_mx_block_layout_probes():
     """The oracle's MX layout probes (one d-block populated, one scale byte raised,
     nibble order) run on the GPU: within tolerance of the oracle for every variant."""
