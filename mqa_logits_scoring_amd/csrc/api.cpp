@@ -142,6 +142,8 @@ idx_status_t check_args(const idx_logits_args_t* a) {
     return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
                 (long long)a->out_row_stride);
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
+  if ((int64_t(a->S_k) + 31) / 32 * 32 * idx::row_bytes_of(f) > (int64_t(1) << 31) - 1)
+    return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
   const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles).n_chunks) * L.n_tiles;
@@ -162,7 +164,8 @@ idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, siz
 // the weighted-query pieces.
 idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
-  hipError_t e = idx::launch_kfrag(f, a->k, a->B, a->S_k, ws + WL.off_kfrag, s);
+  hipError_t e = idx::launch_kfrag(f, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
+                                   idx::has_kscale(f) ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, s);
   if (e != hipSuccess) return fail(IDX_E_HIP, "K reorder launch failed: %s", hipGetErrorString(e));
   if (idx::uses_pieces(f)) {
     e = idx::launch_pieces(f, a->w_dtype, a->q, a->q_scale, a->w, int64_t(a->B) * a->S_q, ws + WL.off_pieces,
@@ -204,6 +207,7 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.pieces = idx::uses_pieces(f) ? ws + WL.off_pieces : nullptr;
   k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
+  k.kscale = idx::has_kscale(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
   k.sink = ws + WL.off_sink;
 
   const bool clean = a->clean_logits != 0;

@@ -104,12 +104,19 @@ inline bool uses_pieces(idx_in_t f) { return f != IDX_IN_BF16; }
 // u*32*ROWB + v*1024 + l*16, so each fragment load is 1 KB contiguous.  The
 // last block is zero-padded.
 // ---------------------------------------------------------------------------
+// Formats with a per-K-row scale also get it in block order: for block u,
+// 64 words, lane l's word being that of column 32u + l%32 as lane half l/32
+// of the scoring kernel uses it (MX: the int32 word shifted right by 8 or 16
+// bits for lane half 1, so that op_sel picks the right E8M0 byte; FP8: the
+// fp32 scale).  Columns past S_k get 0.
+inline bool has_kscale(idx_in_t f) { return f != IDX_IN_BF16; }
+
 inline int row_bytes_of(idx_in_t f) {
   return f == IDX_IN_BF16 ? 256 : (f == IDX_IN_MXFP4_E2M1 ? 64 : 128);
 }
 
 struct WorkspaceLayout {
-  size_t off_plan, off_pieces, off_pscales, off_kfrag, off_sink, total;
+  size_t off_plan, off_pieces, off_pscales, off_kfrag, off_kscale, off_sink, total;
 };
 
 inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k) {
@@ -127,6 +134,10 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
   }
   W.off_kfrag = off;
   off += align256(size_t(B) * size_t((S_k + 31) / 32) * 32 * row_bytes_of(f));
+  if (has_kscale(f)) {
+    W.off_kscale = off;
+    off += align256(size_t(B) * size_t((S_k + 31) / 32) * 64 * 4);
+  }
   // store sink: lanes with nothing to write store here instead of branching
   W.off_sink = off;
   off += 256;
@@ -156,6 +167,7 @@ struct ScoreArgs {
   const unsigned char* pieces;   // [n_rows][kPieces][128] e4m3 codes (formats with pieces)
   const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
+  const uint32_t* kscale;        // K scales in block order, [B][ceil(S_k/32)][64] (not BF16)
   void* sink;                    // 256 bytes of workspace, written by lanes with nothing to store
 };
 
@@ -165,7 +177,8 @@ hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
 hipError_t launch_pieces(idx_in_t fmt, idx_fp_t w_dtype, const void* q, const void* q_scale, const void* w,
                          int64_t n_rows, unsigned char* pieces, uint32_t* pscales, hipStream_t stream);
-hipError_t launch_kfrag(idx_in_t fmt, const void* k, int64_t B, int64_t S_k, unsigned char* kfrag, hipStream_t stream);
+hipError_t launch_kfrag(idx_in_t fmt, const void* k, const void* k_scale, int64_t B, int64_t S_k, unsigned char* kfrag,
+                        uint32_t* kscale, hipStream_t stream);
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);
 hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,

@@ -56,6 +56,13 @@ namespace idx {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
+// format, no swizzle): offsets past num_records read zero and drop writes.
+constexpr int kBufWord3 = 0x00020000;
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for (gfx9 encoding)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int F>
 struct Fmt;
@@ -299,37 +306,34 @@ __global__ void __launch_bounds__(kThreads)
   const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
   const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
 
-  // K in fragment order (internal.h): block kb0 + u holds columns c0 + 32u..
+  // K in fragment order and its scales in block order (internal.h), read with
+  // buffer loads: the block offset is wave-uniform (SGPR), the lane offset a
+  // constant and the chunk offset an immediate, so no vector instruction
+  // computes an address.  Block kb0 + u holds columns c0 + 32u..; blocks past
+  // the end of K are clamped to the last one: always in bounds, and the
+  // columns they feed are never stored.
   const int nblk = (a.S_k + 31) >> 5;
-  const unsigned char* kfb = a.kfrag + int64_t(b) * nblk * (32 * T::ROWB) + lane * 16;
   const int kb0 = c0 >> 5;  // c0 is a multiple of 32
-  const uint32_t* ksb = HAS_KS ? static_cast<const uint32_t*>(a.k_scale) + int64_t(b) * a.S_k : nullptr;
-  const int last_row = a.S_k - 1;
-
-  // B operand of 32-column block u: 1 KB contiguous per chunk, plus the
-  // column's raw scale word (interpreted where it is used, so that nothing
-  // waits for the load before then).  Blocks and rows past the end of K are
-  // clamped to the last ones: always in bounds, and the columns they feed are
-  // never stored.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(a.kfrag) + int64_t(b) * nblk * (32 * T::ROWB), 0, nblk * (32 * T::ROWB), kBufWord3);
+  const __amdgpu_buffer_rsrc_t srs =
+      HAS_KS ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.kscale) + int64_t(b) * nblk * 64, 0,
+                                                 nblk * 256, kBufWord3)
+             : krs;
   auto kload = [&](int u, uint32_t (&bf)[QD], uint32_t& kword) {
-    const unsigned char* p = kfb + int64_t(min(kb0 + u, nblk - 1)) * (32 * T::ROWB);
+    const int blk = min(kb0 + u, nblk - 1);
 #pragma unroll
     for (int v = 0; v < QD / 4; ++v) {
-      const uint4 x = *reinterpret_cast<const uint4*>(p + v * 1024);
-      bf[4 * v + 0] = x.x;
-      bf[4 * v + 1] = x.y;
-      bf[4 * v + 2] = x.z;
-      bf[4 * v + 3] = x.w;
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + v * 1024, blk * (32 * T::ROWB), 0);
+      bf[4 * v + 0] = x[0];
+      bf[4 * v + 1] = x[1];
+      bf[4 * v + 2] = x[2];
+      bf[4 * v + 3] = x[3];
     }
-    if constexpr (HAS_KS) kword = ksb[min(c0 + 32 * u + c, last_row)];
+    if constexpr (HAS_KS) kword = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, blk * 256, 0);
   };
-  // MX: the lane half's E8M0 bytes of the column's scale word
-  auto kscale_mx = [&](uint32_t kword) {
-    if constexpr (T::MX)
-      return g ? (kword >> T::SCALE_SHIFT) : kword;
-    else
-      return kword;
-  };
+  // MX: the lane half's E8M0 bytes of the column's scale word (stored shifted)
+  auto kscale_mx = [&](uint32_t kword) { return kword; };
 
   // all k-steps of one 32x32 block: acc = Q(row t, heads 32*mb..) x K(32 columns)^T
   auto mfma_block = [&](f32x16& acc, const uint32_t (&q)[QD], uint32_t sA, const uint32_t (&bf)[QD],
@@ -516,6 +520,10 @@ __global__ void __launch_bounds__(kThreads)
     uint32_t kws[NB];
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) kload(i, bfs[i], kws[i]);
+    // Everything loaded so far is needed before the first block anyway;
+    // waiting for it here leaves only the loop's own loads pending at the
+    // loop head, so the waits inside the loop need not cover the prologue.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     const int n_iter = (2 * n_pairs + NB - 1) / NB;
     for (int s = 0; s < n_iter; ++s) {
 #pragma unroll
@@ -568,6 +576,10 @@ __global__ void __launch_bounds__(kThreads)
     uint32_t kws[NB];
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) kload(i, bfs[i], kws[i]);
+    // Everything loaded so far is needed before the first block anyway;
+    // waiting for it here leaves only the loop's own loads pending at the
+    // loop head, so the waits inside the loop need not cover the prologue.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     const int n_iter = (2 * n_pairs + NB - 1) / NB;
     for (int s = 0; s < n_iter; ++s) {
 #pragma unroll
