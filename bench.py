@@ -11,9 +11,14 @@ weights and output and rows seeing [0, KV-Q+row) -- the configuration
 DeepGEMM pull request 435 times (Performance section) -- on seeded random
 inputs.
 
+Before the W warm-up steps, untimed calls run for --prewarm-s seconds (1 by
+default): the GPU clock ramps up over the first milliseconds of sustained
+work, and calls timed right after a short warm-up run up to 20 % slower.
+
 Prints one JSON line.  Alongside the whole-call time it reports the roofline
-of the scoring kernel alone: its launches inside the timed steps are
-bracketed by events on the stream they run on.  HBM traffic comes from the
+of the scoring kernel alone, timed over `steps` back-to-back launches on the
+prepared workspace, bracketed by events on the stream they run on (events
+around every launch of the timed calls would add their own gaps to them).  HBM traffic comes from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE counts kept under profiles/ (calibrated
 against a plain copy), and only while the kernel sources are the ones they
 were taken on.  The fp64 CPU oracle is timed on a bounded sample of the same
@@ -205,6 +210,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4_mxfp8",
                     help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned)")
+    ap.add_argument("--prewarm-s", type=float, default=1.0,
+                    help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-variant", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -242,31 +249,43 @@ def main():
         ws = torch.empty(lib.idx_logits_workspace_bytes(cargs[0]), dtype=torch.uint8, device=dev)
         plan = torch.empty(lib.idx_logits_plan_bytes(wl.B, wl.S_q, wl.S_k), dtype=torch.uint8, device=dev)
 
-        def step(i, ev=None):
+        def step(i):
             # one whole call: windows + schedule, K reorder and weighted-query
-            # pieces, then the scoring kernel (bracketed by events when timed)
+            # pieces, then the scoring kernel
             lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
                                 row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
             lib.idx_logits_prepare(cargs[i % 2], ws, stream=stream)
-            if ev is not None:
-                ev[0].record(stream)
             lib.idx_logits_score(cargs[i % 2], plan, ws, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
 
+        # the GPU's clock ramps up over the first milliseconds of sustained
+        # work: run untimed calls for a second before the warm-up steps
+        t_warm = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t_warm < args.prewarm_s:
+            step(i)
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+        # whole calls: exactly `steps` of them between two synchronisations
         t0 = time.perf_counter()
         for i in range(args.steps):
-            step(i, evs[i])
+            step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         us_call = wall / args.steps * 1e6
-        kern = [e0.elapsed_time(e1) * 1000 for e0, e1 in evs]
-        kern_us = statistics.mean(kern)
+        # the scoring kernel alone: `steps` launches on the prepared workspace,
+        # back to back on the stream the library launches on, between two events
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(args.steps):
+            lib.idx_logits_score(cargs[i % 2], plan, ws, stream=stream)
+        ev1.record(stream)
+        ev1.synchronize()
+        kern_us = ev0.elapsed_time(ev1) * 1000 / args.steps
         V = visible_cells(lib, wl, plan)
         # the same call through idx_logits_run gives the same output
         ref = torch.empty_like(outs[0])
@@ -277,9 +296,9 @@ def main():
                                 outs[(args.steps - 1) % 2].view(torch.int16 if odt == torch.bfloat16 else torch.int32)))
         if not same:
             raise RuntimeError("the phased call and idx_logits_run disagree")
-        return wl, V, us_call, kern_us, statistics.median(kern)
+        return wl, V, us_call, kern_us
 
-    wl, V, us_call, kern_us, kern_med = measure(args.workload)
+    wl, V, us_call, kern_us = measure(args.workload)
     flops = 16384.0 * V
     peak = PEAK_TFLOPS[wl.fmt]
     rec = counted_traffic(wl.name, wl.fmt)
@@ -306,12 +325,12 @@ def main():
         "out_gbs": round(out_bytes(wl, V) / (us_call * 1e-6) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "score_kernel", "kernel_us": round(kern_us, 2), "kernel_us_median": round(kern_med, 2),
+                     "kernel": "score_kernel", "kernel_us": round(kern_us, 2),
                      "flop_per_launch": flops, "algorithmic_bytes_per_launch": input_bytes(wl) + out_bytes(wl, V)},
     }
     zero_name = args.workload + "_zero"
     if not args.no_zero_variant and zero_name in W.NAMED:
-        zwl, zV, zus, zk, _ = measure(zero_name)
+        zwl, zV, zus, zk = measure(zero_name)
         res["zero_inputs"] = {"workload": zwl.name, "us_per_call": round(zus, 2), "kernel_us": round(zk, 2),
                               "pages_us_gb200": PAGES_US.get(zero_name),
                               "ratio_to_pages": round(zus / PAGES_US[zero_name], 3) if zero_name in PAGES_US else None}

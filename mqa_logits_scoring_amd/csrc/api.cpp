@@ -164,14 +164,13 @@ idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, siz
 // the weighted-query pieces.
 idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
-  hipError_t e = idx::launch_kfrag(f, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
-                                   idx::has_kscale(f) ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, s);
-  if (e != hipSuccess) return fail(IDX_E_HIP, "K reorder launch failed: %s", hipGetErrorString(e));
-  if (idx::uses_pieces(f)) {
-    e = idx::launch_pieces(f, a->w_dtype, a->q, a->q_scale, a->w, int64_t(a->B) * a->S_q, ws + WL.off_pieces,
-                           reinterpret_cast<uint32_t*>(ws + WL.off_pscales), s);
-    if (e != hipSuccess) return fail(IDX_E_HIP, "weighted-query launch failed: %s", hipGetErrorString(e));
-  }
+  const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f);
+  hipError_t e = idx::launch_prepare(
+      f, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
+      scaled ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, a->q, a->q_scale, a->w,
+      int64_t(a->B) * a->S_q, pieces ? ws + WL.off_pieces : nullptr,
+      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "preparation launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
 }
 

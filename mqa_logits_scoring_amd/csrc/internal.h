@@ -111,6 +111,29 @@ inline bool uses_pieces(idx_in_t f) { return f != IDX_IN_BF16; }
 // fp32 scale).  Columns past S_k get 0.
 inline bool has_kscale(idx_in_t f) { return f != IDX_IN_BF16; }
 
+// Where lane half g of the scoring kernel holds K row bytes: 16-byte chunk v
+// at CBASE * g + CSTRIDE * v (ROWB bytes per row); SHIFT is the right shift of
+// an MX scale word for lane half 1.  The reorder writes K in this placement,
+// and the scoring kernel's operand formats are checked against it.
+template <int F>
+struct KLayout;
+template <>
+struct KLayout<IDX_IN_BF16> {
+  static constexpr int ROWB = 256, CBASE = 128, CSTRIDE = 16, SHIFT = 0;
+};
+template <>
+struct KLayout<IDX_IN_FP8_E4M3> {
+  static constexpr int ROWB = 128, CBASE = 16, CSTRIDE = 32, SHIFT = 0;
+};
+template <>
+struct KLayout<IDX_IN_MXFP8_E4M3> {
+  static constexpr int ROWB = 128, CBASE = 16, CSTRIDE = 32, SHIFT = 8;
+};
+template <>
+struct KLayout<IDX_IN_MXFP4_E2M1> {
+  static constexpr int ROWB = 64, CBASE = 32, CSTRIDE = 16, SHIFT = 16;
+};
+
 inline int row_bytes_of(idx_in_t f) {
   return f == IDX_IN_BF16 ? 256 : (f == IDX_IN_MXFP4_E2M1 ? 64 : 128);
 }
@@ -175,10 +198,12 @@ struct ScoreArgs {
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream);
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
-hipError_t launch_pieces(idx_in_t fmt, idx_fp_t w_dtype, const void* q, const void* q_scale, const void* w,
-                         int64_t n_rows, unsigned char* pieces, uint32_t* pscales, hipStream_t stream);
-hipError_t launch_kfrag(idx_in_t fmt, const void* k, const void* k_scale, int64_t B, int64_t S_k, unsigned char* kfrag,
-                        uint32_t* kscale, hipStream_t stream);
+// K in fragment order, K scales in block order and the weighted-query pieces
+// (those two not for BF16), in one launch.
+hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
+                          int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
+                          const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
+                          hipStream_t stream);
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);
 hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,

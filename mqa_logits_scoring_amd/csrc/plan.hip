@@ -23,16 +23,34 @@ __device__ __forceinline__ uint32_t order_key(int64_t s, int64_t e, int64_t S_k,
   return (eb << 27) | uint32_t(s >> shift);
 }
 
-// Windows of every row and the row order of every tile slot.  One workgroup
-// per kSortRows consecutive rows of a batch; with explicit windows the
-// segment's rows are sorted by (order_key, row) with a bitonic network in LDS.
-__global__ void __launch_bounds__(kSortThreads) window_order_kernel(int32_t S_q, int32_t S_k, const int32_t* offsets,
-                                                                    const int32_t* starts, const int32_t* ends,
-                                                                    unsigned char* plan, PlanLayout L) {
+// The whole plan in one launch: one workgroup per kSortRows consecutive rows
+// of a batch (segments hold whole tiles).  It computes the rows' windows,
+// orders the rows (with explicit windows: a bitonic sort by (order_key, row)
+// in LDS), writes the slot rows and then the coverage of the segment's tiles
+// from the windows it keeps in LDS.  Workgroup 0 also writes the header.
+__global__ void __launch_bounds__(kSortThreads) plan_kernel(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                                                            const int32_t* offsets, const int32_t* starts,
+                                                            const int32_t* ends, unsigned char* plan, PlanLayout L) {
   __shared__ uint64_t key[kSortRows];
+  __shared__ int32_t win_s[kSortRows], win_e[kSortRows];
+  __shared__ int unsorted;
   int32_t* win_start = reinterpret_cast<int32_t*>(plan + L.off_start);
   int32_t* win_end = reinterpret_cast<int32_t*>(plan + L.off_end);
   int32_t* slot_row = reinterpret_cast<int32_t*>(plan + L.off_slot);
+  int32_t* tile_lo = reinterpret_cast<int32_t*>(plan + L.off_lo);
+  int32_t* tile_hi = reinterpret_cast<int32_t*>(plan + L.off_hi);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    PlanHeader* h = reinterpret_cast<PlanHeader*>(plan);
+    h->magic = kPlanMagic;
+    h->B = B;
+    h->S_q = S_q;
+    h->S_k = S_k;
+    h->H = H;
+    h->D = D;
+    h->n_tiles = int32_t(L.n_tiles);
+    h->tile_rows = kTileRows;
+  }
+  const int64_t tpb = tiles_per_batch(S_q);
   const int64_t spb = (int64_t(S_q) + kSortRows - 1) / kSortRows;
   const int64_t b = blockIdx.x / spb, seg = blockIdx.x % spb;
   const int64_t i0 = seg * kSortRows;
@@ -40,7 +58,7 @@ __global__ void __launch_bounds__(kSortThreads) window_order_kernel(int32_t S_q,
   const bool explicit_windows = starts != nullptr && ends != nullptr;
   int shift = 0;
   while ((int64_t(S_k) >> shift) >= (int64_t(1) << 27)) ++shift;
-  const int64_t slot0 = b * tiles_per_batch(S_q) * kTileRows;
+  const int64_t slot0 = b * tpb * kTileRows;
   for (int r = threadIdx.x; r < kSortRows; r += kSortThreads) {
     uint64_t k = ~uint64_t(0);
     if (r < n) {
@@ -59,18 +77,19 @@ __global__ void __launch_bounds__(kSortThreads) window_order_kernel(int32_t S_q,
       }
       win_start[row] = int32_t(s);
       win_end[row] = int32_t(e);
+      win_s[r] = int32_t(s);
+      win_e[r] = int32_t(e);
       k = (uint64_t(order_key(s, e, S_k, shift)) << 32) | uint32_t(r);
     }
     key[r] = k;
   }
+  if (threadIdx.x == 0) unsorted = 0;
+  __syncthreads();
   if (explicit_windows) {
     // sort only the smallest power of two holding the segment's rows, and
     // not at all when they are in order already
     int np2 = 2;
     while (np2 < n) np2 <<= 1;
-    __shared__ int unsorted;
-    if (threadIdx.x == 0) unsorted = 0;
-    __syncthreads();
     for (int r = threadIdx.x + 1; r < n; r += kSortThreads)
       if (key[r - 1] > key[r]) unsorted = 1;
     __syncthreads();
@@ -92,57 +111,40 @@ __global__ void __launch_bounds__(kSortThreads) window_order_kernel(int32_t S_q,
       }
     }
   }
+  // slot rows (the key's low word is the row's index in the segment; padding
+  // keys are all ones and sort last)
   for (int r = threadIdx.x; r < n; r += kSortThreads) {
-    const int64_t local = explicit_windows ? int64_t(uint32_t(key[r])) : int64_t(r);
+    const int local = explicit_windows ? int(uint32_t(key[r])) : r;
     slot_row[slot0 + i0 + r] = int32_t(b * S_q + i0 + local);
   }
   if (seg == spb - 1) {  // padding slots of the batch's last tile
-    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tiles_per_batch(S_q) * kTileRows; i += kSortThreads)
-      slot_row[slot0 + i] = -1;
+    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tpb * kTileRows; i += kSortThreads) slot_row[slot0 + i] = -1;
   }
-}
-
-// Per tile: the union of its rows' windows widened to kColAlign columns.
-__global__ void coverage_kernel(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, unsigned char* plan,
-                                PlanLayout L) {
-  const int64_t tile = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (tile == 0) {
-    PlanHeader* h = reinterpret_cast<PlanHeader*>(plan);
-    h->magic = kPlanMagic;
-    h->B = B;
-    h->S_q = S_q;
-    h->S_k = S_k;
-    h->H = H;
-    h->D = D;
-    h->n_tiles = int32_t(L.n_tiles);
-    h->tile_rows = kTileRows;
-  }
-  if (tile >= L.n_tiles) return;
-  const int32_t* win_start = reinterpret_cast<const int32_t*>(plan + L.off_start);
-  const int32_t* win_end = reinterpret_cast<const int32_t*>(plan + L.off_end);
-  const int32_t* slot_row = reinterpret_cast<const int32_t*>(plan + L.off_slot);
-  int64_t lo = S_k, hi = 0;
-  for (int r = 0; r < kTileRows; ++r) {
-    const int32_t row = slot_row[tile * kTileRows + r];
-    if (row < 0) continue;
-    const int64_t s = win_start[row], e = win_end[row];
-    if (e > s) {
-      lo = s < lo ? s : lo;
-      hi = e > hi ? e : hi;
+  // coverage of the segment's tiles: the union of their rows' windows
+  // widened to kColAlign columns (0, 0 when every row is empty)
+  const int n_tiles_seg = (n + kTileRows - 1) / kTileRows;
+  for (int t = threadIdx.x; t < n_tiles_seg; t += kSortThreads) {
+    int64_t lo = S_k, hi = 0;
+    for (int r = t * kTileRows; r < t * kTileRows + kTileRows && r < n; ++r) {
+      const int local = explicit_windows ? int(uint32_t(key[r])) : r;
+      const int64_t s = win_s[local], e = win_e[local];
+      if (e > s) {
+        lo = s < lo ? s : lo;
+        hi = e > hi ? e : hi;
+      }
     }
+    if (hi <= lo) {
+      lo = 0;
+      hi = 0;
+    } else {
+      lo = lo / kColAlign * kColAlign;
+      hi = (hi + kColAlign - 1) / kColAlign * kColAlign;
+      hi = hi > S_k ? S_k : hi;
+    }
+    const int64_t tile = b * tpb + i0 / kTileRows + t;
+    tile_lo[tile] = int32_t(lo);
+    tile_hi[tile] = int32_t(hi);
   }
-  int32_t* tile_lo = reinterpret_cast<int32_t*>(plan + L.off_lo);
-  int32_t* tile_hi = reinterpret_cast<int32_t*>(plan + L.off_hi);
-  if (hi <= lo) {  // every row of the tile is empty: nothing to compute
-    lo = 0;
-    hi = 0;
-  } else {
-    lo = lo / kColAlign * kColAlign;
-    hi = (hi + kColAlign - 1) / kColAlign * kColAlign;
-    hi = hi > S_k ? S_k : hi;
-  }
-  tile_lo[tile] = int32_t(lo);
-  tile_hi[tile] = int32_t(hi);
 }
 
 __global__ void copy_windows_kernel(const unsigned char* plan, int64_t n_rows, size_t off_start, size_t off_end,
@@ -158,15 +160,9 @@ __global__ void copy_windows_kernel(const unsigned char* plan, int64_t n_rows, s
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream) {
   const PlanLayout L = plan_layout(B, S_q);
-  unsigned char* p = static_cast<unsigned char*>(plan);
   const int64_t segs = int64_t(B) * ((int64_t(S_q) + kSortRows - 1) / kSortRows);
-  hipLaunchKernelGGL(window_order_kernel, dim3(unsigned(segs)), dim3(kSortThreads), 0, stream, S_q, S_k, offsets,
-                     starts, ends, p, L);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int threads = 128;
-  const int64_t blocks = (L.n_tiles + threads - 1) / threads;
-  hipLaunchKernelGGL(coverage_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream, B, S_q, S_k, H, D, p, L);
+  hipLaunchKernelGGL(plan_kernel, dim3(unsigned(segs)), dim3(kSortThreads), 0, stream, B, S_q, S_k, H, D, offsets,
+                     starts, ends, static_cast<unsigned char*>(plan), L);
   return hipGetLastError();
 }
 

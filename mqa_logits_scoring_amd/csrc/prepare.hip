@@ -1,0 +1,246 @@
+// Per-call preparation, one launch: K in MFMA fragment order, the per-row K
+// scales in block order, and the weighted-query pieces (all laid out in
+// internal.h).  The three jobs are independent, so their workgroups share one
+// grid and overlap: the latency-bound pieces workgroups come first, the
+// bandwidth-bound copies fill the machine behind them.
+//
+// Element decoding follows the OCP 8-bit float and OCP Microscaling v1.0
+// definitions; the e4m3 encoder of the pieces rounds to nearest even.
+#include "internal.h"
+
+namespace idx {
+
+namespace {
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : float(m) * 0.001953125f;  // m * 2^-9
+  return (c & 0x80u) ? -v : v;
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float v = e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * float(m);
+  return (c & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ float e8m0_value(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);  // 2^(e-127); 0 -> 2^-127
+}
+
+// |x| <= 448: nearest e4m3 code, ties to even (sign kept)
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float ax = __builtin_fabsf(x);
+  uint32_t code;
+  if (ax < 0.015625f) {  // below 2^-6: multiples of 2^-9 (8 * 2^-9 is the smallest normal, code 0x08)
+    code = uint32_t(__float2int_rn(ax * 512.f));
+  } else {
+    uint32_t a = __float_as_uint(ax);
+    a += 0x7FFFFu + ((a >> 20) & 1u);  // round the fraction to 3 bits, ties to even
+    code = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+  }
+  return sign | code;
+}
+
+struct PrepArgs {
+  // K reorder and K scales
+  const unsigned char* k;
+  const uint32_t* k_scale;
+  int64_t B, S_k, nblk;
+  unsigned char* kfrag;
+  uint32_t* kscale;
+  // weighted-query pieces
+  const void* q;
+  const void* q_scale;
+  const void* w;
+  int64_t n_rows;
+  unsigned char* pieces;
+  uint32_t* pscales;
+  // workgroups of each job, in grid order: pieces, K chunks, K scales
+  int64_t n_pieces, n_kfrag, n_kscale;
+};
+
+// One thread per 16-byte chunk of K in fragment order, reading the matching
+// chunk of a K row (offsets per lane half as the scoring kernel places d).
+template <int ROWB, int CBASE, int CSTRIDE>
+__device__ void kfrag_chunk(const PrepArgs& a, int64_t i) {
+  constexpr int NV = ROWB / 32;  // 16-byte chunks per lane per block
+  if (i >= a.B * a.nblk * NV * 64) return;
+  const int lane = int(i & 63);
+  const int v = int((i >> 6) % NV);
+  const int64_t bu = (i >> 6) / NV;  // b * nblk + u
+  const int64_t b = bu / a.nblk, u = bu % a.nblk;
+  const int c = lane & 31, g = lane >> 5;
+  const int64_t row = u * 32 + c;
+  uint4 x = make_uint4(0, 0, 0, 0);
+  if (row < a.S_k) x = *reinterpret_cast<const uint4*>(a.k + (b * a.S_k + row) * ROWB + CBASE * g + CSTRIDE * v);
+  reinterpret_cast<uint4*>(a.kfrag)[i] = x;
+}
+
+// One thread per word of the K scales in block order.  SHIFT: right shift of
+// an MX word for lane half 1 (0 for the FP8 fp32 scale).
+template <int SHIFT>
+__device__ void kscale_word(const PrepArgs& a, int64_t i) {
+  if (i >= a.B * a.nblk * 64) return;
+  const int lane = int(i & 63);
+  const int64_t bu = i >> 6;
+  const int64_t b = bu / a.nblk, u = bu % a.nblk;
+  const int64_t col = u * 32 + (lane & 31);
+  uint32_t word = col < a.S_k ? a.k_scale[b * a.S_k + col] : 0u;
+  if (lane >= 32) word >>= SHIFT;
+  a.kscale[i] = word;
+}
+
+// Weighted query of one row, qt = sum_h w_h q_h, by a workgroup of 4 waves.
+// Wave v reads heads 16v..16v+15 in 16-byte loads, each load covering 1 KB:
+// lane l holds EPL consecutive elements d0 = (l % LPH) * EPL.. of head
+// 16v + HPL * i + l / LPH.  Each lane accumulates w_h q_h over its heads and
+// leaves its partial sums in LDS; wave 0 adds them in a fixed order (wave,
+// then lane group) into the lane-owns-two-elements layout of the encoder.
+template <int F>
+struct PieceLoad {
+  static constexpr int EPL = F == IDX_IN_MXFP4_E2M1 ? 32 : 16;  // elements per lane per load
+  static constexpr int LPH = 128 / EPL;                         // lanes per head
+  static constexpr int HPL = 64 / LPH;                          // heads per load
+  static constexpr int NLW = 16 / HPL;                          // loads per wave
+  static constexpr int HB = F == IDX_IN_MXFP4_E2M1 ? 64 : 128;  // Q bytes per head
+  static constexpr int GROUPS = 4 * HPL;                        // partial sums per element
+};
+
+template <int F, bool WBF>
+__device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
+  using P = PieceLoad<F>;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int sub = lane % P::LPH, hl = lane / P::LPH;
+  const unsigned char* qrow = static_cast<const unsigned char*>(a.q) + row * (64 * P::HB) + wv * 16 * P::HB;
+  uint4 raw[P::NLW];
+#pragma unroll
+  for (int i = 0; i < P::NLW; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + i * 1024 + lane * 16);
+  float acc[P::EPL];
+#pragma unroll
+  for (int e = 0; e < P::EPL; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < P::NLW; ++i) {
+    const int64_t qh = row * 64 + 16 * wv + P::HPL * i + hl;
+    const float wh = WBF ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.w)[qh]) << 16)
+                         : static_cast<const float*>(a.w)[qh];
+    float sc = 1.f;
+    if constexpr (F != IDX_IN_FP8_E4M3)
+      sc = e8m0_value((static_cast<const uint32_t*>(a.q_scale)[qh] >> (8 * (sub * P::EPL / 32))) & 0xFFu);
+    const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int e = 0; e < P::EPL; ++e) {
+      float v;
+      if constexpr (F == IDX_IN_MXFP4_E2M1)
+        v = e2m1_value((wd[e / 8] >> (4 * (e % 8))) & 15u);
+      else
+        v = e4m3_value((wd[e / 4] >> (8 * (e % 4))) & 0xFFu);
+      acc[e] = __builtin_fmaf(wh, v * sc, acc[e]);
+    }
+  }
+  // partial sums: part[group][d], group = wave * HPL + lane group
+  float* dst = part + (wv * P::HPL + hl) * 128 + sub * P::EPL;
+#pragma unroll
+  for (int e = 0; e < P::EPL; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  __syncthreads();
+  if (wv != 0) return;
+  float r0 = 0.f, r1 = 0.f;
+#pragma unroll 8
+  for (int gi = 0; gi < P::GROUPS; ++gi) {
+    const float2 x = *reinterpret_cast<const float2*>(part + gi * 128 + 2 * lane);
+    r0 += x.x;
+    r1 += x.y;
+  }
+  // pieces: each encodes the exact residual left by the ones before it; lane
+  // l owns elements 2l and 2l+1, so lanes 16b..16b+15 hold 32-element block b
+  for (int p = 0; p < kPieces; ++p) {
+    float m = __builtin_fmaxf(__builtin_fabsf(r0), __builtin_fabsf(r1));
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    const uint32_t mb = __float_as_uint(m);
+    const uint32_t E = (mb >> 23) & 0xFFu;
+    uint32_t sbyte = 127u, c0 = 0u, c1 = 0u;
+    if (E >= 9u) {  // else the residual is below 2^-118: leave it (piece of zeros)
+      // scale 2^k with k the smallest exponent for which |r| / 2^k <= 448
+      const int k = int(E) - 127 - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+      sbyte = uint32_t(127 + k);
+      const float inv = __uint_as_float(uint32_t(127 - k) << 23);  // 2^-k (k in [-118, 120])
+      const float sc = __uint_as_float(sbyte << 23);
+      c0 = e4m3_code(r0 * inv);
+      c1 = e4m3_code(r1 * inv);
+      r0 -= e4m3_value(c0) * sc;  // exact: the decoded piece is within a factor 2 of r
+      r1 -= e4m3_value(c1) * sc;
+    }
+    reinterpret_cast<uint16_t*>(a.pieces + (row * kPieces + p) * 128)[lane] = uint16_t(c0 | (c1 << 8));
+    const uint32_t word = (__shfl(sbyte, 0)) | (__shfl(sbyte, 16) << 8) | (__shfl(sbyte, 32) << 16) |
+                          (__shfl(sbyte, 48) << 24);
+    if (lane == 0) a.pscales[row * kPieces + p] = word;
+  }
+}
+
+template <int F, bool WBF>
+__global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
+  using L = KLayout<F>;
+  __shared__ float part[F == IDX_IN_BF16 ? 1 : PieceLoad<F == IDX_IN_BF16 ? IDX_IN_FP8_E4M3 : F>::GROUPS * 128];
+  int64_t bid = blockIdx.x;
+  if constexpr (F != IDX_IN_BF16) {
+    if (bid < a.n_pieces) {
+      pieces_row<F, WBF>(a, bid, part);
+      return;
+    }
+    bid -= a.n_pieces;
+  }
+  if (bid < a.n_kfrag) {
+    kfrag_chunk<L::ROWB, L::CBASE, L::CSTRIDE>(a, bid * 256 + threadIdx.x);
+    return;
+  }
+  bid -= a.n_kfrag;
+  if constexpr (F != IDX_IN_BF16) kscale_word<L::SHIFT>(a, bid * 256 + threadIdx.x);
+}
+
+template <int F, bool WBF>
+hipError_t launch(const PrepArgs& a, hipStream_t stream) {
+  const int64_t grid = a.n_pieces + a.n_kfrag + a.n_kscale;
+  hipLaunchKernelGGL((prepare_kernel<F, WBF>), dim3(unsigned(grid)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
+                          int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
+                          const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
+                          hipStream_t stream) {
+  PrepArgs a{};
+  a.k = static_cast<const unsigned char*>(k);
+  a.k_scale = static_cast<const uint32_t*>(k_scale);
+  a.B = B;
+  a.S_k = S_k;
+  a.nblk = (S_k + 31) / 32;
+  a.kfrag = kfrag;
+  a.kscale = kscale;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.n_rows = n_rows;
+  a.pieces = pieces;
+  a.pscales = pscales;
+  const bool scaled = has_kscale(fmt);
+  a.n_pieces = uses_pieces(fmt) ? n_rows : 0;
+  a.n_kfrag = (B * a.nblk * (row_bytes_of(fmt) / 32) * 64 + 255) / 256;
+  a.n_kscale = scaled ? (B * a.nblk * 64 + 255) / 256 : 0;
+  if (a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
+  const bool wb = w_dtype == IDX_BF16;
+  switch (fmt) {
+    case IDX_IN_BF16: return launch<IDX_IN_BF16, false>(a, stream);
+    case IDX_IN_FP8_E4M3: return wb ? launch<IDX_IN_FP8_E4M3, true>(a, stream) : launch<IDX_IN_FP8_E4M3, false>(a, stream);
+    case IDX_IN_MXFP8_E4M3:
+      return wb ? launch<IDX_IN_MXFP8_E4M3, true>(a, stream) : launch<IDX_IN_MXFP8_E4M3, false>(a, stream);
+    case IDX_IN_MXFP4_E2M1:
+      return wb ? launch<IDX_IN_MXFP4_E2M1, true>(a, stream) : launch<IDX_IN_MXFP4_E2M1, false>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace idx

@@ -106,6 +106,18 @@ struct Fmt<IDX_IN_MXFP4_E2M1> {
   static constexpr int SCALE_SHIFT = 16, OPSEL_STEP = 1;
 };
 
+template <int F>
+constexpr bool placement_matches() {
+  return Fmt<F>::ROWB == KLayout<F>::ROWB && Fmt<F>::CBASE == KLayout<F>::CBASE &&
+         Fmt<F>::CSTRIDE == KLayout<F>::CSTRIDE;
+}
+static_assert(placement_matches<IDX_IN_BF16>() && placement_matches<IDX_IN_FP8_E4M3>() &&
+                  placement_matches<IDX_IN_MXFP8_E4M3>() && placement_matches<IDX_IN_MXFP4_E2M1>(),
+              "K is reordered in the placement the MFMA operands use");
+static_assert(Fmt<IDX_IN_MXFP8_E4M3>::SCALE_SHIFT == KLayout<IDX_IN_MXFP8_E4M3>::SHIFT &&
+                  Fmt<IDX_IN_MXFP4_E2M1>::SCALE_SHIFT == KLayout<IDX_IN_MXFP4_E2M1>::SHIFT,
+              "K scales are pre-shifted as the MFMA scale operands use them");
+
 // The weighted-query pieces are e4m3 rows (A operand) multiplied with K in
 // its own format (B operand) in the same 32x32x64 MFMA.  Both operands live
 // in one logical k space: an e4m3 lane half g holds k = 16g + [0,16) in bytes
