@@ -207,7 +207,6 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
   k.kscale = idx::has_kscale(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
-  k.sink = ws + WL.off_sink;
 
   const bool clean = a->clean_logits != 0;
   hipError_t e = hipSuccess;

@@ -139,7 +139,7 @@ inline int row_bytes_of(idx_in_t f) {
 }
 
 struct WorkspaceLayout {
-  size_t off_plan, off_pieces, off_pscales, off_kfrag, off_kscale, off_sink, total;
+  size_t off_plan, off_pieces, off_pscales, off_kfrag, off_kscale, total;
 };
 
 inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k) {
@@ -161,9 +161,6 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
     W.off_kscale = off;
     off += align256(size_t(B) * size_t((S_k + 31) / 32) * 64 * 4);
   }
-  // store sink: lanes with nothing to write store here instead of branching
-  W.off_sink = off;
-  off += 256;
   W.total = off;
   return W;
 }
@@ -191,7 +188,6 @@ struct ScoreArgs {
   const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
   const uint32_t* kscale;        // K scales in block order, [B][ceil(S_k/32)][64] (not BF16)
-  void* sink;                    // 256 bytes of workspace, written by lanes with nothing to store
 };
 
 // Launchers (return the hipError_t of the launch).

@@ -61,6 +61,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Fourth word of a raw buffer resource on gfx9-family GPUs (32-bit data
 // format, no swizzle): offsets past num_records read zero and drop writes.
 constexpr int kBufWord3 = 0x00020000;
+// cache policy of the output stores: non-temporal
+constexpr int kNonTemporal = 2;
 // s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for (gfx9 encoding)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
@@ -210,7 +212,9 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int KD = T::KB / 4;  // dwords per lane per k-step
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  // the wave index is wave-uniform; saying so lets everything derived from it
+  // (rows, their windows, the output resources) live in scalar registers
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5, c = lane & 31;
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
@@ -311,9 +315,7 @@ __global__ void __launch_bounds__(kThreads)
     }
   }
 
-  // half-wave g stores row g of the wave; a padding row stores nothing
-  // (its column bound is c0)
-  const bool my_valid = g ? rvalid[1] : rvalid[0];
+  // half-wave g stores row g of the wave: its window relative to c0
   const int my_row = g ? rows[1] : rows[0];
   const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
   const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
@@ -379,29 +381,49 @@ __global__ void __launch_bounds__(kThreads)
     acc = d;
   };
 
-  // Every lane stores unconditionally: lanes with nothing to write (columns
-  // outside the unit, padding rows, and out-of-window cells when not
-  // cleaning) are pointed at a private slot of the workspace sink.  No branch
-  // means nothing can be sunk into one, and no memory wait is forced there.
-  const int my_c1 = my_valid ? c1 : c0;
-  using OutT = typename std::conditional<OBF, uint16_t, float>::type;
-  OutT* const obase = static_cast<OutT*>(a.out) + int64_t(my_row) * a.ld;
-  OutT* const sink = static_cast<OutT*>(a.sink) + lane;
+  // Stores go through one buffer resource per row of the wave, based at the
+  // unit's first column and num_records = the unit's width (0 for a padding
+  // row): the hardware drops every write at an offset past it, so columns
+  // past the unit, the lanes of the other half-wave (offset with the top bit
+  // set) and, when not cleaning, out-of-window cells need no branch and no
+  // address arithmetic beyond one running offset.  No branch means nothing
+  // can be sunk into one.
   // The -inf of a cleaned cell is picked byte-wise by v_perm_b32 rather than
   // by a select: a select on a divergent condition may be turned into a
   // branch with the value's computation (MFMA blocks included) sunk into it,
   // and a matrix instruction under a partial exec mask still writes every
   // lane of its result, clobbering what the masked-off lanes held.
+  constexpr int ES = OBF ? 2 : 4;
+  constexpr uint32_t kDrop = 0x80000000u;
+  __amdgpu_buffer_rsrc_t ors[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+    ors[t] = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<unsigned char*>(a.out) + (int64_t(rows[t]) * a.ld + c0) * ES, 0, rvalid[t] ? (c1 - c0) * ES : 0,
+        kBufWord3);
+  const uint32_t half0 = g ? kDrop : 0u, half1 = g ? 0u : kDrop;
+  const uint32_t s_rel = uint32_t(my_s - c0) * ES;                       // window start, bytes past c0
+  const uint32_t w_len = uint32_t(max(my_e - my_s, 0)) * ES;             // window width in bytes
   auto store = [&](float v, int u) {
-    const int j = c0 + 32 * u + c;
-    const bool inwin = (j >= my_s) & (j < my_e);
-    const bool ok = (j >= c0) & (j < my_c1) & (CLEAN | inwin);
-    OutT* const dst = ok ? obase + j : sink;
+    const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
+    const bool inwin = off - s_rel < w_len;
+    uint32_t o0 = off | half0, o1 = off | half1;
+    if constexpr (!CLEAN) {
+      o0 = inwin ? o0 : kDrop;
+      o1 = inwin ? o1 : kDrop;
+    }
     float val = v;
     if constexpr (CLEAN)
       val = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(v), 0xFF800000u,
                                                   inwin ? 0x07060504u : 0x03020100u));
-    store_out<OBF>(dst, 0, val);
+    if constexpr (OBF) {
+      const uint16_t h = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));  // round to nearest even
+      __builtin_amdgcn_raw_buffer_store_b16(h, ors[0], int(o0), 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b16(h, ors[1], int(o1), 0, kNonTemporal);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[0], int(o0), 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[1], int(o1), 0, kNonTemporal);
+    }
   };
 
   // One pipeline stage: MFMA, 8 VALU, MFMA, 8 VALU, then a full scheduling
