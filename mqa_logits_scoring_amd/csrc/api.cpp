@@ -42,7 +42,7 @@ idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t 
 struct Split {
   int32_t min_chunk, n_chunks, xcd;
 };
-constexpr int64_t kTargetUnits = 2048;  // 8 per CU
+constexpr int64_t kTargetUnits = 1024;  // 4 per CU
 constexpr int64_t kChunkCols = 8192;
 constexpr int64_t kMinChunk = 256;
 Split pick_split(int64_t S_k, int64_t n_tiles) {
@@ -162,14 +162,15 @@ idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, siz
 
 // Per-call preparation: K in MFMA fragment order and, for FP8 / MX inputs,
 // the weighted-query pieces.
-idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws, hipStream_t s) {
+idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws,
+                     const idx::PlanBuild* build, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
   const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f);
   hipError_t e = idx::launch_prepare(
       f, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
       scaled ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, a->q, a->q_scale, a->w,
       int64_t(a->B) * a->S_q, pieces ? ws + WL.off_pieces : nullptr,
-      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, s);
+      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, build, s);
   if (e != hipSuccess) return fail(IDX_E_HIP, "preparation launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
 }
@@ -237,13 +238,11 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p == nullptr) {
-    hipError_t e = idx::launch_plan(a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends,
-                                    ws + WL.off_plan, s);
-    if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
-    p = ws + WL.off_plan;
-  }
-  if ((st = prepare(a, WL, ws, s)) != IDX_OK) return st;
+  // a plan built here shares the preparation launch
+  idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends, ws + WL.off_plan};
+  const bool build_plan = p == nullptr;
+  if (build_plan) p = ws + WL.off_plan;
+  if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, s)) != IDX_OK) return st;
   return score(a, p, WL, ws, s);
 }
 
@@ -253,7 +252,7 @@ idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, siz
   const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
-  return prepare(a, WL, ws, static_cast<hipStream_t>(stream));
+  return prepare(a, WL, ws, nullptr, static_cast<hipStream_t>(stream));
 }
 
 idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,

@@ -32,7 +32,7 @@ constexpr uint32_t kPlanMagic = 0x50584449u;  // "IDXP"
 constexpr int kTileRows = 8;                   // query rows per tile
 constexpr int kColAlign = 32;                  // coverage granularity in columns
 constexpr int kSortRows = 1024;                // rows ordered together when building a plan
-constexpr int kSortThreads = kSortRows / 2;  // one compare-exchange per thread and pass
+constexpr int kSortThreads = 256;
 static_assert(kSortRows % kTileRows == 0, "sort segments hold whole tiles");
 
 struct PlanHeader {
@@ -51,6 +51,11 @@ struct PlanLayout {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 __host__ __device__ inline int64_t tiles_per_batch(int64_t S_q) { return (S_q + kTileRows - 1) / kTileRows; }
+
+// Workgroups that build a plan: one per kSortRows rows of a batch.
+__host__ __device__ inline int64_t plan_segments(int64_t B, int64_t S_q) {
+  return B * ((S_q + kSortRows - 1) / kSortRows);
+}
 
 // Layout of a plan; total == 0 when the sizes overflow.
 inline PlanLayout plan_layout(int64_t B, int64_t S_q) {
@@ -194,12 +199,21 @@ struct ScoreArgs {
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream);
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
+// What a call that builds its own plan passes to the preparation launch.
+struct PlanBuild {
+  int32_t B, S_q, S_k, H, D;
+  const int32_t* offsets;
+  const int32_t* starts;
+  const int32_t* ends;
+  unsigned char* plan;
+};
+
 // K in fragment order, K scales in block order and the weighted-query pieces
-// (those two not for BF16), in one launch.
+// (those two not for BF16), and the plan when `build` is given, in one launch.
 hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
                           int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
-                          hipStream_t stream);
+                          const PlanBuild* build, hipStream_t stream);
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);
 hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,

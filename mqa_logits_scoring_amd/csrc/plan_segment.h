@@ -1,0 +1,172 @@
+// Plan construction, one segment per workgroup: per-row windows, row order
+// and per-tile column coverage (layout in internal.h).  Used by the plan
+// kernel and by the preparation kernel of calls that build their plan.
+//
+// Window rules follow the per-row [start, end) windows of DeepGEMM pull
+// request 435 (Performance section, reproducer: starts, ends, valid columns
+// are those before `ends`) and the q_causal_offsets of cudnn-frontend pull
+// request 416 (What section: offsets folded into per-row windows in 64-bit
+// integers; the legacy kernel it describes adds offset + i + 1).  The offset
+// is aligned so that offset 0 lets the last query row see every key.
+#pragma once
+
+#include "internal.h"
+
+namespace idx {
+
+// Order of a row inside its sort segment: rows with empty windows last, then
+// by which sixteenth of [0, S_k] the window ends in, then by start.  Tiles of
+// consecutive slots then hold rows whose windows nearly coincide, so a tile's
+// coverage (the union of its rows' windows) adds little masked work.  Windows
+// from causal offsets are already in this order.
+__device__ inline uint32_t order_key(int64_t s, int64_t e, int64_t S_k, int shift) {
+  if (e <= s) return 0x80000000u;
+  const uint32_t eb = uint32_t((e * 16) / (S_k + 1));  // 0..15
+  return (eb << 27) | uint32_t(s >> shift);
+}
+
+struct PlanParams {
+  int32_t B, S_q, S_k, H, D;
+  const int32_t* offsets;
+  const int32_t* starts;
+  const int32_t* ends;
+  unsigned char* plan;
+  PlanLayout L;
+};
+
+// Shared memory one segment needs (8-byte aligned).
+struct PlanSmem {
+  uint64_t key[kSortRows];
+  int32_t win_s[kSortRows], win_e[kSortRows];
+  int unsorted;
+};
+
+// One segment of the plan, by one workgroup of kSortThreads threads: the
+// segment's kSortRows consecutive rows of a batch (segments hold whole tiles).
+// It computes the rows' windows, orders the rows (with explicit windows: a
+// bitonic sort by (order_key, row) in LDS), writes the slot rows and then the
+// coverage of the segment's tiles from the windows it keeps in LDS.  Segment
+// 0 also writes the header.
+__device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSmem& sm) {
+  const int32_t B = P.B, S_q = P.S_q, S_k = P.S_k, H = P.H, D = P.D;
+  const int32_t *offsets = P.offsets, *starts = P.starts, *ends = P.ends;
+  unsigned char* plan = P.plan;
+  const PlanLayout& L = P.L;
+  uint64_t* key = sm.key;
+  int32_t* win_s = sm.win_s;
+  int32_t* win_e = sm.win_e;
+  int& unsorted = sm.unsorted;
+  int32_t* win_start = reinterpret_cast<int32_t*>(plan + L.off_start);
+  int32_t* win_end = reinterpret_cast<int32_t*>(plan + L.off_end);
+  int32_t* slot_row = reinterpret_cast<int32_t*>(plan + L.off_slot);
+  int32_t* tile_lo = reinterpret_cast<int32_t*>(plan + L.off_lo);
+  int32_t* tile_hi = reinterpret_cast<int32_t*>(plan + L.off_hi);
+  if (segment == 0 && threadIdx.x == 0) {
+    PlanHeader* h = reinterpret_cast<PlanHeader*>(plan);
+    h->magic = kPlanMagic;
+    h->B = B;
+    h->S_q = S_q;
+    h->S_k = S_k;
+    h->H = H;
+    h->D = D;
+    h->n_tiles = int32_t(L.n_tiles);
+    h->tile_rows = kTileRows;
+  }
+  const int64_t tpb = tiles_per_batch(S_q);
+  const int64_t spb = (int64_t(S_q) + kSortRows - 1) / kSortRows;
+  const int64_t b = segment / spb, seg = segment % spb;
+  const int64_t i0 = seg * kSortRows;
+  const int n = int(min(int64_t(kSortRows), int64_t(S_q) - i0));
+  const bool explicit_windows = starts != nullptr && ends != nullptr;
+  int shift = 0;
+  while ((int64_t(S_k) >> shift) >= (int64_t(1) << 27)) ++shift;
+  const int64_t slot0 = b * tpb * kTileRows;
+  for (int r = threadIdx.x; r < kSortRows; r += kSortThreads) {
+    uint64_t k = ~uint64_t(0);
+    if (r < n) {
+      const int64_t i = i0 + r, row = b * S_q + i;
+      int64_t s, e;
+      if (explicit_windows) {
+        s = starts[row];
+        e = ends[row];
+        s = s < 0 ? 0 : (s > S_k ? S_k : s);
+        e = e < s ? s : (e > S_k ? S_k : e);
+      } else {
+        const int64_t off = offsets != nullptr ? int64_t(offsets[b]) : 0;
+        s = 0;
+        e = int64_t(S_k) - int64_t(S_q) + off + i + 1;
+        e = e < 0 ? 0 : (e > S_k ? S_k : e);
+      }
+      win_start[row] = int32_t(s);
+      win_end[row] = int32_t(e);
+      win_s[r] = int32_t(s);
+      win_e[r] = int32_t(e);
+      k = (uint64_t(order_key(s, e, S_k, shift)) << 32) | uint32_t(r);
+    }
+    key[r] = k;
+  }
+  if (threadIdx.x == 0) unsorted = 0;
+  __syncthreads();
+  if (explicit_windows) {
+    // sort only the smallest power of two holding the segment's rows, and
+    // not at all when they are in order already
+    int np2 = 2;
+    while (np2 < n) np2 <<= 1;
+    for (int r = threadIdx.x + 1; r < n; r += kSortThreads)
+      if (key[r - 1] > key[r]) unsorted = 1;
+    __syncthreads();
+    if (unsorted) {
+      for (int size = 2; size <= np2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          for (int t = threadIdx.x; t < np2 / 2; t += kSortThreads) {
+            const int lo = 2 * stride * (t / stride) + (t % stride);  // bit `stride` of lo is clear
+            const int hi = lo + stride;
+            const bool ascending = (lo & size) == 0;
+            const uint64_t x = key[lo], y = key[hi];
+            if ((x > y) == ascending) {
+              key[lo] = y;
+              key[hi] = x;
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+  // slot rows (the key's low word is the row's index in the segment; padding
+  // keys are all ones and sort last)
+  for (int r = threadIdx.x; r < n; r += kSortThreads) {
+    const int local = explicit_windows ? int(uint32_t(key[r])) : r;
+    slot_row[slot0 + i0 + r] = int32_t(b * S_q + i0 + local);
+  }
+  if (seg == spb - 1) {  // padding slots of the batch's last tile
+    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tpb * kTileRows; i += kSortThreads) slot_row[slot0 + i] = -1;
+  }
+  // coverage of the segment's tiles: the union of their rows' windows
+  // widened to kColAlign columns (0, 0 when every row is empty)
+  const int n_tiles_seg = (n + kTileRows - 1) / kTileRows;
+  for (int t = threadIdx.x; t < n_tiles_seg; t += kSortThreads) {
+    int64_t lo = S_k, hi = 0;
+    for (int r = t * kTileRows; r < t * kTileRows + kTileRows && r < n; ++r) {
+      const int local = explicit_windows ? int(uint32_t(key[r])) : r;
+      const int64_t s = win_s[local], e = win_e[local];
+      if (e > s) {
+        lo = s < lo ? s : lo;
+        hi = e > hi ? e : hi;
+      }
+    }
+    if (hi <= lo) {
+      lo = 0;
+      hi = 0;
+    } else {
+      lo = lo / kColAlign * kColAlign;
+      hi = (hi + kColAlign - 1) / kColAlign * kColAlign;
+      hi = hi > S_k ? S_k : hi;
+    }
+    const int64_t tile = b * tpb + i0 / kTileRows + t;
+    tile_lo[tile] = int32_t(lo);
+    tile_hi[tile] = int32_t(hi);
+  }
+}
+
+}  // namespace idx

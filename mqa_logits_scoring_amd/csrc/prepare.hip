@@ -1,12 +1,13 @@
-// Per-call preparation, one launch: K in MFMA fragment order, the per-row K
-// scales in block order, and the weighted-query pieces (all laid out in
-// internal.h).  The three jobs are independent, so their workgroups share one
-// grid and overlap: the latency-bound pieces workgroups come first, the
-// bandwidth-bound copies fill the machine behind them.
+// Per-call preparation, one launch: the plan when the call builds it
+// (plan_segment.h), K in MFMA fragment order, the per-row K scales in block
+// order, and the weighted-query pieces (all laid out in internal.h).  The jobs
+// are independent, so their workgroups share one grid and overlap: the
+// latency-bound plan and pieces workgroups come first, the bandwidth-bound
+// copies fill the machine behind them.
 //
 // Element decoding follows the OCP 8-bit float and OCP Microscaling v1.0
 // definitions; the e4m3 encoder of the pieces rounds to nearest even.
-#include "internal.h"
+#include "plan_segment.h"
 
 namespace idx {
 
@@ -57,8 +58,11 @@ struct PrepArgs {
   int64_t n_rows;
   unsigned char* pieces;
   uint32_t* pscales;
-  // workgroups of each job, in grid order: pieces, K chunks, K scales
-  int64_t n_pieces, n_kfrag, n_kscale;
+  // the plan, when built here
+  PlanParams plan;
+  // workgroups of each job, in grid order: plan segments, pieces, K chunks,
+  // K scales
+  int64_t n_plan, n_pieces, n_kfrag, n_kscale;
 };
 
 // One thread per 16-byte chunk of K in fragment order, reading the matching
@@ -182,11 +186,20 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
 template <int F, bool WBF>
 __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
   using L = KLayout<F>;
-  __shared__ float part[F == IDX_IN_BF16 ? 1 : PieceLoad<F == IDX_IN_BF16 ? IDX_IN_FP8_E4M3 : F>::GROUPS * 128];
+  constexpr int PART = F == IDX_IN_BF16 ? 1 : PieceLoad<F == IDX_IN_BF16 ? IDX_IN_FP8_E4M3 : F>::GROUPS * 128;
+  __shared__ union {
+    float part[PART];
+    PlanSmem plan;
+  } sm;
   int64_t bid = blockIdx.x;
+  if (bid < a.n_plan) {
+    plan_segment(a.plan, bid, sm.plan);
+    return;
+  }
+  bid -= a.n_plan;
   if constexpr (F != IDX_IN_BF16) {
     if (bid < a.n_pieces) {
-      pieces_row<F, WBF>(a, bid, part);
+      pieces_row<F, WBF>(a, bid, sm.part);
       return;
     }
     bid -= a.n_pieces;
@@ -201,7 +214,7 @@ __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
 
 template <int F, bool WBF>
 hipError_t launch(const PrepArgs& a, hipStream_t stream) {
-  const int64_t grid = a.n_pieces + a.n_kfrag + a.n_kscale;
+  const int64_t grid = a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale;
   hipLaunchKernelGGL((prepare_kernel<F, WBF>), dim3(unsigned(grid)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -211,8 +224,13 @@ hipError_t launch(const PrepArgs& a, hipStream_t stream) {
 hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
                           int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
-                          hipStream_t stream) {
+                          const PlanBuild* build, hipStream_t stream) {
   PrepArgs a{};
+  if (build != nullptr) {
+    a.plan = PlanParams{build->B, build->S_q, build->S_k, build->H, build->D, build->offsets, build->starts,
+                        build->ends, build->plan, plan_layout(build->B, build->S_q)};
+    a.n_plan = plan_segments(build->B, build->S_q);
+  }
   a.k = static_cast<const unsigned char*>(k);
   a.k_scale = static_cast<const uint32_t*>(k_scale);
   a.B = B;
@@ -230,7 +248,7 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.n_pieces = uses_pieces(fmt) ? n_rows : 0;
   a.n_kfrag = (B * a.nblk * (row_bytes_of(fmt) / 32) * 64 + 255) / 256;
   a.n_kscale = scaled ? (B * a.nblk * 64 + 255) / 256 : 0;
-  if (a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
+  if (a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
   const bool wb = w_dtype == IDX_BF16;
   switch (fmt) {
     case IDX_IN_BF16: return launch<IDX_IN_BF16, false>(a, stream);
