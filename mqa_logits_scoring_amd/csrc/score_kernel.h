@@ -195,10 +195,11 @@ constexpr int waves_per_eu() {
 }
 
 // K fragment buffers per wave (even): the load of a block is issued
-// kfrag_ring - 1 blocks before its MFMAs.
+// kfrag_ring - 1 blocks before its MFMAs.  One block ahead covers the L2
+// latency; deeper rings only cost registers (measured, all formats).
 template <int F>
 constexpr int kfrag_ring() {
-  return F == IDX_IN_MXFP4_E2M1 ? 4 : 2;
+  return 2;
 }
 
 template <int F, bool WBF, bool OBF, bool CLEAN>
