@@ -51,6 +51,8 @@ class Oracle:
         P = ctypes.c_void_p
         lib.oracle_windows.argtypes = [ctypes.c_int] * 3 + [P] * 5
         lib.oracle_windows.restype = None
+        lib.oracle_windows_thd.argtypes = [ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+        lib.oracle_windows_thd.restype = None
         lib.oracle_mqa_logits.argtypes = ([ctypes.c_int] * 6 + [P] * 5 + [ctypes.c_int, ctypes.c_double]
                                           + [P, P, P, ctypes.c_int64, P, P, ctypes.c_int])
         lib.oracle_mqa_logits.restype = ctypes.c_int
@@ -66,8 +68,23 @@ class Oracle:
         """One element code -> its exact value (fmt in bf16, e4m3, e2m1, e8m0)."""
         return getattr(self.lib, "oracle_dec_" + fmt)(code)
 
+    def windows_thd(self, cu_q, cu_k, ratio: int, T_q: int, m_total: int) -> tuple[np.ndarray, np.ndarray]:
+        """Packed variable-length windows with ratio-compressed keys, int32 [T_q] arrays."""
+        cq = np.ascontiguousarray(cu_q, np.int32)
+        ck = np.ascontiguousarray(cu_k, np.int32)
+        assert cq.size == ck.size and cq.size >= 2
+        ws = np.empty(T_q, np.int32)
+        we = np.empty(T_q, np.int32)
+        self.lib.oracle_windows_thd(cq.size - 1, _ptr(cq), _ptr(ck), int(ratio), int(T_q), int(m_total), _ptr(ws),
+                                    _ptr(we))
+        return ws, we
+
     def windows(self, wl) -> tuple[np.ndarray, np.ndarray]:
         """Per-row [start, end) of a workload as int32 [B, S_q] arrays."""
+        if getattr(wl, "thd", None) is not None:
+            assert wl.B == 1
+            ws, we = self.windows_thd(wl.thd["cu_q"], wl.thd["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k)
+            return ws.reshape(1, -1), we.reshape(1, -1)
         ws = np.empty((wl.B, wl.S_q), np.int32)
         we = np.empty((wl.B, wl.S_q), np.int32)
         offs = None if wl.offsets is None else np.ascontiguousarray(wl.offsets, np.int32)
@@ -116,6 +133,10 @@ def decode(fmt: str, code: int) -> float:
 
 def windows(wl):
     return default().windows(wl)
+
+
+def windows_thd(cu_q, cu_k, ratio, T_q, m_total):
+    return default().windows_thd(cu_q, cu_k, ratio, T_q, m_total)
 
 
 def logits(wl, rows=None, threads: int = 0, return_threads: bool = False):

@@ -137,6 +137,43 @@ void oracle_windows(int B, int S_q, int S_k, const int32_t* offsets, const int32
   }
 }
 
+/*
+ * Packed variable-length (THD) windows with ratio-compressed keys, as the
+ * cudnn-frontend pull request 416 describes them ("DSA indexer forward",
+ * THD/varlen commit): query tokens of n_seg segments are packed into one row
+ * range (segment s holds rows [cu_q[s], cu_q[s+1])), their compressed keys
+ * into one column range (segment s holds [cu_k[s], cu_k[s+1])), and every row
+ * sees an absolute window that starts at its segment's first key.  The pages
+ * give the start (cu_seqlens_k of the segment) and say the window length is
+ * the ratio-causal visible count without printing it; the reading taken here
+ * is that compressed key c of a segment stands for its query tokens
+ * [c*ratio, (c+1)*ratio) and becomes visible once all of them are, so the
+ * local row t sees floor((t + 1) / ratio) keys.  The window never leaves its
+ * segment; rows outside every segment see nothing.  Everything is clamped to
+ * [0, m_total] in 64-bit integers.
+ */
+void oracle_windows_thd(int n_seg, const int32_t* cu_q, const int32_t* cu_k, int ratio, int T_q, int m_total,
+                        int32_t* win_start, int32_t* win_end) {
+  for (int i = 0; i < T_q; ++i) {
+    win_start[i] = 0;
+    win_end[i] = 0;
+  }
+  for (int seg = 0; seg < n_seg; ++seg) {
+    for (int64_t i = cu_q[seg]; i < cu_q[seg + 1]; ++i) {
+      if (i < 0 || i >= T_q) continue;
+      const int64_t t = i - cu_q[seg];
+      int64_t s = cu_k[seg], e = s + (t + 1) / ratio, lim = cu_k[seg + 1];
+      if (e > lim) e = lim;
+      if (s < 0) s = 0;
+      if (s > m_total) s = m_total;
+      if (e < s) e = s;
+      if (e > m_total) e = m_total;
+      win_start[i] = (int32_t)s;
+      win_end[i] = (int32_t)e;
+    }
+  }
+}
+
 /* Dequantised K of one batch: Kd[j*D + d] and |Kd[j]|_2 in kn[j]. */
 static void dequant_k(int fmt, int S_k, int D, const uint8_t* kb, const void* k_scale_b, double* Kd,
                       double* kn) {

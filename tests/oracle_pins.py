@@ -420,6 +420,68 @@ def pin_windows_clamp(orc):
     assert we.tolist() == [[50] * 4, [0] * 4, [0, 0, 0, 1]]
 
 
+def pin_windows_thd_golden(orc):
+    """Packed variable-length windows over ratio-compressed keys against the hand-worked
+    cases of tests/golden/thd_windows.json (cudnn-frontend pull request 416, THD commit)."""
+    with open(os.path.join(GOLDEN, "thd_windows.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        ws, we = orc.windows_thd(c["cu_q"], c["cu_k"], c["ratio"], c["T_q"], c["m_total"])
+        assert ws.tolist() == c["starts"] and we.tolist() == c["ends"], c["what"]
+
+
+def pin_windows_thd_structure(orc):
+    """THD windows: one segment at ratio 1 is the causal mask [0, t+1); every window stays
+    inside its segment's keys; ends never fall within a segment and grow by at most one key
+    per row; a segment whose length is a multiple of the ratio ends seeing all its keys; and
+    each key count v >= 1 below the last is seen by exactly `ratio` consecutive rows."""
+    T = 37
+    ws, we = orc.windows_thd([0, T], [0, T], 1, T, T)
+    assert np.all(ws == 0) and np.array_equal(we, np.arange(1, T + 1))
+    rng = np.random.default_rng(3)
+    for ratio in (1, 2, 3, 4, 7):
+        lens = rng.integers(0, 40, size=6)
+        lens[2] = 4 * ratio  # one segment with a length that is a multiple of the ratio
+        wl = W.make_thd("bf16", lens, ratio, H=1, D=2, seed=1)
+        cq, ck = wl.thd["cu_q"], wl.thd["cu_k"]
+        ws, we = orc.windows_thd(cq, ck, ratio, wl.S_q, wl.S_k)
+        for sgi in range(len(lens)):
+            a, b = cq[sgi], cq[sgi + 1]
+            if a == b:
+                continue
+            s_, e_ = ws[a:b], we[a:b]
+            assert np.all(s_ == ck[sgi]) and np.all(e_ <= ck[sgi + 1]) and np.all(e_ >= s_)
+            d = np.diff(e_)
+            assert np.all((d == 0) | (d == 1))
+            if (b - a) % ratio == 0:
+                assert e_[-1] == ck[sgi + 1]
+            counts = np.bincount(e_ - s_)
+            for v in range(1, len(counts) - 1):
+                assert counts[v] == ratio, (ratio, sgi, v, counts)
+
+
+def pin_windows_thd_isolation(orc):
+    """Scores of a packed workload equal, row by row, those of each segment scored alone
+    against its own keys with the same windows shifted to the segment: no row sees
+    another segment's keys."""
+    wl = W.make_thd("mxfp8", (5, 0, 9, 6), 2, seed=12, out_dtype="f32")
+    ref, _ = orc.logits(wl)
+    ws, we = orc.windows(wl)
+    cq, ck = wl.thd["cu_q"], wl.thd["cu_k"]
+    for sgi in range(4):
+        a, b, ka, kb = cq[sgi], cq[sgi + 1], ck[sgi], ck[sgi + 1]
+        if a == b or ka == kb:
+            continue
+        one = wl.replace(S_q=int(b - a), S_k=int(kb - ka), q=wl.q[:, a:b], q_scale=wl.q_scale[:, a:b],
+                         w=wl.w[:, a:b], k=wl.k[:, ka:kb], k_scale=wl.k_scale[:, ka:kb], thd=None,
+                         starts=(ws[:, a:b] - ka).astype(np.int32), ends=(we[:, a:b] - ka).astype(np.int32))
+        r1, _ = orc.logits(one)
+        seg = ref[a:b]
+        assert np.array_equal(seg[:, ka:kb], r1)
+        outside = np.concatenate([seg[:, :ka], seg[:, kb:]], axis=1)
+        assert np.all(np.isneginf(outside))
+
+
 def pin_empty_and_batch(orc):
     """Empty windows are all -inf; each batch's slice equals a B=1 run on that batch alone."""
     for fmt in W.FORMATS:

@@ -37,6 +37,10 @@ MUTANTS = [
     ("w_bf16_read_as_f32", "(w_fmt == OR_W_F32)", "(1)", 0),
     ("dot_not_reset", "for (int h = 0; h < H; ++h) dot[h] = 0.0;", "", 0),
     ("bound_without_k_norm", "fabs(sm_scale) * kn[(size_t)b * S_k + j] * bs", "fabs(sm_scale) * bs", 0),
+    ("thd_visible_off_by_one", "e = s + (t + 1) / ratio", "e = s + t / ratio", 0),
+    ("thd_visible_ceil", "e = s + (t + 1) / ratio", "e = s + (t + ratio) / ratio", 0),
+    ("thd_no_segment_clamp", "if (e > lim) e = lim;", "", 0),
+    ("thd_start_global", "int64_t s = cu_k[seg],", "int64_t s = cu_k[0],", 0),
 ]
 
 

@@ -76,6 +76,10 @@ class Workload:
     starts: Optional[np.ndarray]
     ends: Optional[np.ndarray]
     seed: int = 0
+    # packed variable-length rows with ratio-compressed keys (B = 1): dict with
+    # int32 arrays cu_q, cu_k (segment boundaries in rows and in keys) and the
+    # int ratio; the windows then come from these instead of offsets / starts
+    thd: Optional[dict] = None
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -256,6 +260,24 @@ def make_random(fmt: str, B: int, S_q: int, S_k: int, H: int = 64, D: int = 128,
                     k=k, k_scale=k_scale, w=w, offsets=wl_off, starts=wl_s, ends=wl_e, seed=seed)
 
 
+def make_thd(fmt: str, seg_lens, ratio: int, *, w_dtype: str = "f32", out_dtype: str = "f32",
+             sm_scale: float = 1.0, clean: bool = True, seed: int = 0, name: str = "thd", **kw) -> Workload:
+    """Packed variable-length query segments over ratio-compressed keys, the
+    THD layout of cudnn-frontend pull request 416 (THD/varlen commit): the
+    segments' query tokens are packed into one row range and their compressed
+    keys into one column range; segment s has seg_lens[s] query tokens and
+    floor(seg_lens[s] / ratio) compressed keys.  Values as make_random."""
+    lens = np.asarray(seg_lens, np.int64)
+    klens = lens // int(ratio)
+    cu_q = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(klens)]).astype(np.int32)
+    T_q, m_total = int(cu_q[-1]), int(cu_k[-1])
+    wl = make_random(fmt, 1, T_q, max(m_total, 1), w_dtype=w_dtype, out_dtype=out_dtype, sm_scale=sm_scale,
+                     clean=clean, seed=seed, name=name, **kw)
+    return wl.replace(offsets=None, starts=None, ends=None,
+                      thd={"cu_q": cu_q, "cu_k": cu_k, "ratio": int(ratio)})
+
+
 # --------------------------------------------------------------------------
 # the named workloads
 # --------------------------------------------------------------------------
@@ -286,6 +308,14 @@ def _c5(S_q=8192, S_k=65536, seed=5, name="c5_mxfp4_irregular", **kw):
                        windows="irregular", name=name, **kw)
 
 
+def _thd(**kw):
+    # the ragged B=3, T_q=8192, ratio-4 shape the cudnn-frontend page times
+    # (m_total = 2046): BF16 Q/K, FP32 W and scores; the segment lengths are
+    # not printed there, these are one ragged choice with that T_q and m_total
+    return make_thd("bf16", (1027, 3003, 4162), 4, w_dtype="f32", sm_scale=1 / math.sqrt(128), seed=7,
+                    name="thd_bf16_r4", **kw)
+
+
 NAMED = {
     "c1": _c1,
     "c2": _c2,
@@ -297,6 +327,7 @@ NAMED = {
     "c4_mxfp4_zero": lambda **kw: _c4("mxfp4", zero=True, **kw),
     "c5": _c5,
     "c5_nonaligned": lambda **kw: _c5(S_q=129, S_k=4100, seed=6, name="c5_nonaligned", **kw),
+    "thd_bf16_r4": _thd,
 }
 
 
