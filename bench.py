@@ -133,11 +133,25 @@ def device_inputs(wl, dev) -> dict:
         x = torch.from_numpy(a).to(dev)
         return x.view(as_dtype) if as_dtype is not None else x
 
-    return {"q": t(wl.q), "k": t(wl.k), "q_scale": t(wl.q_scale), "k_scale": t(wl.k_scale),
-            "w": t(wl.w, torch.bfloat16 if wl.w_dtype == "bf16" else None),
-            "offsets": t(None if wl.offsets is None else np.asarray(wl.offsets, np.int32)),
-            "starts": t(None if wl.starts is None else np.asarray(wl.starts, np.int32)),
-            "ends": t(None if wl.ends is None else np.asarray(wl.ends, np.int32))}
+    d = {"q": t(wl.q), "k": t(wl.k), "q_scale": t(wl.q_scale), "k_scale": t(wl.k_scale),
+         "w": t(wl.w, torch.bfloat16 if wl.w_dtype == "bf16" else None),
+         "offsets": t(None if wl.offsets is None else np.asarray(wl.offsets, np.int32)),
+         "starts": t(None if wl.starts is None else np.asarray(wl.starts, np.int32)),
+         "ends": t(None if wl.ends is None else np.asarray(wl.ends, np.int32))}
+    if getattr(wl, "thd", None) is not None:
+        d["cu_q"] = t(np.asarray(wl.thd["cu_q"], np.int32))
+        d["cu_k"] = t(np.asarray(wl.thd["cu_k"], np.int32))
+    return d
+
+
+def build_plan(lib, wl, d, plan, stream):
+    """The call's plan: from causal offsets or explicit windows, or for packed
+    variable-length rows from the segment boundaries and the ratio."""
+    if getattr(wl, "thd", None) is not None:
+        return lib.idx_logits_plan_thd(d["cu_q"], d["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k, wl.H, wl.D, plan=plan,
+                                       stream=stream)
+    return lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
+                               row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
 
 
 def call(lib, wl, d, out, plan=None):
@@ -209,7 +223,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4_mxfp8",
-                    help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned)")
+                    help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned, "
+                         "thd_bf16_r4)")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -249,12 +264,16 @@ def main():
         ws = torch.empty(lib.idx_logits_workspace_bytes(cargs[0]), dtype=torch.uint8, device=dev)
         plan = torch.empty(lib.idx_logits_plan_bytes(wl.B, wl.S_q, wl.S_k), dtype=torch.uint8, device=dev)
 
+        thd = getattr(wl, "thd", None) is not None
+
         def step(i):
             # one whole call through the C ABI: the plan (windows + schedule),
             # the K reorder and the weighted-query pieces share one launch,
-            # then the scoring kernel
+            # then the scoring kernel.  Packed variable-length rows build
+            # their plan with idx_logits_plan_thd first.
+            call_plan = build_plan(lib, wl, d, plan, stream) if thd else None
             lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
-                               sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2],
+                               sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], plan=call_plan,
                                q_causal_offsets=d["offsets"], row_starts=d["starts"], row_ends=d["ends"],
                                workspace=ws, stream=stream)
 
@@ -280,8 +299,7 @@ def main():
         # the scoring kernel alone: a plan and a prepared workspace, then
         # `steps` launches back to back on the stream the library launches on,
         # between two events
-        lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
-                            row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
+        build_plan(lib, wl, d, plan, stream)
         lib.idx_logits_prepare(cargs[0], ws, stream=stream)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
@@ -332,6 +350,11 @@ def main():
                      "kernel": "score_kernel", "kernel_us": round(kern_us, 2),
                      "flop_per_launch": flops, "algorithmic_bytes_per_launch": input_bytes(wl) + out_bytes(wl, V)},
     }
+    if getattr(wl, "thd", None) is not None:
+        cq = [int(x) for x in wl.thd["cu_q"]]
+        res["config"]["thd"] = {"segments": len(cq) - 1, "seg_lens": [b - a for a, b in zip(cq, cq[1:])],
+                                "ratio": wl.thd["ratio"], "m_total": wl.S_k}
+        res["config"]["plan"] = "idx_logits_plan_thd in every step"
     zero_name = args.workload + "_zero"
     if not args.no_zero_variant and zero_name in W.NAMED:
         zwl, zV, zus, zk = measure(zero_name)

@@ -135,6 +135,32 @@ idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
                              const int32_t* row_ends, void* plan, size_t plan_bytes, void* stream);
 
 /*
+ * Build a plan for packed variable-length rows over ratio-compressed keys
+ * (the THD layout of cudnn-frontend pull request 416, THD/varlen commit): the
+ * query tokens of n_seg segments are packed into T_q rows and their
+ * compressed keys into m_total columns, and every row's window is absolute.
+ *
+ *  cu_seqlens_q  int32 [n_seg + 1] device array, non-decreasing: segment s
+ *                holds rows [cu_seqlens_q[s], cu_seqlens_q[s+1]).
+ *  cu_seqlens_k  int32 [n_seg + 1] device array, non-decreasing: segment s
+ *                holds keys [cu_seqlens_k[s], cu_seqlens_k[s+1]).
+ *  ratio         query tokens per compressed key, >= 1.
+ *
+ * Local row t of segment s sees [cu_seqlens_k[s], cu_seqlens_k[s] + v) with
+ * v = floor((t + 1) / ratio), never past cu_seqlens_k[s+1] (segment isolation
+ * and the ratio-causal mask together; the page gives the window start and
+ * calls its length the visible count, this is the reading taken).  Windows
+ * are clamped to [0, m_total] in 64-bit integers; rows outside every segment
+ * see nothing.  The boundary arrays are not inspected on the host; arrays
+ * that are not non-decreasing give clamped, in-bounds but unspecified
+ * windows.  The plan serves idx_logits_run and idx_logits_score with B = 1,
+ * S_q = T_q and S_k = m_total (plan buffer as for idx_logits_plan).
+ */
+idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t ratio, int32_t T_q, int32_t m_total, int32_t H, int32_t D, void* plan,
+                                 size_t plan_bytes, void* stream);
+
+/*
  * Device workspace bytes a call to idx_logits_run needs; 0 for invalid
  * arguments.  It covers the plan when the call builds it (plan == NULL) and,
  * for FP8, MXFP8 and MXFP4 inputs, the per-call weighted-query pieces: those

@@ -22,7 +22,8 @@ LIB_PATH = os.path.join(_PKG, "libidx_logits.so")
 IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_workspace_bytes",
+EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
+            "idx_logits_workspace_bytes",
             "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_plan_bytes.argtypes = [I32] * 5
         L.idx_logits_plan.restype = ctypes.c_int
         L.idx_logits_plan.argtypes = [I32] * 5 + [P, P, P, P, SZ, P]
+        L.idx_logits_plan_thd.restype = ctypes.c_int
+        L.idx_logits_plan_thd.argtypes = [I32, P, P] + [I32] * 5 + [P, SZ, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
@@ -123,6 +126,27 @@ def idx_logits_plan(B: int, S_q: int, S_k: int, H: int = 64, D: int = 128, *, q_
     _check("idx_logits_plan", lib().idx_logits_plan(B, S_q, S_k, H, D, _ptr(offs), _ptr(st), _ptr(en), _ptr(plan),
                                                       plan.numel() * plan.element_size(), _stream(stream, device)))
     plan._idx_keep = (offs, st, en)  # keep the window inputs alive until the stream has used them
+    return plan
+
+
+def idx_logits_plan_thd(cu_seqlens_q, cu_seqlens_k, ratio: int, T_q: int, m_total: int, H: int = 64,
+                        D: int = 128, *, plan: Optional[torch.Tensor] = None, device=None,
+                        stream=None) -> torch.Tensor:
+    """Plan for packed variable-length rows over ratio-compressed keys (B = 1,
+    S_q = T_q, S_k = m_total); returns the uint8 plan tensor."""
+    device = torch.device(device if device is not None else (plan.device if plan is not None else "cuda"))
+    nbytes = idx_logits_plan_bytes(1, T_q, m_total, H, D)
+    if plan is None:
+        plan = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    cq = _dev_i32(cu_seqlens_q, device)
+    ck = _dev_i32(cu_seqlens_k, device)
+    if cq is None or ck is None or cq.numel() != ck.numel() or cq.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need n_seg + 1 >= 2 entries each")
+    _check("idx_logits_plan_thd", lib().idx_logits_plan_thd(cq.numel() - 1, _ptr(cq), _ptr(ck), int(ratio), T_q,
+                                                              m_total, H, D, _ptr(plan),
+                                                              plan.numel() * plan.element_size(),
+                                                              _stream(stream, device)))
+    plan._idx_keep = (cq, ck)
     return plan
 
 

@@ -34,10 +34,22 @@ def compile_flags() -> list[str]:
             "-munsafe-fp-atomics"]
 
 
+# Per-source additions.  The BF16 scoring kernel runs one wave per SIMD with
+# more live values than 256 VGPRs; by default the compiler then keeps the MFMA
+# accumulators in AGPRs, and every epilogue read of them costs a copy to a
+# VGPR.  Forcing the accumulators into VGPRs moves other values (MFMA operands,
+# which can be read from AGPRs) there instead.
+EXTRA_FLAGS = {"score_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def flags_for(src: str) -> list[str]:
+    return compile_flags() + EXTRA_FLAGS.get(os.path.basename(src), [])
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *compile_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags_for(src), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

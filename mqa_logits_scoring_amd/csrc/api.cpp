@@ -93,6 +93,25 @@ idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
   return IDX_OK;
 }
 
+idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                 int32_t ratio, int32_t T_q, int32_t m_total, int32_t H, int32_t D, void* plan,
+                                 size_t plan_bytes, void* stream) {
+  idx_status_t st = check_dims(1, T_q, m_total, H, D);
+  if (st != IDX_OK) return st;
+  if (n_seg <= 0) return fail(IDX_E_INVALID, "n_seg must be positive (got %d)", n_seg);
+  if (ratio <= 0) return fail(IDX_E_INVALID, "ratio must be positive (got %d)", ratio);
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+    return fail(IDX_E_INVALID, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
+  const size_t need = idx::plan_layout(1, T_q).total;
+  if (plan_bytes < need) return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
+  hipError_t e = idx::launch_plan_thd(n_seg, cu_seqlens_q, cu_seqlens_k, ratio, T_q, m_total, H, D, plan,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
 size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) {
   if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return 0;
   const idx_in_t f = a->in_dtype;

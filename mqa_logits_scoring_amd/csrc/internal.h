@@ -199,6 +199,10 @@ struct ScoreArgs {
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream);
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream);
+// Plan of packed variable-length rows over ratio-compressed keys (B = 1).
+hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu_k, int32_t ratio, int32_t T_q,
+                           int32_t m_total, int32_t H, int32_t D, void* plan, hipStream_t stream);
+
 // What a call that builds its own plan passes to the preparation launch.
 struct PlanBuild {
   int32_t B, S_q, S_k, H, D;

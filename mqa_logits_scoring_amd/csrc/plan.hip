@@ -23,8 +23,36 @@ __global__ void copy_windows_kernel(const unsigned char* plan, int64_t n_rows, s
 
 hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* offsets,
                        const int32_t* starts, const int32_t* ends, void* plan, hipStream_t stream) {
-  const PlanParams P{B, S_q, S_k, H, D, offsets, starts, ends, static_cast<unsigned char*>(plan), plan_layout(B, S_q)};
+  PlanParams P{};
+  P.B = B;
+  P.S_q = S_q;
+  P.S_k = S_k;
+  P.H = H;
+  P.D = D;
+  P.offsets = offsets;
+  P.starts = starts;
+  P.ends = ends;
+  P.plan = static_cast<unsigned char*>(plan);
+  P.L = plan_layout(B, S_q);
   hipLaunchKernelGGL(plan_kernel, dim3(unsigned(plan_segments(B, S_q))), dim3(kSortThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu_k, int32_t ratio, int32_t T_q,
+                           int32_t m_total, int32_t H, int32_t D, void* plan, hipStream_t stream) {
+  PlanParams P{};
+  P.B = 1;
+  P.S_q = T_q;
+  P.S_k = m_total;
+  P.H = H;
+  P.D = D;
+  P.plan = static_cast<unsigned char*>(plan);
+  P.L = plan_layout(1, T_q);
+  P.cu_q = cu_q;
+  P.cu_k = cu_k;
+  P.n_seg = n_seg;
+  P.ratio = ratio;
+  hipLaunchKernelGGL(plan_kernel, dim3(unsigned(plan_segments(1, T_q))), dim3(kSortThreads), 0, stream, P);
   return hipGetLastError();
 }
 

@@ -32,7 +32,36 @@ struct PlanParams {
   const int32_t* ends;
   unsigned char* plan;
   PlanLayout L;
+  // packed variable-length rows over ratio-compressed keys (B = 1): segment
+  // boundaries in rows and in keys, n_seg + 1 each; cu_q == nullptr otherwise
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t n_seg, ratio;
 };
+
+// Window of packed row i: segment s (the last with cu_q[s] <= i, found by
+// binary search), local row t = i - cu_q[s], keys [cu_k[s], cu_k[s] +
+// floor((t + 1) / ratio)) cut at cu_k[s+1]; rows outside every segment see
+// nothing.  Clamping to [0, S_k] is left to the caller.
+__device__ inline void thd_window(const PlanParams& P, int64_t i, int64_t& s, int64_t& e) {
+  s = 0;
+  e = 0;
+  if (P.n_seg <= 0 || i < P.cu_q[0]) return;
+  int lo = 0, hi = P.n_seg - 1;  // largest seg with cu_q[seg] <= i
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.cu_q[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  if (i >= P.cu_q[lo + 1]) return;
+  const int64_t t = i - P.cu_q[lo];
+  s = P.cu_k[lo];
+  e = s + (t + 1) / P.ratio;
+  const int64_t lim = P.cu_k[lo + 1];
+  if (e > lim) e = lim;
+}
 
 // Shared memory one segment needs (8-byte aligned).
 struct PlanSmem {
@@ -77,7 +106,11 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
   const int64_t b = segment / spb, seg = segment % spb;
   const int64_t i0 = seg * kSortRows;
   const int n = int(min(int64_t(kSortRows), int64_t(S_q) - i0));
-  const bool explicit_windows = starts != nullptr && ends != nullptr;
+  // Packed variable-length rows keep their order: consecutive rows of a
+  // segment see nearly the same keys already, and the first rows of every
+  // segment (empty windows) would otherwise force a full sort.
+  const bool thd = P.cu_q != nullptr;
+  const bool explicit_windows = !thd && starts != nullptr && ends != nullptr;
   int shift = 0;
   while ((int64_t(S_k) >> shift) >= (int64_t(1) << 27)) ++shift;
   const int64_t slot0 = b * tpb * kTileRows;
@@ -86,7 +119,11 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
     if (r < n) {
       const int64_t i = i0 + r, row = b * S_q + i;
       int64_t s, e;
-      if (explicit_windows) {
+      if (thd) {
+        thd_window(P, i, s, e);
+        s = s < 0 ? 0 : (s > S_k ? S_k : s);
+        e = e < s ? s : (e > S_k ? S_k : e);
+      } else if (explicit_windows) {
         s = starts[row];
         e = ends[row];
         s = s < 0 ? 0 : (s > S_k ? S_k : s);

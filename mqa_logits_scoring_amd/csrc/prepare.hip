@@ -227,8 +227,17 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
                           const PlanBuild* build, hipStream_t stream) {
   PrepArgs a{};
   if (build != nullptr) {
-    a.plan = PlanParams{build->B, build->S_q, build->S_k, build->H, build->D, build->offsets, build->starts,
-                        build->ends, build->plan, plan_layout(build->B, build->S_q)};
+    a.plan = PlanParams{};
+    a.plan.B = build->B;
+    a.plan.S_q = build->S_q;
+    a.plan.S_k = build->S_k;
+    a.plan.H = build->H;
+    a.plan.D = build->D;
+    a.plan.offsets = build->offsets;
+    a.plan.starts = build->starts;
+    a.plan.ends = build->ends;
+    a.plan.plan = build->plan;
+    a.plan.L = plan_layout(build->B, build->S_q);
     a.n_plan = plan_segments(build->B, build->S_q);
   }
   a.k = static_cast<const unsigned char*>(k);

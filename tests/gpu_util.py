@@ -31,6 +31,9 @@ def dev_inputs(wl, device=DEV) -> dict:
     d["offsets"] = None if wl.offsets is None else torch.from_numpy(np.asarray(wl.offsets, np.int32)).to(device)
     d["starts"] = None if wl.starts is None else torch.from_numpy(np.asarray(wl.starts, np.int32)).to(device)
     d["ends"] = None if wl.ends is None else torch.from_numpy(np.asarray(wl.ends, np.int32)).to(device)
+    if getattr(wl, "thd", None) is not None:
+        d["cu_q"] = torch.from_numpy(np.asarray(wl.thd["cu_q"], np.int32)).to(device)
+        d["cu_k"] = torch.from_numpy(np.asarray(wl.thd["cu_k"], np.int32)).to(device)
     return d
 
 
@@ -39,12 +42,18 @@ def out_dtype(wl):
 
 
 def make_plan(wl, d):
+    if getattr(wl, "thd", None) is not None:
+        return lib.idx_logits_plan_thd(d["cu_q"], d["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k, wl.H, wl.D,
+                                       device=d["q"].device)
     return lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
                                row_starts=d["starts"], row_ends=d["ends"], device=d["q"].device)
 
 
 def run(wl, d, plan=None, out=None, clean=None):
-    """One library call; plan None builds the plan inside the call."""
+    """One library call; plan None builds the plan inside the call (packed
+    variable-length workloads build theirs with idx_logits_plan_thd first)."""
+    if plan is None and getattr(wl, "thd", None) is not None:
+        plan = make_plan(wl, d)
     return lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
                               sm_scale=wl.sm_scale, clean_logits=wl.clean if clean is None else clean, out=out,
                               out_dtype=out_dtype(wl), plan=plan, q_causal_offsets=d["offsets"],

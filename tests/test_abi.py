@@ -118,3 +118,15 @@ def test_prepare_and_score_need_buffers():
     assert "plan" in lib.idx_last_error()
     assert L.idx_logits_score(ctypes.byref(a), FAKE + 8, FAKE, 1 << 30, None) == lib.IDX_E_INVALID
     assert L.idx_logits_score(ctypes.byref(a), FAKE, None, 0, None) == lib.IDX_E_WORKSPACE
+
+
+def test_plan_thd_rejects():
+    L = lib.lib()
+    assert L.idx_logits_plan_thd(0, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 0, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_thd(2, None, FAKE, 2, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 32, 128, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 0, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE, 8, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID

@@ -3,6 +3,9 @@ the exact relations the method fixes between GPU runs."""
 
 import math
 
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -250,7 +253,7 @@ def test_plan_dimension_mismatch_is_loud():
 # -inf placement of every row, and plan / no-plan equality
 # ---------------------------------------------------------------------------
 
-NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5"]
+NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5", "thd_bf16_r4"]
 
 
 @pytest.mark.parametrize("name", NAMED)
@@ -289,6 +292,51 @@ def test_reordered_plan_several_segments(fmt):
     got = to_f64(out).reshape(wl.B * wl.S_q, wl.S_k)
     compare_rows(wl, got, ref.reshape(wl.B * wl.S_q, wl.S_k), bound.reshape(wl.B * wl.S_q, wl.S_k),
                  what=f"reordered {fmt}")
+
+
+# ---------------------------------------------------------------------------
+# packed variable-length rows over ratio-compressed keys
+# ---------------------------------------------------------------------------
+
+THD_CASES = [((5, 7), 2), ((9,), 1), ((1027, 3003, 4162), 4), ((0, 13, 0, 40, 1, 22), 3), ((300, 2, 700), 7),
+             ((2048,), 4), ((33, 64, 95, 128, 1), 1)]
+
+
+@pytest.mark.parametrize("lens,ratio", THD_CASES, ids=[f"{len(l)}seg-r{r}" for l, r in THD_CASES])
+def test_thd_plan_windows_match_oracle(lens, ratio):
+    wl = W.make_thd("bf16", lens, ratio, H=64, D=128, seed=1)
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    ws, we = lib.idx_logits_plan_windows(plan, 1, wl.S_q, wl.S_k)
+    ows, owe = oracle.windows(wl)
+    assert np.array_equal(ws.cpu().numpy(), ows) and np.array_equal(we.cpu().numpy(), owe)
+
+
+def test_thd_plan_golden_windows():
+    """The hand-worked cases, including key counts that disagree with the rows and rows
+    past the last segment."""
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "thd_windows.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        plan = lib.idx_logits_plan_thd(c["cu_q"], c["cu_k"], c["ratio"], c["T_q"], c["m_total"])
+        ws, we = lib.idx_logits_plan_windows(plan, 1, c["T_q"], c["m_total"])
+        assert ws.cpu().reshape(-1).tolist() == c["starts"] and we.cpu().reshape(-1).tolist() == c["ends"], c["what"]
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_thd_scores_match_oracle(fmt):
+    wl = W.make_thd(fmt, (37, 0, 300, 90, 1), 2, seed=9, w_dtype="bf16", out_dtype="bf16" if fmt == "mxfp4" else "f32")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    ref, bound = oracle.logits(wl)
+    compare_rows(wl, to_f64(out).reshape(wl.S_q, wl.S_k), ref, bound, what=f"thd {fmt}")
+
+
+def test_thd_plan_rejects():
+    with pytest.raises(lib.IdxError):
+        lib.idx_logits_plan_thd([0, 4], [0, 2], 0, 4, 2)
+    with pytest.raises(lib.IdxError):
+        lib.idx_logits_plan_thd([0, 4], [0, 2], 2, 4, 2, H=32)
 
 
 def test_mx_block_layout_probes():

@@ -35,7 +35,7 @@ SCORE_SOURCES = ["score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mx
 
 def device_asm(src: str, out_dir: str) -> str:
     out = os.path.join(out_dir, src + ".s")
-    cmd = [hip_build.hipcc(), *hip_build.compile_flags(), "--cuda-device-only", "-S",
+    cmd = [hip_build.hipcc(), *hip_build.flags_for(src), "--cuda-device-only", "-S",
            os.path.join(hip_build.CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, f"{' '.join(cmd)}\n{r.stderr}"
