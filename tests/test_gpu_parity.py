@@ -339,6 +339,52 @@ def test_thd_plan_rejects():
         lib.idx_logits_plan_thd([0, 4], [0, 2], 2, 4, 2, H=32)
 
 
+@pytest.mark.parametrize("sm_scale", [-0.7, 0.0, 1e-30, 3e4])
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_sm_scale_sign_and_size(fmt, sm_scale):
+    """sm_scale multiplies after the head-sum, whatever its sign or size: a negative one
+    flips every score, zero gives exact zeros inside the windows."""
+    wl = W.make_random(fmt, 1, 19, 130, seed=31, sm_scale=sm_scale, windows="irregular")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    ref, bound = oracle.logits(wl)
+    got = to_f64(out).reshape(wl.S_q, wl.S_k)
+    compare_rows(wl, got, ref, bound, what=f"sm_scale {sm_scale}")
+    if sm_scale == 0.0:
+        inside = ~np.isneginf(ref)
+        assert np.all(got[inside] == 0.0)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_extreme_block_scales(fmt):
+    """E8M0 exponents spread over +-30 around 1 (products of Q and K scales span 2^-60..2^60):
+    the MFMA block scales, the weighted-query pieces and the epilogue stay within tolerance."""
+    wl = W.make_random(fmt, 1, 24, 200, seed=32, scale_lo=-30, scale_hi=30, windows="irregular")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    ref, bound = oracle.logits(wl)
+    compare_rows(wl, to_f64(out).reshape(wl.S_q, wl.S_k), ref, bound, what=f"extreme scales {fmt}")
+
+
+def test_fp8_row_scale_extremes():
+    """FP8 per-row K scales of 0, tiny and huge values (finite and >= 0 as required)."""
+    wl = W.make_random("fp8", 1, 16, 96, seed=33, windows="irregular")
+    ks = wl.k_scale.copy()
+    ks[0, ::7] = 0.0
+    ks[0, 1::7] = 1e-20
+    ks[0, 2::7] = 1e20
+    wl = wl.replace(k_scale=ks)
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    ref, bound = oracle.logits(wl)
+    got = to_f64(out).reshape(wl.S_q, wl.S_k)
+    compare_rows(wl, got, ref, bound, what="fp8 row scale extremes")
+    inside = ~np.isneginf(ref)
+    zero_cols = np.zeros(wl.S_k, bool)
+    zero_cols[::7] = True
+    assert np.all(got[inside & zero_cols[None, :]] == 0.0)
+
+
 def test_mx_block_layout_probes():
     """The oracle's MX layout probes (one d-block populated, one scale byte raised,
     nibble order) run on the GPU: within tolerance of the oracle for every variant."""
