@@ -53,6 +53,10 @@ class Oracle:
         lib.oracle_windows.restype = None
         lib.oracle_windows_thd.argtypes = [ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
         lib.oracle_windows_thd.restype = None
+        lib.oracle_gather_paged.argtypes = [ctypes.c_int] * 4 + [P] * 4 + [ctypes.c_int] * 2 + [P] * 2
+        lib.oracle_gather_paged.restype = None
+        lib.oracle_windows_paged.argtypes = [ctypes.c_int] * 3 + [P] * 3
+        lib.oracle_windows_paged.restype = None
         lib.oracle_mqa_logits.argtypes = ([ctypes.c_int] * 6 + [P] * 5 + [ctypes.c_int, ctypes.c_double]
                                           + [P, P, P, ctypes.c_int64, P, P, ctypes.c_int])
         lib.oracle_mqa_logits.restype = ctypes.c_int
@@ -79,8 +83,36 @@ class Oracle:
                                     _ptr(we))
         return ws, we
 
+    def gather_paged(self, wl):
+        """The dense K ([B, S_k, row bytes] codes) and K scales of a paged workload."""
+        pg = wl.paged
+        cache = np.ascontiguousarray(pg["k_cache"])
+        row_bytes = cache.dtype.itemsize * int(np.prod(cache.shape[2:]))
+        scache = None if pg["k_scale_cache"] is None else np.ascontiguousarray(pg["k_scale_cache"])
+        scale_bytes = 0 if scache is None else scache.dtype.itemsize
+        k = np.empty((wl.B, wl.S_k) + cache.shape[2:], cache.dtype)
+        ks = None if scache is None else np.empty((wl.B, wl.S_k), scache.dtype)
+        bt = np.ascontiguousarray(pg["block_table"], np.int32)
+        ctx = np.ascontiguousarray(pg["ctx"], np.int32)
+        self.lib.oracle_gather_paged(wl.B, wl.S_k, row_bytes, scale_bytes, _ptr(cache), _ptr(scache), _ptr(bt),
+                                     _ptr(ctx), int(pg["page_size"]), bt.shape[1], _ptr(k), _ptr(ks))
+        return k, ks
+
+    def dense(self, wl):
+        """A paged workload with its K gathered (windows still from the context lengths)."""
+        if getattr(wl, "paged", None) is None:
+            return wl
+        k, ks = self.gather_paged(wl)
+        return wl.replace(k=k, k_scale=ks)
+
     def windows(self, wl) -> tuple[np.ndarray, np.ndarray]:
         """Per-row [start, end) of a workload as int32 [B, S_q] arrays."""
+        if getattr(wl, "paged", None) is not None:
+            ws = np.empty((wl.B, wl.S_q), np.int32)
+            we = np.empty((wl.B, wl.S_q), np.int32)
+            ctx = np.ascontiguousarray(wl.paged["ctx"], np.int32)
+            self.lib.oracle_windows_paged(wl.B, wl.S_q, wl.S_k, _ptr(ctx), _ptr(ws), _ptr(we))
+            return ws, we
         if getattr(wl, "thd", None) is not None:
             assert wl.B == 1
             ws, we = self.windows_thd(wl.thd["cu_q"], wl.thd["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k)
@@ -99,6 +131,7 @@ class Oracle:
         rows: global row ids b*S_q+i to evaluate (None: all rows).  Returns
         (ref, bound) as float64 [n_rows, S_k] (and the thread count if asked)."""
         ws, we = self.windows(wl)
+        wl = self.dense(wl)
         if rows is None:
             n_rows, rows_arr = wl.B * wl.S_q, None
         else:

@@ -174,6 +174,58 @@ void oracle_windows_thd(int n_seg, const int32_t* cu_q, const int32_t* cu_k, int
   }
 }
 
+/*
+ * Paged keys (decode): request b holds ctx[b] keys in pages of page_size
+ * rows; its logical key j is row j % page_size of physical page
+ * block_table[b * max_pages + j / page_size].  The pages name paged MQA
+ * logits (DeepGEMM pull request 435, Validation section: the paged test
+ * shares the scoring core) without printing the layout; this is the plainest
+ * one, and the windows follow: query token i of the request's S_q newest
+ * tokens sees [0, ctx - S_q + i + 1), clamped to [0, S_k] (ctx itself clamped
+ * to [0, S_k]).
+ *
+ * oracle_gather_paged writes the dense K of every request ([B, S_k] rows of
+ * row_bytes, and its per-row scale words when scale_bytes > 0), zero past the
+ * request's keys.
+ */
+void oracle_gather_paged(int B, int S_k, int row_bytes, int scale_bytes, const uint8_t* k_cache,
+                         const uint8_t* k_scale_cache, const int32_t* block_table, const int32_t* ctx,
+                         int page_size, int max_pages, uint8_t* k_out, uint8_t* k_scale_out) {
+  for (int b = 0; b < B; ++b) {
+    int64_t n = ctx[b];
+    if (n < 0) n = 0;
+    if (n > S_k) n = S_k;
+    for (int64_t j = 0; j < S_k; ++j) {
+      uint8_t* dst = k_out + ((int64_t)b * S_k + j) * row_bytes;
+      uint8_t* sdst = scale_bytes ? k_scale_out + ((int64_t)b * S_k + j) * scale_bytes : 0;
+      if (j < n) {
+        const int64_t page = block_table[(int64_t)b * max_pages + j / page_size];
+        const int64_t row = page * page_size + j % page_size;
+        memcpy(dst, k_cache + row * row_bytes, (size_t)row_bytes);
+        if (scale_bytes) memcpy(sdst, k_scale_cache + row * scale_bytes, (size_t)scale_bytes);
+      } else {
+        memset(dst, 0, (size_t)row_bytes);
+        if (scale_bytes) memset(sdst, 0, (size_t)scale_bytes);
+      }
+    }
+  }
+}
+
+void oracle_windows_paged(int B, int S_q, int S_k, const int32_t* ctx, int32_t* win_start, int32_t* win_end) {
+  for (int b = 0; b < B; ++b) {
+    int64_t n = ctx[b];
+    if (n < 0) n = 0;
+    if (n > S_k) n = S_k;
+    for (int i = 0; i < S_q; ++i) {
+      int64_t e = n - S_q + i + 1;
+      if (e < 0) e = 0;
+      if (e > S_k) e = S_k;
+      win_start[(int64_t)b * S_q + i] = 0;
+      win_end[(int64_t)b * S_q + i] = (int32_t)e;
+    }
+  }
+}
+
 /* Dequantised K of one batch: Kd[j*D + d] and |Kd[j]|_2 in kn[j]. */
 static void dequant_k(int fmt, int S_k, int D, const uint8_t* kb, const void* k_scale_b, double* Kd,
                       double* kn) {

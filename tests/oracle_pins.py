@@ -482,6 +482,65 @@ def pin_windows_thd_isolation(orc):
         assert np.all(np.isneginf(outside))
 
 
+def pin_paged_identity(orc):
+    """Pages laid out in order (request b owns pages b*max_pages..) with every context full:
+    the gathered K is the cache read straight through, and the scores equal those of the
+    dense workload with causal offset 0 (row i sees [0, S_k - S_q + i + 1))."""
+    for fmt in W.FORMATS:
+        B, n, ps, S_k = 3, 4, 16, 80
+        wl = W.make_paged(fmt, B, n, [S_k] * B, ps, extra_pages=0, seed=5)
+        mp = wl.paged["block_table"].shape[1]
+        wl.paged["block_table"] = np.arange(B * mp, dtype=np.int32).reshape(B, mp)
+        k, ks = orc.gather_paged(wl)
+        assert np.array_equal(k.reshape(-1), wl.paged["k_cache"].reshape(-1))
+        dense = wl.replace(paged=None, k=k, k_scale=ks, offsets=np.zeros(B, np.int32))
+        a, _ = full(orc, wl)
+        b, _ = full(orc, dense)
+        assert np.array_equal(a, b)
+
+
+def pin_paged_relabel_and_unused(orc):
+    """Renumbering the physical pages (block table relabelled to match) changes nothing,
+    and neither do cache rows no request can see (unused pages, rows past a context)."""
+    wl = W.make_paged("mxfp8", 3, 2, [37, 0, 64], 16, S_k=64, extra_pages=4, seed=6)
+    base, _ = full(orc, wl)
+    pg = wl.paged
+    k, ks = orc.gather_paged(wl)  # the gather itself never reads past a context: zeros there
+    for b, n in enumerate(pg["ctx"]):
+        assert np.all(k[b, n:] == 0) and np.all(ks[b, n:] == 0)
+    n_pages = pg["k_cache"].shape[0]
+    relabel = np.random.default_rng(1).permutation(n_pages)
+    inv = np.argsort(relabel)
+    moved = dict(pg, k_cache=pg["k_cache"][inv], k_scale_cache=pg["k_scale_cache"][inv],
+                 block_table=relabel[pg["block_table"]].astype(np.int32))
+    a, _ = full(orc, wl.replace(paged=moved))
+    assert np.array_equal(a, base)
+    noisy = dict(pg, k_cache=pg["k_cache"].copy(), k_scale_cache=pg["k_scale_cache"].copy())
+    used = set()
+    for b in range(3):
+        for j in range(int(pg["ctx"][b])):
+            used.add((int(pg["block_table"][b, j // 16]), j % 16))
+    for page in range(n_pages):
+        for r in range(16):
+            if (page, r) not in used:
+                noisy["k_cache"][page, r] ^= 0x11
+                noisy["k_scale_cache"][page, r] ^= 0x01010101
+    a, _ = full(orc, wl.replace(paged=noisy))
+    assert np.array_equal(a, base)
+
+
+def pin_paged_windows(orc):
+    """Context windows: the newest S_q tokens of a request with ctx keys see
+    [0, ctx - S_q + i + 1); ctx past S_k is clamped; a context shorter than S_q leaves the
+    first rows empty; they equal the causal offsets ctx - S_k of the dense path."""
+    wl = W.make_paged("bf16", 4, 3, [50, 80, 2, 0], 8, S_k=50, H=1, D=2)
+    ws, we = orc.windows(wl)
+    assert np.all(ws == 0)
+    assert we.tolist() == [[48, 49, 50], [48, 49, 50], [0, 1, 2], [0, 0, 0]]
+    dense = W.make_random("bf16", 4, 3, 50, H=1, D=2, offsets=[0, 0, 2 - 50, 0 - 50])
+    assert np.array_equal(orc.windows(dense)[1], we)
+
+
 def pin_empty_and_batch(orc):
     """Empty windows are all -inf; each batch's slice equals a B=1 run on that batch alone."""
     for fmt in W.FORMATS:

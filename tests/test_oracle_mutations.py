@@ -37,6 +37,10 @@ MUTANTS = [
     ("w_bf16_read_as_f32", "(w_fmt == OR_W_F32)", "(1)", 0),
     ("dot_not_reset", "for (int h = 0; h < H; ++h) dot[h] = 0.0;", "", 0),
     ("bound_without_k_norm", "fabs(sm_scale) * kn[(size_t)b * S_k + j] * bs", "fabs(sm_scale) * bs", 0),
+    ("paged_row_in_page", "row = page * page_size + j % page_size;", "row = page * page_size + j / page_size;", 0),
+    ("paged_request_ignored", "block_table[(int64_t)b * max_pages + j / page_size]", "block_table[j / page_size]", 0),
+    ("paged_window_off_by_one", "int64_t e = n - S_q + i + 1;", "int64_t e = n - S_q + i;", 0),
+    ("paged_context_not_cut", "if (j < n) {", "if (j < S_k) {", 0),
     ("thd_visible_off_by_one", "e = s + (t + 1) / ratio", "e = s + t / ratio", 0),
     ("thd_visible_ceil", "e = s + (t + 1) / ratio", "e = s + (t + ratio) / ratio", 0),
     ("thd_no_segment_clamp", "if (e > lim) e = lim;", "", 0),

@@ -80,6 +80,11 @@ class Workload:
     # int32 arrays cu_q, cu_k (segment boundaries in rows and in keys) and the
     # int ratio; the windows then come from these instead of offsets / starts
     thd: Optional[dict] = None
+    # paged keys (decode), k and k_scale then None: dict with k_cache
+    # [num_pages, page_size, row], k_scale_cache [num_pages, page_size] or
+    # None, block_table int32 [B, max_pages], ctx int32 [B] (keys each request
+    # holds) and page_size; S_k is the widest context the output covers
+    paged: Optional[dict] = None
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -276,6 +281,36 @@ def make_thd(fmt: str, seg_lens, ratio: int, *, w_dtype: str = "f32", out_dtype:
                      clean=clean, seed=seed, name=name, **kw)
     return wl.replace(offsets=None, starts=None, ends=None,
                       thd={"cu_q": cu_q, "cu_k": cu_k, "ratio": int(ratio)})
+
+
+def make_paged(fmt: str, B: int, next_n: int, ctx_lens, page_size: int, *, S_k: Optional[int] = None,
+               extra_pages: int = 3, w_dtype: str = "f32", out_dtype: str = "f32", sm_scale: float = 1.0,
+               clean: bool = True, seed: int = 0, name: str = "paged", **kw) -> Workload:
+    """Decode-style workload over a paged K cache: B requests, each scoring its
+    next_n newest query tokens against the ctx_lens[b] keys it holds in pages of
+    page_size rows.  Every request owns ceil(S_k / page_size) logical pages
+    (S_k defaults to the longest context); the physical pages are a seeded
+    shuffle of all num_pages = B * max_pages + extra_pages pages, so pages are
+    scattered and some are unused.  Values as make_random."""
+    ctx = np.asarray(ctx_lens, np.int32).reshape(B)
+    if S_k is None:
+        S_k = max(int(ctx.max()), 1)
+    max_pages = (S_k + page_size - 1) // page_size
+    num_pages = B * max_pages + extra_pages
+    base = make_random(fmt, 1, B * next_n, num_pages * page_size, w_dtype=w_dtype, out_dtype=out_dtype,
+                       sm_scale=sm_scale, clean=clean, seed=seed, name=name, **kw)
+    rng = np.random.default_rng(seed + 1000)
+    perm = rng.permutation(num_pages).astype(np.int32)
+    block_table = perm[: B * max_pages].reshape(B, max_pages)
+    q = base.q.reshape((B, next_n) + base.q.shape[2:])
+    k_cache = base.k.reshape((num_pages, page_size) + base.k.shape[2:])
+    k_scale_cache = None if base.k_scale is None else base.k_scale.reshape(num_pages, page_size)
+    return Workload(name=name, B=B, S_q=next_n, S_k=S_k, H=base.H, D=base.D, fmt=fmt, w_dtype=w_dtype,
+                    out_dtype=out_dtype, sm_scale=float(sm_scale), clean=clean, q=q,
+                    q_scale=None if base.q_scale is None else base.q_scale.reshape(B, next_n, -1), k=None,
+                    k_scale=None, w=base.w.reshape(B, next_n, -1), offsets=None, starts=None, ends=None, seed=seed,
+                    paged={"k_cache": k_cache, "k_scale_cache": k_scale_cache, "block_table": block_table,
+                           "ctx": ctx, "page_size": int(page_size)})
 
 
 # --------------------------------------------------------------------------
