@@ -141,6 +141,13 @@ def device_inputs(wl, dev) -> dict:
     if getattr(wl, "thd", None) is not None:
         d["cu_q"] = t(np.asarray(wl.thd["cu_q"], np.int32))
         d["cu_k"] = t(np.asarray(wl.thd["cu_k"], np.int32))
+    if getattr(wl, "paged", None) is not None:
+        import mqa_logits_scoring_amd as lib
+        pg = wl.paged
+        d["k_cache"], d["k_scale_cache"] = t(pg["k_cache"]), t(pg["k_scale_cache"])
+        d["block_table"] = t(np.asarray(pg["block_table"], np.int32))
+        d["ctx"] = t(np.asarray(pg["ctx"], np.int32))
+        d["kv"] = lib.make_paged_k(d["k_cache"], d["block_table"], d["ctx"], d["k_scale_cache"])
     return d
 
 
@@ -150,6 +157,8 @@ def build_plan(lib, wl, d, plan, stream):
     if getattr(wl, "thd", None) is not None:
         return lib.idx_logits_plan_thd(d["cu_q"], d["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k, wl.H, wl.D, plan=plan,
                                        stream=stream)
+    if getattr(wl, "paged", None) is not None:
+        return lib.idx_logits_plan_paged(wl.B, wl.S_q, wl.S_k, d["ctx"], wl.H, wl.D, plan=plan, stream=stream)
     return lib.idx_logits_plan(wl.B, wl.S_q, wl.S_k, wl.H, wl.D, q_causal_offsets=d["offsets"],
                                row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
 
@@ -169,11 +178,16 @@ def visible_cells(lib, wl, plan) -> int:
 
 
 def input_bytes(wl) -> int:
-    n = wl.q.nbytes + wl.k.nbytes + wl.w.nbytes
-    for a in (wl.q_scale, wl.k_scale):
-        if a is not None:
-            n += a.nbytes
-    return n
+    """Bytes of the inputs a call must read once: for a paged cache, the rows
+    inside the requests' (clamped) contexts."""
+    n = wl.q.nbytes + wl.w.nbytes + (0 if wl.q_scale is None else wl.q_scale.nbytes)
+    if getattr(wl, "paged", None) is not None:
+        pg = wl.paged
+        rows = int(np.clip(np.asarray(pg["ctx"], np.int64), 0, wl.S_k).sum())
+        row_bytes = pg["k_cache"].nbytes // (pg["k_cache"].shape[0] * pg["k_cache"].shape[1])
+        scale_bytes = 0 if pg["k_scale_cache"] is None else pg["k_scale_cache"].dtype.itemsize
+        return n + rows * (row_bytes + scale_bytes)
+    return n + wl.k.nbytes + (0 if wl.k_scale is None else wl.k_scale.nbytes)
 
 
 def out_bytes(wl, V: int) -> int:
@@ -224,7 +238,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c4_mxfp8",
                     help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned, "
-                         "thd_bf16_r4)")
+                         "thd_bf16_r4, paged_mxfp8_decode)")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
                     help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -259,8 +273,13 @@ def main():
         stream = torch.cuda.current_stream(dev)
         odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         outs = [torch.empty((wl.B, wl.S_q, wl.S_k), dtype=odt, device=dev) for _ in range(2)]
-        cargs = [lib.make_args(d["q"], d["k"], d["w"], o, in_dtype=wl.fmt, q_scale=d["q_scale"],
-                               k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
+        paged = getattr(wl, "paged", None) is not None
+        if paged:
+            cargs = [lib.make_paged_args(d["q"], d["w"], o, wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                                         sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
+        else:
+            cargs = [lib.make_args(d["q"], d["k"], d["w"], o, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                                   k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
         ws = torch.empty(lib.idx_logits_workspace_bytes(cargs[0]), dtype=torch.uint8, device=dev)
         plan = torch.empty(lib.idx_logits_plan_bytes(wl.B, wl.S_q, wl.S_k), dtype=torch.uint8, device=dev)
 
@@ -271,7 +290,14 @@ def main():
             # the K reorder and the weighted-query pieces share one launch,
             # then the scoring kernel.  Packed variable-length rows build
             # their plan with idx_logits_plan_thd first.
+            # Paged calls gather their keys through the block table in the
+            # same preparation launch.
             call_plan = build_plan(lib, wl, d, plan, stream) if thd else None
+            if paged:
+                lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                                         sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], workspace=ws,
+                                         stream=stream)
+                return
             lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
                                sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], plan=call_plan,
                                q_causal_offsets=d["offsets"], row_starts=d["starts"], row_ends=d["ends"],
@@ -300,7 +326,10 @@ def main():
         # `steps` launches back to back on the stream the library launches on,
         # between two events
         build_plan(lib, wl, d, plan, stream)
-        lib.idx_logits_prepare(cargs[0], ws, stream=stream)
+        if paged:
+            lib.idx_logits_prepare_paged(cargs[0], d["kv"], ws, stream=stream)
+        else:
+            lib.idx_logits_prepare(cargs[0], ws, stream=stream)
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
@@ -355,6 +384,12 @@ def main():
         res["config"]["thd"] = {"segments": len(cq) - 1, "seg_lens": [b - a for a, b in zip(cq, cq[1:])],
                                 "ratio": wl.thd["ratio"], "m_total": wl.S_k}
         res["config"]["plan"] = "idx_logits_plan_thd in every step"
+    if getattr(wl, "paged", None) is not None:
+        pg = wl.paged
+        res["config"]["paged"] = {"page_size": pg["page_size"], "num_pages": int(pg["k_cache"].shape[0]),
+                                  "max_pages": int(np.asarray(pg["block_table"]).shape[1]),
+                                  "context_keys": int(np.clip(np.asarray(pg["ctx"], np.int64), 0, wl.S_k).sum())}
+        res["config"]["plan"] = "built in every step from the context lengths"
     zero_name = args.workload + "_zero"
     if not args.no_zero_variant and zero_name in W.NAMED:
         zwl, zV, zus, zk = measure(zero_name)

@@ -206,13 +206,70 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
  * w) contents and dimensions; nothing checks that the workspace matches, so
  * a stale one gives wrong scores.  It may be called any number of times on
  * one prepared workspace (another out, sm_scale, clean_logits or out_dtype).
- * Every argument check of idx_logits_run applies to both; a non-OK status
- * means nothing was enqueued.
+ * Every argument check of idx_logits_run applies to both, except that
+ * idx_logits_score reads neither k nor k_scale, which may then be NULL (as
+ * after idx_logits_prepare_paged); a non-OK status means nothing was enqueued.
  */
 idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream);
 
 idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/*
+ * Paged keys (decode).  The pages name paged MQA logits (DeepGEMM pull request
+ * 435, Validation section: the paged test exercises the same scoring core)
+ * without printing a layout; this is the plainest one.  Request b (of B)
+ * holds context_lens[b] keys in pages of page_size rows: its logical key j is
+ * row j % page_size of physical page block_table[b * max_pages + j / page_size].
+ * Its S_q newest query tokens are scored against them: token i sees
+ * [0, ctx - S_q + i + 1) with ctx = clamp(context_lens[b], 0, S_k), where S_k
+ * (the widest context the output covers) must not exceed max_pages * page_size.
+ *
+ *  k_cache        [num_pages, page_size, D] elements (MXFP4: D/2 bytes per
+ *                 row), 16-byte aligned, in the call's in_dtype.
+ *  k_scale_cache  FP8: fp32 [num_pages, page_size]; MX: int32 [num_pages,
+ *                 page_size] packed as k_scale; BF16: NULL.  16-byte aligned.
+ *  block_table    int32 [B, max_pages], device.  Entries for pages past a
+ *                 request's context are never read; the others must lie in
+ *                 [0, num_pages) (out-of-range entries are clamped, giving
+ *                 wrong but in-bounds keys).
+ *  context_lens   int32 [B], device.
+ * All are device memory owned by the caller and are only read.
+ */
+typedef struct {
+  const void* k_cache;
+  const void* k_scale_cache;
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  int32_t num_pages, page_size, max_pages;
+} idx_paged_k_t;
+
+/*
+ * Plan for paged calls: the windows above from context_lens, for the
+ * dimensions (B, S_q, S_k, H, D) of the calls it serves (plan buffer as for
+ * idx_logits_plan).
+ */
+idx_status_t idx_logits_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                                   const int32_t* context_lens, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * idx_logits_prepare for paged keys: the requests' keys are gathered through
+ * the block table into the workspace in fragment order (zero past each
+ * context), so idx_logits_score then scores them like contiguous keys.
+ * a->k and a->k_scale are not used (they may be NULL); every other field and
+ * check of idx_logits_prepare applies, and `kv` is checked as described above.
+ */
+idx_status_t idx_logits_prepare_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * One paged call: idx_logits_prepare_paged then idx_logits_score.  With
+ * plan == NULL the plan is first built from kv->context_lens into the
+ * workspace (idx_logits_workspace_bytes(a) bytes), sharing the preparation
+ * launch; the result is bitwise that of a call with a precomputed plan.
+ */
+idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, const void* plan,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Copy the windows stored in a plan into caller device arrays

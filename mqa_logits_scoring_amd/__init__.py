@@ -23,7 +23,7 @@ IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
-            "idx_logits_workspace_bytes",
+            "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_workspace_bytes",
             "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
@@ -35,6 +35,13 @@ class IdxLogitsArgs(ctypes.Structure):
                 ("w", ctypes.c_void_p), ("w_dtype", ctypes.c_int), ("sm_scale", ctypes.c_float),
                 ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int), ("out_row_stride", ctypes.c_int64),
                 ("clean_logits", ctypes.c_int32)]
+
+
+class IdxPagedK(ctypes.Structure):
+    """Mirror of idx_paged_k_t."""
+    _fields_ = [("k_cache", ctypes.c_void_p), ("k_scale_cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("context_lens", ctypes.c_void_p), ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
 
 
 class IdxError(RuntimeError):
@@ -64,6 +71,12 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_plan.argtypes = [I32] * 5 + [P, P, P, P, SZ, P]
         L.idx_logits_plan_thd.restype = ctypes.c_int
         L.idx_logits_plan_thd.argtypes = [I32, P, P] + [I32] * 5 + [P, SZ, P]
+        L.idx_logits_plan_paged.restype = ctypes.c_int
+        L.idx_logits_plan_paged.argtypes = [I32] * 5 + [P, P, SZ, P]
+        L.idx_logits_prepare_paged.restype = ctypes.c_int
+        L.idx_logits_prepare_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, SZ, P]
+        L.idx_logits_run_paged.restype = ctypes.c_int
+        L.idx_logits_run_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
@@ -255,3 +268,96 @@ def idx_logits_score(args: IdxLogitsArgs, plan: torch.Tensor, workspace: torch.T
     _check("idx_logits_score", lib().idx_logits_score(ctypes.byref(args), _ptr(plan), _ptr(workspace),
                                                         workspace.numel() * workspace.element_size(),
                                                         _stream(stream, workspace.device)))
+
+
+def make_paged_k(k_cache: torch.Tensor, block_table: torch.Tensor, context_lens: torch.Tensor,
+                 k_scale_cache: Optional[torch.Tensor] = None) -> IdxPagedK:
+    """Fill an idx_paged_k_t from device tensors: k_cache [num_pages, page_size,
+    row], block_table int32 [B, max_pages], context_lens int32 [B], k_scale_cache
+    [num_pages, page_size] (FP8 / MX).  The tensors must outlive the calls."""
+    for name, t in (("k_cache", k_cache), ("block_table", block_table), ("context_lens", context_lens),
+                    ("k_scale_cache", k_scale_cache)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if block_table.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_table and context_lens must be int32")
+    kv = IdxPagedK()
+    kv.k_cache, kv.k_scale_cache = _ptr(k_cache), _ptr(k_scale_cache)
+    kv.block_table, kv.context_lens = _ptr(block_table), _ptr(context_lens)
+    kv.num_pages, kv.page_size = k_cache.shape[0], k_cache.shape[1]
+    kv.max_pages = block_table.shape[1]
+    return kv
+
+
+def idx_logits_plan_paged(B: int, S_q: int, S_k: int, context_lens: torch.Tensor, H: int = 64, D: int = 128, *,
+                          plan: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Plan for paged calls (windows from the context lengths)."""
+    device = context_lens.device
+    nbytes = idx_logits_plan_bytes(B, S_q, S_k, H, D)
+    if plan is None:
+        plan = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    ctx = _dev_i32(context_lens, device)
+    _check("idx_logits_plan_paged", lib().idx_logits_plan_paged(B, S_q, S_k, H, D, _ptr(ctx), _ptr(plan),
+                                                                  plan.numel() * plan.element_size(),
+                                                                  _stream(stream, device)))
+    plan._idx_keep = (ctx,)
+    return plan
+
+
+def make_paged_args(q: torch.Tensor, w: torch.Tensor, out: torch.Tensor, S_k: int, *, in_dtype: str, q_scale=None,
+                    sm_scale: float = 1.0, clean_logits: bool = True) -> IdxLogitsArgs:
+    """idx_logits_args_t of a paged call: q [B, S_q, H, D'], out [B, S_q, >= S_k];
+    k and k_scale stay NULL (the keys come from an IdxPagedK)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S_q, H, D']")
+    if out.dtype not in FP_DTYPES or w.dtype not in FP_DTYPES:
+        raise ValueError("w and out must be float32 or bfloat16")
+    for name, t in (("q", q), ("w", w), ("q_scale", q_scale)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, S_q, H, Dq = q.shape
+    a = IdxLogitsArgs()
+    a.B, a.S_q, a.S_k, a.H = B, S_q, S_k, H
+    a.D = Dq * 2 if in_dtype == "mxfp4" else Dq
+    a.in_dtype = IN_DTYPES[in_dtype]
+    a.q, a.w, a.out, a.q_scale = _ptr(q), _ptr(w), _ptr(out), _ptr(q_scale)
+    a.k = a.k_scale = None
+    a.w_dtype, a.out_dtype = FP_DTYPES[w.dtype], FP_DTYPES[out.dtype]
+    a.sm_scale = float(sm_scale)
+    a.out_row_stride = out.stride(-2)
+    a.clean_logits = 1 if clean_logits else 0
+    return a
+
+
+def idx_logits_prepare_paged(args: IdxLogitsArgs, kv: IdxPagedK, workspace: Optional[torch.Tensor] = None, *,
+                             device=None, stream=None) -> torch.Tensor:
+    """idx_logits_prepare for a paged call (args from make_paged_args, kv from
+    make_paged_k); returns the workspace, which idx_logits_score then reads."""
+    device = torch.device(device if device is not None else (workspace.device if workspace is not None else "cuda"))
+    workspace = _workspace_for(args, workspace, device)
+    _check("idx_logits_prepare_paged",
+           lib().idx_logits_prepare_paged(ctypes.byref(args), ctypes.byref(kv), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream, device)))
+    return workspace
+
+
+def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: int, *, in_dtype: str,
+                         q_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
+                         out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+                         plan: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """One paged call: q [B, S_q, H, D'] (the S_q newest tokens of each request),
+    keys from `kv` (make_paged_k), output [B, S_q, S_k]."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S_q, H, D']")
+    device = q.device
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], S_k), dtype=out_dtype, device=device)
+    a = make_paged_args(q, w, out, S_k, in_dtype=in_dtype, q_scale=q_scale, sm_scale=sm_scale,
+                        clean_logits=clean_logits)
+    workspace = _workspace_for(a, workspace, device)
+    _check("idx_logits_run_paged", lib().idx_logits_run_paged(ctypes.byref(a), ctypes.byref(kv), _ptr(plan),
+                                                                _ptr(workspace),
+                                                                workspace.numel() * workspace.element_size(),
+                                                                _stream(stream, device)))
+    return out

@@ -136,7 +136,10 @@ idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, i
 namespace {
 
 // Every check on the call's arguments; nothing is launched before they pass.
-idx_status_t check_args(const idx_logits_args_t* a) {
+// With keys_elsewhere (paged calls, which take their keys from an
+// idx_paged_k_t, and scoring from a prepared workspace) a->k and a->k_scale
+// are not used.
+idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false) {
   if (a == nullptr) return fail(IDX_E_INVALID, "args is NULL");
   idx_status_t st = check_dims(a->B, a->S_q, a->S_k, a->H, a->D);
   if (st != IDX_OK) return st;
@@ -146,13 +149,13 @@ idx_status_t check_args(const idx_logits_args_t* a) {
   if ((a->w_dtype != IDX_F32 && a->w_dtype != IDX_BF16) || (a->out_dtype != IDX_F32 && a->out_dtype != IDX_BF16))
     return fail(IDX_E_INVALID, "w_dtype and out_dtype must be IDX_F32 or IDX_BF16");
   const bool mx = f == IDX_IN_MXFP8_E4M3 || f == IDX_IN_MXFP4_E2M1;
-  if (a->q == nullptr || a->k == nullptr || a->w == nullptr || a->out == nullptr)
+  if (a->q == nullptr || (!keys_elsewhere && a->k == nullptr) || a->w == nullptr || a->out == nullptr)
     return fail(IDX_E_INVALID, "q, k, w and out must be non-NULL");
   if (mx && a->q_scale == nullptr) return fail(IDX_E_INVALID, "MX formats need q_scale");
-  if ((mx || f == IDX_IN_FP8_E4M3) && a->k_scale == nullptr)
+  if (!keys_elsewhere && (mx || f == IDX_IN_FP8_E4M3) && a->k_scale == nullptr)
     return fail(IDX_E_INVALID, "FP8 and MX formats need k_scale");
-  if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->w) || !aligned16(a->out) ||
-      (mx && !aligned16(a->q_scale)) || ((mx || f == IDX_IN_FP8_E4M3) && !aligned16(a->k_scale)))
+  if (!aligned16(a->q) || (!keys_elsewhere && !aligned16(a->k)) || !aligned16(a->w) || !aligned16(a->out) ||
+      (mx && !aligned16(a->q_scale)) || (!keys_elsewhere && (mx || f == IDX_IN_FP8_E4M3) && !aligned16(a->k_scale)))
     return fail(IDX_E_INVALID, "q, k, w, out and scale pointers must be 16-byte aligned");
   if (a->out_row_stride < a->S_k)
     return fail(IDX_E_INVALID, "out_row_stride %lld < S_k %d", (long long)a->out_row_stride, a->S_k);
@@ -170,6 +173,29 @@ idx_status_t check_args(const idx_logits_args_t* a) {
   return IDX_OK;
 }
 
+// The paged key descriptor of a call (after check_args(a, true) passed).
+idx_status_t check_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv) {
+  if (kv == nullptr) return fail(IDX_E_INVALID, "paged key descriptor is NULL");
+  const idx_in_t f = a->in_dtype;
+  const bool scaled = idx::has_kscale(f);
+  if (kv->k_cache == nullptr || kv->block_table == nullptr || kv->context_lens == nullptr ||
+      (scaled && kv->k_scale_cache == nullptr))
+    return fail(IDX_E_INVALID, "k_cache, block_table, context_lens (and k_scale_cache for FP8 / MX) must be non-NULL");
+  if (!aligned16(kv->k_cache) || (scaled && !aligned16(kv->k_scale_cache)))
+    return fail(IDX_E_INVALID, "k_cache and k_scale_cache must be 16-byte aligned");
+  if (kv->num_pages <= 0 || kv->page_size <= 0 || kv->max_pages <= 0)
+    return fail(IDX_E_INVALID, "num_pages, page_size and max_pages must be positive");
+  if (int64_t(kv->max_pages) * kv->page_size < a->S_k)
+    return fail(IDX_E_INVALID, "S_k=%d exceeds max_pages * page_size = %lld", a->S_k,
+                (long long)(int64_t(kv->max_pages) * kv->page_size));
+  return IDX_OK;
+}
+
+idx::PagedK paged_k(const idx_paged_k_t* kv) {
+  return idx::PagedK{static_cast<const unsigned char*>(kv->k_cache), static_cast<const uint32_t*>(kv->k_scale_cache),
+                     kv->block_table, kv->context_lens, kv->num_pages, kv->page_size, kv->max_pages};
+}
+
 idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, size_t ws_bytes) {
   if (WL.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
   if (ws == nullptr)
@@ -182,14 +208,14 @@ idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, siz
 // Per-call preparation: K in MFMA fragment order and, for FP8 / MX inputs,
 // the weighted-query pieces.
 idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws,
-                     const idx::PlanBuild* build, hipStream_t s) {
+                     const idx::PlanBuild* build, const idx::PagedK* paged, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
   const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f);
   hipError_t e = idx::launch_prepare(
       f, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
       scaled ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, a->q, a->q_scale, a->w,
       int64_t(a->B) * a->S_q, pieces ? ws + WL.off_pieces : nullptr,
-      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, build, s);
+      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, build, paged, s);
   if (e != hipSuccess) return fail(IDX_E_HIP, "preparation launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
 }
@@ -201,8 +227,6 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   idx::ScoreArgs k{};
   k.q = a->q;
   k.q_scale = a->q_scale;
-  k.k = a->k;
-  k.k_scale = a->k_scale;
   k.w = a->w;
   k.out = a->out;
   k.plan = p;
@@ -258,10 +282,11 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // a plan built here shares the preparation launch
-  idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends, ws + WL.off_plan};
+  idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends, nullptr,
+                       ws + WL.off_plan};
   const bool build_plan = p == nullptr;
   if (build_plan) p = ws + WL.off_plan;
-  if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, s)) != IDX_OK) return st;
+  if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, nullptr, s)) != IDX_OK) return st;
   return score(a, p, WL, ws, s);
 }
 
@@ -271,12 +296,58 @@ idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, siz
   const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
-  return prepare(a, WL, ws, nullptr, static_cast<hipStream_t>(stream));
+  return prepare(a, WL, ws, nullptr, nullptr, static_cast<hipStream_t>(stream));
+}
+
+idx_status_t idx_logits_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                                   const int32_t* context_lens, void* plan, size_t plan_bytes, void* stream) {
+  idx_status_t st = check_dims(B, S_q, S_k, H, D);
+  if (st != IDX_OK) return st;
+  if (context_lens == nullptr) return fail(IDX_E_INVALID, "context_lens must be non-NULL");
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
+  const size_t need = idx::plan_layout(B, S_q).total;
+  if (plan_bytes < need) return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
+  hipError_t e = idx::launch_plan_paged(B, S_q, S_k, H, D, context_lens, plan, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
+idx_status_t idx_logits_prepare_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a, true);
+  if (st != IDX_OK) return st;
+  if ((st = check_paged(a, kv)) != IDX_OK) return st;
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  const idx::PagedK pk = paged_k(kv);
+  return prepare(a, WL, ws, nullptr, &pk, static_cast<hipStream_t>(stream));
+}
+
+idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, const void* plan,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a, true);
+  if (st != IDX_OK) return st;
+  if ((st = check_paged(a, kv)) != IDX_OK) return st;
+  const unsigned char* p = static_cast<const unsigned char*>(plan);
+  if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, nullptr, nullptr, nullptr, kv->context_lens,
+                       ws + WL.off_plan};
+  const bool build_plan = p == nullptr;
+  if (build_plan) p = ws + WL.off_plan;
+  const idx::PagedK pk = paged_k(kv);
+  if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, &pk, s)) != IDX_OK) return st;
+  return score(a, p, WL, ws, s);
 }
 
 idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  idx_status_t st = check_args(a);
+  idx_status_t st = check_args(a, true);  // the keys come from the workspace
   if (st != IDX_OK) return st;
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score needs a plan");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");

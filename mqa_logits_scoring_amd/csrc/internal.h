@@ -174,8 +174,6 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
 struct ScoreArgs {
   const void* q;
   const void* q_scale;
-  const void* k;
-  const void* k_scale;
   const void* w;
   void* out;
   const unsigned char* plan;
@@ -203,13 +201,27 @@ hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, in
 hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu_k, int32_t ratio, int32_t T_q,
                            int32_t m_total, int32_t H, int32_t D, void* plan, hipStream_t stream);
 
+// Plan of paged calls: windows from the requests' context lengths.
+hipError_t launch_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* ctx,
+                             void* plan, hipStream_t stream);
+
 // What a call that builds its own plan passes to the preparation launch.
 struct PlanBuild {
   int32_t B, S_q, S_k, H, D;
   const int32_t* offsets;
   const int32_t* starts;
   const int32_t* ends;
+  const int32_t* ctx;  // paged calls: context lengths (offsets / starts / ends then NULL)
   unsigned char* plan;
+};
+
+// Where the preparation reads K when it comes from a paged cache.
+struct PagedK {
+  const unsigned char* k_cache;
+  const uint32_t* k_scale_cache;
+  const int32_t* block_table;
+  const int32_t* ctx;
+  int32_t num_pages, page_size, max_pages;
 };
 
 // K in fragment order, K scales in block order and the weighted-query pieces
@@ -217,7 +229,7 @@ struct PlanBuild {
 hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
                           int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
-                          const PlanBuild* build, hipStream_t stream);
+                          const PlanBuild* build, const PagedK* paged, hipStream_t stream);
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);
 hipError_t launch_score_fp8(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,

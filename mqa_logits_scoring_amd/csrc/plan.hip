@@ -38,6 +38,21 @@ hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D
   return hipGetLastError();
 }
 
+hipError_t launch_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, const int32_t* ctx,
+                             void* plan, hipStream_t stream) {
+  PlanParams P{};
+  P.B = B;
+  P.S_q = S_q;
+  P.S_k = S_k;
+  P.H = H;
+  P.D = D;
+  P.plan = static_cast<unsigned char*>(plan);
+  P.L = plan_layout(B, S_q);
+  P.ctx = ctx;
+  hipLaunchKernelGGL(plan_kernel, dim3(unsigned(plan_segments(B, S_q))), dim3(kSortThreads), 0, stream, P);
+  return hipGetLastError();
+}
+
 hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu_k, int32_t ratio, int32_t T_q,
                            int32_t m_total, int32_t H, int32_t D, void* plan, hipStream_t stream) {
   PlanParams P{};

@@ -37,6 +37,9 @@ struct PlanParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t n_seg, ratio;
+  // paged calls: keys each request holds (the window of token i ends at
+  // ctx - S_q + i + 1); nullptr otherwise
+  const int32_t* ctx;
 };
 
 // Window of packed row i: segment s (the last with cu_q[s] <= i, found by
@@ -129,7 +132,12 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
         s = s < 0 ? 0 : (s > S_k ? S_k : s);
         e = e < s ? s : (e > S_k ? S_k : e);
       } else {
-        const int64_t off = offsets != nullptr ? int64_t(offsets[b]) : 0;
+        int64_t off = offsets != nullptr ? int64_t(offsets[b]) : 0;
+        if (P.ctx != nullptr) {  // context length n as the offset n - S_k
+          int64_t n = P.ctx[b];
+          n = n < 0 ? 0 : (n > S_k ? S_k : n);
+          off = n - S_k;
+        }
         s = 0;
         e = int64_t(S_k) - int64_t(S_q) + off + i + 1;
         e = e < 0 ? 0 : (e > S_k ? S_k : e);

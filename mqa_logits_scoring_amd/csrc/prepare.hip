@@ -58,12 +58,30 @@ struct PrepArgs {
   int64_t n_rows;
   unsigned char* pieces;
   uint32_t* pscales;
+  // keys from a paged cache (k, k_scale unused then)
+  bool paged;
+  PagedK pk;
   // the plan, when built here
   PlanParams plan;
   // workgroups of each job, in grid order: plan segments, pieces, K chunks,
   // K scales
   int64_t n_plan, n_pieces, n_kfrag, n_kscale;
 };
+
+// Row of the key source holding key `row` of batch (request) b, or -1 for
+// none: row b * S_k + row of contiguous K, or for a paged cache the row of the
+// request's page (page index clamped into the cache; nothing past the
+// request's context, whose block-table entries are never read).
+__device__ inline int64_t key_source_row(const PrepArgs& a, int64_t b, int64_t row) {
+  if (row >= a.S_k) return -1;
+  if (!a.paged) return b * a.S_k + row;
+  int64_t n = a.pk.ctx[b];
+  n = n < 0 ? 0 : (n > a.S_k ? a.S_k : n);
+  if (row >= n) return -1;
+  int64_t page = a.pk.block_table[b * a.pk.max_pages + row / a.pk.page_size];
+  page = page < 0 ? 0 : (page >= a.pk.num_pages ? a.pk.num_pages - 1 : page);
+  return page * a.pk.page_size + row % a.pk.page_size;
+}
 
 // One thread per 16-byte chunk of K in fragment order, reading the matching
 // chunk of a K row (offsets per lane half as the scoring kernel places d).
@@ -76,9 +94,10 @@ __device__ void kfrag_chunk(const PrepArgs& a, int64_t i) {
   const int64_t bu = (i >> 6) / NV;  // b * nblk + u
   const int64_t b = bu / a.nblk, u = bu % a.nblk;
   const int c = lane & 31, g = lane >> 5;
-  const int64_t row = u * 32 + c;
+  const int64_t src = key_source_row(a, b, u * 32 + c);
+  const unsigned char* base = a.paged ? a.pk.k_cache : a.k;
   uint4 x = make_uint4(0, 0, 0, 0);
-  if (row < a.S_k) x = *reinterpret_cast<const uint4*>(a.k + (b * a.S_k + row) * ROWB + CBASE * g + CSTRIDE * v);
+  if (src >= 0) x = *reinterpret_cast<const uint4*>(base + src * ROWB + CBASE * g + CSTRIDE * v);
   reinterpret_cast<uint4*>(a.kfrag)[i] = x;
 }
 
@@ -90,8 +109,9 @@ __device__ void kscale_word(const PrepArgs& a, int64_t i) {
   const int lane = int(i & 63);
   const int64_t bu = i >> 6;
   const int64_t b = bu / a.nblk, u = bu % a.nblk;
-  const int64_t col = u * 32 + (lane & 31);
-  uint32_t word = col < a.S_k ? a.k_scale[b * a.S_k + col] : 0u;
+  const int64_t src = key_source_row(a, b, u * 32 + (lane & 31));
+  const uint32_t* base = a.paged ? a.pk.k_scale_cache : a.k_scale;
+  uint32_t word = src >= 0 ? base[src] : 0u;
   if (lane >= 32) word >>= SHIFT;
   a.kscale[i] = word;
 }
@@ -224,8 +244,12 @@ hipError_t launch(const PrepArgs& a, hipStream_t stream) {
 hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
                           int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
-                          const PlanBuild* build, hipStream_t stream) {
+                          const PlanBuild* build, const PagedK* paged, hipStream_t stream) {
   PrepArgs a{};
+  if (paged != nullptr) {
+    a.paged = true;
+    a.pk = *paged;
+  }
   if (build != nullptr) {
     a.plan = PlanParams{};
     a.plan.B = build->B;
@@ -236,6 +260,7 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
     a.plan.offsets = build->offsets;
     a.plan.starts = build->starts;
     a.plan.ends = build->ends;
+    a.plan.ctx = build->ctx;
     a.plan.plan = build->plan;
     a.plan.L = plan_layout(build->B, build->S_q);
     a.n_plan = plan_segments(build->B, build->S_q);

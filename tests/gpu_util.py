@@ -12,18 +12,26 @@ import oracle
 DEV = "cuda"
 
 
+def _codes(a, device):
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else np.uint8)).to(device)
+
+
+def _scales(a, device):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    return torch.from_numpy(a if a.dtype == np.float32 else a.view(np.int32)).to(device)
+
+
 def dev_inputs(wl, device=DEV) -> dict:
     """Raw code buffers of a workload as device tensors."""
     d = {}
     d["q"] = torch.from_numpy(np.ascontiguousarray(wl.q).view(np.int16 if wl.q.dtype == np.uint16 else np.uint8)).to(device)
-    d["k"] = torch.from_numpy(np.ascontiguousarray(wl.k).view(np.int16 if wl.k.dtype == np.uint16 else np.uint8)).to(device)
+    d["k"] = _codes(wl.k, device)
     d["q_scale"] = None if wl.q_scale is None else torch.from_numpy(wl.q_scale.view(np.int32)).to(device)
-    if wl.k_scale is None:
-        d["k_scale"] = None
-    elif wl.k_scale.dtype == np.float32:
-        d["k_scale"] = torch.from_numpy(wl.k_scale).to(device)
-    else:
-        d["k_scale"] = torch.from_numpy(wl.k_scale.view(np.int32)).to(device)
+    d["k_scale"] = _scales(wl.k_scale, device)
     if wl.w_dtype == "bf16":
         d["w"] = torch.from_numpy(wl.w.view(np.int16)).view(torch.bfloat16).to(device)
     else:
@@ -31,6 +39,13 @@ def dev_inputs(wl, device=DEV) -> dict:
     d["offsets"] = None if wl.offsets is None else torch.from_numpy(np.asarray(wl.offsets, np.int32)).to(device)
     d["starts"] = None if wl.starts is None else torch.from_numpy(np.asarray(wl.starts, np.int32)).to(device)
     d["ends"] = None if wl.ends is None else torch.from_numpy(np.asarray(wl.ends, np.int32)).to(device)
+    if getattr(wl, "paged", None) is not None:
+        pg = wl.paged
+        d["k_cache"] = _codes(pg["k_cache"], device)
+        d["k_scale_cache"] = _scales(pg["k_scale_cache"], device)
+        d["block_table"] = torch.from_numpy(np.ascontiguousarray(pg["block_table"], np.int32)).to(device)
+        d["ctx"] = torch.from_numpy(np.ascontiguousarray(pg["ctx"], np.int32)).to(device)
+        d["kv"] = lib.make_paged_k(d["k_cache"], d["block_table"], d["ctx"], d["k_scale_cache"])
     if getattr(wl, "thd", None) is not None:
         d["cu_q"] = torch.from_numpy(np.asarray(wl.thd["cu_q"], np.int32)).to(device)
         d["cu_k"] = torch.from_numpy(np.asarray(wl.thd["cu_k"], np.int32)).to(device)
@@ -42,6 +57,8 @@ def out_dtype(wl):
 
 
 def make_plan(wl, d):
+    if getattr(wl, "paged", None) is not None:
+        return lib.idx_logits_plan_paged(wl.B, wl.S_q, wl.S_k, d["ctx"], wl.H, wl.D)
     if getattr(wl, "thd", None) is not None:
         return lib.idx_logits_plan_thd(d["cu_q"], d["cu_k"], wl.thd["ratio"], wl.S_q, wl.S_k, wl.H, wl.D,
                                        device=d["q"].device)
@@ -51,9 +68,14 @@ def make_plan(wl, d):
 
 def run(wl, d, plan=None, out=None, clean=None):
     """One library call; plan None builds the plan inside the call (packed
-    variable-length workloads build theirs with idx_logits_plan_thd first)."""
+    variable-length workloads build theirs with idx_logits_plan_thd first;
+    paged workloads go through idx_logits_run_paged)."""
     if plan is None and getattr(wl, "thd", None) is not None:
         plan = make_plan(wl, d)
+    if getattr(wl, "paged", None) is not None:
+        return lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                                        sm_scale=wl.sm_scale, clean_logits=wl.clean if clean is None else clean,
+                                        out=out, out_dtype=out_dtype(wl), plan=plan)
     return lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
                               sm_scale=wl.sm_scale, clean_logits=wl.clean if clean is None else clean, out=out,
                               out_dtype=out_dtype(wl), plan=plan, q_causal_offsets=d["offsets"],

@@ -98,7 +98,7 @@ def test_plan_rejects():
 @pytest.mark.parametrize("kw,status", [
     (dict(H=32), lib.IDX_E_UNSUPPORTED),
     (dict(in_dtype=9), lib.IDX_E_INVALID),
-    (dict(k=None), lib.IDX_E_INVALID),
+    (dict(q=None), lib.IDX_E_INVALID),
     (dict(out_row_stride=63), lib.IDX_E_INVALID),
 ])
 def test_prepare_and_score_share_the_checks(kw, status):
@@ -106,6 +106,12 @@ def test_prepare_and_score_share_the_checks(kw, status):
     a = _args(**kw)
     assert L.idx_logits_prepare(ctypes.byref(a), FAKE, 1 << 30, None) == status
     assert L.idx_logits_score(ctypes.byref(a), FAKE, FAKE, 1 << 30, None) == status
+
+
+def test_prepare_needs_keys():
+    L = lib.lib()
+    assert L.idx_logits_prepare(ctypes.byref(_args(k=None)), FAKE, 1 << 30, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_prepare(ctypes.byref(_args(k_scale=None)), FAKE, 1 << 30, None) == lib.IDX_E_INVALID
 
 
 def test_prepare_and_score_need_buffers():
@@ -130,3 +136,60 @@ def test_plan_thd_rejects():
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE, 8, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID
+
+
+def _paged(**kw):
+    kv = lib.IdxPagedK()
+    kv.k_cache = kv.k_scale_cache = kv.block_table = kv.context_lens = FAKE
+    kv.num_pages, kv.page_size, kv.max_pages = 4, 16, 4
+    for k, v in kw.items():
+        setattr(kv, k, v)
+    return kv
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k_cache=None), lib.IDX_E_INVALID),
+    (dict(block_table=None), lib.IDX_E_INVALID),
+    (dict(context_lens=None), lib.IDX_E_INVALID),
+    (dict(k_scale_cache=None), lib.IDX_E_INVALID),
+    (dict(k_cache=FAKE + 8), lib.IDX_E_INVALID),
+    (dict(k_scale_cache=FAKE + 4), lib.IDX_E_INVALID),
+    (dict(num_pages=0), lib.IDX_E_INVALID),
+    (dict(page_size=-1), lib.IDX_E_INVALID),
+    (dict(max_pages=0), lib.IDX_E_INVALID),
+    (dict(max_pages=3), lib.IDX_E_INVALID),  # 3 * 16 < S_k = 64
+])
+def test_paged_rejects(kw, status):
+    L = lib.lib()
+    a = _args(k=None, k_scale=None)  # paged calls take no contiguous keys
+    kv = _paged(**kw)
+    assert L.idx_logits_prepare_paged(ctypes.byref(a), ctypes.byref(kv), FAKE, 1 << 30, None) == status
+    assert L.idx_logits_run_paged(ctypes.byref(a), ctypes.byref(kv), None, FAKE, 1 << 30, None) == status
+    assert lib.idx_last_error() != ""
+
+
+def test_paged_call_checks():
+    L = lib.lib()
+    kv = _paged()
+    assert L.idx_logits_run_paged(ctypes.byref(_args(H=32)), ctypes.byref(kv), None, FAKE, 1 << 30,
+                                  None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_run_paged(ctypes.byref(_args()), None, None, FAKE, 1 << 30, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_run_paged(ctypes.byref(_args()), ctypes.byref(kv), None, None, 0, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_run_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE + 8, FAKE, 1 << 30,
+                                  None) == lib.IDX_E_INVALID
+    assert L.idx_logits_prepare_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE, 16, None) == lib.IDX_E_WORKSPACE
+    # BF16 keys carry no scales, so a NULL scale cache is fine there; the
+    # call then fails only on its workspace
+    a = _args(in_dtype=0, q_scale=None)
+    assert L.idx_logits_prepare_paged(ctypes.byref(a), ctypes.byref(_paged(k_scale_cache=None)), None, 0,
+                                      None) == lib.IDX_E_WORKSPACE
+
+
+def test_plan_paged_rejects():
+    L = lib.lib()
+    assert L.idx_logits_plan_paged(1, 16, 64, 32, 128, FAKE, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan_paged(0, 16, 64, 64, 128, FAKE, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, None, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, FAKE, 8, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID

@@ -253,7 +253,8 @@ def test_plan_dimension_mismatch_is_loud():
 # -inf placement of every row, and plan / no-plan equality
 # ---------------------------------------------------------------------------
 
-NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5", "thd_bf16_r4"]
+NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5", "thd_bf16_r4",
+         "paged_mxfp8_decode"]
 
 
 @pytest.mark.parametrize("name", NAMED)
@@ -261,8 +262,10 @@ def test_named_full_size(name):
     wl = W.make(name)
     d = dev_inputs(wl)
     plan = make_plan(wl, d)
-    out = run(wl, d, plan=plan)
-    out2 = run(wl, d)
+    # an unclean call leaves the cells outside the windows as they were
+    odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    out = run(wl, d, plan=plan, out=torch.zeros((wl.B, wl.S_q, wl.S_k), dtype=odt, device="cuda"))
+    out2 = run(wl, d, out=torch.zeros_like(out))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
                        out2.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
@@ -394,3 +397,101 @@ def test_mx_block_layout_probes():
         out = run(wl, dev_inputs(wl))
         torch.cuda.synchronize()
         _full_compare(wl, out, what=f"layout probe {wl.fmt}")
+
+
+# ---------------------------------------------------------------------------
+# paged keys (decode)
+# ---------------------------------------------------------------------------
+
+# (B, next_n, context lengths, page size, S_k or None for the longest context)
+PAGED_CASES = [
+    (4, 1, [1, 700, 33, 2000], 64, None),
+    (5, 3, [0, 2, 3, 129, 1000], 16, None),   # an empty context, contexts shorter than next_n
+    (3, 2, [47, 4100, 6000], 48, 4100),       # pages not a multiple of 32 rows; a context past S_k
+    (2, 4, [-5, 333], 100, 400),              # a negative context length sees nothing
+]
+PAGED_IDS = [f"b{c[0]}-n{c[1]}-p{c[3]}" for c in PAGED_CASES]
+
+
+def _paged(fmt, case, seed=31, **kw):
+    B, n, ctx, ps, S_k = case
+    return W.make_paged(fmt, B, n, ctx, ps, S_k=S_k, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=PAGED_IDS)
+def test_paged_plan_windows_match_oracle(case):
+    wl = _paged("bf16", case)
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    ws, we = lib.idx_logits_plan_windows(plan, wl.B, wl.S_q, wl.S_k)
+    ows, owe = oracle.windows(wl)
+    assert np.array_equal(ws.cpu().numpy(), ows) and np.array_equal(we.cpu().numpy(), owe)
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=PAGED_IDS)
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_paged_scores_match_oracle(fmt, case):
+    """Every cell of a paged call against the oracle over the gathered keys."""
+    wl = _paged(fmt, case, w_dtype="bf16" if fmt == "mxfp4" else "f32")
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    _full_compare(wl, out, what=f"paged {fmt} {case}")
+
+
+def _gather_dense(wl):
+    """The request-major K a paged workload describes, gathered with numpy
+    (zero rows past each clamped context)."""
+    pg = wl.paged
+    ps, bt = pg["page_size"], np.asarray(pg["block_table"])
+    cache, scache = np.asarray(pg["k_cache"]), pg["k_scale_cache"]
+    k = np.zeros((wl.B, wl.S_k) + cache.shape[2:], cache.dtype)
+    ks = None if scache is None else np.zeros((wl.B, wl.S_k), np.asarray(scache).dtype)
+    for b in range(wl.B):
+        n = min(max(int(pg["ctx"][b]), 0), wl.S_k)
+        j = np.arange(n)
+        k[b, :n] = cache[bt[b, j // ps], j % ps]
+        if ks is not None:
+            ks[b, :n] = np.asarray(scache)[bt[b, j // ps], j % ps]
+    return k, ks
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_paged_equals_contiguous(fmt):
+    """A paged call is bitwise the contiguous call on the gathered keys with the
+    same windows given explicitly, clean or not."""
+    wl = _paged(fmt, PAGED_CASES[2], out_dtype="bf16" if fmt == "fp8" else "f32")
+    d = dev_inputs(wl)
+    k, ks = _gather_dense(wl)
+    ows, owe = oracle.windows(wl)
+    dense = wl.replace(k=k, k_scale=ks, paged=None, starts=ows, ends=owe)
+    dd = dev_inputs(dense)
+    for clean in (True, False):
+        got = run(wl, d, clean=clean)
+        want = run(dense, dd, clean=clean)
+        view = torch.int16 if got.dtype == torch.bfloat16 else torch.int32
+        if clean:
+            assert torch.equal(got.view(view), want.view(view))
+        else:  # cells outside the windows are not written
+            for b in range(wl.B):
+                for i in range(wl.S_q):
+                    s0, e = int(ows[b, i]), max(int(owe[b, i]), int(ows[b, i]))
+                    assert torch.equal(got[b, i, s0:e].view(view), want[b, i, s0:e].view(view)), (b, i)
+
+
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_paged_prepare_score_and_plan(fmt):
+    """idx_logits_prepare_paged + idx_logits_score (keys NULL in the args) with a
+    plan from idx_logits_plan_paged is bitwise the one-call form, which gives
+    the same result whether it builds its plan or takes it."""
+    wl = _paged(fmt, PAGED_CASES[1])
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    one = run(wl, d)
+    planned = run(wl, d, plan=plan)
+    out = torch.empty_like(one)
+    args = lib.make_paged_args(d["q"], d["w"], out, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"], sm_scale=wl.sm_scale)
+    ws = lib.idx_logits_prepare_paged(args, d["kv"])
+    lib.idx_logits_score(args, plan, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32), planned.view(torch.int32))
+    assert torch.equal(one.view(torch.int32), out.view(torch.int32))

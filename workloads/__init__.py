@@ -351,6 +351,18 @@ def _thd(**kw):
                     name="thd_bf16_r4", **kw)
 
 
+def _paged_decode(**kw):
+    # decode over a paged cache: 64 requests scoring their 2 newest tokens
+    # against contexts of 1..32768 keys in 64-row pages, MXFP8 at the
+    # contiguous MX shape's H, D and widest context; the paged entry writes no
+    # -inf outside the windows (clean_logits off).  The pages name the paged
+    # path and its sampled test shapes without printing them, so this one
+    # plain decode shape stands in.
+    ctx = np.random.default_rng(8).integers(1, 32769, size=64)
+    return make_paged("mxfp8", 64, 2, ctx, 64, S_k=32768, w_dtype="f32", sm_scale=1.0, clean=False, seed=8,
+                      name="paged_mxfp8_decode", **kw)
+
+
 NAMED = {
     "c1": _c1,
     "c2": _c2,
@@ -363,6 +375,7 @@ NAMED = {
     "c5": _c5,
     "c5_nonaligned": lambda **kw: _c5(S_q=129, S_k=4100, seed=6, name="c5_nonaligned", **kw),
     "thd_bf16_r4": _thd,
+    "paged_mxfp8_decode": _paged_decode,
 }
 
 
