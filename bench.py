@@ -350,7 +350,7 @@ def main():
         return wl, V, us_call, kern_us
 
     wl, V, us_call, kern_us = measure(args.workload)
-    flops = 16384.0 * V
+    flops = 2.0 * wl.H * wl.D * V  # 2 H D per visible cell
     peak = PEAK_TFLOPS[wl.fmt]
     rec = counted_traffic(wl.name, wl.fmt)
     traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]

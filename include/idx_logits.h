@@ -5,10 +5,10 @@
  * For every query row i of batch b and every key column j inside the row's
  * visibility window [start, end):
  *
- *     out[b,i,j] = sm_scale * sum_{h<64} w[b,i,h] * max(0, q[b,i,h,:] . k[b,j,:])
+ *     out[b,i,j] = sm_scale * sum_{h<H} w[b,i,h] * max(0, q[b,i,h,:] . k[b,j,:])
  *
- * 64 query heads share one 128-wide key head.  With clean_logits set, every
- * other column of the row is -inf.
+ * H = 64 (or 8, 16, 32) query heads share one 128-wide key head.  With
+ * clean_logits set, every other column of the row is -inf.
  *
  * Where this is defined: DeepGEMM pull request 435, "Improve SM100 MX MQA
  * logits clean-output performance" (Performance section and standalone
@@ -20,6 +20,8 @@
  * q_causal_offsets folded into per-row windows, 16-byte-aligned bases, -inf
  * outside the causal window).  The ReLU on each head's dot before the
  * weighting is the plainest reading of the "head-sum" those pages describe.
+ * Other head counts: the DeepGEMM page screens H = 8, 32 and 64 (Performance
+ * section) and the cudnn-frontend page names qhead_per_kv_head = 32.
  *
  * Conventions shared by every entry point:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -48,7 +50,7 @@ extern "C" {
 typedef enum {
   IDX_OK = 0,
   IDX_E_INVALID = 1,     /* bad pointer, size, alignment, stride or scalar      */
-  IDX_E_UNSUPPORTED = 2, /* valid request outside the supported set (H!=64...)  */
+  IDX_E_UNSUPPORTED = 2, /* valid request outside the supported set (H, D)      */
   IDX_E_WORKSPACE = 3,   /* plan / workspace buffer missing or too small         */
   IDX_E_HIP = 4          /* a HIP launch failed                                  */
 } idx_status_t;
@@ -82,7 +84,8 @@ typedef enum { IDX_F32 = 0, IDX_BF16 = 1 } idx_fp_t;
  *                0: those columns are left untouched; in-window values are
  *                bitwise identical to the clean_logits=1 call.
  *
- * H must be 64 and D 128 (else IDX_E_UNSUPPORTED).  q, k, w, out and the
+ * H must be 8, 16, 32 or 64 and D 128 (else IDX_E_UNSUPPORTED); a plan is
+ * built for one H (its tiles hold 512 / H rows).  q, k, w, out and the
  * scale pointers must be 16-byte aligned; out_row_stride >= S_k.
  * sm_scale must be finite.  Results are deterministic: the same inputs give
  * bitwise identical outputs, with or without a precomputed plan, for any B.
@@ -108,7 +111,8 @@ int32_t idx_abi_version(void);
 
 /*
  * Size in bytes of the plan (windows + schedule metadata) for these
- * dimensions; 0 when a dimension is <= 0 or the size would overflow.
+ * dimensions; 0 when a dimension is <= 0, H is not supported or the size
+ * would overflow.
  * The plan plays the role of the schedule metadata that the DeepGEMM
  * pull request 435 reproducer precomputes outside timing.
  */

@@ -24,9 +24,9 @@ bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) 
 idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D) {
   if (B <= 0 || S_q <= 0 || S_k <= 0 || H <= 0 || D <= 0)
     return fail(IDX_E_INVALID, "dimensions must be positive (B=%d S_q=%d S_k=%d H=%d D=%d)", B, S_q, S_k, H, D);
-  if (H != 64 || D != 128)
-    return fail(IDX_E_UNSUPPORTED, "only H=64 query heads and D=128 are supported (got H=%d D=%d)", H, D);
-  const idx::PlanLayout L = idx::plan_layout(B, S_q);
+  if (!idx::supported_heads(H) || D != 128)
+    return fail(IDX_E_UNSUPPORTED, "H must be 8, 16, 32 or 64 query heads and D must be 128 (got H=%d D=%d)", H, D);
+  const idx::PlanLayout L = idx::plan_layout(B, S_q, H);
   if (L.total == 0) return fail(IDX_E_INVALID, "B*S_q=%lld rows is too large", (long long)B * S_q);
   return IDX_OK;
 }
@@ -72,7 +72,7 @@ const char* idx_last_error(void) { return g_err; }
 
 size_t idx_logits_plan_bytes(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D) {
   if (B <= 0 || S_q <= 0 || S_k <= 0 || H <= 0 || D <= 0) return 0;
-  return idx::plan_layout(B, S_q).total;
+  return idx::plan_layout(B, S_q, H).total;
 }
 
 idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
@@ -84,7 +84,7 @@ idx_status_t idx_logits_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
     return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
-  const size_t need = idx::plan_layout(B, S_q).total;
+  const size_t need = idx::plan_layout(B, S_q, H).total;
   if (plan_bytes < need)
     return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
   hipError_t e = idx::launch_plan(B, S_q, S_k, H, D, q_causal_offsets, row_starts, row_ends, plan,
@@ -104,7 +104,7 @@ idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, con
     return fail(IDX_E_INVALID, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
-  const size_t need = idx::plan_layout(1, T_q).total;
+  const size_t need = idx::plan_layout(1, T_q, H).total;
   if (plan_bytes < need) return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
   hipError_t e = idx::launch_plan_thd(n_seg, cu_seqlens_q, cu_seqlens_k, ratio, T_q, m_total, H, D, plan,
                                       static_cast<hipStream_t>(stream));
@@ -116,7 +116,7 @@ size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) {
   if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return 0;
   const idx_in_t f = a->in_dtype;
   if (f != IDX_IN_BF16 && f != IDX_IN_FP8_E4M3 && f != IDX_IN_MXFP8_E4M3 && f != IDX_IN_MXFP4_E2M1) return 0;
-  return idx::workspace_layout(f, a->B, a->S_q, a->S_k).total;
+  return idx::workspace_layout(f, a->B, a->S_q, a->S_k, a->H).total;
 }
 
 idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
@@ -166,7 +166,7 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
   if ((int64_t(a->S_k) + 31) / 32 * 32 * idx::row_bytes_of(f) > (int64_t(1) << 31) - 1)
     return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
-  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
   const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles).n_chunks) * L.n_tiles;
   if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
@@ -210,7 +210,7 @@ idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, siz
 idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws,
                      const idx::PlanBuild* build, const idx::PagedK* paged, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
-  const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f);
+  const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f, a->H);
   hipError_t e = idx::launch_prepare(
       f, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
       scaled ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, a->q, a->q_scale, a->w,
@@ -223,7 +223,7 @@ idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL,
 idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
                    unsigned char* ws, hipStream_t s) {
   const idx_in_t f = a->in_dtype;
-  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q);
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   idx::ScoreArgs k{};
   k.q = a->q;
   k.q_scale = a->q_scale;
@@ -236,7 +236,9 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.S_q = a->S_q;
   k.S_k = a->S_k;
   k.n_tiles = int32_t(L.n_tiles);
-  k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q));
+  k.H = a->H;
+  k.tile_rows = L.tile_rows;
+  k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q, L.tile_rows));
   const Split sp = pick_split(a->S_k, L.n_tiles);
   k.min_chunk = sp.min_chunk;
   k.n_chunks = sp.n_chunks;
@@ -247,8 +249,8 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.off_slot = uint32_t(L.off_slot);
   k.off_lo = uint32_t(L.off_lo);
   k.off_hi = uint32_t(L.off_hi);
-  k.pieces = idx::uses_pieces(f) ? ws + WL.off_pieces : nullptr;
-  k.pscales = idx::uses_pieces(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
+  k.pieces = idx::uses_pieces(f, a->H) ? ws + WL.off_pieces : nullptr;
+  k.pscales = idx::uses_pieces(f, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
   k.kscale = idx::has_kscale(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
 
@@ -277,7 +279,7 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
     return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
   if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -293,7 +295,7 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
 idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
   idx_status_t st = check_args(a);
   if (st != IDX_OK) return st;
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   return prepare(a, WL, ws, nullptr, nullptr, static_cast<hipStream_t>(stream));
@@ -306,7 +308,7 @@ idx_status_t idx_logits_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t 
   if (context_lens == nullptr) return fail(IDX_E_INVALID, "context_lens must be non-NULL");
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "plan buffer is NULL");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan buffer must be 256-byte aligned");
-  const size_t need = idx::plan_layout(B, S_q).total;
+  const size_t need = idx::plan_layout(B, S_q, H).total;
   if (plan_bytes < need) return fail(IDX_E_WORKSPACE, "plan buffer has %zu bytes, %zu needed", plan_bytes, need);
   hipError_t e = idx::launch_plan_paged(B, S_q, S_k, H, D, context_lens, plan, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(IDX_E_HIP, "plan launch failed: %s", hipGetErrorString(e));
@@ -318,7 +320,7 @@ idx_status_t idx_logits_prepare_paged(const idx_logits_args_t* a, const idx_page
   idx_status_t st = check_args(a, true);
   if (st != IDX_OK) return st;
   if ((st = check_paged(a, kv)) != IDX_OK) return st;
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   const idx::PagedK pk = paged_k(kv);
@@ -332,7 +334,7 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
   if ((st = check_paged(a, kv)) != IDX_OK) return st;
   const unsigned char* p = static_cast<const unsigned char*>(plan);
   if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -351,7 +353,7 @@ idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void
   if (st != IDX_OK) return st;
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score needs a plan");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k);
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
   return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream));

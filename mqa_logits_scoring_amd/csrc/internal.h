@@ -16,7 +16,7 @@ namespace idx {
 //   PlanHeader                      (256 B)
 //   int32 win_start[B*S_q]          window start per row
 //   int32 win_end[B*S_q]            window end per row
-//   int32 slot_row[n_tiles*kTileRows]  global row (b*S_q+i) of every tile slot,
+//   int32 slot_row[n_tiles*tile_rows]  global row (b*S_q+i) of every tile slot,
 //                                   -1 for the padding slots of a ragged tail;
 //                                   with explicit windows the rows of every
 //                                   kSortRows-row segment are reordered so that
@@ -24,16 +24,22 @@ namespace idx {
 //   int32 tile_lo[n_tiles]          first column computed for the tile
 //   int32 tile_hi[n_tiles]          one past the last column computed
 //
-// A tile is kTileRows consecutive slots of one batch.  [tile_lo,
+// A tile is tile_rows consecutive slots of one batch.  [tile_lo,
 // tile_hi) is the union of its rows' windows widened to kColAlign columns
 // and clipped to [0, S_k); cells of a row outside it are cleanup work.
+// A tile always holds 512 (row, head) pairs, so tile_rows = 512 / H: 8 rows
+// at 64 heads, 16 at 32, 32 at 16, 64 at 8.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kPlanMagic = 0x50584449u;  // "IDXP"
-constexpr int kTileRows = 8;                   // query rows per tile
+constexpr int kTileRows = 8;                   // query rows per tile at 64 heads
 constexpr int kColAlign = 32;                  // coverage granularity in columns
 constexpr int kSortRows = 1024;                // rows ordered together when building a plan
 constexpr int kSortThreads = 256;
-static_assert(kSortRows % kTileRows == 0, "sort segments hold whole tiles");
+static_assert(kSortRows % 64 == 0, "sort segments hold whole tiles at every head count");
+
+// Query heads per row the kernels are built for, and the tile height for each.
+__host__ __device__ constexpr bool supported_heads(int H) { return H == 8 || H == 16 || H == 32 || H == 64; }
+__host__ __device__ constexpr int tile_rows_for(int H) { return supported_heads(H) ? 512 / H : 0; }
 
 struct PlanHeader {
   uint32_t magic;
@@ -46,31 +52,36 @@ static_assert(sizeof(PlanHeader) == 256, "plan header is one 256-byte section");
 struct PlanLayout {
   size_t off_start, off_end, off_slot, off_lo, off_hi, total;
   int64_t n_rows, n_tiles;
+  int32_t tile_rows;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-__host__ __device__ inline int64_t tiles_per_batch(int64_t S_q) { return (S_q + kTileRows - 1) / kTileRows; }
+__host__ __device__ inline int64_t tiles_per_batch(int64_t S_q, int64_t tile_rows) {
+  return (S_q + tile_rows - 1) / tile_rows;
+}
 
 // Workgroups that build a plan: one per kSortRows rows of a batch.
 __host__ __device__ inline int64_t plan_segments(int64_t B, int64_t S_q) {
   return B * ((S_q + kSortRows - 1) / kSortRows);
 }
 
-// Layout of a plan; total == 0 when the sizes overflow.
-inline PlanLayout plan_layout(int64_t B, int64_t S_q) {
+// Layout of a plan for H heads; total == 0 when the sizes overflow or H is
+// not supported.  The window arrays do not depend on H.
+inline PlanLayout plan_layout(int64_t B, int64_t S_q, int H) {
   PlanLayout L{};
+  L.tile_rows = tile_rows_for(H);
+  if (L.tile_rows == 0 || B <= 0 || S_q <= 0) return L;
   L.n_rows = B * S_q;
-  L.n_tiles = B * tiles_per_batch(S_q);
-  if (B <= 0 || S_q <= 0 || L.n_rows > (int64_t(1) << 31) - 1 || L.n_tiles * kTileRows > (int64_t(1) << 31) - 1)
-    return L;
+  L.n_tiles = B * tiles_per_batch(S_q, L.tile_rows);
+  if (L.n_rows > (int64_t(1) << 31) - 1 || L.n_tiles * L.tile_rows > (int64_t(1) << 31) - 1) return L;
   size_t off = align256(sizeof(PlanHeader));
   L.off_start = off;
   off += align256(size_t(L.n_rows) * 4);
   L.off_end = off;
   off += align256(size_t(L.n_rows) * 4);
   L.off_slot = off;
-  off += align256(size_t(L.n_tiles) * kTileRows * 4);
+  off += align256(size_t(L.n_tiles) * L.tile_rows * 4);
   L.off_lo = off;
   off += align256(size_t(L.n_tiles) * 4);
   L.off_hi = off;
@@ -96,7 +107,9 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q) {
 // ---------------------------------------------------------------------------
 constexpr int kPieces = 6;
 
-inline bool uses_pieces(idx_in_t f) { return f != IDX_IN_BF16; }
+// Only the 64-head kernels take the linear term from pieces; the others use
+// max + FMA.
+inline bool uses_pieces(idx_in_t f, int H) { return f != IDX_IN_BF16 && H == 64; }
 
 // ---------------------------------------------------------------------------
 // K in fragment order
@@ -147,14 +160,14 @@ struct WorkspaceLayout {
   size_t off_plan, off_pieces, off_pscales, off_kfrag, off_kscale, total;
 };
 
-inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k) {
+inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int64_t S_k, int H) {
   WorkspaceLayout W{};
-  const PlanLayout L = plan_layout(B, S_q);
+  const PlanLayout L = plan_layout(B, S_q, H);
   if (L.total == 0 || S_k <= 0) return W;
   size_t off = 0;
   W.off_plan = off;
   off += L.total;
-  if (uses_pieces(f)) {
+  if (uses_pieces(f, H)) {
     W.off_pieces = off;
     off += align256(size_t(L.n_rows) * kPieces * 128);
     W.off_pscales = off;
@@ -179,8 +192,8 @@ struct ScoreArgs {
   const unsigned char* plan;
   int64_t ld;  // output row stride in elements
   float sm_scale;
-  int32_t B, S_q, S_k;
-  int32_t n_tiles, tiles_per_batch;
+  int32_t B, S_q, S_k, H;
+  int32_t n_tiles, tiles_per_batch, tile_rows;
   int32_t min_chunk;     // fewest columns per compute unit (multiple of 64)
   int32_t n_chunks;      // compute units per tile: its coverage in n_chunks equal
                          // parts of at least min_chunk columns (upper bound)
@@ -224,8 +237,9 @@ struct PagedK {
   int32_t num_pages, page_size, max_pages;
 };
 
-// K in fragment order, K scales in block order and the weighted-query pieces
-// (those two not for BF16), and the plan when `build` is given, in one launch.
+// K in fragment order, K scales in block order (not for BF16), the
+// weighted-query pieces when `pieces` is given, and the plan when `build` is
+// given, in one launch.
 hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
                           int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,

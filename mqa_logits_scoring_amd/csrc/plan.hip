@@ -33,7 +33,7 @@ hipError_t launch_plan(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D
   P.starts = starts;
   P.ends = ends;
   P.plan = static_cast<unsigned char*>(plan);
-  P.L = plan_layout(B, S_q);
+  P.L = plan_layout(B, S_q, H);
   hipLaunchKernelGGL(plan_kernel, dim3(unsigned(plan_segments(B, S_q))), dim3(kSortThreads), 0, stream, P);
   return hipGetLastError();
 }
@@ -47,7 +47,7 @@ hipError_t launch_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int
   P.H = H;
   P.D = D;
   P.plan = static_cast<unsigned char*>(plan);
-  P.L = plan_layout(B, S_q);
+  P.L = plan_layout(B, S_q, H);
   P.ctx = ctx;
   hipLaunchKernelGGL(plan_kernel, dim3(unsigned(plan_segments(B, S_q))), dim3(kSortThreads), 0, stream, P);
   return hipGetLastError();
@@ -62,7 +62,7 @@ hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu
   P.H = H;
   P.D = D;
   P.plan = static_cast<unsigned char*>(plan);
-  P.L = plan_layout(1, T_q);
+  P.L = plan_layout(1, T_q, H);
   P.cu_q = cu_q;
   P.cu_k = cu_k;
   P.n_seg = n_seg;
@@ -72,7 +72,7 @@ hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu
 }
 
 hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream) {
-  const PlanLayout L = plan_layout(1, n_rows);
+  const PlanLayout L = plan_layout(1, n_rows, 64);  // the window arrays do not depend on H
   const int threads = 256;
   const int64_t blocks = (n_rows + threads - 1) / threads;
   hipLaunchKernelGGL(copy_windows_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream,

@@ -102,9 +102,10 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
     h->H = H;
     h->D = D;
     h->n_tiles = int32_t(L.n_tiles);
-    h->tile_rows = kTileRows;
+    h->tile_rows = L.tile_rows;
   }
-  const int64_t tpb = tiles_per_batch(S_q);
+  const int TR = L.tile_rows;
+  const int64_t tpb = tiles_per_batch(S_q, TR);
   const int64_t spb = (int64_t(S_q) + kSortRows - 1) / kSortRows;
   const int64_t b = segment / spb, seg = segment % spb;
   const int64_t i0 = seg * kSortRows;
@@ -116,7 +117,7 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
   const bool explicit_windows = !thd && starts != nullptr && ends != nullptr;
   int shift = 0;
   while ((int64_t(S_k) >> shift) >= (int64_t(1) << 27)) ++shift;
-  const int64_t slot0 = b * tpb * kTileRows;
+  const int64_t slot0 = b * tpb * TR;
   for (int r = threadIdx.x; r < kSortRows; r += kSortThreads) {
     uint64_t k = ~uint64_t(0);
     if (r < n) {
@@ -185,14 +186,14 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
     slot_row[slot0 + i0 + r] = int32_t(b * S_q + i0 + local);
   }
   if (seg == spb - 1) {  // padding slots of the batch's last tile
-    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tpb * kTileRows; i += kSortThreads) slot_row[slot0 + i] = -1;
+    for (int64_t i = int64_t(S_q) + threadIdx.x; i < tpb * TR; i += kSortThreads) slot_row[slot0 + i] = -1;
   }
   // coverage of the segment's tiles: the union of their rows' windows
   // widened to kColAlign columns (0, 0 when every row is empty)
-  const int n_tiles_seg = (n + kTileRows - 1) / kTileRows;
+  const int n_tiles_seg = (n + TR - 1) / TR;
   for (int t = threadIdx.x; t < n_tiles_seg; t += kSortThreads) {
     int64_t lo = S_k, hi = 0;
-    for (int r = t * kTileRows; r < t * kTileRows + kTileRows && r < n; ++r) {
+    for (int r = t * TR; r < t * TR + TR && r < n; ++r) {
       const int local = explicit_windows ? int(uint32_t(key[r])) : r;
       const int64_t s = win_s[local], e = win_e[local];
       if (e > s) {
@@ -208,7 +209,7 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
       hi = (hi + kColAlign - 1) / kColAlign * kColAlign;
       hi = hi > S_k ? S_k : hi;
     }
-    const int64_t tile = b * tpb + i0 / kTileRows + t;
+    const int64_t tile = b * tpb + i0 / TR + t;
     tile_lo[tile] = int32_t(lo);
     tile_hi[tile] = int32_t(hi);
   }

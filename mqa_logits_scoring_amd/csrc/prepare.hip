@@ -262,7 +262,7 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
     a.plan.ends = build->ends;
     a.plan.ctx = build->ctx;
     a.plan.plan = build->plan;
-    a.plan.L = plan_layout(build->B, build->S_q);
+    a.plan.L = plan_layout(build->B, build->S_q, build->H);
     a.n_plan = plan_segments(build->B, build->S_q);
   }
   a.k = static_cast<const unsigned char*>(k);
@@ -279,7 +279,7 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.pieces = pieces;
   a.pscales = pscales;
   const bool scaled = has_kscale(fmt);
-  a.n_pieces = uses_pieces(fmt) ? n_rows : 0;
+  a.n_pieces = pieces != nullptr ? n_rows : 0;  // only 64-head calls of the formats with pieces
   a.n_kfrag = (B * a.nblk * (row_bytes_of(fmt) / 32) * 64 + 255) / 256;
   a.n_kscale = scaled ? (B * a.nblk * 64 + 255) / 256 : 0;
   if (a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;

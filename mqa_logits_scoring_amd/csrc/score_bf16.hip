@@ -1,21 +1,12 @@
-// Scoring kernels for bf16 Q/K: every weight type x output type x clean flag.
-#include "score_kernel.h"
+// Scoring kernels for bf16 Q/K: every head count x weight type x output
+// type x clean flag.
+#include "score_kernel_gh.h"
 
 namespace idx {
 
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream) {
-  const bool wb = w_dtype == IDX_BF16, ob = out_dtype == IDX_BF16;
-  if (wb) {
-    if (ob) return clean ? launch_score_t<IDX_IN_BF16, true, true, true>(a, stream)
-                         : launch_score_t<IDX_IN_BF16, true, true, false>(a, stream);
-    return clean ? launch_score_t<IDX_IN_BF16, true, false, true>(a, stream)
-                 : launch_score_t<IDX_IN_BF16, true, false, false>(a, stream);
-  }
-  if (ob) return clean ? launch_score_t<IDX_IN_BF16, false, true, true>(a, stream)
-                       : launch_score_t<IDX_IN_BF16, false, true, false>(a, stream);
-  return clean ? launch_score_t<IDX_IN_BF16, false, false, true>(a, stream)
-               : launch_score_t<IDX_IN_BF16, false, false, false>(a, stream);
+  return launch_score_fmt<IDX_IN_BF16>(w_dtype, out_dtype, clean, a, stream);
 }
 
 }  // namespace idx

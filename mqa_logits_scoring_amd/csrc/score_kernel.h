@@ -155,10 +155,10 @@ __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   }
 }
 
-// Cells of a tile's rows outside its computed coverage: -inf when cleaning.
+// Cells of a tile's TR rows outside its computed coverage: -inf when cleaning.
 // With a plan that does not match the call, every row of the tile is filled
 // with quiet NaN instead, so the mismatch cannot pass unnoticed.
-template <bool OBF, bool CLEAN>
+template <bool OBF, bool CLEAN, int TR>
 __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
   if (plan_ok && !CLEAN) return;
   const int32_t* slot_row = reinterpret_cast<const int32_t*>(a.plan + a.off_slot);
@@ -170,13 +170,13 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
     fill = -__builtin_inff();
   }
   const int tpb = a.tiles_per_batch;
-  for (int r = 0; r < kTileRows; ++r) {
+  for (int r = 0; r < TR; ++r) {
     int64_t row;
     if (plan_ok) {
-      row = slot_row[int64_t(tile) * kTileRows + r];
+      row = slot_row[int64_t(tile) * TR + r];
       if (row < 0) continue;
     } else {
-      const int64_t i = int64_t(tile % tpb) * kTileRows + r;
+      const int64_t i = int64_t(tile % tpb) * TR + r;
       if (i >= a.S_q) continue;
       row = int64_t(tile / tpb) * a.S_q + i;
     }
@@ -184,6 +184,32 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
     for (int j = threadIdx.x; j < lo; j += kThreads) store_out<OBF>(a.out, base + j, fill);
     for (int j = hi + threadIdx.x; j < a.S_k; j += kThreads) store_out<OBF>(a.out, base + j, fill);
   }
+}
+
+// The tile and key columns [c0, c1) of compute unit `bid`; false when the
+// unit has no columns.  Workgroups are dealt to the 8 XCDs round-robin
+// (bid % 8).  When the chunk count is a multiple of 8, XCD x only ever gets
+// chunks x, x+8, ... so its slice of K stays in its own L2; consecutive units
+// of one XCD share a tile so that tile's Q is fetched once per XCD.  Longest
+// tiles go first: under causal windows the last rows see the most keys.  The
+// tile's coverage is cut in n_chunks equal parts (multiples of 64 columns, at
+// least min_chunk), so every unit of a tile gets the same amount of work.
+__device__ __forceinline__ bool unit_columns(const ScoreArgs& a, int bid, int& tile, int& c0, int& c1) {
+  int chunk;
+  if (a.xcd_chunks) {
+    const int x = bid & 7, i = bid >> 3, cpx = a.n_chunks >> 3;
+    tile = a.n_tiles - 1 - i / cpx;
+    chunk = x + 8 * (i % cpx);
+  } else {
+    tile = a.n_tiles - 1 - bid / a.n_chunks;
+    chunk = bid % a.n_chunks;
+  }
+  const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
+  const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
+  const int ccols = max(a.min_chunk, ((hi - lo + a.n_chunks - 1) / a.n_chunks + 63) & ~63);
+  c0 = lo + chunk * ccols;
+  c1 = min(hi, c0 + ccols);
+  return c0 < hi;
 }
 
 // Waves per SIMD the kernel is built for: the FP8-family and FP4 kernels fit in
@@ -222,33 +248,13 @@ __global__ void __launch_bounds__(kThreads)
                        hdr->H == 64 && hdr->D == 128 && hdr->tile_rows == kTileRows && hdr->n_tiles == a.n_tiles;
   const int bid = blockIdx.x;
   if (bid >= a.n_compute) {
-    cleanup_unit<OBF, CLEAN>(a, bid - a.n_compute, plan_ok);
+    cleanup_unit<OBF, CLEAN, kTileRows>(a, bid - a.n_compute, plan_ok);
     return;
   }
   if (!plan_ok) return;
 
-  // Workgroups are dealt to the 8 XCDs round-robin (bid % 8).  When the chunk
-  // count is a multiple of 8, XCD x only ever gets chunks x, x+8, ... so its
-  // slice of K stays in its own L2; consecutive units of one XCD share a tile
-  // so that tile's Q is fetched once per XCD.  Longest tiles go first: under
-  // causal windows the last rows see the most keys.
-  int tile, chunk;
-  if (a.xcd_chunks) {
-    const int x = bid & 7, i = bid >> 3, cpx = a.n_chunks >> 3;
-    tile = a.n_tiles - 1 - i / cpx;
-    chunk = x + 8 * (i % cpx);
-  } else {
-    tile = a.n_tiles - 1 - bid / a.n_chunks;
-    chunk = bid % a.n_chunks;
-  }
-  const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
-  const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
-  // the tile's coverage in n_chunks equal parts (multiples of 64 columns, at
-  // least min_chunk): every unit of a tile gets the same amount of work
-  const int ccols = max(a.min_chunk, ((hi - lo + a.n_chunks - 1) / a.n_chunks + 63) & ~63);
-  const int c0 = lo + chunk * ccols;
-  if (c0 >= hi) return;
-  const int c1 = min(hi, c0 + ccols);  // columns [c0, c1) are this unit's
+  int tile, c0, c1;
+  if (!unit_columns(a, bid, tile, c0, c1)) return;  // columns [c0, c1) of the tile are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
 

@@ -30,6 +30,9 @@ def test_exports_every_declared_symbol():
 
 def test_plan_bytes():
     assert lib.idx_logits_plan_bytes(1, 128, 512) > 0
+    # tiles hold 512 / H rows: fewer, taller tiles at fewer heads
+    assert lib.idx_logits_plan_bytes(1, 4096, 512, H=8) < lib.idx_logits_plan_bytes(1, 4096, 512, H=64)
+    assert lib.idx_logits_plan_bytes(1, 128, 512, H=24) == 0
     assert lib.idx_logits_plan_bytes(0, 128, 512) == 0
     assert lib.idx_logits_plan_bytes(1, -1, 512) == 0
     a = lib.idx_logits_plan_bytes(1, 2048, 32768)
@@ -59,7 +62,8 @@ def _run(a, plan=None, ws=None, ws_bytes=0):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(H=32), lib.IDX_E_UNSUPPORTED),
+    (dict(H=24), lib.IDX_E_UNSUPPORTED),
+    (dict(H=128), lib.IDX_E_UNSUPPORTED),
     (dict(D=64), lib.IDX_E_UNSUPPORTED),
     (dict(B=0), lib.IDX_E_INVALID),
     (dict(S_k=-3), lib.IDX_E_INVALID),
@@ -88,7 +92,7 @@ def test_run_needs_plan_or_workspace():
 
 def test_plan_rejects():
     L = lib.lib()
-    assert L.idx_logits_plan(1, 16, 64, 32, 128, None, None, None, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan(1, 16, 64, 48, 128, None, None, None, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, FAKE, None, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan(1, 16, 64, 64, 128, None, None, None, FAKE, 8, None) == lib.IDX_E_WORKSPACE
@@ -96,7 +100,7 @@ def test_plan_rejects():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(H=32), lib.IDX_E_UNSUPPORTED),
+    (dict(H=24), lib.IDX_E_UNSUPPORTED),
     (dict(in_dtype=9), lib.IDX_E_INVALID),
     (dict(q=None), lib.IDX_E_INVALID),
     (dict(out_row_stride=63), lib.IDX_E_INVALID),
@@ -131,7 +135,7 @@ def test_plan_thd_rejects():
     assert L.idx_logits_plan_thd(0, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 0, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_thd(2, None, FAKE, 2, 16, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
-    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 32, 128, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 4, 128, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 0, 8, 64, 128, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan_thd(2, FAKE, FAKE, 2, 16, 8, 64, 128, FAKE, 8, None) == lib.IDX_E_WORKSPACE
@@ -171,7 +175,7 @@ def test_paged_rejects(kw, status):
 def test_paged_call_checks():
     L = lib.lib()
     kv = _paged()
-    assert L.idx_logits_run_paged(ctypes.byref(_args(H=32)), ctypes.byref(kv), None, FAKE, 1 << 30,
+    assert L.idx_logits_run_paged(ctypes.byref(_args(H=24)), ctypes.byref(kv), None, FAKE, 1 << 30,
                                   None) == lib.IDX_E_UNSUPPORTED
     assert L.idx_logits_run_paged(ctypes.byref(_args()), None, None, FAKE, 1 << 30, None) == lib.IDX_E_INVALID
     assert L.idx_logits_run_paged(ctypes.byref(_args()), ctypes.byref(kv), None, None, 0, None) == lib.IDX_E_WORKSPACE
@@ -187,7 +191,7 @@ def test_paged_call_checks():
 
 def test_plan_paged_rejects():
     L = lib.lib()
-    assert L.idx_logits_plan_paged(1, 16, 64, 32, 128, FAKE, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
+    assert L.idx_logits_plan_paged(1, 16, 64, 12, 128, FAKE, FAKE, 1 << 20, None) == lib.IDX_E_UNSUPPORTED
     assert L.idx_logits_plan_paged(0, 16, 64, 64, 128, FAKE, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, None, FAKE, 1 << 20, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, None, 1 << 20, None) == lib.IDX_E_WORKSPACE

@@ -254,7 +254,7 @@ def test_plan_dimension_mismatch_is_loud():
 # ---------------------------------------------------------------------------
 
 NAMED = ["c2", "c3", "c3_noclean", "c4_mxfp8", "c4_mxfp4", "c4_mxfp8_zero", "c4_mxfp4_zero", "c5", "thd_bf16_r4",
-         "paged_mxfp8_decode"]
+         "paged_mxfp8_decode", "screen_h8", "screen_h32"]
 
 
 @pytest.mark.parametrize("name", NAMED)
@@ -339,7 +339,7 @@ def test_thd_plan_rejects():
     with pytest.raises(lib.IdxError):
         lib.idx_logits_plan_thd([0, 4], [0, 2], 0, 4, 2)
     with pytest.raises(lib.IdxError):
-        lib.idx_logits_plan_thd([0, 4], [0, 2], 2, 4, 2, H=32)
+        lib.idx_logits_plan_thd([0, 4], [0, 2], 2, 4, 2, H=24)
 
 
 @pytest.mark.parametrize("sm_scale", [-0.7, 0.0, 1e-30, 3e4])
@@ -495,3 +495,51 @@ def test_paged_prepare_score_and_plan(fmt):
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int32), planned.view(torch.int32))
     assert torch.equal(one.view(torch.int32), out.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# 8, 16 and 32 query heads sharing the key head (tiles of 512 / H rows)
+# ---------------------------------------------------------------------------
+
+HEAD_CASES = [(f, H) for f in W.FORMATS for H in (8, 16, 32)]
+HEAD_IDS = [f"{f}-h{H}" for f, H in HEAD_CASES]
+
+
+@pytest.mark.parametrize("fmt,H", HEAD_CASES, ids=HEAD_IDS)
+def test_other_head_counts(fmt, H):
+    """Every cell against the oracle: two batches of two full tiles and a
+    ragged one, a ragged key tail, causal offsets of both signs, bf16 weights
+    and output for half the cases; a precomputed plan gives the same bits."""
+    tr = 512 // H
+    bf = H != 16
+    wl = W.make_random(fmt, 2, 2 * tr + 5, 3 * 32 * 7 + 13, H=H, seed=40 + H, offsets=[0, -17],
+                       w_dtype="bf16" if bf else "f32", out_dtype="bf16" if bf else "f32",
+                       sm_scale=1 / math.sqrt(128))
+    d = dev_inputs(wl)
+    out = run(wl, d)
+    _full_compare(wl, out, what=f"{fmt} H={H}")
+    out2 = run(wl, d, plan=make_plan(wl, d))
+    view = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out.view(view), out2.view(view))
+
+
+@pytest.mark.parametrize("fmt,H", HEAD_CASES, ids=HEAD_IDS)
+def test_other_head_counts_irregular(fmt, H):
+    """Irregular windows (reordered rows, empty rows, nonzero starts), clean
+    and not: values inside the windows, -inf placement when cleaning."""
+    wl = W.make_random(fmt, 1, 300, 1500, H=H, seed=60 + H, windows="irregular")
+    d = dev_inputs(wl)
+    _full_compare(wl, run(wl, d), what=f"{fmt} H={H} irregular")
+    _full_compare(wl, run(wl, d, clean=False), clean=False, what=f"{fmt} H={H} irregular unclean")
+
+
+@pytest.mark.parametrize("H", (8, 32))
+def test_other_head_counts_thd_and_paged(H):
+    """The packed variable-length and paged entry points at other head counts."""
+    wl = W.make_thd("mxfp8", (37, 0, 300, 90, 1), 2, H=H, seed=9)
+    d = dev_inputs(wl)
+    ref, bound = oracle.logits(wl)
+    compare_rows(wl, to_f64(run(wl, d)).reshape(wl.S_q, wl.S_k), ref, bound, what=f"thd H={H}")
+    wl = _paged("mxfp4", PAGED_CASES[1], H=H)
+    d = dev_inputs(wl)
+    _full_compare(wl, run(wl, d), what=f"paged H={H}")

@@ -363,6 +363,14 @@ def _paged_decode(**kw):
                       name="paged_mxfp8_decode", **kw)
 
 
+def _screen(H, **kw):
+    # the head-count screen of the DeepGEMM pull request 435 page (H = 8, 32,
+    # 64 at Q = KV = 8192, Performance section): MXFP8, causal, fp32 weights
+    # and scores; the screen's other settings are not printed
+    return make_random("mxfp8", 1, 8192, 8192, H=H, w_dtype="f32", sm_scale=1.0, seed=10 + H, offsets=[0],
+                       name=f"screen_h{H}_mxfp8_q8192", **kw)
+
+
 NAMED = {
     "c1": _c1,
     "c2": _c2,
@@ -376,6 +384,9 @@ NAMED = {
     "c5_nonaligned": lambda **kw: _c5(S_q=129, S_k=4100, seed=6, name="c5_nonaligned", **kw),
     "thd_bf16_r4": _thd,
     "paged_mxfp8_decode": _paged_decode,
+    "screen_h8": lambda **kw: _screen(8, **kw),
+    "screen_h32": lambda **kw: _screen(32, **kw),
+    "screen_h64": lambda **kw: _screen(64, **kw),
 }
 
 
