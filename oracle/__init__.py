@@ -60,6 +60,8 @@ class Oracle:
         lib.oracle_mqa_logits.argtypes = ([ctypes.c_int] * 6 + [P] * 5 + [ctypes.c_int, ctypes.c_double]
                                           + [P, P, P, ctypes.c_int64, P, P, ctypes.c_int])
         lib.oracle_mqa_logits.restype = ctypes.c_int
+        lib.oracle_topk.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P, P, ctypes.c_int, P, P]
+        lib.oracle_topk.restype = ctypes.c_int
         for name, argt in (("oracle_dec_bf16", ctypes.c_uint16), ("oracle_dec_e4m3", ctypes.c_uint8),
                            ("oracle_dec_e2m1", ctypes.c_uint8), ("oracle_dec_e8m0", ctypes.c_uint8)):
             fn = getattr(lib, name)
@@ -125,6 +127,27 @@ class Oracle:
         self.lib.oracle_windows(wl.B, wl.S_q, wl.S_k, _ptr(offs), _ptr(st), _ptr(en), _ptr(ws), _ptr(we))
         return ws, we
 
+    def topk(self, vals: np.ndarray, win_start: np.ndarray, win_end: np.ndarray, k: int):
+        """Top-k of every row of `vals` ([n_rows, >= S_k] fp32, or bf16 given as
+        uint16 bits) inside its window: (idx int32 [n_rows, k], val fp32
+        [n_rows, k]).  win_start / win_end: [n_rows] int32, within [0, S_k]."""
+        v = np.asarray(vals)
+        if v.dtype == np.uint16:
+            v = (v.astype(np.uint32) << 16).view(np.float32)
+        v = np.ascontiguousarray(v, np.float32)
+        assert v.ndim == 2
+        ws = np.ascontiguousarray(np.asarray(win_start).reshape(-1), np.int32)
+        we = np.ascontiguousarray(np.asarray(win_end).reshape(-1), np.int32)
+        n_rows = v.shape[0]
+        assert ws.size == n_rows and we.size == n_rows and k >= 1
+        assert np.all(ws >= 0) and np.all(we <= v.shape[1])
+        idx = np.empty((n_rows, k), np.int32)
+        val = np.empty((n_rows, k), np.float32)
+        if self.lib.oracle_topk(n_rows, v.shape[1], _ptr(v), v.shape[1], _ptr(ws), _ptr(we), int(k), _ptr(idx),
+                                _ptr(val)) != 0:
+            raise MemoryError("oracle_topk")
+        return idx, val
+
     def logits(self, wl, rows: Optional[Sequence[int]] = None, threads: int = 0, return_threads: bool = False):
         """fp64 scores and per-cell error scales.
 
@@ -174,3 +197,7 @@ def windows_thd(cu_q, cu_k, ratio, T_q, m_total):
 
 def logits(wl, rows=None, threads: int = 0, return_threads: bool = False):
     return default().logits(wl, rows=rows, threads=threads, return_threads=return_threads)
+
+
+def topk(vals, win_start, win_end, k):
+    return default().topk(vals, win_start, win_end, k)

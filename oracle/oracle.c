@@ -350,3 +350,62 @@ int oracle_mqa_logits(int B, int S_q, int S_k, int H, int D, int fmt, const void
   free(kn);
   return fail ? -1 : used;
 }
+
+/*
+ * Top-k selection over scores (the selection the pages place after the
+ * indexer: the sparse-attention page consumes a fixed number of key indices
+ * per query, 2048 for its DSv3.2 configurations, without saying how they are
+ * chosen).  The plainest reading, written out: among the columns of row r's
+ * window [win_start[r], win_end[r]), rank by score, larger first, equal
+ * scores (+0 and -0 are equal) by smaller column first, NaN after every
+ * number; the first k ranked columns are the selection, in rank order.
+ * Rows with fewer than k window columns fill the rest with column -1 and
+ * score -inf.  The sort is the C library's qsort on that ranking.
+ *
+ * vals: [n_rows, ld] fp32 scores (bf16 scores widened exactly by the caller).
+ * Out: idx [n_rows, k] int32, val [n_rows, k] fp32.  Returns 0, -1 on
+ * allocation failure.
+ */
+typedef struct {
+  float v;
+  int32_t j;
+} or_cand;
+
+static int or_rank(const void* pa, const void* pb) {
+  const or_cand* a = (const or_cand*)pa;
+  const or_cand* b = (const or_cand*)pb;
+  const int an = isnan(a->v) != 0, bn = isnan(b->v) != 0;
+  if (an != bn) return an ? 1 : -1;  /* NaN after every number */
+  if (!an) {
+    if (a->v > b->v) return -1;      /* larger score first */
+    if (a->v < b->v) return 1;
+  }
+  return (a->j > b->j) - (a->j < b->j);  /* equal scores: smaller column first */
+}
+
+int oracle_topk(int64_t n_rows, int S_k, const float* vals, int64_t ld, const int32_t* win_start,
+                const int32_t* win_end, int k, int32_t* idx, float* val) {
+  or_cand* c = (or_cand*)malloc(sizeof(or_cand) * (size_t)(S_k > 0 ? S_k : 1));
+  if (!c) return -1;
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int32_t s = win_start[r], e = win_end[r];
+    int n = 0;
+    for (int32_t j = s; j < e; ++j) {
+      c[n].v = vals[r * ld + j];
+      c[n].j = j;
+      ++n;
+    }
+    qsort(c, (size_t)n, sizeof(or_cand), or_rank);
+    for (int t = 0; t < k; ++t) {
+      if (t < n) {
+        idx[r * k + t] = c[t].j;
+        val[r * k + t] = c[t].v;
+      } else {
+        idx[r * k + t] = -1;
+        val[r * k + t] = -INFINITY;
+      }
+    }
+  }
+  free(c);
+  return 0;
+}

@@ -582,4 +582,90 @@ def pin_bound_dominates(orc):
         assert np.all(np.abs(ref[fin]) <= bound[fin] * (1 + 1e-12))
 
 
+
+
+# --------------------------------------------------------------------------
+# top-k selection
+# --------------------------------------------------------------------------
+
+def _f32(s: str) -> np.float32:
+    return np.float32(float(s))
+
+
+def pin_topk_golden(orc):
+    """The hand-worked selections of tests/golden/topk_cases.json (ties, signed zeros,
+    NaN, -inf, short and empty windows)."""
+    with open(os.path.join(GOLDEN, "topk_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        v = np.array([[_f32(x) for x in c["row"]]], np.float32)
+        idx, val = orc.topk(v, [c["start"]], [c["end"]], c["k"])
+        assert idx[0].tolist() == c["idx"], c["what"]
+        want = np.array([_f32(x) for x in c["val"]], np.float32)
+        # compare bit patterns (NaN and -0 included)
+        assert np.array_equal(val[0].view(np.uint32), want.view(np.uint32)) or (
+            np.array_equal(np.isnan(val[0]), np.isnan(want))
+            and np.array_equal(val[0][~np.isnan(want)].view(np.uint32), want[~np.isnan(want)].view(np.uint32))), \
+            c["what"]
+
+
+def pin_topk_matches_stable_argsort(orc):
+    """Without NaN the ranking is numpy's stable descending argsort of the window (a
+    library routine): scores drawn from a handful of values (many ties, both zeros) and
+    from a continuum, windows of every kind, k below, at and above the window size."""
+    rng = np.random.default_rng(5)
+    S_k = 300
+    pool = np.array([-2.5, -1.0, -0.0, 0.0, 0.5, 3.0, -np.inf], np.float32)
+    for trial in range(40):
+        n_rows = 7
+        if trial % 2:
+            v = pool[rng.integers(0, pool.size, size=(n_rows, S_k))]
+        else:
+            v = rng.standard_normal((n_rows, S_k)).astype(np.float32)
+        s = rng.integers(0, S_k, size=n_rows)
+        e = np.minimum(S_k, s + rng.integers(0, S_k, size=n_rows))
+        s[0], e[0] = 0, S_k
+        k = int(rng.choice([1, 5, 64, 200, 400]))
+        idx, val = orc.topk(v, s.astype(np.int32), e.astype(np.int32), k)
+        for r in range(n_rows):
+            order = np.argsort(-v[r, s[r]:e[r]], kind="stable")[:k] + s[r]
+            m = order.size
+            assert idx[r, :m].tolist() == order.tolist()
+            assert np.all(idx[r, m:] == -1) and np.all(np.isneginf(val[r, m:]))
+            assert np.array_equal(val[r, :m].view(np.uint32), v[r, order].view(np.uint32))
+
+
+def pin_topk_selection_property(orc):
+    """With NaN present: the selection holds min(k, n) distinct window columns, every
+    selected score ranks at or above every unselected one (a number above NaN), an equal
+    unselected score only ever sits at a larger column than every equal selected one, and
+    the listed scores are those of the listed columns."""
+    rng = np.random.default_rng(6)
+    S_k = 120
+    for _ in range(30):
+        v = rng.integers(-3, 4, size=(5, S_k)).astype(np.float32)
+        v[rng.random(v.shape) < 0.1] = np.nan
+        s = rng.integers(0, 40, size=5).astype(np.int32)
+        e = (s + rng.integers(0, 80, size=5)).astype(np.int32)
+        k = int(rng.integers(1, 60))
+        idx, val = orc.topk(v, s, e, k)
+        for r in range(5):
+            n = int(e[r] - s[r])
+            sel = [j for j in idx[r].tolist() if j >= 0]
+            assert len(sel) == min(k, n) and len(set(sel)) == len(sel)
+            assert all(s[r] <= j < e[r] for j in sel)
+            rest = [j for j in range(s[r], e[r]) if j not in set(sel)]
+            for j in sel:
+                for u in rest:
+                    a, b = v[r, j], v[r, u]
+                    if np.isnan(a):
+                        assert np.isnan(b) and j < u
+                    elif not np.isnan(b):
+                        assert a > b or (a == b and j < u)
+            got = val[r, :len(sel)]
+            want = v[r, sel]
+            assert np.array_equal(np.isnan(got), np.isnan(want))
+            assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

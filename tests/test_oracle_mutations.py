@@ -45,6 +45,11 @@ MUTANTS = [
     ("thd_visible_ceil", "e = s + (t + 1) / ratio", "e = s + (t + ratio) / ratio", 0),
     ("thd_no_segment_clamp", "if (e > lim) e = lim;", "", 0),
     ("thd_start_global", "int64_t s = cu_k[seg],", "int64_t s = cu_k[0],", 0),
+    ("topk_ascending", "if (a->v > b->v) return -1;", "if (a->v < b->v) return -1;", 0),
+    ("topk_ties_to_larger_column", "return (a->j > b->j) - (a->j < b->j);", "return (a->j < b->j) - (a->j > b->j);", 0),
+    ("topk_nan_first", "if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;", 0),
+    ("topk_window_start_ignored", "for (int32_t j = s; j < e; ++j) {", "for (int32_t j = 0; j < e; ++j) {", 0),
+    ("topk_padding_score_zero", "val[r * k + t] = -INFINITY;", "val[r * k + t] = 0.0f;", 0),
 ]
 
 
