@@ -23,7 +23,8 @@ IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
-            "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_workspace_bytes",
+            "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_topk",
+            "idx_logits_workspace_bytes",
             "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_prepare_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, SZ, P]
         L.idx_logits_run_paged.restype = ctypes.c_int
         L.idx_logits_run_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
+        L.idx_logits_topk.restype = ctypes.c_int
+        L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, P, P, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
@@ -361,3 +364,37 @@ def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: i
                                                                 workspace.numel() * workspace.element_size(),
                                                                 _stream(stream, device)))
     return out
+
+
+MAX_TOPK = 2048
+
+
+def idx_logits_topk(plan: torch.Tensor, logits: torch.Tensor, k: int, *, B: Optional[int] = None, H: int = 64,
+                    D: int = 128, S_k: Optional[int] = None, with_values: bool = True,
+                    out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+                    stream=None):
+    """Top-k columns of every row's window in `logits` ([B, S_q, ld] or
+    [S_q, ld], float32 or bfloat16, rows contiguous), from the plan the scores
+    were made with.  Returns (idx int32 [..., S_q, k], val float32 or None)."""
+    if logits.dtype not in FP_DTYPES:
+        raise ValueError("logits must be float32 or bfloat16")
+    if logits.stride(-1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    lead = tuple(logits.shape[:-1])
+    S_q = logits.shape[-2]
+    if B is None:
+        B = logits.shape[0] if logits.dim() == 3 else 1
+    if logits.dim() == 3 and logits.stride(0) != S_q * logits.stride(-2):
+        raise ValueError("logits batches must be packed at S_q * row stride")
+    if S_k is None:
+        S_k = logits.shape[-1]
+    device = logits.device
+    if out_idx is None:
+        out_idx = torch.empty(lead + (k,), dtype=torch.int32, device=device)
+    if with_values and out_val is None:
+        out_val = torch.empty(lead + (k,), dtype=torch.float32, device=device)
+    _check("idx_logits_topk", lib().idx_logits_topk(_ptr(plan), B, S_q, S_k, H, D, _ptr(logits),
+                                                      FP_DTYPES[logits.dtype], logits.stride(-2), k, _ptr(out_idx),
+                                                      _ptr(out_val) if with_values else None,
+                                                      _stream(stream, device)))
+    return out_idx, (out_val if with_values else None)

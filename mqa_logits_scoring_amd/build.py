@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libidx_logits.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
+SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "topk.hip", "score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
 HEADERS = ["internal.h", "score_kernel.h", "score_kernel_gh.h", "plan_segment.h", os.path.join("..", "..", "include", "idx_logits.h")]
 ARCH = "gfx950"
 

@@ -347,6 +347,32 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
   return score(a, p, WL, ws, s);
 }
 
+idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                             const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, int32_t* topk_idx,
+                             float* topk_val, void* stream) {
+  idx_status_t st = check_dims(B, S_q, S_k, H, D);
+  if (st != IDX_OK) return st;
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_topk needs the plan the scores were made with");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  if (logits_dtype != IDX_F32 && logits_dtype != IDX_BF16)
+    return fail(IDX_E_INVALID, "logits_dtype must be IDX_F32 or IDX_BF16");
+  const uintptr_t es = logits_dtype == IDX_BF16 ? 2 : 4;
+  if (logits == nullptr || topk_idx == nullptr) return fail(IDX_E_INVALID, "logits and topk_idx must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(logits) % es) != 0 || (reinterpret_cast<uintptr_t>(topk_idx) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(topk_val) & 3u) != 0)
+    return fail(IDX_E_INVALID, "logits, topk_idx and topk_val must be aligned to their element size");
+  if (k < 1 || k > idx::kMaxTopK) return fail(IDX_E_UNSUPPORTED, "k=%d outside [1, %d]", k, idx::kMaxTopK);
+  if (ld < S_k) return fail(IDX_E_INVALID, "ld %lld < S_k %d", (long long)ld, S_k);
+  const int64_t rows = int64_t(B) * S_q;
+  if (ld > (int64_t(1) << 40) || rows * ld > (int64_t(1) << 40))
+    return fail(IDX_E_INVALID, "scores of %lld rows x stride %lld elements are too large", (long long)rows,
+                (long long)ld);
+  hipError_t e = idx::launch_topk(plan, B, S_q, S_k, H, D, logits, logits_dtype == IDX_BF16, ld, k, topk_idx,
+                                  topk_val, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(IDX_E_HIP, "top-k launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
 idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void* workspace, size_t workspace_bytes,
                               void* stream) {
   idx_status_t st = check_args(a, true);  // the keys come from the workspace

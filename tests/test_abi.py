@@ -197,3 +197,24 @@ def test_plan_paged_rejects():
     assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, None, 1 << 20, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, FAKE, 8, None) == lib.IDX_E_WORKSPACE
     assert L.idx_logits_plan_paged(1, 16, 64, 64, 128, FAKE, FAKE + 64, 1 << 20, None) == lib.IDX_E_INVALID
+
+
+def test_topk_rejects():
+    L = lib.lib()
+
+    def call(plan=FAKE, B=1, S_q=16, S_k=64, H=64, D=128, logits=FAKE, dt=0, ld=64, k=8, idx=FAKE, val=FAKE):
+        return L.idx_logits_topk(plan, B, S_q, S_k, H, D, logits, dt, ld, k, idx, val, None)
+
+    assert call(H=24) == lib.IDX_E_UNSUPPORTED
+    assert call(B=0) == lib.IDX_E_INVALID
+    assert call(plan=None) == lib.IDX_E_WORKSPACE
+    assert call(plan=FAKE + 64) == lib.IDX_E_INVALID
+    assert call(dt=7) == lib.IDX_E_INVALID
+    assert call(logits=None) == lib.IDX_E_INVALID
+    assert call(idx=None) == lib.IDX_E_INVALID
+    assert call(logits=FAKE + 2) == lib.IDX_E_INVALID   # fp32 scores need 4-byte alignment
+    assert call(val=FAKE + 2) == lib.IDX_E_INVALID
+    assert call(k=0) == lib.IDX_E_UNSUPPORTED
+    assert call(k=lib.MAX_TOPK + 1) == lib.IDX_E_UNSUPPORTED
+    assert call(ld=63) == lib.IDX_E_INVALID
+    assert "ld" in lib.idx_last_error()
