@@ -280,11 +280,13 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
  * sparse-attention page, FlashInfer SM120 sparse MLA, consumes: 2048 keys per
  * query token for its DSv3.2 configurations; the pages do not say how the
  * list is chosen, this is the plainest reading).  For every row r = b*S_q + i
- * of `plan` (built for B, S_q, S_k, H, D) with window [start, end):
- *   topk_idx[r, 0..k) = the columns of [start, end) ranked by score, larger
- *                       first; equal scores (+0 and -0 are equal) go to the
- *                       smaller column; NaN ranks after every number.  When
- *                       the window has n < k columns, entries n..k-1 are -1.
+ * of `plan` (built for B, S_q, S_k, H, D) with window [start, end), rank the
+ * columns of [start, end) by score, larger first; equal scores (+0 and -0 are
+ * equal) go to the smaller column; NaN ranks after every number.  The
+ * selection is the first min(k, n) ranked columns (n = end - start):
+ *   topk_idx[r, 0..k) = the selection in ascending column order
+ *                       (IDX_TOPK_BY_COLUMN) or in rank order
+ *                       (IDX_TOPK_BY_SCORE), then -1 for entries n..k-1.
  *   topk_val[r, 0..k) = those columns' scores as stored in `logits` (widened
  *                       to fp32), -inf for the -1 entries.  May be NULL.
  *  logits        [B, S_q, ld] in logits_dtype (IDX_F32 or IDX_BF16), the
@@ -297,9 +299,11 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
  * entry is then -1 (and NaN in topk_val).  Deterministic: the selection is
  * unique, so it does not depend on the launch.
  */
+typedef enum { IDX_TOPK_BY_COLUMN = 0, IDX_TOPK_BY_SCORE = 1 } idx_topk_order_t;
+
 idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
-                             const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, int32_t* topk_idx,
-                             float* topk_val, void* stream);
+                             const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, idx_topk_order_t order,
+                             int32_t* topk_idx, float* topk_val, void* stream);
 
 /*
  * Copy the windows stored in a plan into caller device arrays

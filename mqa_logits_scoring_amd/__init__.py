@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_run_paged.restype = ctypes.c_int
         L.idx_logits_run_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
         L.idx_logits_topk.restype = ctypes.c_int
-        L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, P, P, P]
+        L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, ctypes.c_int, P, P, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
@@ -369,13 +369,18 @@ def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: i
 MAX_TOPK = 2048
 
 
-def idx_logits_topk(plan: torch.Tensor, logits: torch.Tensor, k: int, *, B: Optional[int] = None, H: int = 64,
-                    D: int = 128, S_k: Optional[int] = None, with_values: bool = True,
-                    out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
-                    stream=None):
+TOPK_ORDERS = {"column": 0, "score": 1}
+
+
+def idx_logits_topk(plan: torch.Tensor, logits: torch.Tensor, k: int, *, order: str = "column",
+                    B: Optional[int] = None, H: int = 64, D: int = 128, S_k: Optional[int] = None,
+                    with_values: bool = True, out_idx: Optional[torch.Tensor] = None,
+                    out_val: Optional[torch.Tensor] = None, stream=None):
     """Top-k columns of every row's window in `logits` ([B, S_q, ld] or
     [S_q, ld], float32 or bfloat16, rows contiguous), from the plan the scores
-    were made with.  Returns (idx int32 [..., S_q, k], val float32 or None)."""
+    were made with, listed by ascending column (order="column") or in rank
+    order (order="score").  Returns (idx int32 [..., S_q, k], val float32 or
+    None)."""
     if logits.dtype not in FP_DTYPES:
         raise ValueError("logits must be float32 or bfloat16")
     if logits.stride(-1) != 1:
@@ -394,7 +399,8 @@ def idx_logits_topk(plan: torch.Tensor, logits: torch.Tensor, k: int, *, B: Opti
     if with_values and out_val is None:
         out_val = torch.empty(lead + (k,), dtype=torch.float32, device=device)
     _check("idx_logits_topk", lib().idx_logits_topk(_ptr(plan), B, S_q, S_k, H, D, _ptr(logits),
-                                                      FP_DTYPES[logits.dtype], logits.stride(-2), k, _ptr(out_idx),
+                                                      FP_DTYPES[logits.dtype], logits.stride(-2), k,
+                                                      TOPK_ORDERS[order], _ptr(out_idx),
                                                       _ptr(out_val) if with_values else None,
                                                       _stream(stream, device)))
     return out_idx, (out_val if with_values else None)

@@ -348,8 +348,8 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
 }
 
 idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
-                             const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, int32_t* topk_idx,
-                             float* topk_val, void* stream) {
+                             const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, idx_topk_order_t order,
+                             int32_t* topk_idx, float* topk_val, void* stream) {
   idx_status_t st = check_dims(B, S_q, S_k, H, D);
   if (st != IDX_OK) return st;
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_topk needs the plan the scores were made with");
@@ -362,13 +362,15 @@ idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S
       (reinterpret_cast<uintptr_t>(topk_val) & 3u) != 0)
     return fail(IDX_E_INVALID, "logits, topk_idx and topk_val must be aligned to their element size");
   if (k < 1 || k > idx::kMaxTopK) return fail(IDX_E_UNSUPPORTED, "k=%d outside [1, %d]", k, idx::kMaxTopK);
+  if (order != IDX_TOPK_BY_COLUMN && order != IDX_TOPK_BY_SCORE)
+    return fail(IDX_E_INVALID, "order must be IDX_TOPK_BY_COLUMN or IDX_TOPK_BY_SCORE");
   if (ld < S_k) return fail(IDX_E_INVALID, "ld %lld < S_k %d", (long long)ld, S_k);
   const int64_t rows = int64_t(B) * S_q;
   if (ld > (int64_t(1) << 40) || rows * ld > (int64_t(1) << 40))
     return fail(IDX_E_INVALID, "scores of %lld rows x stride %lld elements are too large", (long long)rows,
                 (long long)ld);
-  hipError_t e = idx::launch_topk(plan, B, S_q, S_k, H, D, logits, logits_dtype == IDX_BF16, ld, k, topk_idx,
-                                  topk_val, static_cast<hipStream_t>(stream));
+  hipError_t e = idx::launch_topk(plan, B, S_q, S_k, H, D, logits, logits_dtype == IDX_BF16, ld, k,
+                                  order == IDX_TOPK_BY_SCORE, topk_idx, topk_val, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(IDX_E_HIP, "top-k launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
 }

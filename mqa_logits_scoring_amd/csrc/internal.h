@@ -245,11 +245,12 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
                           const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
                           const PlanBuild* build, const PagedK* paged, hipStream_t stream);
 // Top-k selection over the scores a call wrote (topk.hip): for each of the
-// plan's rows, the k <= kMaxTopK best columns of its window in rank order.
+// plan's rows, the k <= kMaxTopK best columns of its window, by column or in
+// rank order.
 constexpr int kMaxTopK = 2048;
 hipError_t launch_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
-                       const void* logits, bool logits_bf16, int64_t ld, int32_t k, int32_t* out_idx,
-                       float* out_val, hipStream_t stream);
+                       const void* logits, bool logits_bf16, int64_t ld, int32_t k, bool by_score,
+                       int32_t* out_idx, float* out_val, hipStream_t stream);
 
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);

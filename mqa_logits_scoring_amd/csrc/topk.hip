@@ -1,47 +1,58 @@
 // Top-k selection over the scores of a scoring call (gfx950).
 //
-// For each query row, the k columns of its window with the largest scores,
-// larger first, equal scores by smaller column, NaN after every number
-// (+0 and -0 equal); columns past the window's size are -1 with score -inf.
-// The sparse-attention page (FlashInfer SM120 sparse MLA, Summary and the
-// DSv3.2 prefill notes) consumes such a per-query list of 2048 key indices;
-// the pages do not say how it is chosen, so the ranking above is the plain
-// one and the algorithm is this file's own.
+// For each query row, the k columns of its window with the largest scores:
+// larger first, equal scores by smaller column, NaN after every number (+0
+// and -0 equal); listed by ascending column or in that rank order; columns
+// past the window's size are -1 with score -inf.  The sparse-attention page
+// (FlashInfer SM120 sparse MLA, Summary and the DSv3.2 prefill notes)
+// consumes such a per-query list of 2048 key indices; the pages do not say
+// how it is chosen, so the ranking above is the plain one and the algorithm
+// is this file's own.
 //
-// One workgroup per row.  Scores become 32-bit keys whose unsigned order is
-// the ranking (sign-magnitude flipped to two's-complement-like order, -0
-// folded onto +0, NaN to 0).  A radix select finds the k-th largest key T in
-// three histogram passes over 12 + 12 + 8 key bits (4096 LDS bins, one atomic
-// per candidate; each pass only counts keys that match the digits fixed so
-// far).  When more keys equal T than the selection still needs, the same
-// select runs on the column (smaller column = larger secondary key) among
-// the keys equal to T.  The selected k are written to LDS as 64-bit (key,
-// ~column) pairs and put in rank order by a bitonic sort.
+// One workgroup of 512 threads per row.  Scores become 32-bit keys whose
+// unsigned order is the ranking (sign-magnitude flipped, -0 folded onto +0,
+// NaN to 0).  Thread t holds columns s + ch*kChunk + m*512 + t (m < 64) of
+// chunk ch in registers, so every load instruction of a wave reads 64
+// consecutive scores; rows up to kChunk columns are read once, longer rows
+// once per pass.
 //
-// Layout: thread t of the workgroup holds columns s + ch*kChunk + m*kTopkThreads
-// + t (m < kPerThread) of chunk ch, so every load instruction of a wave reads
-// 64 consecutive scores.  Rows up to kChunk columns keep their keys in
-// registers across the passes; longer rows read their chunks again in every
-// pass (from L2).
+//  1. A histogram of the top 12 key bits (4096 LDS bins) fixes the bucket b
+//     holding the k-th largest key: every key above b is selected.
+//  2. When b holds at most kCand keys, they are compacted into LDS with their
+//     columns and the rest of the selection is a radix select over that short
+//     list (key bits 19..8, 7..0, then the column for keys equal to the
+//     threshold).  A flat row (b holding more) runs those passes over the
+//     registers instead.  Either way the result is a threshold (T, T2): a key
+//     is selected when it is above T, or equal to T with a column no larger
+//     than the one T2 names.
+//  3. The selected keys are written out: by column, each wave ballots its
+//     selection per register and one block scan over the (register, wave)
+//     counts gives every selected column its place; in rank order they go to
+//     LDS as (key, ~column) pairs and a bitonic sort orders them.
 #include "internal.h"
 
 namespace idx {
 
 namespace {
 
-constexpr int kTopkThreads = 512;
-constexpr int kPerThread = 64;
-constexpr int kChunk = kTopkThreads * kPerThread;  // 32768 columns
-constexpr int kBins = 4096;
+constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-static_assert(kBins % kTopkThreads == 0, "every thread owns whole bins");
-constexpr int kBinsPerThread = kBins / kTopkThreads;
+constexpr int kPerThread = 32;
+constexpr int kChunk = kTopkThreads * kPerThread;  // 32768 columns
+constexpr int kBins1 = 1024;                        // first pass: key bits 31..22
+constexpr int kCopies1 = 8;                         // lane-interleaved copies of the first histogram
+constexpr int kBins = 4096;                         // later passes: up to 12 bits
+constexpr int kCand = 4096;                         // threshold-bucket keys kept in LDS
+static_assert(kBins1 * kCopies1 >= kBins, "the first histogram's storage holds the later ones");
+static_assert(kBins % kTopkThreads == 0 && kBins1 % kTopkThreads == 0, "every thread owns whole bins");
+constexpr int kCounts = kPerThread * kTopkWaves;  // (register, wave) counts of the column-order output
+static_assert(kCounts <= kTopkThreads, "one (register, wave) count per thread at most");
 
 // Unsigned order of the result = the ranking of the scores (NaN lowest).
 __device__ __forceinline__ uint32_t rank_key(uint32_t u) {
-  u = u == 0x80000000u ? 0u : u;                       // -0 ranks as +0
+  u = u == 0x80000000u ? 0u : u;  // -0 ranks as +0
   const uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
-  return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;      // NaN
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;  // NaN
 }
 
 template <bool BF>
@@ -53,11 +64,26 @@ __device__ __forceinline__ uint32_t score_bits(const void* logits, int64_t i) {
 }
 
 struct TopkSmem {
-  uint32_t hist[kBins];
-  uint64_t sel[kMaxTopK];
+  uint32_t hist[kBins1 * kCopies1];  // first pass: bin b, copy c at b * kCopies1 + c
+  union {
+    struct {
+      uint32_t key[kCand];
+      uint32_t rel[kCand];
+    } cand;                  // the threshold bucket's keys and columns (past s)
+    uint64_t sel[kMaxTopK];  // rank order: the selection as (key, ~column) pairs
+    struct {
+      int32_t idx[kMaxTopK];
+      uint32_t bits[kMaxTopK];
+    } out;                   // column order: the selection staged for coalesced stores
+  };
+  uint32_t wcount[kCounts];  // selected per (register m, wave), in column order
   uint32_t wsum[kTopkWaves];
-  uint32_t digit, above, count, n_sel;
+  uint32_t digit, above, count, n_cand, n_sel;
 };
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
 
 // Inclusive prefix sum of v over the workgroup's threads (thread order);
 // `total` receives the sum over all threads.  Contains barriers.
@@ -83,34 +109,40 @@ __device__ uint32_t block_scan(uint32_t v, TopkSmem& sm, uint32_t& total) {
   return x + before;
 }
 
-// One radix-select pass: among the candidates (cand(key2, ...) true), count the
-// digit (key >> shift) & dmask, then find the digit d holding the want-th
-// largest candidate.  Returns d; `above` = candidates with a larger digit,
-// `count` = candidates with digit d.
 struct PassResult {
   uint32_t digit, above, count;
 };
 
+// After a histogram pass over NB bins of C copies each: the digit d whose
+// bin holds the want-th largest counted key; `above` = keys counted in higher
+// bins, `count` = in bin d.
+template <int NB, int C>
 __device__ PassResult find_digit(TopkSmem& sm, uint32_t want) {
+  constexpr int BPT = NB / kTopkThreads;
   __syncthreads();  // histogram complete
   const int t = threadIdx.x;
-  uint32_t local = 0;
+  uint32_t h[BPT], local = 0;
 #pragma unroll
-  for (int b = 0; b < kBinsPerThread; ++b) local += sm.hist[t * kBinsPerThread + b];
+  for (int b = 0; b < BPT; ++b) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) x += sm.hist[(t * BPT + b) * C + c];
+    h[b] = x;
+    local += x;
+  }
   uint32_t total;
   const uint32_t incl = block_scan(local, sm, total);
-  const uint32_t above = total - incl;  // candidates in the bins of higher threads
+  const uint32_t above = total - incl;  // keys in the bins of higher threads
   if (above < want && above + local >= want) {
     uint32_t cum = above;
-    for (int b = kBinsPerThread - 1; b >= 0; --b) {
-      const uint32_t h = sm.hist[t * kBinsPerThread + b];
-      if (cum + h >= want) {
-        sm.digit = uint32_t(t * kBinsPerThread + b);
+#pragma unroll
+    for (int b = BPT - 1; b >= 0; --b) {
+      if (cum < want && cum + h[b] >= want) {
+        sm.digit = uint32_t(t * BPT + b);
         sm.above = cum;
-        sm.count = h;
-        break;
+        sm.count = h[b];
       }
-      cum += h;
+      cum += h[b];
     }
   }
   __syncthreads();
@@ -119,18 +151,28 @@ __device__ PassResult find_digit(TopkSmem& sm, uint32_t want) {
   return r;
 }
 
+template <int N>
 __device__ __forceinline__ void clear_hist(TopkSmem& sm) {
-  for (int i = threadIdx.x; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+  for (int i = threadIdx.x; i < N; i += kTopkThreads) sm.hist[i] = 0;
   __syncthreads();
 }
 
-template <bool BF>
+// Score bits back from a key: exact except for the two keys that several
+// bit patterns share (+0 for -0 too, 0 for every NaN), which the caller reads
+// again.
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7FFFFFFFu) : ~k; }
+__device__ __forceinline__ bool key_is_shared(uint32_t k) { return k == 0x80000000u || k == 0u; }
+
+// MULTI: rows may span several chunks (S_k > kChunk).  The single-chunk
+// kernel reads its row once and has one load site, which keeps the load
+// offsets out of the registers the rest of the kernel needs.
+template <bool BF, bool BY_SCORE, bool MULTI>
 __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char* plan, int32_t B, int32_t S_q,
                                                              int32_t S_k, int32_t H, int32_t D, const void* logits,
                                                              int64_t ld, int32_t k, int32_t* out_idx,
                                                              float* out_val, uint32_t off_start, uint32_t off_end) {
   __shared__ TopkSmem sm;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t row = blockIdx.x;
   int32_t* oi = out_idx + row * k;
   float* ov = out_val != nullptr ? out_val + row * k : nullptr;
@@ -149,16 +191,36 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
   const int64_t e = reinterpret_cast<const int32_t*>(plan + off_end)[row];
   const int64_t n = e > s ? e - s : 0;
   const int64_t base = row * ld + s;
-  const int nch = int((n + kChunk - 1) / kChunk);
+  const int n_out = int(n < k ? n : k);  // entries that name a column
+  for (int i = n_out + t; i < k; i += kTopkThreads) {
+    oi[i] = -1;
+    if (ov) ov[i] = -__builtin_inff();
+  }
+  if (n == 0) return;
+  if (!BY_SCORE && n <= k) {  // the whole window, in column order
+    for (int i = t; i < n_out; i += kTopkThreads) {
+      oi[i] = int32_t(s + i);
+      if (ov) ov[i] = __uint_as_float(score_bits<BF>(logits, base + i));
+    }
+    return;
+  }
+  const int nch = MULTI ? int((n + kChunk - 1) / kChunk) : 1;
+  auto value_of = [&](uint32_t kk, uint32_t rel) {  // the score's exact bits
+    return key_is_shared(kk) ? score_bits<BF>(logits, base + rel) : key_bits(kk);
+  };
 
   // A chunk is read through a buffer resource based at its first column
   // (num_records = its width in bytes): the lane offset is the thread's, the
-  // per-element offset a scalar constant, so addresses take no registers.
+  // per-register offset a scalar constant, so addresses take no registers.
+  // Registers hold keys; columns past the window get key 0, the NaN key, and
+  // lose every tie to the window's own NaN (larger column), so when n > k
+  // they can never be selected and need no check.
   constexpr int ES = BF ? 2 : 4;
   uint32_t key[kPerThread];
   auto load = [&](int ch) {
     const int64_t c0 = int64_t(ch) * kChunk;
     const int64_t w = n - c0 < kChunk ? n - c0 : kChunk;
+    const int mv = w > t ? int((w - t + kTopkThreads - 1) / kTopkThreads) : 0;  // registers inside the window
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(static_cast<const unsigned char*>(logits)) + (base + c0) * ES, 0, int(w * ES),
         0x00020000);
@@ -169,37 +231,96 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
         bits = uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rs, t * ES, m * kTopkThreads * ES, 0)) << 16;
       else
         bits = __builtin_amdgcn_raw_buffer_load_b32(rs, t * ES, m * kTopkThreads * ES, 0);
-      key[m] = rank_key(bits);  // past the chunk's width: never a candidate (m >= valid(ch))
+      // masked, not selected: a select on m < mv gets the load sunk into a
+      // branch of its own, which then waits for it alone
+      key[m] = rank_key(bits) & (0u - uint32_t(m < mv));
     }
   };
-  // elements m < valid(ch) of this thread lie inside the window (32-bit
-  // arithmetic: a chunk is at most kChunk columns)
-  auto valid = [&](int ch) {
-    const int64_t w = n - int64_t(ch) * kChunk;
-    const int wc = w < kChunk ? int(w) : kChunk;
-    return wc > t ? (wc - t + kTopkThreads - 1) / kTopkThreads : 0;
-  };
+  if (!MULTI) load(0);
 
-  // threshold: select key > T, and key == T with secondary key >= T2, where the
-  // secondary key of column s + rel is (2^nbits - 1) - rel
-  uint32_t T = 0, T2 = 0;
+  // ---- the threshold ---------------------------------------------------------
+  // selected: column inside the window and (key > T, or key == T and
+  // (nbits == 0 or top - rel >= T2)); rel counts columns past s, up to the
+  // padded width nch * kChunk, so the secondary key top - rel never wraps.
+  uint32_t T = 0, T2 = 0, top = 0;
   int nbits = 0;
-  if (n > k) {
-    if (nch == 1) load(0);
-    uint32_t want = uint32_t(k), prefix = 0, mask = 0, count_eq = 0;
+  // One histogram pass over the registers: count digit (v >> shift) & dmask
+  // of every key with (key & msk) == pre, or in a tie pass (v = top - rel)
+  // of every key equal to T with (v & msk) == pre; `copies` interleaved
+  // histograms (1 or kCopies1).
+  auto reg_pass = [&](bool tie, int shift, uint32_t dmask, uint32_t pre, uint32_t msk, uint32_t copies) {
+    const uint32_t copy = uint32_t(lane) & (copies - 1u);
+    for (int ch = 0; ch < nch; ++ch) {
+      if (MULTI) load(ch);
+      uint32_t v0 = top - uint32_t(ch) * kChunk - uint32_t(t);  // tie key of register 0
+      // opaque to the optimiser: the 64 tie keys v0 - m * 512 are then formed
+      // inside the pass, not hoisted out of the passes into 64 live registers
+      asm volatile("" : "+v"(v0));
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {  // key bits [31:20], [19:8], [7:0]
-      const int shift = p == 0 ? 20 : (p == 1 ? 8 : 0);
-      const uint32_t dmask = p == 2 ? 0xFFu : 0xFFFu;
-      clear_hist(sm);
-      for (int ch = 0; ch < nch; ++ch) {
-        if (nch > 1) load(ch);
-        const int mv = valid(ch);
-#pragma unroll
-        for (int m = 0; m < kPerThread; ++m)
-          if (m < mv && (key[m] & mask) == prefix) atomicAdd(&sm.hist[(key[m] >> shift) & dmask], 1u);
+      for (int m = 0; m < kPerThread; ++m) {
+        const uint32_t kk = key[m];
+        const uint32_t v = tie ? v0 - uint32_t(m * kTopkThreads) : kk;
+        const bool c = tie ? (kk == T && (v & msk) == pre) : ((kk & msk) == pre);
+        if (c) atomicAdd(&sm.hist[(((v >> shift) & dmask) * copies) | copy], 1u);
       }
-      const PassResult r = find_digit(sm, want);
+    }
+  };
+  // The same over the candidates in LDS.
+  auto cand_pass = [&](int nc, bool tie, int shift, uint32_t dmask, uint32_t pre, uint32_t msk) {
+    for (int i = t; i < nc; i += kTopkThreads) {
+      const uint32_t kk = sm.cand.key[i];
+      const uint32_t v = tie ? top - sm.cand.rel[i] : kk;
+      const bool c = tie ? (kk == T && (v & msk) == pre) : ((kk & msk) == pre);
+      if (c) atomicAdd(&sm.hist[(v >> shift) & dmask], 1u);
+    }
+  };
+  if (n > k) {
+    uint32_t want = uint32_t(k);
+    while ((int64_t(1) << nbits) < int64_t(nch) * kChunk) ++nbits;
+    top = nbits == 32 ? 0xFFFFFFFFu : (1u << nbits) - 1u;
+    // 1. key bits 31..22 over the whole row, into lane-interleaved copies so
+    //    that lanes counting the same bin rarely touch the same word
+    clear_hist<kBins1 * kCopies1>(sm);
+    if (t == 0) sm.n_cand = 0;
+    reg_pass(false, 22, kBins1 - 1, 0u, 0u, kCopies1);
+    const PassResult r1 = find_digit<kBins1, kCopies1>(sm, want);
+    want -= r1.above;
+    uint32_t prefix = r1.digit << 22, mask = 0xFFC00000u, count_eq = r1.count;
+    // 2. the bucket's keys and columns into LDS when they fit (the passes
+    //    below then read the short list), else the passes read the registers
+    const bool listed = r1.count <= uint32_t(kCand);
+    if (listed) {
+      for (int ch = 0; ch < nch; ++ch) {
+        if (MULTI) load(ch);
+        uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);
+        asm volatile("" : "+v"(rel0));  // per-register columns formed here, not hoisted
+#pragma unroll
+        for (int m = 0; m < kPerThread; ++m) {
+          const bool in = (key[m] & mask) == prefix;
+          const uint64_t b = __ballot(in);
+          if (b != 0) {
+            uint32_t pos = 0;
+            if (lane == 0) pos = atomicAdd(&sm.n_cand, uint32_t(__popcll(b)));
+            pos = __shfl(pos, 0, 64) + lanes_below(b);
+            if (in && pos < uint32_t(kCand)) {
+              sm.cand.key[pos] = key[m];
+              sm.cand.rel[pos] = rel0 + uint32_t(m * kTopkThreads);
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+    const int nc = int(r1.count);  // == n_cand when listed
+    for (int p = 0; p < 2; ++p) {  // key bits [21:10], [9:0]
+      const int shift = p == 0 ? 10 : 0;
+      const uint32_t dmask = p == 0 ? 0xFFFu : 0x3FFu;
+      clear_hist<kBins>(sm);
+      if (listed)
+        cand_pass(nc, false, shift, dmask, prefix, mask);
+      else
+        reg_pass(false, shift, dmask, prefix, mask, 1u);
+      const PassResult r = find_digit<kBins, 1>(sm, want);
       want -= r.above;
       prefix |= r.digit << shift;
       mask |= dmask << shift;
@@ -207,101 +328,172 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
     }
     T = prefix;
     if (want < count_eq) {  // ties at T: the smallest columns among them
-      while ((int64_t(1) << nbits) < n) ++nbits;
-      const uint32_t top = nbits == 32 ? 0xFFFFFFFFu : (1u << nbits) - 1u;
       uint32_t prefix2 = 0, mask2 = 0;
       for (int hi = nbits; hi > 0; hi -= 12) {
         const int lo = hi > 12 ? hi - 12 : 0;
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
-        clear_hist(sm);
-        for (int ch = 0; ch < nch; ++ch) {
-          if (nch > 1) load(ch);
-          const int mv = valid(ch);
-          const uint32_t k2c = top - uint32_t(ch) * kChunk - uint32_t(t);  // secondary key of element 0
-#pragma unroll
-          for (int m = 0; m < kPerThread; ++m) {
-            const uint32_t k2 = k2c - uint32_t(m * kTopkThreads);
-            if (m < mv && key[m] == T && (k2 & mask2) == prefix2) atomicAdd(&sm.hist[(k2 >> lo) & dmask], 1u);
-          }
-        }
-        const PassResult r = find_digit(sm, want);
+        clear_hist<kBins>(sm);
+        if (listed)
+          cand_pass(nc, true, lo, dmask, prefix2, mask2);
+        else
+          reg_pass(true, lo, dmask, prefix2, mask2, 1u);
+        const PassResult r = find_digit<kBins, 1>(sm, want);
         want -= r.above;
         prefix2 |= r.digit << lo;
         mask2 |= dmask << lo;
       }
       T2 = prefix2;
+    } else {
+      nbits = 0;  // every key equal to T is selected
     }
   }
+  // n <= k (rank order only) selects every column of the window: T = 0, nbits = 0
+  const uint32_t n_rel = uint32_t(n);
+  auto selected = [&](uint32_t kk, uint32_t rel) {
+    return rel < n_rel && (kk > T || (kk == T && (nbits == 0 || top - rel >= T2)));
+  };
 
-  // gather the selection (exactly min(k, n) entries) as (key, ~column) pairs
-  if (t == 0) sm.n_sel = 0;
-  __syncthreads();
-  const uint32_t top = nbits == 0 ? 0u : (nbits == 32 ? 0xFFFFFFFFu : (1u << nbits) - 1u);
-  for (int ch = 0; ch < nch; ++ch) {
-    if (nch > 1 || n <= k) load(ch);
-    const int mv = valid(ch);
-    const uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);  // column of element 0, past s
+  // ---- the output ------------------------------------------------------------
+  if constexpr (!BY_SCORE) {
+    // by column: per chunk, every (register, wave) count in column order, one
+    // block scan, each selected column staged at its place in LDS, then
+    // written out with coalesced stores
+    uint32_t done = 0;  // selected columns of the earlier chunks
+    for (int ch = 0; ch < nch; ++ch) {
+      if (MULTI) load(ch);
+      uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);
+      asm volatile("" : "+v"(rel0));  // per-register columns formed here, not hoisted
+      uint64_t selm = 0;  // bit m: register m is selected
 #pragma unroll
-    for (int m = 0; m < kPerThread; ++m) {
-      const uint32_t rel = rel0 + uint32_t(m * kTopkThreads);
-      const bool take =
-          m < mv && (n <= k || key[m] > T || (key[m] == T && (nbits == 0 || top - rel >= T2)));
-      if (take) {
-        const uint32_t pos = atomicAdd(&sm.n_sel, 1u);
-        if (pos < uint32_t(kMaxTopK))  // exactly min(k, n) <= kMaxTopK by construction
-          sm.sel[pos] = (uint64_t(key[m]) << 32) | uint64_t(0xFFFFFFFFu - rel);
-      }
-    }
-  }
-  __syncthreads();
-  // pad to a power of two with 0 (below every real pair) and sort descending
-  int P = 1;
-  while (P < k) P <<= 1;
-  const int n_sel = int(min(sm.n_sel, uint32_t(kMaxTopK)));
-  for (int i = n_sel + t; i < P; i += kTopkThreads) sm.sel[i] = 0;
-  __syncthreads();
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < P / 2; i += kTopkThreads) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool descending = (lo & size) == 0;
-        const uint64_t x = sm.sel[lo], y = sm.sel[hi];
-        if ((x < y) == descending) {
-          sm.sel[lo] = y;
-          sm.sel[hi] = x;
-        }
+      for (int m = 0; m < kPerThread; ++m) {
+        const bool in = selected(key[m], rel0 + uint32_t(m * kTopkThreads));
+        selm |= uint64_t(in) << m;
+        const uint64_t b = __ballot(in);
+        if (lane == 0) sm.wcount[m * kTopkWaves + wave] = uint32_t(__popcll(b));
       }
       __syncthreads();
+      uint32_t total;
+      const uint32_t mine = t < kCounts ? sm.wcount[t] : 0u;
+      const uint32_t excl = block_scan(mine, sm, total) - mine;
+      if (t < kCounts) sm.wcount[t] = excl;  // entry t = (m, wave) in column order: its first place
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < kPerThread; ++m) {
+        const bool in = (selm >> m) & 1u;
+        const uint64_t b = __ballot(in);
+        if (in) {
+          const uint32_t pos = done + sm.wcount[m * kTopkWaves + wave] + lanes_below(b);
+          if (pos < uint32_t(n_out)) {  // exactly n_out are selected
+            sm.out.idx[pos] = int32_t(rel0 + uint32_t(m * kTopkThreads));
+            sm.out.bits[pos] = key[m];
+          }
+        }
+      }
+      done += total;
+      __syncthreads();  // wcount is rewritten by the next chunk; the staging is complete
+    }
+    for (int i = t; i < n_out; i += kTopkThreads) {
+      const uint32_t rel = uint32_t(sm.out.idx[i]);
+      oi[i] = int32_t(s + rel);
+      if (ov) ov[i] = __uint_as_float(value_of(sm.out.bits[i], rel));
+    }
+  } else {
+    // rank order: the selection as (key, ~column) pairs into LDS, bitonic sort
+    if (t == 0) sm.n_sel = 0;
+    __syncthreads();
+    for (int ch = 0; ch < nch; ++ch) {
+      if (MULTI) load(ch);
+      uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);
+      asm volatile("" : "+v"(rel0));  // per-register columns formed here, not hoisted
+#pragma unroll
+      for (int m = 0; m < kPerThread; ++m) {
+        const uint32_t rel = rel0 + uint32_t(m * kTopkThreads);
+        const bool in = selected(key[m], rel);
+        const uint64_t b = __ballot(in);
+        if (b != 0) {
+          uint32_t pos = 0;
+          if (lane == 0) pos = atomicAdd(&sm.n_sel, uint32_t(__popcll(b)));
+          pos = __shfl(pos, 0, 64) + lanes_below(b);
+          if (in && pos < uint32_t(kMaxTopK)) sm.sel[pos] = (uint64_t(key[m]) << 32) | uint64_t(0xFFFFFFFFu - rel);
+        }
+      }
+    }
+    __syncthreads();
+    // pad to a power of two with 0 (below every real pair) and sort
+    // descending.  Wave w owns pairs [128w, 128w + 128), so stages with a
+    // stride below 256 elements stay inside its own 256 elements and need no
+    // workgroup barrier: a wave's LDS accesses are performed in order.
+    int P = 1, logP = 0;
+    while (P < k) {
+      P <<= 1;
+      ++logP;
+    }
+    for (int i = n_out + t; i < P; i += kTopkThreads) sm.sel[i] = 0;
+    __syncthreads();
+    for (int lsize = 1; lsize <= logP; ++lsize) {
+      for (int lstride = lsize - 1; lstride >= 0; --lstride) {
+        const int stride = 1 << lstride;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = 128 * wave + 64 * h + lane;
+          if (i < P / 2) {
+            const int lo = ((i >> lstride) << (lstride + 1)) | (i & (stride - 1));
+            const int hi = lo + stride;
+            const bool descending = ((lo >> lsize) & 1) == 0;
+            const uint64_t x = sm.sel[lo], y = sm.sel[hi];
+            if ((x < y) == descending) {
+              sm.sel[lo] = y;
+              sm.sel[hi] = x;
+            }
+          }
+        }
+        if (stride >= 256 || (lstride == 0 && lsize >= 8))
+          __syncthreads();  // the next stage reads other waves' elements
+        else
+          __builtin_amdgcn_wave_barrier();
+      }
+    }
+    __syncthreads();
+    for (int i = t; i < n_out; i += kTopkThreads) {
+      const uint64_t c = sm.sel[i];
+      const uint32_t rel = 0xFFFFFFFFu - uint32_t(c);
+      oi[i] = int32_t(s + rel);
+      if (ov) ov[i] = __uint_as_float(value_of(uint32_t(c >> 32), rel));
     }
   }
-  for (int i = t; i < k; i += kTopkThreads) {
-    const uint64_t c = sm.sel[i];
-    if (c == 0) {
-      oi[i] = -1;
-      if (ov) ov[i] = -__builtin_inff();
-    } else {
-      const int64_t col = s + int64_t(0xFFFFFFFFu - uint32_t(c));
-      oi[i] = int32_t(col);
-      if (ov) ov[i] = __uint_as_float(score_bits<BF>(logits, row * ld + col));
-    }
-  }
+}
+
+template <bool BF, bool BY_SCORE>
+void launch_t(dim3 grid, const unsigned char* p, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+              const void* logits, int64_t ld, int32_t k, int32_t* out_idx, float* out_val, const PlanLayout& L,
+              hipStream_t stream) {
+  if (S_k > kChunk)
+    hipLaunchKernelGGL((topk_kernel<BF, BY_SCORE, true>), grid, dim3(kTopkThreads), 0, stream, p, B, S_q, S_k, H, D,
+                       logits, ld, k, out_idx, out_val, uint32_t(L.off_start), uint32_t(L.off_end));
+  else
+    hipLaunchKernelGGL((topk_kernel<BF, BY_SCORE, false>), grid, dim3(kTopkThreads), 0, stream, p, B, S_q, S_k, H, D,
+                       logits, ld, k, out_idx, out_val, uint32_t(L.off_start), uint32_t(L.off_end));
 }
 
 }  // namespace
 
 hipError_t launch_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
-                       const void* logits, bool logits_bf16, int64_t ld, int32_t k, int32_t* out_idx,
-                       float* out_val, hipStream_t stream) {
+                       const void* logits, bool logits_bf16, int64_t ld, int32_t k, bool by_score,
+                       int32_t* out_idx, float* out_val, hipStream_t stream) {
   const PlanLayout L = plan_layout(B, S_q, H);
   const unsigned char* p = static_cast<const unsigned char*>(plan);
-  const dim3 grid(unsigned(L.n_rows)), block(kTopkThreads);
-  if (logits_bf16)
-    hipLaunchKernelGGL(topk_kernel<true>, grid, block, 0, stream, p, B, S_q, S_k, H, D, logits, ld, k, out_idx,
-                       out_val, uint32_t(L.off_start), uint32_t(L.off_end));
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, grid, block, 0, stream, p, B, S_q, S_k, H, D, logits, ld, k, out_idx,
-                       out_val, uint32_t(L.off_start), uint32_t(L.off_end));
+  const dim3 grid(unsigned(L.n_rows));
+  if (logits_bf16) {
+    if (by_score)
+      launch_t<true, true>(grid, p, B, S_q, S_k, H, D, logits, ld, k, out_idx, out_val, L, stream);
+    else
+      launch_t<true, false>(grid, p, B, S_q, S_k, H, D, logits, ld, k, out_idx, out_val, L, stream);
+  } else {
+    if (by_score)
+      launch_t<false, true>(grid, p, B, S_q, S_k, H, D, logits, ld, k, out_idx, out_val, L, stream);
+    else
+      launch_t<false, false>(grid, p, B, S_q, S_k, H, D, logits, ld, k, out_idx, out_val, L, stream);
+  }
   return hipGetLastError();
 }
 

@@ -60,7 +60,8 @@ class Oracle:
         lib.oracle_mqa_logits.argtypes = ([ctypes.c_int] * 6 + [P] * 5 + [ctypes.c_int, ctypes.c_double]
                                           + [P, P, P, ctypes.c_int64, P, P, ctypes.c_int])
         lib.oracle_mqa_logits.restype = ctypes.c_int
-        lib.oracle_topk.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P, P, ctypes.c_int, P, P]
+        lib.oracle_topk.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_int64, P, P, ctypes.c_int, ctypes.c_int,
+                                    P, P]
         lib.oracle_topk.restype = ctypes.c_int
         for name, argt in (("oracle_dec_bf16", ctypes.c_uint16), ("oracle_dec_e4m3", ctypes.c_uint8),
                            ("oracle_dec_e2m1", ctypes.c_uint8), ("oracle_dec_e8m0", ctypes.c_uint8)):
@@ -127,10 +128,11 @@ class Oracle:
         self.lib.oracle_windows(wl.B, wl.S_q, wl.S_k, _ptr(offs), _ptr(st), _ptr(en), _ptr(ws), _ptr(we))
         return ws, we
 
-    def topk(self, vals: np.ndarray, win_start: np.ndarray, win_end: np.ndarray, k: int):
+    def topk(self, vals: np.ndarray, win_start: np.ndarray, win_end: np.ndarray, k: int, by_column: bool = False):
         """Top-k of every row of `vals` ([n_rows, >= S_k] fp32, or bf16 given as
         uint16 bits) inside its window: (idx int32 [n_rows, k], val fp32
-        [n_rows, k]).  win_start / win_end: [n_rows] int32, within [0, S_k]."""
+        [n_rows, k]), in rank order or by ascending column.  win_start /
+        win_end: [n_rows] int32, within [0, S_k]."""
         v = np.asarray(vals)
         if v.dtype == np.uint16:
             v = (v.astype(np.uint32) << 16).view(np.float32)
@@ -143,8 +145,8 @@ class Oracle:
         assert np.all(ws >= 0) and np.all(we <= v.shape[1])
         idx = np.empty((n_rows, k), np.int32)
         val = np.empty((n_rows, k), np.float32)
-        if self.lib.oracle_topk(n_rows, v.shape[1], _ptr(v), v.shape[1], _ptr(ws), _ptr(we), int(k), _ptr(idx),
-                                _ptr(val)) != 0:
+        if self.lib.oracle_topk(n_rows, v.shape[1], _ptr(v), v.shape[1], _ptr(ws), _ptr(we), int(k),
+                                int(bool(by_column)), _ptr(idx), _ptr(val)) != 0:
             raise MemoryError("oracle_topk")
         return idx, val
 
@@ -199,5 +201,5 @@ def logits(wl, rows=None, threads: int = 0, return_threads: bool = False):
     return default().logits(wl, rows=rows, threads=threads, return_threads=return_threads)
 
 
-def topk(vals, win_start, win_end, k):
-    return default().topk(vals, win_start, win_end, k)
+def topk(vals, win_start, win_end, k, by_column=False):
+    return default().topk(vals, win_start, win_end, k, by_column=by_column)

@@ -358,9 +358,10 @@ int oracle_mqa_logits(int B, int S_q, int S_k, int H, int D, int fmt, const void
  * chosen).  The plainest reading, written out: among the columns of row r's
  * window [win_start[r], win_end[r]), rank by score, larger first, equal
  * scores (+0 and -0 are equal) by smaller column first, NaN after every
- * number; the first k ranked columns are the selection, in rank order.
- * Rows with fewer than k window columns fill the rest with column -1 and
- * score -inf.  The sort is the C library's qsort on that ranking.
+ * number; the first k ranked columns are the selection.  It is listed in
+ * rank order (by_column = 0) or by ascending column (by_column = 1).  Rows
+ * with fewer than k window columns fill the rest with column -1 and score
+ * -inf.  The sorts are the C library's qsort.
  *
  * vals: [n_rows, ld] fp32 scores (bf16 scores widened exactly by the caller).
  * Out: idx [n_rows, k] int32, val [n_rows, k] fp32.  Returns 0, -1 on
@@ -383,8 +384,14 @@ static int or_rank(const void* pa, const void* pb) {
   return (a->j > b->j) - (a->j < b->j);  /* equal scores: smaller column first */
 }
 
+static int or_by_column(const void* pa, const void* pb) {
+  const or_cand* a = (const or_cand*)pa;
+  const or_cand* b = (const or_cand*)pb;
+  return (a->j > b->j) - (a->j < b->j);
+}
+
 int oracle_topk(int64_t n_rows, int S_k, const float* vals, int64_t ld, const int32_t* win_start,
-                const int32_t* win_end, int k, int32_t* idx, float* val) {
+                const int32_t* win_end, int k, int by_column, int32_t* idx, float* val) {
   or_cand* c = (or_cand*)malloc(sizeof(or_cand) * (size_t)(S_k > 0 ? S_k : 1));
   if (!c) return -1;
   for (int64_t r = 0; r < n_rows; ++r) {
@@ -396,6 +403,7 @@ int oracle_topk(int64_t n_rows, int S_k, const float* vals, int64_t ld, const in
       ++n;
     }
     qsort(c, (size_t)n, sizeof(or_cand), or_rank);
+    if (by_column) qsort(c, (size_t)(n < k ? n : k), sizeof(or_cand), or_by_column);
     for (int t = 0; t < k; ++t) {
       if (t < n) {
         idx[r * k + t] = c[t].j;

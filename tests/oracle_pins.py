@@ -668,4 +668,25 @@ def pin_topk_selection_property(orc):
             assert np.array_equal(got[~np.isnan(want)], want[~np.isnan(want)])
 
 
+def pin_topk_by_column(orc):
+    """Listing by column keeps the selection and orders it by ascending column: it is
+    numpy's sort of the rank-order list (NaN-free ties and signed zeros included), and
+    the padding stays at the end."""
+    rng = np.random.default_rng(8)
+    pool = np.array([-1.0, -0.0, 0.0, 2.0, 5.0], np.float32)
+    v = pool[rng.integers(0, pool.size, size=(6, 90))]
+    s = np.array([0, 3, 10, 50, 89, 40], np.int32)
+    e = np.array([90, 60, 11, 50, 90, 70], np.int32)
+    for k in (1, 4, 30, 95):
+        ri, rv = orc.topk(v, s, e, k)
+        ci, cv = orc.topk(v, s, e, k, by_column=True)
+        for r in range(6):
+            m = int(np.sum(ri[r] >= 0))
+            order = np.argsort(ri[r, :m], kind="stable")
+            assert ci[r, :m].tolist() == ri[r, :m][order].tolist()
+            assert np.array_equal(cv[r, :m].view(np.uint32), rv[r, :m][order].view(np.uint32))
+            assert np.all(ci[r, m:] == -1) and np.all(np.isneginf(cv[r, m:]))
+            assert m == min(k, max(int(e[r] - s[r]), 0))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -202,8 +202,9 @@ def test_plan_paged_rejects():
 def test_topk_rejects():
     L = lib.lib()
 
-    def call(plan=FAKE, B=1, S_q=16, S_k=64, H=64, D=128, logits=FAKE, dt=0, ld=64, k=8, idx=FAKE, val=FAKE):
-        return L.idx_logits_topk(plan, B, S_q, S_k, H, D, logits, dt, ld, k, idx, val, None)
+    def call(plan=FAKE, B=1, S_q=16, S_k=64, H=64, D=128, logits=FAKE, dt=0, ld=64, k=8, order=0, idx=FAKE,
+             val=FAKE):
+        return L.idx_logits_topk(plan, B, S_q, S_k, H, D, logits, dt, ld, k, order, idx, val, None)
 
     assert call(H=24) == lib.IDX_E_UNSUPPORTED
     assert call(B=0) == lib.IDX_E_INVALID
@@ -216,5 +217,6 @@ def test_topk_rejects():
     assert call(val=FAKE + 2) == lib.IDX_E_INVALID
     assert call(k=0) == lib.IDX_E_UNSUPPORTED
     assert call(k=lib.MAX_TOPK + 1) == lib.IDX_E_UNSUPPORTED
+    assert call(order=2) == lib.IDX_E_INVALID
     assert call(ld=63) == lib.IDX_E_INVALID
     assert "ld" in lib.idx_last_error()

@@ -17,13 +17,20 @@ from gpu_util import dev_inputs, make_plan, run
 pytestmark = pytest.mark.gpu
 
 
-def _check(plan, logits, k, ws, we, what, B=None, H=64, S_k=None):
-    idx, val = lib.idx_logits_topk(plan, logits, k, B=B, H=H, S_k=S_k)
+def _check(plan, logits, k, ws, we, what, B=None, H=64, S_k=None, orders=("column", "score")):
+    for order in orders:
+        got = _check_one(plan, logits, k, ws, we, f"{what} by {order}", B, H, S_k, order)
+    return got
+
+
+def _check_one(plan, logits, k, ws, we, what, B, H, S_k, order):
+    idx, val = lib.idx_logits_topk(plan, logits, k, order=order, B=B, H=H, S_k=S_k)
     torch.cuda.synchronize()
     S_k = logits.shape[-1] if S_k is None else S_k
     flat = logits.reshape(-1, logits.shape[-1])[:, :S_k]
     host = flat.view(torch.int16).cpu().numpy().view(np.uint16) if flat.dtype == torch.bfloat16 else flat.cpu().numpy()
-    want_idx, want_val = oracle.topk(host, np.asarray(ws).reshape(-1), np.asarray(we).reshape(-1), k)
+    want_idx, want_val = oracle.topk(host, np.asarray(ws).reshape(-1), np.asarray(we).reshape(-1), k,
+                                     by_column=order == "column")
     got_idx = idx.reshape(-1, k).cpu().numpy()
     got_val = val.reshape(-1, k).cpu().numpy()
     bad = np.argwhere(got_idx != want_idx)
@@ -134,7 +141,7 @@ def test_topk_without_values_and_plan_mismatch():
     plan = _windows_plan(1, 8, 500, starts, ends)
     idx, val = lib.idx_logits_topk(plan, v, 16, with_values=False)
     assert val is None
-    want, _ = oracle.topk(v.reshape(8, 500).cpu().numpy(), starts, ends, 16)
+    want, _ = oracle.topk(v.reshape(8, 500).cpu().numpy(), starts, ends, 16, by_column=True)
     assert np.array_equal(idx.reshape(8, 16).cpu().numpy(), want)
     # a plan for other dimensions gives -1 / NaN everywhere, not a plausible list
     other = _windows_plan(1, 8, 400, starts, np.full(8, 400))

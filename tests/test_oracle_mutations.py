@@ -50,6 +50,9 @@ MUTANTS = [
     ("topk_nan_first", "if (an != bn) return an ? 1 : -1;", "if (an != bn) return an ? -1 : 1;", 0),
     ("topk_window_start_ignored", "for (int32_t j = s; j < e; ++j) {", "for (int32_t j = 0; j < e; ++j) {", 0),
     ("topk_padding_score_zero", "val[r * k + t] = -INFINITY;", "val[r * k + t] = 0.0f;", 0),
+    ("topk_by_column_sorts_all", "qsort(c, (size_t)(n < k ? n : k), sizeof(or_cand), or_by_column);",
+     "qsort(c, (size_t)n, sizeof(or_cand), or_by_column);", 0),
+    ("topk_by_column_ignored", "if (by_column) qsort(", "if (0) qsort(", 0),
 ]
 
 
