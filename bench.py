@@ -52,10 +52,13 @@ CSRC = os.path.join(ROOT, "mqa_logits_scoring_amd", "csrc")
 
 
 def kernel_source_hash(fmt: str) -> str:
-    """sha256 over the sources of the scoring kernel of one input format."""
+    """sha256 over the sources of the scoring kernel of one input format
+    (fmt "topk": of the top-k kernel)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("score_kernel.h", "internal.h", f"score_{fmt}.hip"):
+    files = ("topk.hip", "internal.h") if fmt == "topk" else ("score_kernel.h", "score_kernel_gh.h", "internal.h",
+                                                              f"score_{fmt}.hip")
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -91,18 +94,24 @@ def _counter_per_dispatch(path: str, counter: str, kernel_re: str) -> float:
 
 
 def write_traffic(argv) -> None:
+    """argv: workload fetch.csv write.csv copy_fetch.csv copy_write.csv copy_bytes [copy_re [topk_k]].
+    With topk_k the record is the top-k kernel's (key topk<k>:<workload>)."""
     workload, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes = argv[:6]
     copy_re = argv[6] if len(argv) > 6 else "copy"
+    topk_k = int(argv[7]) if len(argv) > 7 else 0
     import workloads as W
     wl = W.make(workload)
     fmt, workload = wl.fmt, wl.name
+    kernel_re = "score_kernel"
+    if topk_k:
+        fmt, workload, kernel_re = "topk", f"topk{topk_k}:{wl.name}", "topk_kernel"
     copy_bytes = int(copy_bytes)
     kib = 1024.0
     # the copy kernel reads and writes copy_bytes per dispatch
     f_cal = copy_bytes / (_counter_per_dispatch(cfetch_csv, "FETCH_SIZE", copy_re) * kib)
     w_cal = copy_bytes / (_counter_per_dispatch(cwrite_csv, "WRITE_SIZE", copy_re) * kib)
-    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "score_kernel") * kib * f_cal
-    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", "score_kernel") * kib * w_cal
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", kernel_re) * kib * f_cal
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE", kernel_re) * kib * w_cal
     try:
         with open(TRAFFIC_FILE) as fh:
             data = json.load(fh)
@@ -243,6 +252,8 @@ def main():
                     help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-variant", action="store_true")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="also time top-k selection (this k, by column) over the call's scores")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes `steps` times (counter calibration)")
     args = ap.parse_args()
@@ -347,9 +358,36 @@ def main():
         iv = torch.int16 if odt == torch.bfloat16 else torch.int32
         if not bool(torch.equal(ref.view(iv), outs[0].view(iv))):
             raise RuntimeError("the phased call and idx_logits_run disagree")
-        return wl, V, us_call, kern_us
+        topk = None
+        if args.topk:
+            # top-k over the scores the timed calls wrote: `steps` launches
+            # back to back between two events, after a few untimed ones
+            k = args.topk
+            tidx = torch.empty((wl.B, wl.S_q, k), dtype=torch.int32, device=dev)
+            tval = torch.empty((wl.B, wl.S_q, k), dtype=torch.float32, device=dev)
+            sel = lambda: lib.idx_logits_topk(plan, outs[0], k, order="column", B=wl.B, H=wl.H, D=wl.D, S_k=wl.S_k,
+                                              out_idx=tidx, out_val=tval, stream=stream)
+            for _ in range(3):
+                sel()
+            ev0.record(stream)
+            for _ in range(args.steps):
+                sel()
+            ev1.record(stream)
+            ev1.synchronize()
+            t_us = ev0.elapsed_time(ev1) * 1000 / args.steps
+            # algorithmic bytes: every window score read once, k (index, score) pairs written per row
+            read = (2 if odt == torch.bfloat16 else 4) * V
+            written = 8 * wl.B * wl.S_q * k
+            gbs = (read + written) / (t_us * 1e-6) / 1e9
+            rec = counted_traffic(f"topk{k}:{wl.name}", "topk")
+            topk = {"k": k, "order": "column", "kernel": "topk_kernel", "kernel_us": round(t_us, 2),
+                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                                 "frac": round(gbs / 8000.0, 4),
+                                 "traffic": None if rec is None else rec["fetch_bytes"] + rec["write_bytes"],
+                                 "algorithmic_bytes_per_launch": read + written}}
+        return wl, V, us_call, kern_us, topk
 
-    wl, V, us_call, kern_us = measure(args.workload)
+    wl, V, us_call, kern_us, topk = measure(args.workload)
     flops = 2.0 * wl.H * wl.D * V  # 2 H D per visible cell
     peak = PEAK_TFLOPS[wl.fmt]
     rec = counted_traffic(wl.name, wl.fmt)
@@ -392,10 +430,12 @@ def main():
         res["config"]["plan"] = "built in every step from the context lengths"
     zero_name = args.workload + "_zero"
     if not args.no_zero_variant and zero_name in W.NAMED:
-        zwl, zV, zus, zk = measure(zero_name)
+        zwl, zV, zus, zk, _ = measure(zero_name)
         res["zero_inputs"] = {"workload": zwl.name, "us_per_call": round(zus, 2), "kernel_us": round(zk, 2),
                               "pages_us_gb200": PAGES_US.get(zero_name),
                               "ratio_to_pages": round(zus / PAGES_US[zero_name], 3) if zero_name in PAGES_US else None}
+    if topk is not None:
+        res["topk"] = topk
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, V)
     print(json.dumps(res), flush=True)
