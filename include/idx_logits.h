@@ -259,7 +259,9 @@ idx_status_t idx_logits_plan_paged(int32_t B, int32_t S_q, int32_t S_k, int32_t 
 /*
  * idx_logits_prepare for paged keys: the requests' keys are gathered through
  * the block table into the workspace in fragment order (zero past each
- * context), so idx_logits_score then scores them like contiguous keys.
+ * context inside its last 32-key block; blocks wholly past a context are not
+ * written, as no window reaches them), so idx_logits_score then scores them
+ * like contiguous keys.
  * a->k and a->k_scale are not used (they may be NULL); every other field and
  * check of idx_logits_prepare applies, and `kv` is checked as described above.
  */

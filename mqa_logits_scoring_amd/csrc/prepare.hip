@@ -83,6 +83,17 @@ __device__ inline int64_t key_source_row(const PrepArgs& a, int64_t b, int64_t r
   return page * a.pk.page_size + row % a.pk.page_size;
 }
 
+// Paged calls skip the 32-key blocks that lie wholly past a request's
+// context: no window reaches them, so the scoring kernel stores nothing
+// computed from them (it may read one block past a chunk's end, and those
+// columns are never stored).  Contiguous K is copied whole.
+__device__ inline bool block_unused(const PrepArgs& a, int64_t b, int64_t u) {
+  if (!a.paged) return false;
+  int64_t n = a.pk.ctx[b];
+  n = n < 0 ? 0 : (n > a.S_k ? a.S_k : n);
+  return u * 32 >= n;
+}
+
 // One thread per 16-byte chunk of K in fragment order, reading the matching
 // chunk of a K row (offsets per lane half as the scoring kernel places d).
 template <int ROWB, int CBASE, int CSTRIDE>
@@ -93,6 +104,7 @@ __device__ void kfrag_chunk(const PrepArgs& a, int64_t i) {
   const int v = int((i >> 6) % NV);
   const int64_t bu = (i >> 6) / NV;  // b * nblk + u
   const int64_t b = bu / a.nblk, u = bu % a.nblk;
+  if (block_unused(a, b, u)) return;
   const int c = lane & 31, g = lane >> 5;
   const int64_t src = key_source_row(a, b, u * 32 + c);
   const unsigned char* base = a.paged ? a.pk.k_cache : a.k;
@@ -109,6 +121,7 @@ __device__ void kscale_word(const PrepArgs& a, int64_t i) {
   const int lane = int(i & 63);
   const int64_t bu = i >> 6;
   const int64_t b = bu / a.nblk, u = bu % a.nblk;
+  if (block_unused(a, b, u)) return;
   const int64_t src = key_source_row(a, b, u * 32 + (lane & 31));
   const uint32_t* base = a.paged ? a.pk.k_scale_cache : a.k_scale;
   uint32_t word = src >= 0 ? base[src] : 0u;

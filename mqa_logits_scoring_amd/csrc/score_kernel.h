@@ -269,6 +269,9 @@ __global__ void __launch_bounds__(kThreads)
     rvalid[t] = r >= 0;
     rows[t] = r >= 0 ? r : first_row;
   }
+  // a wave with padding rows only (short tiles, e.g. two-token decode) has
+  // nothing to store; the kernel has no barrier, so it can leave
+  if (!rvalid[0] && !rvalid[1]) return;
 
   // Q fragments of head 32*mb + c for both rows, and their MX scale words
   uint32_t qf[TW][2][QD];

@@ -75,6 +75,10 @@ __global__ void __launch_bounds__(kThreads)
     rvalid[t] = r >= 0;
     rows[t] = r >= 0 ? r : first_row;
   }
+  bool any_row = false;
+#pragma unroll
+  for (int t = 0; t < WR; ++t) any_row = any_row || rvalid[t];
+  if (!any_row) return;  // padding rows only: nothing to store, and no barrier to meet
 
   // Q fragments: block j, M row c = (query row j*RPB + c/H, head c%H); the
   // row differs between lanes when H < 32, so its index is read per lane
