@@ -269,10 +269,13 @@ idx_status_t idx_logits_prepare_paged(const idx_logits_args_t* a, const idx_page
                                       size_t workspace_bytes, void* stream);
 
 /*
- * One paged call: idx_logits_prepare_paged then idx_logits_score.  With
- * plan == NULL the plan is first built from kv->context_lens into the
- * workspace (idx_logits_workspace_bytes(a) bytes), sharing the preparation
- * launch; the result is bitwise that of a call with a precomputed plan.
+ * One paged call: the results of idx_logits_prepare_paged then
+ * idx_logits_score, bitwise.  With plan == NULL the plan is first built from
+ * kv->context_lens into the workspace (idx_logits_workspace_bytes(a) bytes),
+ * sharing the preparation launch; the result is bitwise that of a call with
+ * a precomputed plan.  With H = 64, a page size of 32 * 2^j keys and a
+ * cache (and scale cache) under 2 GiB, the scoring kernel reads the keys
+ * straight from the cache and nothing is gathered.
  */
 idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, const void* plan,
                                   void* workspace, size_t workspace_bytes, void* stream);

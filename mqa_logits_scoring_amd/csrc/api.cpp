@@ -193,7 +193,18 @@ idx_status_t check_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv) {
 
 idx::PagedK paged_k(const idx_paged_k_t* kv) {
   return idx::PagedK{static_cast<const unsigned char*>(kv->k_cache), static_cast<const uint32_t*>(kv->k_scale_cache),
-                     kv->block_table, kv->context_lens, kv->num_pages, kv->page_size, kv->max_pages};
+                     kv->block_table, kv->context_lens, kv->num_pages, kv->page_size, kv->max_pages, false};
+}
+
+// Whether a one-call paged request can score straight from the cache: the
+// 64-head kernel, pages of 32 * 2^j keys (whole 32-key blocks, found with a
+// shift), and a cache (and scale cache) addressable with 31-bit offsets.
+// Other calls gather K first.
+bool direct_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv) {
+  const int64_t rows = int64_t(kv->num_pages) * kv->page_size;
+  const int32_t bpp = kv->page_size / 32;
+  return a->H == 64 && kv->page_size % 32 == 0 && (bpp & (bpp - 1)) == 0 &&
+         rows * idx::row_bytes_of(a->in_dtype) < (int64_t(1) << 31) && rows * 4 < (int64_t(1) << 31);
 }
 
 idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, size_t ws_bytes) {
@@ -220,8 +231,10 @@ idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL,
   return IDX_OK;
 }
 
+// direct: a paged call whose scoring kernel reads the cache itself (see
+// direct_paged), else NULL.
 idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
-                   unsigned char* ws, hipStream_t s) {
+                   unsigned char* ws, hipStream_t s, const idx::PagedK* direct = nullptr) {
   const idx_in_t f = a->in_dtype;
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   idx::ScoreArgs k{};
@@ -253,6 +266,15 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.pscales = idx::uses_pieces(f, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
   k.kscale = idx::has_kscale(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
+  if (direct != nullptr) {
+    k.kcache = direct->k_cache;
+    k.kscache = direct->k_scale_cache;
+    k.btable = direct->block_table;
+    k.num_pages = direct->num_pages;
+    k.page_size = direct->page_size;
+    k.max_pages = direct->max_pages;
+    while ((32 << k.bpp_shift) < direct->page_size) ++k.bpp_shift;
+  }
 
   const bool clean = a->clean_logits != 0;
   hipError_t e = hipSuccess;
@@ -342,9 +364,10 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
                        ws + WL.off_plan};
   const bool build_plan = p == nullptr;
   if (build_plan) p = ws + WL.off_plan;
-  const idx::PagedK pk = paged_k(kv);
+  idx::PagedK pk = paged_k(kv);
+  pk.skip_gather = direct_paged(a, kv);
   if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, &pk, s)) != IDX_OK) return st;
-  return score(a, p, WL, ws, s);
+  return score(a, p, WL, ws, s, pk.skip_gather ? &pk : nullptr);
 }
 
 idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,

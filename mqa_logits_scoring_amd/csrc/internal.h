@@ -183,6 +183,17 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
   return W;
 }
 
+// Unsigned 32-bit division by a divisor fixed per launch, as one 64 x 64-bit
+// high multiply (Lemire, Kaser and Kurz, "Faster remainder by direct
+// computation", 2019: with M = floor((2^64 - 1) / d) + 1, n / d is the high
+// word of M * n for every 32-bit n and d >= 2).
+struct FastDiv {
+  uint64_t M;
+  uint32_t d;
+  static FastDiv make(uint32_t d) { return FastDiv{d > 1 ? ~uint64_t(0) / d + 1 : 0, d}; }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const { return d > 1 ? uint32_t(__umul64hi(M, n)) : n; }
+};
+
 // Everything a scoring kernel needs, passed by value.
 struct ScoreArgs {
   const void* q;
@@ -204,6 +215,13 @@ struct ScoreArgs {
   const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
   const uint32_t* kscale;        // K scales in block order, [B][ceil(S_k/32)][64] (not BF16)
+  // Paged keys read straight from the cache (pages of 32 * 2^bpp_shift rows,
+  // cache under 2 GiB): block u of request b is rows [32 (u % bpp), +32) of
+  // page btable[b][u / bpp], bpp = 2^bpp_shift; kfrag / kscale are then unused.
+  const unsigned char* kcache;   // [num_pages][page_size][ROWB]
+  const uint32_t* kscache;       // [num_pages][page_size] (not BF16)
+  const int32_t* btable;         // [B][max_pages]
+  int32_t num_pages, page_size, max_pages, bpp_shift;
 };
 
 // Launchers (return the hipError_t of the launch).
@@ -235,6 +253,7 @@ struct PagedK {
   const int32_t* block_table;
   const int32_t* ctx;
   int32_t num_pages, page_size, max_pages;
+  bool skip_gather;  // the scoring kernel reads the cache itself: no K copy
 };
 
 // K in fragment order, K scales in block order (not for BF16), the

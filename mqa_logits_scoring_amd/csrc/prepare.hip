@@ -49,6 +49,8 @@ struct PrepArgs {
   const unsigned char* k;
   const uint32_t* k_scale;
   int64_t B, S_k, nblk;
+  FastDiv by_nblk, by_page;  // division by nblk and by the page size
+  int32_t kgroup;             // K chunks (and K scale words) per thread, 1..kMaxGroup
   unsigned char* kfrag;
   uint32_t* kscale;
   // weighted-query pieces
@@ -78,9 +80,10 @@ __device__ inline int64_t key_source_row(const PrepArgs& a, int64_t b, int64_t r
   int64_t n = a.pk.ctx[b];
   n = n < 0 ? 0 : (n > a.S_k ? a.S_k : n);
   if (row >= n) return -1;
-  int64_t page = a.pk.block_table[b * a.pk.max_pages + row / a.pk.page_size];
+  const uint32_t pi = a.by_page.div(uint32_t(row));  // row < S_k < 2^31
+  int64_t page = a.pk.block_table[b * a.pk.max_pages + pi];
   page = page < 0 ? 0 : (page >= a.pk.num_pages ? a.pk.num_pages - 1 : page);
-  return page * a.pk.page_size + row % a.pk.page_size;
+  return page * a.pk.page_size + (uint32_t(row) - pi * uint32_t(a.pk.page_size));
 }
 
 // Paged calls skip the 32-key blocks that lie wholly past a request's
@@ -94,39 +97,70 @@ __device__ inline bool block_unused(const PrepArgs& a, int64_t b, int64_t u) {
   return u * 32 >= n;
 }
 
-// One thread per 16-byte chunk of K in fragment order, reading the matching
-// chunk of a K row (offsets per lane half as the scoring kernel places d).
+// K chunks and scale words per thread at most: a thread issues all its loads
+// before its stores, so the dependent reads of a paged gather (context, block
+// table, cache row) overlap instead of queueing one after another.
+constexpr int kMaxGroup = 8;
+
+// One thread per 16-byte chunk of K in fragment order (kgroup of them per
+// thread, 256 consecutive chunks apart), reading the matching chunk of a K
+// row (offsets per lane half as the scoring kernel places d).
 template <int ROWB, int CBASE, int CSTRIDE>
-__device__ void kfrag_chunk(const PrepArgs& a, int64_t i) {
+__device__ void kfrag_group(const PrepArgs& a, int64_t wg) {
   constexpr int NV = ROWB / 32;  // 16-byte chunks per lane per block
-  if (i >= a.B * a.nblk * NV * 64) return;
-  const int lane = int(i & 63);
-  const int v = int((i >> 6) % NV);
-  const int64_t bu = (i >> 6) / NV;  // b * nblk + u
-  const int64_t b = bu / a.nblk, u = bu % a.nblk;
-  if (block_unused(a, b, u)) return;
-  const int c = lane & 31, g = lane >> 5;
-  const int64_t src = key_source_row(a, b, u * 32 + c);
+  const int64_t n = a.B * a.nblk * NV * 64;
   const unsigned char* base = a.paged ? a.pk.k_cache : a.k;
-  uint4 x = make_uint4(0, 0, 0, 0);
-  if (src >= 0) x = *reinterpret_cast<const uint4*>(base + src * ROWB + CBASE * g + CSTRIDE * v);
-  reinterpret_cast<uint4*>(a.kfrag)[i] = x;
+  uint4 x[kMaxGroup];
+  int64_t at[kMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    at[j] = -1;
+    x[j] = make_uint4(0, 0, 0, 0);
+    const int64_t i = (wg * a.kgroup + j) * 256 + threadIdx.x;
+    if (j >= a.kgroup || i >= n) continue;
+    const int lane = int(i & 63);
+    const int v = int((i >> 6) % NV);
+    const uint32_t bu = uint32_t((i >> 6) / NV);  // b * nblk + u (< 2^32, checked on the host)
+    const uint32_t b32 = a.by_nblk.div(bu);
+    const int64_t b = b32, u = bu - b32 * uint32_t(a.nblk);
+    if (block_unused(a, b, u)) continue;
+    at[j] = i;
+    const int c = lane & 31, g = lane >> 5;
+    const int64_t src = key_source_row(a, b, u * 32 + c);
+    if (src >= 0) x[j] = *reinterpret_cast<const uint4*>(base + src * ROWB + CBASE * g + CSTRIDE * v);
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j)
+    if (at[j] >= 0) reinterpret_cast<uint4*>(a.kfrag)[at[j]] = x[j];
 }
 
-// One thread per word of the K scales in block order.  SHIFT: right shift of
-// an MX word for lane half 1 (0 for the FP8 fp32 scale).
+// One thread per word of the K scales in block order (kgroup per thread, as
+// above).  SHIFT: right shift of an MX word for lane half 1 (0 for the FP8
+// fp32 scale).
 template <int SHIFT>
-__device__ void kscale_word(const PrepArgs& a, int64_t i) {
-  if (i >= a.B * a.nblk * 64) return;
-  const int lane = int(i & 63);
-  const int64_t bu = i >> 6;
-  const int64_t b = bu / a.nblk, u = bu % a.nblk;
-  if (block_unused(a, b, u)) return;
-  const int64_t src = key_source_row(a, b, u * 32 + (lane & 31));
+__device__ void kscale_group(const PrepArgs& a, int64_t wg) {
+  const int64_t n = a.B * a.nblk * 64;
   const uint32_t* base = a.paged ? a.pk.k_scale_cache : a.k_scale;
-  uint32_t word = src >= 0 ? base[src] : 0u;
-  if (lane >= 32) word >>= SHIFT;
-  a.kscale[i] = word;
+  uint32_t word[kMaxGroup];
+  int64_t at[kMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    at[j] = -1;
+    word[j] = 0u;
+    const int64_t i = (wg * a.kgroup + j) * 256 + threadIdx.x;
+    if (j >= a.kgroup || i >= n) continue;
+    const int lane = int(i & 63);
+    const uint32_t bu = uint32_t(i >> 6);
+    const uint32_t b32 = a.by_nblk.div(bu);
+    const int64_t b = b32, u = bu - b32 * uint32_t(a.nblk);
+    if (block_unused(a, b, u)) continue;
+    at[j] = i;
+    const int64_t src = key_source_row(a, b, u * 32 + (lane & 31));
+    if (src >= 0) word[j] = base[src];
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j)
+    if (at[j] >= 0) a.kscale[at[j]] = (threadIdx.x & 32) ? word[j] >> SHIFT : word[j];
 }
 
 // Weighted query of one row, qt = sum_h w_h q_h, by a workgroup of 4 waves.
@@ -238,16 +272,17 @@ __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
     bid -= a.n_pieces;
   }
   if (bid < a.n_kfrag) {
-    kfrag_chunk<L::ROWB, L::CBASE, L::CSTRIDE>(a, bid * 256 + threadIdx.x);
+    kfrag_group<L::ROWB, L::CBASE, L::CSTRIDE>(a, bid);
     return;
   }
   bid -= a.n_kfrag;
-  if constexpr (F != IDX_IN_BF16) kscale_word<L::SHIFT>(a, bid * 256 + threadIdx.x);
+  if constexpr (F != IDX_IN_BF16) kscale_group<L::SHIFT>(a, bid);
 }
 
 template <int F, bool WBF>
 hipError_t launch(const PrepArgs& a, hipStream_t stream) {
   const int64_t grid = a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale;
+  if (grid == 0) return hipSuccess;  // e.g. BF16 keys read from a paged cache, plan given
   hipLaunchKernelGGL((prepare_kernel<F, WBF>), dim3(unsigned(grid)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -283,6 +318,9 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.B = B;
   a.S_k = S_k;
   a.nblk = (S_k + 31) / 32;
+  if (B * a.nblk >= (int64_t(1) << 32)) return hipErrorInvalidValue;  // block indices are 32-bit
+  a.by_nblk = FastDiv::make(uint32_t(a.nblk));
+  a.by_page = FastDiv::make(paged != nullptr ? uint32_t(paged->page_size) : 1u);
   a.kfrag = kfrag;
   a.kscale = kscale;
   a.q = q;
@@ -293,8 +331,15 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.pscales = pscales;
   const bool scaled = has_kscale(fmt);
   a.n_pieces = pieces != nullptr ? n_rows : 0;  // only 64-head calls of the formats with pieces
-  a.n_kfrag = (B * a.nblk * (row_bytes_of(fmt) / 32) * 64 + 255) / 256;
-  a.n_kscale = scaled ? (B * a.nblk * 64 + 255) / 256 : 0;
+  // several chunks per thread only when that still leaves at least 2048
+  // workgroups of K copy
+  const bool copy_k = paged == nullptr || !paged->skip_gather;
+  const int64_t n_chunks = copy_k ? B * a.nblk * (row_bytes_of(fmt) / 32) * 64 : 0;
+  const int64_t per_wg = 256 * 2048;
+  a.kgroup = int32_t(n_chunks / per_wg < 1 ? 1 : (n_chunks / per_wg > kMaxGroup ? kMaxGroup : n_chunks / per_wg));
+  const int64_t span = 256 * int64_t(a.kgroup);
+  a.n_kfrag = (n_chunks + span - 1) / span;
+  a.n_kscale = scaled && copy_k ? (B * a.nblk * 64 + span - 1) / span : 0;
   if (a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
   const bool wb = w_dtype == IDX_BF16;
   switch (fmt) {

@@ -228,7 +228,9 @@ constexpr int kfrag_ring() {
   return 2;
 }
 
-template <int F, bool WBF, bool OBF, bool CLEAN>
+// PD: keys straight from a paged cache (ScoreArgs::kcache) instead of the
+// fragment-order copy.
+template <int F, bool WBF, bool OBF, bool CLEAN, bool PD = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<F>(), waves_per_eu<F>()))) score_kernel(const ScoreArgs a) {
   using T = Fmt<F>;
@@ -344,17 +346,52 @@ __global__ void __launch_bounds__(kThreads)
       HAS_KS ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.kscale) + int64_t(b) * nblk * 64, 0,
                                                  nblk * 256, kBufWord3)
              : krs;
+  // From a paged cache the block's 32 keys are 32 consecutive rows of one
+  // page: lane (c, g) reads row c at its chunk offsets, the page's first row
+  // of the block is the scalar offset (block table entry clamped into the
+  // cache, as the gather clamps it), and MX scale words are shifted here.
+  const __amdgpu_buffer_rsrc_t pkrs =
+      PD ? __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(a.kcache), 0,
+                                             int(uint32_t(a.num_pages) * uint32_t(a.page_size) * T::ROWB), kBufWord3)
+         : krs;
+  const __amdgpu_buffer_rsrc_t psrs =
+      PD && HAS_KS ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.kscache), 0,
+                                                       int(uint32_t(a.num_pages) * uint32_t(a.page_size) * 4u),
+                                                       kBufWord3)
+                   : srs;
+  const int32_t* btrow = PD ? a.btable + int64_t(b) * a.max_pages : nullptr;
   auto kload = [&](int u, uint32_t (&bf)[QD], uint32_t& kword) {
     const int blk = min(kb0 + u, nblk - 1);
+    if constexpr (PD) {
+      const uint32_t slot = uint32_t(blk) >> a.bpp_shift;
+      const uint32_t rem = uint32_t(blk) & ((1u << a.bpp_shift) - 1u);
+      int pg = __builtin_amdgcn_readfirstlane(btrow[slot]);
+      pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+      const uint32_t row0 = uint32_t(pg) * uint32_t(a.page_size) + rem * 32u;
 #pragma unroll
-    for (int v = 0; v < QD / 4; ++v) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + v * 1024, blk * (32 * T::ROWB), 0);
-      bf[4 * v + 0] = x[0];
-      bf[4 * v + 1] = x[1];
-      bf[4 * v + 2] = x[2];
-      bf[4 * v + 3] = x[3];
+      for (int v = 0; v < QD / 4; ++v) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pkrs, c * T::ROWB + g * T::CBASE + v * T::CSTRIDE,
+                                                              int(row0 * T::ROWB), 0);
+        bf[4 * v + 0] = x[0];
+        bf[4 * v + 1] = x[1];
+        bf[4 * v + 2] = x[2];
+        bf[4 * v + 3] = x[3];
+      }
+      if constexpr (HAS_KS) {
+        kword = __builtin_amdgcn_raw_buffer_load_b32(psrs, c * 4, int(row0 * 4u), 0);
+        if constexpr (T::MX) kword = g ? kword >> T::SCALE_SHIFT : kword;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < QD / 4; ++v) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + v * 1024, blk * (32 * T::ROWB), 0);
+        bf[4 * v + 0] = x[0];
+        bf[4 * v + 1] = x[1];
+        bf[4 * v + 2] = x[2];
+        bf[4 * v + 3] = x[3];
+      }
+      if constexpr (HAS_KS) kword = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, blk * 256, 0);
     }
-    if constexpr (HAS_KS) kword = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, blk * 256, 0);
   };
   // MX: the lane half's E8M0 bytes of the column's scale word (stored shifted)
   auto kscale_mx = [&](uint32_t kword) { return kword; };
@@ -642,7 +679,10 @@ __global__ void __launch_bounds__(kThreads)
 template <int F, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   const int64_t grid = int64_t(a.n_compute) + a.n_tiles;
-  hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+  if (a.kcache != nullptr)
+    hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -543,3 +543,22 @@ def test_other_head_counts_thd_and_paged(H):
     wl = _paged("mxfp4", PAGED_CASES[1], H=H)
     d = dev_inputs(wl)
     _full_compare(wl, run(wl, d), what=f"paged H={H}")
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 128])
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_paged_direct_equals_gather(fmt, page_size):
+    """Pages of 32 * 2^j keys are scored straight from the cache by the one-call
+    entry point; the result is bitwise that of the gathered two-phase call, and
+    within tolerance of the oracle."""
+    wl = W.make_paged(fmt, 3, 2, [5000, 1, 2300], page_size, seed=41, w_dtype="bf16" if fmt == "fp8" else "f32")
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    one = run(wl, d, plan=plan)
+    out = torch.empty_like(one)
+    args = lib.make_paged_args(d["q"], d["w"], out, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"], sm_scale=wl.sm_scale)
+    ws = lib.idx_logits_prepare_paged(args, d["kv"])
+    lib.idx_logits_score(args, plan, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32), out.view(torch.int32))
+    _full_compare(wl, one, what=f"paged direct {fmt} p{page_size}")
