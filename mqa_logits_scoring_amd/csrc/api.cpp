@@ -45,10 +45,16 @@ struct Split {
 constexpr int64_t kTargetUnits = 1024;  // 4 per CU
 constexpr int64_t kChunkCols = 8192;
 constexpr int64_t kMinChunk = 256;
-Split pick_split(int64_t S_k, int64_t n_tiles) {
+// S_q and tile_rows: when a batch has fewer query rows than a tile, the waves
+// holding only padding rows leave at once, so more units keep the CUs fed.
+Split pick_split(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows) {
   const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
   Split sp{};
-  int64_t want = (kTargetUnits + n_tiles - 1) / n_tiles;  // chunks per tile
+  const int64_t rows_per_wave = tile_rows / 4;
+  const int64_t rows = S_q < tile_rows ? S_q : tile_rows;
+  const int64_t active = (rows + rows_per_wave - 1) / rows_per_wave;  // waves of a tile with a real row
+  const int64_t target = kTargetUnits * 4 / active;
+  int64_t want = (target + n_tiles - 1) / n_tiles;  // chunks per tile
   const int64_t by_len = (span + kChunkCols - 1) / kChunkCols;
   want = want > by_len ? want : by_len;
   const int64_t most = (span + kMinChunk - 1) / kMinChunk;
@@ -168,7 +174,7 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
     return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
-  const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles).n_chunks) * L.n_tiles;
+  const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles, a->S_q, L.tile_rows).n_chunks) * L.n_tiles;
   if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
   return IDX_OK;
 }
@@ -252,7 +258,7 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.H = a->H;
   k.tile_rows = L.tile_rows;
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q, L.tile_rows));
-  const Split sp = pick_split(a->S_k, L.n_tiles);
+  const Split sp = pick_split(a->S_k, L.n_tiles, a->S_q, L.tile_rows);
   k.min_chunk = sp.min_chunk;
   k.n_chunks = sp.n_chunks;
   k.xcd_chunks = sp.xcd;
