@@ -41,18 +41,22 @@ constexpr int kPerThread = 32;
 constexpr int kChunk = kTopkThreads * kPerThread;  // 32768 columns
 constexpr int kBins1 = 1024;                        // first pass: key bits 31..22
 constexpr int kCopies1 = 8;                         // lane-interleaved copies of the first histogram
+constexpr int kCopyStride = kBins1 + 1;             // words between copies: bin b of copy c is in bank (b + c) % 32
 constexpr int kBins = 4096;                         // later passes: up to 12 bits
 constexpr int kCand = 4096;                         // threshold-bucket keys kept in LDS
-static_assert(kBins1 * kCopies1 >= kBins, "the first histogram's storage holds the later ones");
+static_assert(kCopyStride * kCopies1 >= kBins, "the first histogram's storage holds the later ones");
 static_assert(kBins % kTopkThreads == 0 && kBins1 % kTopkThreads == 0, "every thread owns whole bins");
 constexpr int kCounts = kPerThread * kTopkWaves;  // (register, wave) counts of the column-order output
 static_assert(kCounts <= kTopkThreads, "one (register, wave) count per thread at most");
+static_assert(kPerThread <= 32, "a thread's registers fit one 32-bit mask");
 
 // Unsigned order of the result = the ranking of the scores (NaN lowest).
 __device__ __forceinline__ uint32_t rank_key(uint32_t u) {
-  u = u == 0x80000000u ? 0u : u;  // -0 ranks as +0
-  const uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
-  return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;  // NaN
+  // negative: -u as an unsigned (so -0 lands on +0's key 0x80000000),
+  // positive: u with the top bit set; NaN: 0
+  const uint32_t neg = uint32_t(int32_t(u) >> 31);
+  const uint32_t k = ((u ^ neg) - neg) ^ (~neg & 0x80000000u);
+  return __builtin_isnan(__uint_as_float(u)) ? 0u : k;
 }
 
 template <bool BF>
@@ -64,7 +68,7 @@ __device__ __forceinline__ uint32_t score_bits(const void* logits, int64_t i) {
 }
 
 struct TopkSmem {
-  uint32_t hist[kBins1 * kCopies1];  // first pass: bin b, copy c at b * kCopies1 + c
+  uint32_t hist[kCopyStride * kCopies1];  // first pass: bin b, copy c at c * kCopyStride + b
   union {
     struct {
       uint32_t key[kCand];
@@ -126,7 +130,7 @@ __device__ PassResult find_digit(TopkSmem& sm, uint32_t want) {
   for (int b = 0; b < BPT; ++b) {
     uint32_t x = 0;
 #pragma unroll
-    for (int c = 0; c < C; ++c) x += sm.hist[(t * BPT + b) * C + c];
+    for (int c = 0; c < C; ++c) x += sm.hist[c * kCopyStride + t * BPT + b];
     h[b] = x;
     local += x;
   }
@@ -160,7 +164,7 @@ __device__ __forceinline__ void clear_hist(TopkSmem& sm) {
 // Score bits back from a key: exact except for the two keys that several
 // bit patterns share (+0 for -0 too, 0 for every NaN), which the caller reads
 // again.
-__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7FFFFFFFu) : ~k; }
+__device__ __forceinline__ uint32_t key_bits(uint32_t k) { return (k >> 31) ? (k & 0x7FFFFFFFu) : 0u - k; }
 __device__ __forceinline__ bool key_is_shared(uint32_t k) { return k == 0x80000000u || k == 0u; }
 
 // MULTI: rows may span several chunks (S_k > kChunk).  The single-chunk
@@ -220,7 +224,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
   auto load = [&](int ch) {
     const int64_t c0 = int64_t(ch) * kChunk;
     const int64_t w = n - c0 < kChunk ? n - c0 : kChunk;
-    const int mv = w > t ? int((w - t + kTopkThreads - 1) / kTopkThreads) : 0;  // registers inside the window
+    const int wc = int(w);  // <= kChunk
+    const int mv = wc > t ? (wc - t + kTopkThreads - 1) / kTopkThreads : 0;  // registers inside the window
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<unsigned char*>(static_cast<const unsigned char*>(logits)) + (base + c0) * ES, 0, int(w * ES),
         0x00020000);
@@ -246,10 +251,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
   int nbits = 0;
   // One histogram pass over the registers: count digit (v >> shift) & dmask
   // of every key with (key & msk) == pre, or in a tie pass (v = top - rel)
-  // of every key equal to T with (v & msk) == pre; `copies` interleaved
-  // histograms (1 or kCopies1).
-  auto reg_pass = [&](bool tie, int shift, uint32_t dmask, uint32_t pre, uint32_t msk, uint32_t copies) {
-    const uint32_t copy = uint32_t(lane) & (copies - 1u);
+  // of every key equal to T with (v & msk) == pre.
+  auto reg_pass = [&](bool tie, int shift, uint32_t dmask, uint32_t pre, uint32_t msk) {
     for (int ch = 0; ch < nch; ++ch) {
       if (MULTI) load(ch);
       uint32_t v0 = top - uint32_t(ch) * kChunk - uint32_t(t);  // tie key of register 0
@@ -261,7 +264,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
         const uint32_t kk = key[m];
         const uint32_t v = tie ? v0 - uint32_t(m * kTopkThreads) : kk;
         const bool c = tie ? (kk == T && (v & msk) == pre) : ((kk & msk) == pre);
-        if (c) atomicAdd(&sm.hist[(((v >> shift) & dmask) * copies) | copy], 1u);
+        if (c) atomicAdd(&sm.hist[(v >> shift) & dmask], 1u);
       }
     }
   };
@@ -280,9 +283,16 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
     top = nbits == 32 ? 0xFFFFFFFFu : (1u << nbits) - 1u;
     // 1. key bits 31..22 over the whole row, into lane-interleaved copies so
     //    that lanes counting the same bin rarely touch the same word
-    clear_hist<kBins1 * kCopies1>(sm);
+    clear_hist<kCopyStride * kCopies1>(sm);
     if (t == 0) sm.n_cand = 0;
-    reg_pass(false, 22, kBins1 - 1, 0u, 0u, kCopies1);
+    {  // every key counts: no condition, fixed digit and copies
+      const uint32_t copy = (uint32_t(lane) & (kCopies1 - 1u)) * kCopyStride;
+      for (int ch = 0; ch < nch; ++ch) {
+        if (MULTI) load(ch);
+#pragma unroll
+        for (int m = 0; m < kPerThread; ++m) atomicAdd(&sm.hist[(key[m] >> 22) + copy], 1u);
+      }
+    }
     const PassResult r1 = find_digit<kBins1, kCopies1>(sm, want);
     want -= r1.above;
     uint32_t prefix = r1.digit << 22, mask = 0xFFC00000u, count_eq = r1.count;
@@ -290,24 +300,31 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
     //    below then read the short list), else the passes read the registers
     const bool listed = r1.count <= uint32_t(kCand);
     if (listed) {
+      // each thread's candidates at its place from one block scan of the
+      // per-thread counts (thread-major order; the selection below does not
+      // depend on the list's order)
+      uint32_t done = 0;  // candidates of the earlier chunks
       for (int ch = 0; ch < nch; ++ch) {
         if (MULTI) load(ch);
         uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);
         asm volatile("" : "+v"(rel0));  // per-register columns formed here, not hoisted
+        uint32_t cm = 0;  // bit m: register m is a candidate
+#pragma unroll
+        for (int m = 0; m < kPerThread; ++m) cm |= uint32_t((key[m] & mask) == prefix) << m;
+        const uint32_t mine = uint32_t(__builtin_popcount(cm));
+        uint32_t total;
+        uint32_t pos = done + block_scan(mine, sm, total) - mine;
 #pragma unroll
         for (int m = 0; m < kPerThread; ++m) {
-          const bool in = (key[m] & mask) == prefix;
-          const uint64_t b = __ballot(in);
-          if (b != 0) {
-            uint32_t pos = 0;
-            if (lane == 0) pos = atomicAdd(&sm.n_cand, uint32_t(__popcll(b)));
-            pos = __shfl(pos, 0, 64) + lanes_below(b);
-            if (in && pos < uint32_t(kCand)) {
+          if ((cm >> m) & 1u) {
+            if (pos < uint32_t(kCand)) {
               sm.cand.key[pos] = key[m];
               sm.cand.rel[pos] = rel0 + uint32_t(m * kTopkThreads);
             }
+            ++pos;
           }
         }
+        done += total;
       }
       __syncthreads();
     }
@@ -319,7 +336,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
       if (listed)
         cand_pass(nc, false, shift, dmask, prefix, mask);
       else
-        reg_pass(false, shift, dmask, prefix, mask, 1u);
+        reg_pass(false, shift, dmask, prefix, mask);
       const PassResult r = find_digit<kBins, 1>(sm, want);
       want -= r.above;
       prefix |= r.digit << shift;
@@ -336,7 +353,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
         if (listed)
           cand_pass(nc, true, lo, dmask, prefix2, mask2);
         else
-          reg_pass(true, lo, dmask, prefix2, mask2, 1u);
+          reg_pass(true, lo, dmask, prefix2, mask2);
         const PassResult r = find_digit<kBins, 1>(sm, want);
         want -= r.above;
         prefix2 |= r.digit << lo;
@@ -363,26 +380,31 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
       if (MULTI) load(ch);
       uint32_t rel0 = uint32_t(ch) * kChunk + uint32_t(t);
       asm volatile("" : "+v"(rel0));  // per-register columns formed here, not hoisted
-      uint64_t selm = 0;  // bit m: register m is selected
+      uint32_t selm = 0;  // bit m: register m is selected
+#pragma unroll
+      for (int m = 0; m < kPerThread; ++m) selm |= uint32_t(selected(key[m], rel0 + uint32_t(m * kTopkThreads))) << m;
+      // this wave's count per register, gathered into lane m, written at once
+      uint32_t cnt = 0;
 #pragma unroll
       for (int m = 0; m < kPerThread; ++m) {
-        const bool in = selected(key[m], rel0 + uint32_t(m * kTopkThreads));
-        selm |= uint64_t(in) << m;
-        const uint64_t b = __ballot(in);
-        if (lane == 0) sm.wcount[m * kTopkWaves + wave] = uint32_t(__popcll(b));
+        const uint32_t c_m = uint32_t(__popcll(__ballot((selm >> m) & 1u)));  // wave-uniform
+        cnt = lane == m ? c_m : cnt;
       }
+      if (lane < kPerThread) sm.wcount[lane * kTopkWaves + wave] = cnt;
       __syncthreads();
       uint32_t total;
       const uint32_t mine = t < kCounts ? sm.wcount[t] : 0u;
       const uint32_t excl = block_scan(mine, sm, total) - mine;
       if (t < kCounts) sm.wcount[t] = excl;  // entry t = (m, wave) in column order: its first place
       __syncthreads();
+      const uint32_t bases = lane < kPerThread ? sm.wcount[lane * kTopkWaves + wave] : 0u;
 #pragma unroll
       for (int m = 0; m < kPerThread; ++m) {
         const bool in = (selm >> m) & 1u;
         const uint64_t b = __ballot(in);
+        const uint32_t base_m = __builtin_amdgcn_readlane(bases, m);
         if (in) {
-          const uint32_t pos = done + sm.wcount[m * kTopkWaves + wave] + lanes_below(b);
+          const uint32_t pos = done + base_m + lanes_below(b);
           if (pos < uint32_t(n_out)) {  // exactly n_out are selected
             sm.out.idx[pos] = int32_t(rel0 + uint32_t(m * kTopkThreads));
             sm.out.bits[pos] = key[m];
