@@ -97,15 +97,30 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q, int H) {
 //   sum_h w_h ReLU(S_h) = ( sum_h w_h |S_h| + qt . k ) / 2,  qt = sum_h w_h q_h,
 // so the epilogue needs one FMA (with |.| as a free source modifier) per head
 // instead of a max and an FMA, and the linear term qt . k comes from one more
-// MFMA block.  qt (fp32) is written as kPieces e4m3 rows with one E8M0 scale
-// per 32 elements, each piece encoding the exact fp32 residual of the ones
-// before it, so the pieces sum to qt within 2^-(4 kPieces) of its block maxima.
+// MFMA block.  qt (fp32) is written as pieces with one E8M0 scale per 32
+// elements, each piece encoding the exact fp32 residual of the ones before it:
+//  - FP8 / MXFP8: kPieces e4m3 rows (128 B); each shrinks the residual's block
+//    maximum 16-fold, so they sum to qt within 2^-24 of its block maxima;
+//  - MXFP4: kPiecesE2M1 e2m1 rows (64 B, packed like MXFP4 Q), so the linear
+//    block multiplies e2m1 by e2m1 at the fp4 rate; with the block maximum
+//    scaled into [2, 4) each piece shrinks it at least 4-fold, 2^-16 in all.
 //
 // Workspace layout (256-byte aligned sections):
-//   [plan, when the call builds it]  [pieces: n_rows x kPieces x 128 B]
-//   [piece scales: n_rows x kPieces x uint32]
+//   [plan, when the call builds it]
+//   [pieces: n_rows x 768 B: kPieces x 128 B, or kPiecesE2M1 x 64 B]
+//   [piece scales: n_rows x kPieceSlots x uint32]
 // ---------------------------------------------------------------------------
 constexpr int kPieces = 6;
+constexpr int kPiecesE2M1 = 8;
+constexpr int kPieceSlots = 8;        // scale words reserved per row
+constexpr int kPieceRowBytes = 768;   // piece bytes reserved per row
+template <int F>
+struct PieceFmt {
+  static constexpr int N = F == IDX_IN_MXFP4_E2M1 ? kPiecesE2M1 : kPieces;   // pieces per row
+  static constexpr int BYTES = F == IDX_IN_MXFP4_E2M1 ? 64 : 128;           // bytes per piece
+  static constexpr int SLOTS = F == IDX_IN_MXFP4_E2M1 ? kPieceSlots : kPieces;  // scale words per row
+  static_assert(N * BYTES <= kPieceRowBytes && SLOTS <= kPieceSlots && N <= 8, "pieces fit their row");
+};
 
 // Only the 64-head kernels take the linear term from pieces; the others use
 // max + FMA.
@@ -169,9 +184,9 @@ inline WorkspaceLayout workspace_layout(idx_in_t f, int64_t B, int64_t S_q, int6
   off += L.total;
   if (uses_pieces(f, H)) {
     W.off_pieces = off;
-    off += align256(size_t(L.n_rows) * kPieces * 128);
+    off += align256(size_t(L.n_rows) * kPieceRowBytes);
     W.off_pscales = off;
-    off += align256(size_t(L.n_rows) * kPieces * 4);
+    off += align256(size_t(L.n_rows) * kPieceSlots * 4);
   }
   W.off_kfrag = off;
   off += align256(size_t(B) * size_t((S_k + 31) / 32) * 32 * row_bytes_of(f));
@@ -211,8 +226,8 @@ struct ScoreArgs {
   int32_t n_compute;     // n_tiles * n_chunks
   int32_t xcd_chunks;    // 1: n_chunks % 8 == 0 and chunk c runs on XCD c % 8
   uint32_t off_start, off_end, off_slot, off_lo, off_hi;
-  const unsigned char* pieces;   // [n_rows][kPieces][128] e4m3 codes (formats with pieces)
-  const uint32_t* pscales;       // [n_rows][kPieces] E8M0 words
+  const unsigned char* pieces;   // per row PieceFmt<F>::N pieces of PieceFmt<F>::BYTES (formats with pieces)
+  const uint32_t* pscales;       // per row PieceFmt<F>::SLOTS E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
   const uint32_t* kscale;        // K scales in block order, [B][ceil(S_k/32)][64] (not BF16)
   // Paged keys read straight from the cache (pages of 32 * 2^bpp_shift rows,

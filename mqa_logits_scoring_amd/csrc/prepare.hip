@@ -44,6 +44,21 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
   return sign | code;
 }
 
+// |x| < 4: nearest e2m1 code, ties to even (sign kept); the grid below 4 is
+// {0, .5, 1, 1.5, 2, 3, 4}
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 8u;
+  const float ax = __builtin_fabsf(x);
+  const uint32_t code = ax <= 0.25f ? 0u
+                        : ax < 0.75f ? 1u
+                        : ax <= 1.25f ? 2u
+                        : ax < 1.75f ? 3u
+                        : ax <= 2.5f ? 4u
+                        : ax < 3.5f ? 5u
+                        : 6u;
+  return sign | code;
+}
+
 struct PrepArgs {
   // K reorder and K scales
   const unsigned char* k;
@@ -225,7 +240,9 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
   }
   // pieces: each encodes the exact residual left by the ones before it; lane
   // l owns elements 2l and 2l+1, so lanes 16b..16b+15 hold 32-element block b
-  for (int p = 0; p < kPieces; ++p) {
+  using PF = PieceFmt<F>;
+  constexpr bool E2M1 = F == IDX_IN_MXFP4_E2M1;
+  for (int p = 0; p < PF::N; ++p) {
     float m = __builtin_fmaxf(__builtin_fabsf(r0), __builtin_fabsf(r1));
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
@@ -233,20 +250,32 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
     const uint32_t E = (mb >> 23) & 0xFFu;
     uint32_t sbyte = 127u, c0 = 0u, c1 = 0u;
     if (E >= 9u) {  // else the residual is below 2^-118: leave it (piece of zeros)
-      // scale 2^k with k the smallest exponent for which |r| / 2^k <= 448
-      const int k = int(E) - 127 - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+      // e4m3: scale 2^k with k the smallest exponent for which |r| / 2^k <= 448;
+      // e2m1: k = e - 1 for |r|max = 1.f 2^e, so |r| / 2^k < 4
+      const int k = E2M1 ? int(E) - 128 : int(E) - 127 - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
       sbyte = uint32_t(127 + k);
-      const float inv = __uint_as_float(uint32_t(127 - k) << 23);  // 2^-k (k in [-118, 120])
+      const float inv = __uint_as_float(uint32_t(127 - k) << 23);  // 2^-k (k in [-119, 126])
       const float sc = __uint_as_float(sbyte << 23);
-      c0 = e4m3_code(r0 * inv);
-      c1 = e4m3_code(r1 * inv);
-      r0 -= e4m3_value(c0) * sc;  // exact: the decoded piece is within a factor 2 of r
-      r1 -= e4m3_value(c1) * sc;
+      if constexpr (E2M1) {
+        c0 = e2m1_code(r0 * inv);
+        c1 = e2m1_code(r1 * inv);
+        r0 -= e2m1_value(c0) * sc;  // exact: the decoded piece is 0 or within a factor 2 of r
+        r1 -= e2m1_value(c1) * sc;
+      } else {
+        c0 = e4m3_code(r0 * inv);
+        c1 = e4m3_code(r1 * inv);
+        r0 -= e4m3_value(c0) * sc;  // exact: the decoded piece is within a factor 2 of r
+        r1 -= e4m3_value(c1) * sc;
+      }
     }
-    reinterpret_cast<uint16_t*>(a.pieces + (row * kPieces + p) * 128)[lane] = uint16_t(c0 | (c1 << 8));
+    unsigned char* dst = a.pieces + row * kPieceRowBytes + p * PF::BYTES;
+    if constexpr (E2M1)
+      dst[lane] = uint8_t(c0 | (c1 << 4));  // elements 2l (low nibble) and 2l+1
+    else
+      reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(c0 | (c1 << 8));
     const uint32_t word = (__shfl(sbyte, 0)) | (__shfl(sbyte, 16) << 8) | (__shfl(sbyte, 32) << 16) |
                           (__shfl(sbyte, 48) << 24);
-    if (lane == 0) a.pscales[row * kPieces + p] = word;
+    if (lane == 0) a.pscales[row * kPieceSlots + p] = word;
   }
 }
 

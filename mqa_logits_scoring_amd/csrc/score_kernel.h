@@ -497,27 +497,48 @@ __global__ void __launch_bounds__(kThreads)
     // puts in lane half t, registers 0-5: after the head-sum swap, lane half t
     // holds row t's columns, so the linear term adds in place.
     using LN = Lin<F>;
-    uint32_t lf[16];
+    using PF = PieceFmt<F>;
+    // MXFP4 pieces are e2m1 rows packed like Q, so the linear block is an
+    // ordinary fp4 block (A operand in Q's placement); the e4m3 pieces of the
+    // FP8 formats sit at the offsets Lin<> gives
+    constexpr bool E2M1 = F == IDX_IN_MXFP4_E2M1;
+    constexpr int LFD = E2M1 ? QD : 16;
+    uint32_t lf[LFD];
     uint32_t sl;
     {
       const int tt = (c >> 2) & 1, pc = (c & 3) + 4 * (c >> 3);
-      const bool has = c < 16 && pc < kPieces;
-      const int64_t prow = int64_t(rows[tt]) * kPieces + (has ? pc : 0);
-      const unsigned char* src = a.pieces + prow * 128 + 16 * g;
+      const bool has = c < 16 && pc < PF::N;
+      const unsigned char* src = a.pieces + int64_t(rows[tt]) * kPieceRowBytes + (has ? pc : 0) * PF::BYTES;
+      if constexpr (E2M1) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint4 x = has ? *reinterpret_cast<const uint4*>(src + LN::OFF[v]) : make_uint4(0, 0, 0, 0);
-        lf[4 * v + 0] = x.x;
-        lf[4 * v + 1] = x.y;
-        lf[4 * v + 2] = x.z;
-        lf[4 * v + 3] = x.w;
+        for (int v = 0; v < QD / 4; ++v) {
+          const uint4 x = has ? *reinterpret_cast<const uint4*>(src + g * T::CBASE + v * T::CSTRIDE)
+                              : make_uint4(0, 0, 0, 0);
+          lf[4 * v + 0] = x.x;
+          lf[4 * v + 1] = x.y;
+          lf[4 * v + 2] = x.z;
+          lf[4 * v + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 x = has ? *reinterpret_cast<const uint4*>(src + 16 * g + LN::OFF[v]) : make_uint4(0, 0, 0, 0);
+          lf[4 * v + 0] = x.x;
+          lf[4 * v + 1] = x.y;
+          lf[4 * v + 2] = x.z;
+          lf[4 * v + 3] = x.w;
+        }
       }
-      const uint32_t word = has ? a.pscales[prow] : 0x7F7F7F7Fu;
-      sl = g ? (word >> LN::SCALE_SHIFT) : word;
+      const uint32_t word = has ? a.pscales[int64_t(rows[tt]) * kPieceSlots + pc] : 0x7F7F7F7Fu;
+      sl = g ? (word >> LN::SCALE_SHIFT) : word;  // 16 for e2m1 pieces, as for MXFP4 Q
     }
     const float half_scale = 0.5f * a.sm_scale;
 
     auto mfma_lin = [&](f32x16& acc, const uint32_t (&bf)[QD], uint32_t sb) {
+      if constexpr (E2M1) {
+        mfma_block(acc, lf, sl, bf, sb);
+        return;
+      }
       f32x16 d = {};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -545,7 +566,7 @@ __global__ void __launch_bounds__(kThreads)
     auto epi_lin = [&](const f32x16& acc) {
       float v = acc[0];
 #pragma unroll
-      for (int r = 1; r < kPieces; ++r) v += acc[r];
+      for (int r = 1; r < PF::N; ++r) v += acc[r];
       return v;
     };
     // weight and sum |S| of the lane's 16 heads of one block (fixed order)
