@@ -335,9 +335,8 @@ def main():
         us_call = wall / args.steps * 1e6
         # the scoring kernel alone: a plan and a prepared workspace, then
         # `steps` launches back to back on the stream the library launches on,
-        # between two events.  A paged call that reads the cache directly has
-        # no K copy to prepare: there the timed launches are whole calls with
-        # the plan given (the weighted-query pieces and the scoring kernel).
+        # between two events (paged: the paged scoring phase, which reads the
+        # cache directly where the one-call form does).
         build_plan(lib, wl, d, plan, stream)
         if paged:
             lib.idx_logits_prepare_paged(cargs[0], d["kv"], ws, stream=stream)
@@ -346,9 +345,7 @@ def main():
 
         def timed(i):
             if paged:
-                lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
-                                         sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], plan=plan,
-                                         workspace=ws, stream=stream)
+                lib.idx_logits_score_paged(cargs[i % 2], d["kv"], plan, ws, stream=stream)
             else:
                 lib.idx_logits_score(cargs[i % 2], plan, ws, stream=stream)
 
@@ -443,7 +440,6 @@ def main():
                                 "ratio": wl.thd["ratio"], "m_total": wl.S_k}
         res["config"]["plan"] = "idx_logits_plan_thd in every step"
     if getattr(wl, "paged", None) is not None:
-        res["roofline"]["kernel_us_covers"] = "whole calls with the plan given (pieces + scoring from the cache)"
         pg = wl.paged
         res["config"]["paged"] = {"page_size": pg["page_size"], "num_pages": int(pg["k_cache"].shape[0]),
                                   "max_pages": int(np.asarray(pg["block_table"]).shape[1]),

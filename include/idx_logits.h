@@ -281,6 +281,19 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Second phase of a paged call: score into a->out from a workspace that
+ * idx_logits_prepare_paged filled for the same a and kv, with a plan from
+ * idx_logits_plan_paged.  Where idx_logits_run_paged reads the keys straight
+ * from the cache (H = 64, page size 32 * 2^j, cache under 2 GiB) so does this
+ * call, using only the weighted-query pieces of the workspace; otherwise it
+ * reads the gathered keys.  Either way the result is bitwise that of
+ * idx_logits_run_paged.  Same checks and errors as idx_logits_run_paged;
+ * plan must be non-NULL (IDX_E_WORKSPACE).
+ */
+idx_status_t idx_logits_score_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, const void* plan,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Top-k selection over the scores of a call (the per-query key list that the
  * sparse-attention page, FlashInfer SM120 sparse MLA, consumes: 2048 keys per
  * query token for its DSv3.2 configurations; the pages do not say how the

@@ -23,7 +23,8 @@ IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
-            "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_topk",
+            "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_score_paged",
+            "idx_logits_topk",
             "idx_logits_workspace_bytes",
             "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_prepare_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, SZ, P]
         L.idx_logits_run_paged.restype = ctypes.c_int
         L.idx_logits_run_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
+        L.idx_logits_score_paged.restype = ctypes.c_int
+        L.idx_logits_score_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
         L.idx_logits_topk.restype = ctypes.c_int
         L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, ctypes.c_int, P, P, P]
         L.idx_logits_workspace_bytes.restype = SZ
@@ -364,6 +367,15 @@ def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: i
                                                                 workspace.numel() * workspace.element_size(),
                                                                 _stream(stream, device)))
     return out
+
+
+def idx_logits_score_paged(args: IdxLogitsArgs, kv: IdxPagedK, plan: torch.Tensor, workspace: torch.Tensor, *,
+                           stream=None) -> None:
+    """Second phase of a paged call: score into args.out from a workspace that
+    idx_logits_prepare_paged filled for the same args and kv."""
+    _check("idx_logits_score_paged",
+           lib().idx_logits_score_paged(ctypes.byref(args), ctypes.byref(kv), _ptr(plan), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream, workspace.device)))
 
 
 MAX_TOPK = 2048

@@ -376,6 +376,22 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
   return score(a, p, WL, ws, s, pk.skip_gather ? &pk : nullptr);
 }
 
+idx_status_t idx_logits_score_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv, const void* plan,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a, true);
+  if (st != IDX_OK) return st;
+  if ((st = check_paged(a, kv)) != IDX_OK) return st;
+  if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score_paged needs a plan");
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  idx::PagedK pk = paged_k(kv);
+  pk.skip_gather = direct_paged(a, kv);
+  return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream),
+               pk.skip_gather ? &pk : nullptr);
+}
+
 idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
                              const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, idx_topk_order_t order,
                              int32_t* topk_idx, float* topk_val, void* stream) {

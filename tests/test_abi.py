@@ -169,6 +169,7 @@ def test_paged_rejects(kw, status):
     kv = _paged(**kw)
     assert L.idx_logits_prepare_paged(ctypes.byref(a), ctypes.byref(kv), FAKE, 1 << 30, None) == status
     assert L.idx_logits_run_paged(ctypes.byref(a), ctypes.byref(kv), None, FAKE, 1 << 30, None) == status
+    assert L.idx_logits_score_paged(ctypes.byref(a), ctypes.byref(kv), FAKE, FAKE, 1 << 30, None) == status
     assert lib.idx_last_error() != ""
 
 
@@ -182,6 +183,13 @@ def test_paged_call_checks():
     assert L.idx_logits_run_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE + 8, FAKE, 1 << 30,
                                   None) == lib.IDX_E_INVALID
     assert L.idx_logits_prepare_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE, 16, None) == lib.IDX_E_WORKSPACE
+    # the scoring phase needs a plan, aligned, and a workspace
+    assert L.idx_logits_score_paged(ctypes.byref(_args()), ctypes.byref(kv), None, FAKE, 1 << 30,
+                                    None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_score_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE + 8, FAKE, 1 << 30,
+                                    None) == lib.IDX_E_INVALID
+    assert L.idx_logits_score_paged(ctypes.byref(_args()), ctypes.byref(kv), FAKE, FAKE, 16,
+                                    None) == lib.IDX_E_WORKSPACE
     # BF16 keys carry no scales, so a NULL scale cache is fine there; the
     # call then fails only on its workspace
     a = _args(in_dtype=0, q_scale=None)

@@ -480,8 +480,9 @@ def test_paged_equals_contiguous(fmt):
 
 @pytest.mark.parametrize("fmt", W.FORMATS)
 def test_paged_prepare_score_and_plan(fmt):
-    """idx_logits_prepare_paged + idx_logits_score (keys NULL in the args) with a
-    plan from idx_logits_plan_paged is bitwise the one-call form, which gives
+    """idx_logits_prepare_paged + idx_logits_score (keys NULL in the args), or +
+    idx_logits_score_paged, with a plan from idx_logits_plan_paged is bitwise
+    the one-call form, which gives
     the same result whether it builds its plan or takes it."""
     wl = _paged(fmt, PAGED_CASES[1])
     d = dev_inputs(wl)
@@ -492,9 +493,14 @@ def test_paged_prepare_score_and_plan(fmt):
     args = lib.make_paged_args(d["q"], d["w"], out, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"], sm_scale=wl.sm_scale)
     ws = lib.idx_logits_prepare_paged(args, d["kv"])
     lib.idx_logits_score(args, plan, ws)
+    out2 = torch.full_like(one, float("nan"))
+    args2 = lib.make_paged_args(d["q"], d["w"], out2, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"],
+                                sm_scale=wl.sm_scale)
+    lib.idx_logits_score_paged(args2, d["kv"], plan, ws)
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int32), planned.view(torch.int32))
     assert torch.equal(one.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(one.view(torch.int32), out2.view(torch.int32))
 
 
 # ---------------------------------------------------------------------------
@@ -559,6 +565,12 @@ def test_paged_direct_equals_gather(fmt, page_size):
     args = lib.make_paged_args(d["q"], d["w"], out, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"], sm_scale=wl.sm_scale)
     ws = lib.idx_logits_prepare_paged(args, d["kv"])
     lib.idx_logits_score(args, plan, ws)
+    # the paged scoring phase takes the direct path where the one-call form does
+    out2 = torch.full_like(one, float("nan"))
+    args2 = lib.make_paged_args(d["q"], d["w"], out2, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"],
+                                sm_scale=wl.sm_scale)
+    lib.idx_logits_score_paged(args2, d["kv"], plan, ws)
     torch.cuda.synchronize()
     assert torch.equal(one.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(one.view(torch.int32), out2.view(torch.int32))
     _full_compare(wl, one, what=f"paged direct {fmt} p{page_size}")
