@@ -37,6 +37,10 @@
 // max + FMA epilogue needs about 19, the split form about 8.  BF16 inputs are
 // MFMA-bound with either form and keep max + FMA.
 //
+// FP8 and MXFP8 keys at 64 heads go to score_kernel_x16 below instead: the
+// same units and epilogue on 16x16x128 MFMAs, which make the linear term half
+// as expensive.  score_kernel serves BF16 and MXFP4.
+//
 // Operand layout inside a lane: any permutation of d applied alike to Q and K
 // leaves every dot product unchanged, so each format places d where loads are
 // wide and where the MFMA's block scales line up with the E8M0 bytes.  Lane
@@ -697,13 +701,341 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// ---------------------------------------------------------------------------
+// 64-head kernel for FP8 and MXFP8 keys in fragment order, on 16x16x128 MFMAs
+//
+// Same units, rows per wave, windows, stores and cleanup as score_kernel; the
+// contraction and the linear term are cut differently.  A 16x16x128 block
+// takes all 128 d at once: A = 16 heads of one query row, B = 16 key columns.
+// Per 32 columns a wave issues 2 rows x 4 head blocks x 2 column halves = 16
+// of them (32 cycles each at the e4m3 rate, as many cycles as the eight
+// 32x32x64 blocks of score_kernel), but the linear term qt . k now takes two
+// blocks of 32 cycles instead of two of 64: A rows 0-3 / 8-11 (first column
+// half) and 4-7 / 12-15 (second half) hold the first four weighted-query
+// pieces of rows 0 / 1, chained into one accumulator, so lane l ends up with
+// row l/32, column l%32 of the linear term -- where the head-sum below puts
+// the same cell.
+//
+// gfx950 operand placement of the scaled 16x16x128 e4m3 MFMA (probed on the
+// GPU with random codes and scales): lane (n, q), n = l%16, q = l/16, holds
+// row / column n, bytes 0-15 at k = 16q + [0,16) and bytes 16-31 at
+// k = 64 + 16q + [0,16); k-block b = [32b, 32b+32) takes lane group b's scale
+// byte.  With k = d, lane (n, q) therefore holds d-chunks q and q + 4 of 16
+// bytes, and its scale byte is byte q of the E8M0 word (d-block q).  K in
+// fragment order keeps chunk p of column c at (p/2)*1024 + (32*(p%2) + c)*16
+// of its block, so each column half is two 16-byte loads per lane at a
+// constant lane offset.
+//
+// Output: lane (n, q) register r = A row 4q + r, column n.  Each lane weights
+// and sums its 4 heads per block into p[row][half]; two permlane32 swaps then
+// one permlane16 swap fold the four lane groups so that lane l holds row l/32,
+// column l%32 (16 (l/16 % 2) + l%16).
+//
+// Four weighted-query pieces leave a residual below 2^-16 of each d-block
+// maximum of qt; by Cauchy-Schwarz its share of a score is at most
+// 2^-16 sqrt(32) / 2 < 4.4e-5 of sm_scale * sum_h |w_h| |q_h| |k|.
+template <int F, bool WBF, bool OBF, bool CLEAN, bool PD>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    score_kernel_x16(const ScoreArgs a) {
+  static_assert(F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3, "e4m3 formats only");
+  using T = Fmt<F>;
+  static_assert(T::ROWB == 128 && T::CBASE == 16 && T::CSTRIDE == 32, "K fragment placement of the e4m3 formats");
+  constexpr bool MX = T::MX;
+  constexpr int TW = 2;  // query rows per wave
+  constexpr int kLinPieces = 4;
+  static_assert(kLinPieces <= PieceFmt<F>::N, "pieces written by the preparation");
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, q = lane >> 4, g = lane >> 5, c = lane & 31;
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
+  const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
+                       hdr->H == 64 && hdr->D == 128 && hdr->tile_rows == kTileRows && hdr->n_tiles == a.n_tiles;
+  const int bid = blockIdx.x;
+  if (bid >= a.n_compute) {
+    cleanup_unit<OBF, CLEAN, kTileRows>(a, bid - a.n_compute, plan_ok);
+    return;
+  }
+  if (!plan_ok) return;
+
+  int tile, c0, c1;
+  if (!unit_columns(a, bid, tile, c0, c1)) return;
+  const int n_pairs = (c1 - c0 + 63) / 64;
+  const int b = tile / a.tiles_per_batch;
+
+  const int32_t* slot_row = reinterpret_cast<const int32_t*>(a.plan + a.off_slot);
+  const int32_t first_row = slot_row[int64_t(tile) * kTileRows];
+  int rows[TW];
+  bool rvalid[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int r = slot_row[int64_t(tile) * kTileRows + wave * TW + t];
+    rvalid[t] = r >= 0;
+    rows[t] = r >= 0 ? r : first_row;
+  }
+  if (!rvalid[0] && !rvalid[1]) return;
+
+  // Q: head 16 mb + n of row t, d-chunks q and q + 4, scale byte q
+  i32x8 qf[TW][4];
+  uint32_t sq[TW][4];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int64_t qrow = int64_t(rows[t]) * 64 + 16 * mb + n;
+      const unsigned char* src = static_cast<const unsigned char*>(a.q) + qrow * 128 + 16 * q;
+      const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(src + 64);
+      qf[t][mb] = i32x8{int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+      sq[t][mb] = MX ? uint32_t(static_cast<const uint8_t*>(a.q_scale)[qrow * 4 + q]) : 127u;
+    }
+  }
+  // weights of the lane's output heads: register r of head block mb is head
+  // 16 mb + 4 q + r
+  float wv[TW][4][4];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int64_t off = int64_t(rows[t]) * 64 + 16 * mb + 4 * q;
+      if constexpr (WBF) {
+        const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.w) + off);
+        wv[t][mb][0] = __uint_as_float(x.x << 16);
+        wv[t][mb][1] = __uint_as_float(x.x & 0xFFFF0000u);
+        wv[t][mb][2] = __uint_as_float(x.y << 16);
+        wv[t][mb][3] = __uint_as_float(x.y & 0xFFFF0000u);
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + off);
+        wv[t][mb][0] = x.x;
+        wv[t][mb][1] = x.y;
+        wv[t][mb][2] = x.z;
+        wv[t][mb][3] = x.w;
+      }
+    }
+  }
+  // pieces: A row n is piece n%4 of row n/8, in the first column half's
+  // operand (le) when n%8 < 4, else in the second's (lo); zero elsewhere
+  i32x8 le, lo;
+  uint32_t sle, slo;
+  {
+    const int t = n >> 3, p = n & 3;
+    const bool odd = (n & 4) != 0;
+    const int64_t prow = t ? rows[1] : rows[0];
+    const unsigned char* src = a.pieces + prow * kPieceRowBytes + p * PieceFmt<F>::BYTES + 16 * q;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(src);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(src + 64);
+    const i32x8 v = {int(x0.x), int(x0.y), int(x0.z), int(x0.w), int(x1.x), int(x1.y), int(x1.z), int(x1.w)};
+    const i32x8 z = {};
+    const uint32_t sb = static_cast<const uint8_t*>(static_cast<const void*>(a.pscales))[(prow * kPieceSlots + p) * 4 + q];
+    le = odd ? z : v;
+    lo = odd ? v : z;
+    sle = odd ? 127u : sb;
+    slo = odd ? sb : 127u;
+  }
+
+  // half-wave g stores row g of the wave: its window relative to c0
+  const int my_row = g ? rows[1] : rows[0];
+  const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
+  const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
+
+  // K column halves: lane (n, q) reads column 16 h + n, d-chunks q and q + 4;
+  // MX: the E8M0 byte of d-block q of that column; FP8: the fp32 row scale of
+  // column l%32, which the lane stores.  Blocks past the end of K are clamped
+  // to the last one: in bounds, and never stored.  From a paged cache (PD) a
+  // block's 32 keys are 32 consecutive rows of one page, as in score_kernel.
+  const int nblk = (a.S_k + 31) >> 5;
+  const int kb0 = c0 >> 5;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(a.kfrag) + int64_t(b) * nblk * (32 * 128), 0, nblk * (32 * 128), kBufWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.kscale) + int64_t(b) * nblk * 64, 0, nblk * 256, kBufWord3);
+  const __amdgpu_buffer_rsrc_t pkrs =
+      PD ? __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(a.kcache), 0,
+                                             int(uint32_t(a.num_pages) * uint32_t(a.page_size) * 128u), kBufWord3)
+         : krs;
+  const __amdgpu_buffer_rsrc_t psrs =
+      PD ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.kscache), 0,
+                                             int(uint32_t(a.num_pages) * uint32_t(a.page_size) * 4u), kBufWord3)
+         : srs;
+  const int32_t* btrow = PD ? a.btable + int64_t(b) * a.max_pages : nullptr;
+  const int koff = (q >> 1) * 1024 + (32 * (q & 1) + n) * 16;
+  auto kload = [&](int u, i32x8 (&bf)[2], uint32_t (&sb)[2], uint32_t& ks) {
+    const int blk = min(kb0 + u, nblk - 1);
+    if constexpr (PD) {
+      const uint32_t slot = uint32_t(blk) >> a.bpp_shift;
+      const uint32_t rem = uint32_t(blk) & ((1u << a.bpp_shift) - 1u);
+      int pg = __builtin_amdgcn_readfirstlane(btrow[slot]);
+      pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+      const uint32_t row0 = uint32_t(pg) * uint32_t(a.page_size) + rem * 32u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(pkrs, (16 * h + n) * 128 + 16 * q, int(row0 * 128u), 0);
+        const u32x4 x1 =
+            __builtin_amdgcn_raw_buffer_load_b128(pkrs, (16 * h + n) * 128 + 16 * q + 64, int(row0 * 128u), 0);
+        bf[h] = i32x8{int(x0[0]), int(x0[1]), int(x0[2]), int(x0[3]), int(x1[0]), int(x1[1]), int(x1[2]), int(x1[3])};
+        if constexpr (MX)
+          sb[h] = uint32_t(__builtin_amdgcn_raw_buffer_load_b8(psrs, (16 * h + n) * 4 + q, int(row0 * 4u), 0));
+        else
+          sb[h] = 127u;
+      }
+      if constexpr (!MX) ks = __builtin_amdgcn_raw_buffer_load_b32(psrs, c * 4, int(row0 * 4u), 0);
+      return;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 x0 = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 256 * h, blk * (32 * 128), 0);
+      const u32x4 x1 = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 256 * h + 2048, blk * (32 * 128), 0);
+      bf[h] = i32x8{int(x0[0]), int(x0[1]), int(x0[2]), int(x0[3]), int(x1[0]), int(x1[1]), int(x1[2]), int(x1[3])};
+      if constexpr (MX)
+        sb[h] = uint32_t(__builtin_amdgcn_raw_buffer_load_b8(srs, (16 * h + n) * 4 + q, blk * 256, 0));
+      else
+        sb[h] = 127u;
+    }
+    if constexpr (!MX) ks = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, blk * 256, 0);
+  };
+
+  auto mfma16 = [&](const i32x8& av, uint32_t sA, const i32x8& bv, uint32_t sB, const f32x4& acc) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 0, 0, 0, int(sA), 0, int(sB));
+  };
+
+  // stores: as in score_kernel (one buffer resource per row, drops instead of
+  // branches, -inf picked byte-wise)
+  constexpr int ES = OBF ? 2 : 4;
+  constexpr uint32_t kDrop = 0x80000000u;
+  __amdgpu_buffer_rsrc_t ors[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+    ors[t] = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<unsigned char*>(a.out) + (int64_t(rows[t]) * a.ld + c0) * ES, 0, rvalid[t] ? (c1 - c0) * ES : 0,
+        kBufWord3);
+  const uint32_t half0 = g ? kDrop : 0u, half1 = g ? 0u : kDrop;
+  const uint32_t s_rel = uint32_t(my_s - c0) * ES;
+  const uint32_t w_len = uint32_t(max(my_e - my_s, 0)) * ES;
+  auto store = [&](float v, int u) {
+    const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
+    const bool inwin = off - s_rel < w_len;
+    uint32_t o0 = off | half0, o1 = off | half1;
+    if constexpr (!CLEAN) {
+      o0 = inwin ? o0 : kDrop;
+      o1 = inwin ? o1 : kDrop;
+    }
+    float val = v;
+    if constexpr (CLEAN)
+      val = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(v), 0xFF800000u,
+                                                  inwin ? 0x07060504u : 0x03020100u));
+    if constexpr (OBF) {
+      const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
+      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[0], int(o0), 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[1], int(o1), 0, kNonTemporal);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[0], int(o0), 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[1], int(o1), 0, kNonTemporal);
+    }
+  };
+
+  const float half_scale = 0.5f * a.sm_scale;
+  // p[row][half]: weighted |S| of the lane's heads; fold the lane groups
+  auto combine = [&](const float (&p)[TW][2], float lin, float ks) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][0]), __float_as_uint(p[1][0]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][1]), __float_as_uint(p[1][1]), false, false);
+    const float x = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const float y = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float tot = (__uint_as_float(s2[0]) + __uint_as_float(s2[1])) + lin;
+    return tot * (MX ? half_scale : half_scale * ks);
+  };
+
+  // Software pipeline over steps: per 32-column block 18 MFMAs (the two linear
+  // ones, then (row, head block, half) in order); the epilogue of a step runs
+  // three steps later, behind three other MFMAs, so it never waits for the
+  // matrix pipe.  Accumulators rotate over four slots (36 steps per loop
+  // iteration of two blocks is a multiple of four).  A block's head-sum is
+  // folded and stored one step after its last epilogue.
+  constexpr int kSteps = 18, kLag = 3;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accL[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float p[2][TW][2] = {};
+  float lin[2] = {0.f, 0.f};
+  float kblk[2] = {1.f, 1.f};
+  i32x8 bfs[2][2];
+  uint32_t sbs[2][2];
+  uint32_t kss[2] = {0u, 0u};
+
+  // epilogue of step j (0 <= j < 2 kSteps) of a loop iteration
+  auto epilogue = [&](int j) {
+    const int i = j / kSteps, k = j % kSteps;
+    if (k == 1) {
+      const f32x4& r = accL[i];
+      lin[i] = (r[0] + r[1]) + (r[2] + r[3]);
+    } else if (k >= 2) {
+      const int hb = k - 2, t = hb >> 3, mb = (hb >> 1) & 3, h = hb & 1;
+      float s = mb == 0 ? 0.f : p[i][t][h];
+      const f32x4& r = acc[j & 3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_fmaf(wv[t][mb][e], __builtin_fabsf(r[e]), s);
+      p[i][t][h] = s;
+    }
+  };
+
+  kload(0, bfs[0], sbs[0], kss[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const int n_iter = n_pairs;  // two blocks per iteration
+  for (int s = 0; s < n_iter; ++s) {
+#pragma unroll
+    for (int j = 0; j < 2 * kSteps; ++j) {
+      const int i = j / kSteps, k = j % kSteps;
+      const int u = 2 * s + i;
+      if (k == 0) {
+        kblk[i] = __uint_as_float(kss[i]);
+        kload(u + 1, bfs[1 - i], sbs[1 - i], kss[1 - i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (k == 0) {
+        accL[i] = mfma16(le, sle, bfs[i][0], sbs[i][0], f32x4{0.f, 0.f, 0.f, 0.f});
+      } else if (k == 1) {
+        accL[i] = mfma16(lo, slo, bfs[i][1], sbs[i][1], accL[i]);
+      } else {
+        const int hb = k - 2, t = hb >> 3, mb = (hb >> 1) & 3, h = hb & 1;
+        acc[j & 3] = mfma16(qf[t][mb], sq[t][mb], bfs[i][h], sbs[i][h], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+      // the epilogue of step j - kLag (of the previous iteration for j < kLag)
+      epilogue((j - kLag + 2 * kSteps) % (2 * kSteps));
+      // the previous block's last epilogue ran one step ago: fold and store it
+      if (k == kLag) {
+        const int pi = 1 - i;
+        store(combine(p[pi], lin[pi], kblk[pi]), u - 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // drain: the last block's final epilogues, then its fold and store
+#pragma unroll
+  for (int j = 2 * kSteps - kLag; j < 2 * kSteps; ++j) epilogue(j);
+  store(combine(p[1], lin[1], kblk[1]), 2 * n_iter - 1);
+}
+
 template <int F, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   const int64_t grid = int64_t(a.n_compute) + a.n_tiles;
-  if (a.kcache != nullptr)
+  const bool pd = a.kcache != nullptr;
+  if constexpr (F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3) {
+    if (pd)
+      hipLaunchKernelGGL((score_kernel_x16<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                         a);
+    else
+      hipLaunchKernelGGL((score_kernel_x16<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0,
+                         stream, a);
+  } else if (pd) {
     hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
