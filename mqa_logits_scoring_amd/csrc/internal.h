@@ -96,11 +96,13 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q, int H) {
 // Those formats score with ReLU(x) = (x + |x|) / 2:
 //   sum_h w_h ReLU(S_h) = ( sum_h w_h |S_h| + qt . k ) / 2,  qt = sum_h w_h q_h,
 // so the epilogue needs one FMA (with |.| as a free source modifier) per head
-// instead of a max and an FMA, and the linear term qt . k comes from one more
-// MFMA block.  qt (fp32) is written as pieces with one E8M0 scale per 32
-// elements, each piece encoding the exact fp32 residual of the ones before it:
+// instead of a max and an FMA, and the linear term qt . k comes from MFMA
+// blocks of its own.  qt (fp32) is written as pieces with one E8M0 scale per
+// 32 elements, each piece encoding the exact fp32 residual of the ones before
+// it:
 //  - FP8 / MXFP8: kPieces e4m3 rows (128 B); each shrinks the residual's block
-//    maximum 16-fold, so they sum to qt within 2^-24 of its block maxima;
+//    maximum 16-fold, so they sum to qt within 2^-16 of its block maxima (the
+//    scoring kernel's 16x16 linear blocks hold four pieces per row);
 //  - MXFP4: kPiecesE2M1 e2m1 rows (64 B, packed like MXFP4 Q), so the linear
 //    block multiplies e2m1 by e2m1 at the fp4 rate; with the block maximum
 //    scaled into [2, 4) each piece shrinks it at least 4-fold, 2^-16 in all.
@@ -110,7 +112,7 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q, int H) {
 //   [pieces: n_rows x 768 B: kPieces x 128 B, or kPiecesE2M1 x 64 B]
 //   [piece scales: n_rows x kPieceSlots x uint32]
 // ---------------------------------------------------------------------------
-constexpr int kPieces = 6;
+constexpr int kPieces = 4;
 constexpr int kPiecesE2M1 = 8;
 constexpr int kPieceSlots = 8;        // scale words reserved per row
 constexpr int kPieceRowBytes = 768;   // piece bytes reserved per row

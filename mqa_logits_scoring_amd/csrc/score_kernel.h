@@ -48,7 +48,7 @@
 // c) as 16-byte chunks; Fmt<> gives their offsets, the k-steps that use them,
 // and how the scale word is shifted per lane half so that op_sel picks the
 // right E8M0 byte (the scaled f8f6f4 MFMA places e4m3 and e2m1 operands
-// differently, see Fmt<> and Lin<>).
+// differently, see Fmt<>).
 #pragma once
 
 #include <type_traits>
@@ -123,26 +123,6 @@ static_assert(placement_matches<IDX_IN_BF16>() && placement_matches<IDX_IN_FP8_E
 static_assert(Fmt<IDX_IN_MXFP8_E4M3>::SCALE_SHIFT == KLayout<IDX_IN_MXFP8_E4M3>::SHIFT &&
                   Fmt<IDX_IN_MXFP4_E2M1>::SCALE_SHIFT == KLayout<IDX_IN_MXFP4_E2M1>::SHIFT,
               "K scales are pre-shifted as the MFMA scale operands use them");
-
-// The weighted-query pieces are e4m3 rows (A operand) multiplied with K in
-// its own format (B operand) in the same 32x32x64 MFMA.  Both operands live
-// in one logical k space: an e4m3 lane half g holds k = 16g + [0,16) in bytes
-// 0-15 and k = 32 + 16g + [0,16) in bytes 16-31 (scale block kb from lane half
-// kb); an e2m1 lane half g holds k = 32g + [0,32) (its own scale).  So pieces
-// are loaded with the Q chunk offsets for e4m3 K, and for e2m1 K with chunks
-// at 16g + {0, 64, 32, 96} (k-step s pairs elements 32s+16g.. with
-// 64+32s+16g..), lane half g scaling piece block s+2g (op_sel s on the word
-// shifted right by 16g).
-template <int F>
-struct Lin {
-  static constexpr int OFF[4] = {0, 32, 64, 96};  // + 16 g
-  static constexpr int SCALE_SHIFT = 8, OPSEL_STEP = 2;
-};
-template <>
-struct Lin<IDX_IN_MXFP4_E2M1> {
-  static constexpr int OFF[4] = {0, 64, 32, 96};
-  static constexpr int SCALE_SHIFT = 16, OPSEL_STEP = 1;
-};
 
 constexpr int kThreads = 256;
 
@@ -492,81 +472,39 @@ __global__ void __launch_bounds__(kThreads)
   // alternating; the fragments of later 32-column blocks are loaded while the
   // current one is computed.
   f32x16 accA = {}, accB = {};
-  float p0 = 0.f, p1 = 0.f, kprev = 1.f;
+  float p0 = 0.f, p1 = 0.f;
 
   if constexpr (F != IDX_IN_BF16) {
-    // Blocks per 32-column block u: L (linear term of both rows from the
-    // weighted-query pieces), then (row 0 | row 1) x (heads 0-31 | 32-63).
-    // Pieces of row t sit on A rows {0-3, 8, 9} + 4t, which the 32x32 output
-    // puts in lane half t, registers 0-5: after the head-sum swap, lane half t
-    // holds row t's columns, so the linear term adds in place.
-    using LN = Lin<F>;
+    // MXFP4 (FP8 and MXFP8 run score_kernel_x16).  Blocks per 32-column
+    // block u: L (linear term of both rows from the weighted-query pieces),
+    // then (row 0 | row 1) x (heads 0-31 | 32-63).  The pieces are e2m1 rows
+    // packed like Q, so L is an ordinary fp4 block with the pieces as A rows:
+    // piece p of row t on A row (p % 4) + 4t + 8 (p / 4), which the 32x32
+    // output puts in lane half t, registers 0-7.  After the head-sum swap,
+    // lane half t holds row t's columns, so the linear term adds in place.
+    static_assert(F == IDX_IN_MXFP4_E2M1, "the FP8 formats use score_kernel_x16");
     using PF = PieceFmt<F>;
-    // MXFP4 pieces are e2m1 rows packed like Q, so the linear block is an
-    // ordinary fp4 block (A operand in Q's placement); the e4m3 pieces of the
-    // FP8 formats sit at the offsets Lin<> gives
-    constexpr bool E2M1 = F == IDX_IN_MXFP4_E2M1;
-    constexpr int LFD = E2M1 ? QD : 16;
-    uint32_t lf[LFD];
+    uint32_t lf[QD];
     uint32_t sl;
     {
       const int tt = (c >> 2) & 1, pc = (c & 3) + 4 * (c >> 3);
       const bool has = c < 16 && pc < PF::N;
       const unsigned char* src = a.pieces + int64_t(rows[tt]) * kPieceRowBytes + (has ? pc : 0) * PF::BYTES;
-      if constexpr (E2M1) {
 #pragma unroll
-        for (int v = 0; v < QD / 4; ++v) {
-          const uint4 x = has ? *reinterpret_cast<const uint4*>(src + g * T::CBASE + v * T::CSTRIDE)
-                              : make_uint4(0, 0, 0, 0);
-          lf[4 * v + 0] = x.x;
-          lf[4 * v + 1] = x.y;
-          lf[4 * v + 2] = x.z;
-          lf[4 * v + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const uint4 x = has ? *reinterpret_cast<const uint4*>(src + 16 * g + LN::OFF[v]) : make_uint4(0, 0, 0, 0);
-          lf[4 * v + 0] = x.x;
-          lf[4 * v + 1] = x.y;
-          lf[4 * v + 2] = x.z;
-          lf[4 * v + 3] = x.w;
-        }
+      for (int v = 0; v < QD / 4; ++v) {
+        const uint4 x = has ? *reinterpret_cast<const uint4*>(src + g * T::CBASE + v * T::CSTRIDE)
+                            : make_uint4(0, 0, 0, 0);
+        lf[4 * v + 0] = x.x;
+        lf[4 * v + 1] = x.y;
+        lf[4 * v + 2] = x.z;
+        lf[4 * v + 3] = x.w;
       }
       const uint32_t word = has ? a.pscales[int64_t(rows[tt]) * kPieceSlots + pc] : 0x7F7F7F7Fu;
-      sl = g ? (word >> LN::SCALE_SHIFT) : word;  // 16 for e2m1 pieces, as for MXFP4 Q
+      sl = g ? (word >> T::SCALE_SHIFT) : word;  // as for MXFP4 Q
     }
     const float half_scale = 0.5f * a.sm_scale;
 
-    auto mfma_lin = [&](f32x16& acc, const uint32_t (&bf)[QD], uint32_t sb) {
-      if constexpr (E2M1) {
-        mfma_block(acc, lf, sl, bf, sb);
-        return;
-      }
-      f32x16 d = {};
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        i32x8 av, bv = {};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) av[e] = int(lf[8 * s + e]);
-#pragma unroll
-        for (int e = 0; e < KD; ++e) bv[e] = int(bf[s * KD + e]);
-        constexpr int OA = LN::OPSEL_STEP;
-        if constexpr (T::MX) {
-          constexpr int OB = T::OPSEL_STEP;
-          if (s == 0)
-            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, 0, sl, 0, sb);
-          else
-            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, OA, sl, OB, sb);
-        } else {
-          if (s == 0)
-            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, 0, sl, 0, 127);
-          else
-            d = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, d, 0, T::CODE, OA, sl, 0, 127);
-        }
-      }
-      acc = d;
-    };
+    auto mfma_lin = [&](f32x16& acc, const uint32_t (&bf)[QD], uint32_t sb) { mfma_block(acc, lf, sl, bf, sb); };
     auto epi_lin = [&](const f32x16& acc) {
       float v = acc[0];
 #pragma unroll
@@ -579,12 +517,10 @@ __global__ void __launch_bounds__(kThreads)
       for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[r], __builtin_fabsf(acc[r]), p);
       return p;
     };
-    auto combine_abs = [&](float q0, float q1, float lin, float kscl) {
+    auto combine_abs = [&](float q0, float q1, float lin) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
       const float tot = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) + lin;
-      float scale = half_scale;
-      if constexpr (T::ROWSCALE) scale = half_scale * kscl;
-      return tot * scale;
+      return tot * half_scale;
     };
 
     float linv = 0.f;
@@ -595,10 +531,9 @@ __global__ void __launch_bounds__(kThreads)
     // work.
     auto block_abs = [&](const uint32_t (&bf)[QD], uint32_t kword, int u, f32x16& X, f32x16& Y) {
       const uint32_t sb = kscale_mx(kword);
-      const float ks = __uint_as_float(kword);
       mfma_lin(X, bf, sb);                        // L of u                       ||
       p1 = epi_abs(Y, wv[1][1], p1);              //   (row 1, heads 32-63) of u-1, completing u-1
-      const float v = combine_abs(p0, p1, linv, kprev);
+      const float v = combine_abs(p0, p1, linv);
       interleave_stage();
       mfma_block(Y, qf[0][0], sa[0][0], bf, sb);  // (row 0, heads 0-31) of u    ||
       linv = epi_lin(X);                          //   L of u
@@ -612,7 +547,6 @@ __global__ void __launch_bounds__(kThreads)
       mfma_block(X, qf[1][1], sa[1][1], bf, sb);  // (row 1, heads 32-63)        ||
       p1 = epi_abs(Y, wv[1][0], 0.f);             //   (row 1, heads 0-31)
       interleave_stage();
-      kprev = ks;
       store(v, u - 1);
     };
 
@@ -644,7 +578,7 @@ __global__ void __launch_bounds__(kThreads)
       }
     }
     p1 = epi_abs(accB, wv[1][1], p1);
-    store(combine_abs(p0, p1, linv, kprev), NB * n_iter - 1);
+    store(combine_abs(p0, p1, linv), NB * n_iter - 1);
   } else {
     // ReLU as a signed-integer max of the float's bits: for every non-NaN x,
     // x > 0 exactly when its bits are a positive int32, so max(bits, 0) is
@@ -711,7 +645,7 @@ __global__ void __launch_bounds__(kThreads)
 // of them (32 cycles each at the e4m3 rate, as many cycles as the eight
 // 32x32x64 blocks of score_kernel), but the linear term qt . k now takes two
 // blocks of 32 cycles instead of two of 64: A rows 0-3 / 8-11 (first column
-// half) and 4-7 / 12-15 (second half) hold the first four weighted-query
+// half) and 4-7 / 12-15 (second half) hold the four weighted-query
 // pieces of rows 0 / 1, chained into one accumulator, so lane l ends up with
 // row l/32, column l%32 of the linear term -- where the head-sum below puts
 // the same cell.
