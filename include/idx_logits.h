@@ -170,8 +170,10 @@ idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, con
  * for FP8, MXFP8 and MXFP4 inputs, the per-call weighted-query pieces: those
  * formats use ReLU(x) = (x + |x|) / 2, so sum_h w_h ReLU(S_h) is half of
  * sum_h w_h |S_h| (one FMA per head in the epilogue) plus qt . k with
- * qt = sum_h w_h q_h, taken by one extra MFMA block from qt written exactly
- * as six e4m3 pieces with E8M0 block scales.
+ * qt = sum_h w_h q_h, taken by extra MFMA blocks from qt written as pieces
+ * with E8M0 block scales, each the exact residual of the ones before it
+ * (four e4m3 pieces for FP8 / MXFP8, within 2^-16 of qt's block maxima;
+ * eight e2m1 pieces for MXFP4, also within 2^-16).
  */
 size_t idx_logits_workspace_bytes(const idx_logits_args_t* a);
 
