@@ -178,28 +178,59 @@ __device__ void kscale_group(const PrepArgs& a, int64_t wg) {
     if (at[j] >= 0) a.kscale[at[j]] = (threadIdx.x & 32) ? word[j] >> SHIFT : word[j];
 }
 
-// Weighted query of one row, qt = sum_h w_h q_h, by a workgroup of 4 waves.
-// Wave v reads heads 16v..16v+15 in 16-byte loads, each load covering 1 KB:
-// lane l holds EPL consecutive elements d0 = (l % LPH) * EPL.. of head
-// 16v + HPL * i + l / LPH.  Each lane accumulates w_h q_h over its heads and
-// leaves its partial sums in LDS; wave 0 adds them in a fixed order (wave,
-// then lane group) into the lane-owns-two-elements layout of the encoder.
+// Weighted query of one row, qt = sum_h w_h q_h, and its pieces, by one wave
+// (a workgroup of 256 threads does 4 rows).  Lane l reads 16 bytes at
+// l*16 + 1024*i of the row's 64 heads (i < 8 for e4m3, < 4 for e2m1): EPL
+// consecutive elements d0 = (l % LPH) * EPL.. of head l / LPH + HPL * i.  Each
+// lane decodes them exactly (the scaled converts with scale 1, then the E8M0
+// block scale as a multiply, as the definition reads) and accumulates
+// w_h * q_h over its heads.  A butterfly over the lanes that share d0 then
+// leaves, stage by stage, half of the running sums in each lane
+// (reduce-scatter; the order of every sum is fixed), until lane l holds
+// qt[e], qt[e+1] with e = d0 + 2 * (l / LPH): the layout the encoder and the
+// piece stores use.
 template <int F>
 struct PieceLoad {
-  static constexpr int EPL = F == IDX_IN_MXFP4_E2M1 ? 32 : 16;  // elements per lane per load
-  static constexpr int LPH = 128 / EPL;                         // lanes per head
-  static constexpr int HPL = 64 / LPH;                          // heads per load
-  static constexpr int NLW = 16 / HPL;                          // loads per wave
-  static constexpr int HB = F == IDX_IN_MXFP4_E2M1 ? 64 : 128;  // Q bytes per head
-  static constexpr int GROUPS = 4 * HPL;                        // partial sums per element
+  static constexpr bool E2M1 = F == IDX_IN_MXFP4_E2M1;
+  static constexpr int EPL = E2M1 ? 32 : 16;  // elements per lane per load
+  static constexpr int LPH = 128 / EPL;       // lanes per head (4 or 8)
+  static constexpr int HPL = 64 / LPH;        // heads per load (16 or 8)
+  static constexpr int NLW = 64 / HPL;        // loads per lane (4 or 8)
+  static constexpr int HB = E2M1 ? 64 : 128;  // Q bytes per head
 };
 
+// x from lane l ^ 8 (a rotation by 8 inside each row of 16 lanes)
+__device__ __forceinline__ float xor8(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+// x from lane l ^ 4 (swizzle inside each group of 32 lanes)
+__device__ __forceinline__ float xor4(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+}
+// x from lane l ^ 1
+__device__ __forceinline__ float xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float max_swap32(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float max_swap16(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
 template <int F, bool WBF>
-__device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
+__device__ void pieces_rows(const PrepArgs& a, int64_t wg) {
   using P = PieceLoad<F>;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  using PF = PieceFmt<F>;
+  constexpr bool E2M1 = P::E2M1;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = wg * 4 + (threadIdx.x >> 6);
+  if (row >= a.n_rows) return;
   const int sub = lane % P::LPH, hl = lane / P::LPH;
-  const unsigned char* qrow = static_cast<const unsigned char*>(a.q) + row * (64 * P::HB) + wv * 16 * P::HB;
+  const int blk = sub * P::EPL / 32;  // the lane's 32-element block
+  const unsigned char* qrow = static_cast<const unsigned char*>(a.q) + row * (64 * P::HB);
   uint4 raw[P::NLW];
 #pragma unroll
   for (int i = 0; i < P::NLW; ++i) raw[i] = *reinterpret_cast<const uint4*>(qrow + i * 1024 + lane * 16);
@@ -208,44 +239,88 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
   for (int e = 0; e < P::EPL; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int i = 0; i < P::NLW; ++i) {
-    const int64_t qh = row * 64 + 16 * wv + P::HPL * i + hl;
+    const int64_t qh = row * 64 + P::HPL * i + hl;
     const float wh = WBF ? __uint_as_float(uint32_t(static_cast<const uint16_t*>(a.w)[qh]) << 16)
                          : static_cast<const float*>(a.w)[qh];
     float sc = 1.f;
     if constexpr (F != IDX_IN_FP8_E4M3)
-      sc = e8m0_value((static_cast<const uint32_t*>(a.q_scale)[qh] >> (8 * (sub * P::EPL / 32))) & 0xFFu);
+      sc = e8m0_value((static_cast<const uint32_t*>(a.q_scale)[qh] >> (8 * blk)) & 0xFFu);
     const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    auto add2 = [&](int e, f2 v) {
+      acc[e] = __builtin_fmaf(wh, v.x * sc, acc[e]);
+      acc[e + 1] = __builtin_fmaf(wh, v.y * sc, acc[e + 1]);
+    };
 #pragma unroll
-    for (int e = 0; e < P::EPL; ++e) {
-      float v;
-      if constexpr (F == IDX_IN_MXFP4_E2M1)
-        v = e2m1_value((wd[e / 8] >> (4 * (e % 8))) & 15u);
-      else
-        v = e4m3_value((wd[e / 4] >> (8 * (e % 4))) & 0xFFu);
-      acc[e] = __builtin_fmaf(wh, v * sc, acc[e]);
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (E2M1) {  // byte s of the word: elements 8k + 2s (low nibble), 8k + 2s + 1
+        add2(8 * k + 0, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[k], 1.f, 0));
+        add2(8 * k + 2, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[k], 1.f, 1));
+        add2(8 * k + 4, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[k], 1.f, 2));
+        add2(8 * k + 6, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[k], 1.f, 3));
+      } else {  // bytes 0-1 and 2-3 of the word: elements 4k.. 4k + 3
+        add2(4 * k + 0, __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[k], 1.f, false));
+        add2(4 * k + 2, __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wd[k], 1.f, true));
+      }
     }
   }
-  // partial sums: part[group][d], group = wave * HPL + lane group
-  float* dst = part + (wv * P::HPL + hl) * 128 + sub * P::EPL;
+  // reduce-scatter over the lanes sharing d0 (lane bits above log2(LPH)):
+  // each stage halves the sums a lane keeps, splitting the element index on
+  // its highest remaining bit, so the two left are adjacent elements
+  float r0, r1;
+  {
+    float v32[P::EPL / 2];  // after lane ^ 32: element j + (EPL/2) * bit5
 #pragma unroll
-  for (int e = 0; e < P::EPL; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
-  __syncthreads();
-  if (wv != 0) return;
-  float r0 = 0.f, r1 = 0.f;
-#pragma unroll 8
-  for (int gi = 0; gi < P::GROUPS; ++gi) {
-    const float2 x = *reinterpret_cast<const float2*>(part + gi * 128 + 2 * lane);
-    r0 += x.x;
-    r1 += x.y;
+    for (int j = 0; j < P::EPL / 2; ++j) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j]), __float_as_uint(acc[j + P::EPL / 2]),
+                                                       false, false);
+      v32[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    constexpr int N16 = P::EPL / 4;
+    float v16[N16];  // after lane ^ 16
+#pragma unroll
+    for (int j = 0; j < N16; ++j) {
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v32[j]), __float_as_uint(v32[j + N16]), false,
+                                                       false);
+      v16[j] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    constexpr int N8 = P::EPL / 8;
+    const bool b3 = (lane & 8) != 0;
+    float v8[N8];  // after lane ^ 8
+#pragma unroll
+    for (int j = 0; j < N8; ++j) {
+      const float keep = b3 ? v16[j + N8] : v16[j], send = b3 ? v16[j] : v16[j + N8];
+      v8[j] = keep + xor8(send);
+    }
+    if constexpr (E2M1) {
+      const bool b2 = (lane & 4) != 0;
+      float v4[2];  // after lane ^ 4
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float keep = b2 ? v8[j + 2] : v8[j], send = b2 ? v8[j] : v8[j + 2];
+        v4[j] = keep + xor4(send);
+      }
+      r0 = v4[0];
+      r1 = v4[1];
+    } else {
+      r0 = v8[0];
+      r1 = v8[1];
+    }
   }
-  // pieces: each encodes the exact residual left by the ones before it; lane
-  // l owns elements 2l and 2l+1, so lanes 16b..16b+15 hold 32-element block b
-  using PF = PieceFmt<F>;
-  constexpr bool E2M1 = F == IDX_IN_MXFP4_E2M1;
+  // lane holds elements e0 = d0 + 2 * hl and e0 + 1
+  const int e0 = sub * P::EPL + 2 * hl;
+  // pieces: each encodes the exact residual left by the ones before it; the
+  // block maximum runs over the 16 lanes of the lane's 32-element block
   for (int p = 0; p < PF::N; ++p) {
     float m = __builtin_fmaxf(__builtin_fabsf(r0), __builtin_fabsf(r1));
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o));
+    if constexpr (E2M1) {
+      m = __builtin_fmaxf(m, xor4(m));
+    } else {
+      m = __builtin_fmaxf(m, xor1(m));
+    }
+    m = __builtin_fmaxf(m, xor8(m));
+    m = max_swap16(m);
+    m = max_swap32(m);
     const uint32_t mb = __float_as_uint(m);
     const uint32_t E = (mb >> 23) & 0xFFu;
     uint32_t sbyte = 127u, c0 = 0u, c1 = 0u;
@@ -255,26 +330,30 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
       const int k = E2M1 ? int(E) - 128 : int(E) - 127 - 8 + ((mb & 0x7FFFFFu) > 0x600000u ? 1 : 0);
       sbyte = uint32_t(127 + k);
       const float inv = __uint_as_float(uint32_t(127 - k) << 23);  // 2^-k (k in [-119, 126])
-      const float sc = __uint_as_float(sbyte << 23);
+      const float scl = __uint_as_float(sbyte << 23);
       if constexpr (E2M1) {
         c0 = e2m1_code(r0 * inv);
         c1 = e2m1_code(r1 * inv);
-        r0 -= e2m1_value(c0) * sc;  // exact: the decoded piece is 0 or within a factor 2 of r
-        r1 -= e2m1_value(c1) * sc;
+        r0 -= e2m1_value(c0) * scl;  // exact: the decoded piece is 0 or within a factor 2 of r
+        r1 -= e2m1_value(c1) * scl;
       } else {
         c0 = e4m3_code(r0 * inv);
         c1 = e4m3_code(r1 * inv);
-        r0 -= e4m3_value(c0) * sc;  // exact: the decoded piece is within a factor 2 of r
-        r1 -= e4m3_value(c1) * sc;
+        r0 -= e4m3_value(c0) * scl;  // exact: the decoded piece is within a factor 2 of r
+        r1 -= e4m3_value(c1) * scl;
       }
     }
     unsigned char* dst = a.pieces + row * kPieceRowBytes + p * PF::BYTES;
     if constexpr (E2M1)
-      dst[lane] = uint8_t(c0 | (c1 << 4));  // elements 2l (low nibble) and 2l+1
+      dst[e0 / 2] = uint8_t(c0 | (c1 << 4));  // elements e0 (low nibble) and e0 + 1
     else
-      reinterpret_cast<uint16_t*>(dst)[lane] = uint16_t(c0 | (c1 << 8));
-    const uint32_t word = (__shfl(sbyte, 0)) | (__shfl(sbyte, 16) << 8) | (__shfl(sbyte, 32) << 16) |
-                          (__shfl(sbyte, 48) << 24);
+      reinterpret_cast<uint16_t*>(dst)[e0 / 2] = uint16_t(c0 | (c1 << 8));
+    // block b's byte from its first lane (sub = b * 32 / EPL, hl = 0)
+    constexpr int LPB = 32 / P::EPL;  // lanes of sub per block (1 or 2)
+    const uint32_t word = uint32_t(__builtin_amdgcn_readlane(int(sbyte), 0)) |
+                          (uint32_t(__builtin_amdgcn_readlane(int(sbyte), 1 * LPB)) << 8) |
+                          (uint32_t(__builtin_amdgcn_readlane(int(sbyte), 2 * LPB)) << 16) |
+                          (uint32_t(__builtin_amdgcn_readlane(int(sbyte), 3 * LPB)) << 24);
     if (lane == 0) a.pscales[row * kPieceSlots + p] = word;
   }
 }
@@ -282,9 +361,7 @@ __device__ void pieces_row(const PrepArgs& a, int64_t row, float* part) {
 template <int F, bool WBF>
 __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
   using L = KLayout<F>;
-  constexpr int PART = F == IDX_IN_BF16 ? 1 : PieceLoad<F == IDX_IN_BF16 ? IDX_IN_FP8_E4M3 : F>::GROUPS * 128;
   __shared__ union {
-    float part[PART];
     PlanSmem plan;
   } sm;
   int64_t bid = blockIdx.x;
@@ -295,7 +372,7 @@ __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
   bid -= a.n_plan;
   if constexpr (F != IDX_IN_BF16) {
     if (bid < a.n_pieces) {
-      pieces_row<F, WBF>(a, bid, sm.part);
+      pieces_rows<F, WBF>(a, bid);
       return;
     }
     bid -= a.n_pieces;
@@ -359,7 +436,7 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.pieces = pieces;
   a.pscales = pscales;
   const bool scaled = has_kscale(fmt);
-  a.n_pieces = pieces != nullptr ? n_rows : 0;  // only 64-head calls of the formats with pieces
+  a.n_pieces = pieces != nullptr ? (n_rows + 3) / 4 : 0;  // only 64-head calls of the formats with pieces
   // several chunks per thread only when that still leaves at least 2048
   // workgroups of K copy
   const bool copy_k = paged == nullptr || !paged->skip_gather;
