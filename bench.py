@@ -301,8 +301,9 @@ def main():
             # the K reorder and the weighted-query pieces share one launch,
             # then the scoring kernel.  Packed variable-length rows build
             # their plan with idx_logits_plan_thd first.
-            # Paged calls gather their keys through the block table in the
-            # same preparation launch.
+            # Paged calls read their keys straight from the cache where the
+            # library can (64 heads, pages of 32 * 2^j keys), else gather them
+            # through the block table in the same preparation launch.
             call_plan = build_plan(lib, wl, d, plan, stream) if thd else None
             if paged:
                 lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],

@@ -12,8 +12,8 @@
 // share one K head across the H query heads as here.
 //
 // Epilogue: ReLU as a signed-integer max of the float's bits and one FMA per
-// head (the weighted-query pieces of the 64-head kernels need six extra
-// A rows per query row, a whole extra MFMA block per wave at these H).
+// head (the weighted-query pieces of the 64-head kernels need four to eight
+// extra A rows per query row, a whole extra MFMA block per wave at these H).
 // Lane (c, g) of a 32x32 accumulator holds column c and the block's M rows
 // 8(r/4) + 4g + r%4 in register r; with H <= 32 those rows belong to query
 // row r / (16 / RPB) of the block whatever g is, so each lane keeps one

@@ -9,26 +9,28 @@
 // how it is chosen, so the ranking above is the plain one and the algorithm
 // is this file's own.
 //
-// One workgroup of 512 threads per row.  Scores become 32-bit keys whose
+// One workgroup of 1024 threads per row.  Scores become 32-bit keys whose
 // unsigned order is the ranking (sign-magnitude flipped, -0 folded onto +0,
-// NaN to 0).  Thread t holds columns s + ch*kChunk + m*512 + t (m < 64) of
+// NaN to 0).  Thread t holds columns s + ch*kChunk + m*1024 + t (m < 32) of
 // chunk ch in registers, so every load instruction of a wave reads 64
-// consecutive scores; rows up to kChunk columns are read once, longer rows
-// once per pass.
+// consecutive scores; rows up to kChunk = 32768 columns are read once, longer
+// rows once per pass.
 //
-//  1. A histogram of the top 12 key bits (4096 LDS bins) fixes the bucket b
-//     holding the k-th largest key: every key above b is selected.
+//  1. A histogram of key bits 31..22 (1024 LDS bins, 8 copies spread over the
+//     banks by lane) fixes the bucket b holding the k-th largest key: every
+//     key above b is selected.
 //  2. When b holds at most kCand keys, they are compacted into LDS with their
-//     columns and the rest of the selection is a radix select over that short
-//     list (key bits 19..8, 7..0, then the column for keys equal to the
-//     threshold).  A flat row (b holding more) runs those passes over the
-//     registers instead.  Either way the result is a threshold (T, T2): a key
-//     is selected when it is above T, or equal to T with a column no larger
-//     than the one T2 names.
+//     columns (one block scan of the per-thread counts places them) and the
+//     rest of the selection is a radix select over that short list (key bits
+//     21..10, 9..0, then the column for keys equal to the threshold).  A flat
+//     row (b holding more) runs those passes over the registers instead.
+//     Either way the result is a threshold (T, T2): a key is selected when it
+//     is above T, or equal to T with a column no larger than the one T2 names.
 //  3. The selected keys are written out: by column, each wave ballots its
 //     selection per register and one block scan over the (register, wave)
 //     counts gives every selected column its place; in rank order they go to
 //     LDS as (key, ~column) pairs and a bitonic sort orders them.
+
 #include "internal.h"
 
 namespace idx {
