@@ -52,12 +52,13 @@ CSRC = os.path.join(ROOT, "mqa_logits_scoring_amd", "csrc")
 
 
 def kernel_source_hash(fmt: str) -> str:
-    """sha256 over the sources of the scoring kernel of one input format
-    (fmt "topk": of the top-k kernel)."""
+    """sha256 over the sources of the scoring kernel of one input format,
+    with the host code that splits its work into units (fmt "topk": of the
+    top-k kernel)."""
     import hashlib
     h = hashlib.sha256()
     files = ("topk.hip", "internal.h") if fmt == "topk" else ("score_kernel.h", "score_kernel_gh.h", "internal.h",
-                                                              f"score_{fmt}.hip")
+                                                              f"score_{fmt}.hip", "api.cpp")
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
