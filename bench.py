@@ -228,6 +228,67 @@ def cpu_baseline(wl, V: int, target_s: float = 12.0) -> dict:
                       f"scaled by visible cells to the full call", "cpu_model": _cpu_model()}
 
 
+def measure_peaks(dev, settle_s: float = 0.3) -> dict | None:
+    """The matrix-core throughput of every MFMA shape the scoring kernels use
+    (libidx_peak.so: independent MFMAs on register operands, pseudo-random or
+    zero codes, two waves per SIMD) and a plain 1 GiB device copy, measured
+    here.  Each case runs `settle_s` seconds before 10 timed launches, so the
+    clock has settled under its own power draw."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "mqa_logits_scoring_amd", "libidx_peak.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.idx_peak_mfma.restype = ctypes.c_int32
+    L.idx_peak_mfma.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    L.idx_peak_flop_per_mfma.restype = ctypes.c_double
+    L.idx_peak_flop_per_mfma.argtypes = [ctypes.c_int32]
+    groups = 512  # two 4-wave workgroups per CU
+    out = torch.empty(groups * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = {0: "bf16_32x32x16", 1: "fp8_32x32x64", 2: "fp8_16x16x128", 3: "fp4_32x32x64", 4: "fp4_16x16x128"}
+    res = {}
+    for kind, name in names.items():
+        flop1 = L.idx_peak_flop_per_mfma(kind)
+        iters = max(1, int(4e12 / (groups * 4 * 8 * flop1)))
+        flop = groups * 4 * 8 * iters * flop1
+        res[name] = {}
+        for zero in (0, 1):
+            def go():
+                st = L.idx_peak_mfma(kind, groups, iters, zero, out.data_ptr(), stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(f"idx_peak_mfma({kind}) failed with status {st}")
+            t0 = time.perf_counter()
+            while time.perf_counter() - t0 < settle_s:
+                go()
+                torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                go()
+            e1.record(stream)
+            e1.synchronize()
+            res[name]["zero" if zero else "random"] = round(10 * flop / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record(stream)
+    e1.synchronize()
+    copy_gbs = 5 * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    return {"mfma_tflops": res, "copy_gbs": round(copy_gbs, 1),
+            "note": "MFMA: independent MFMAs per shape, 2 waves per SIMD, random or zero operands; "
+                    "copy: 1 GiB device-to-device, read + write bytes"}
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -253,8 +314,11 @@ def main():
                     help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-variant", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-shape and copy peak measurement")
     ap.add_argument("--topk", type=int, default=0,
                     help="also time top-k selection (this k, by column) over the call's scores")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the MFMA throughput per shape and a device copy (libidx_peak.so)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes `steps` times (counter calibration)")
     args = ap.parse_args()
@@ -269,6 +333,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.peaks:
+        print(json.dumps(measure_peaks(dev, settle_s=1.0)), flush=True)
+        return
 
     if args.copy_bytes:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
@@ -455,6 +523,16 @@ def main():
                               "ratio_to_pages": round(zus / PAGES_US[zero_name], 3) if zero_name in PAGES_US else None}
     if topk is not None:
         res["topk"] = topk
+    if not args.no_peaks:
+        pk = measure_peaks(dev)
+        if pk is not None and res["roofline"]["bound"] == "mfma" and wl.H == 64:
+            # the MFMA shape the 64-head scoring kernel of this input format issues
+            shape = {"bf16": "bf16_32x32x16", "fp8": "fp8_16x16x128", "mxfp8": "fp8_16x16x128",
+                     "mxfp4": "fp4_32x32x64"}[wl.fmt]
+            meas = pk["mfma_tflops"][shape]["random"]
+            pk["kernel_shape"] = shape
+            pk["kernel_frac_of_measured_random"] = round(res["roofline"]["achieved"] / meas, 4)
+        res["peaks_measured"] = pk
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, V)
     print(json.dumps(res), flush=True)

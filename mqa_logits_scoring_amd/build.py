@@ -14,6 +14,9 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libidx_logits.so")
+# the matrix-core throughput probe bench.py reports beside the roofline
+PEAK_LIB = os.path.join(PKG, "libidx_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "topk.hip", "score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
 HEADERS = ["internal.h", "score_kernel.h", "score_kernel_gh.h", "plan_segment.h", os.path.join("..", "..", "include", "idx_logits.h")]
@@ -60,15 +63,16 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libidx_logits.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+        objs = list(ex.map(_compile, SOURCES + PEAK_SOURCES))
+    for lib, part in ((LIB, objs[:len(SOURCES)]), (PEAK_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *part, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 

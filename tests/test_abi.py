@@ -228,3 +228,53 @@ def test_topk_rejects():
     assert call(order=2) == lib.IDX_E_INVALID
     assert call(ld=63) == lib.IDX_E_INVALID
     assert "ld" in lib.idx_last_error()
+
+
+# ---------------------------------------------------------------------------
+# the matrix-core throughput probe beside the library (include/idx_peak.h)
+# ---------------------------------------------------------------------------
+
+PEAK_HEADER = os.path.join(os.path.dirname(HEADER), "idx_peak.h")
+PEAK_LIB = os.path.join(os.path.dirname(lib.LIB_PATH), "libidx_peak.so")
+
+
+def _peak_lib():
+    L = ctypes.CDLL(PEAK_LIB)
+    L.idx_peak_mfma.restype = ctypes.c_int32
+    L.idx_peak_mfma.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
+    L.idx_peak_flop_per_mfma.restype = ctypes.c_double
+    L.idx_peak_flop_per_mfma.argtypes = [ctypes.c_int32]
+    return L
+
+
+def test_peak_probe_exports_and_checks():
+    text = re.sub(r"/\*.*?\*/", "", open(PEAK_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text)))
+    assert names == ["idx_peak_flop_per_mfma", "idx_peak_mfma"], names
+    L = _peak_lib()
+    assert [L.idx_peak_flop_per_mfma(k) for k in range(5)] == [32768.0, 131072.0, 65536.0, 131072.0, 65536.0]
+    assert L.idx_peak_flop_per_mfma(9) == 0.0
+    # rejected on the host, nothing launched
+    assert L.idx_peak_mfma(1, 0, 10, 0, 16, None) == 1
+    assert L.idx_peak_mfma(1, 4, 0, 0, 16, None) == 1
+    assert L.idx_peak_mfma(1, 4, 10, 0, None, None) == 1
+    assert L.idx_peak_mfma(9, 4, 10, 0, 16, None) == 2
+
+
+@pytest.mark.gpu
+def test_peak_probe_runs_every_shape():
+    import torch
+    L = _peak_lib()
+    out = torch.zeros(8 * 256, dtype=torch.float32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for kind in range(5):
+        for zero in (0, 1):
+            out.zero_()
+            assert L.idx_peak_mfma(kind, 8, 3, zero, out.data_ptr(), s) == 0
+            torch.cuda.synchronize()
+            # every accumulator starts at a nonzero value; zero operands leave it
+            assert bool(torch.isfinite(out).all()), (kind, zero)
+            if zero:
+                # 8 accumulators starting at 1..8, every element summed
+                per = 16 if kind in (0, 1, 3) else 4
+                assert bool((out == float(per * 36)).all()), (kind, out[:4])
