@@ -1,4 +1,5 @@
-"""Build libidx_logits.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
+"""Build libidx_logits.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree,
+and libidx_peak.so, the MFMA throughput probe bench.py reports beside it.
 
 Usage: python -m mqa_logits_scoring_amd.build   (or build() from Python)
 """
