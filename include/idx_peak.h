@@ -38,6 +38,23 @@ double idx_peak_flop_per_mfma(int32_t kind);
  */
 int32_t idx_peak_mfma(int32_t kind, int32_t groups, int32_t iters, int32_t zero, float* out, void* stream);
 
+/*
+ * The scoring kernels' issue pattern at its own rate: `groups` workgroups of 4
+ * waves (launch 2 waves per SIMD, i.e. groups = 2 x the CU count, for the
+ * scoring kernels' occupancy); every wave runs iters x 8 steps of one
+ * v_mfma_scale_f32_16x16x128_f8f6f4 (e4m3, pseudo-random codes) followed by
+ * `valu` dependent fp32 FMAs on the absolute values of the accumulator of
+ * three MFMAs earlier.  Writes one float per thread to `out` (groups * 256
+ * floats) and, per wave w of workgroup g, the shader-clock cycles of its loop
+ * to wave_cycles[4 g + w] (groups * 4 entries); both device memory owned by
+ * the caller.  With two waves per SIMD the matrix pipe's share of the cycles
+ * is 32 * 16 * iters / wave_cycles (a 16x16x128 MFMA occupies it 32 cycles).
+ * `valu` is one of 0, 2, 3, 4, 5, 6, 8.  Returns 0, 1 for invalid arguments
+ * (nothing enqueued), 2 for an unsupported `valu`, 4 for a launch failure.
+ */
+int32_t idx_peak_mfma_valu(int32_t valu, int32_t groups, int32_t iters, float* out, int64_t* wave_cycles,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,6 +83,58 @@ hipError_t launch(int groups, int iters, int zero, float* out, hipStream_t strea
   return hipGetLastError();
 }
 
+// The scoring kernels' issue pattern: each 16x16x128 e4m3 MFMA followed by
+// V dependent FMAs on the absolute values of the accumulator written three
+// MFMAs earlier (one chain per MFMA, as the ReLU-weighted head sum runs), two
+// waves per SIMD.  Each wave records the shader cycles its loop took, so the
+// cost of the VALU work beside the matrix pipe reads off in cycles per MFMA,
+// independent of the clock.
+template <int V>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    overlap_kernel(int iters, float* out, long long* cycles) {
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  i32x8 a[8], b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[i][e] = int(mix(gid * 64u + uint32_t(8 * i + e) + 1u) & 0x77777777u);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = int(mix(gid * 64u + 100u + uint32_t(e)) & 0x77777777u);
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{} + float(i + 1);
+  float w[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) w[v] = float(mix(gid + 7u * uint32_t(v)) & 255u) * 1e-3f;
+  float sum = 0.f;
+  const long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // accumulating into acc[i] keeps the MFMA inside the loop; eight
+      // accumulators leave it independent of the previous seven
+      acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, acc[i], 0, 0, 0, 127, 0, 127);
+      const f32x4 r = acc[(i + 5) & 7];
+#pragma unroll
+      for (int v = 0; v < V; ++v) sum = __builtin_fmaf(w[v], __builtin_fabsf(r[v & 3]), sum);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  const long long t1 = clock64();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sum += (acc[i][0] + acc[i][1]) + (acc[i][2] + acc[i][3]);
+  out[gid] = sum;
+  if ((threadIdx.x & 63) == 0) cycles[blockIdx.x * 4 + (threadIdx.x >> 6)] = t1 - t0;
+}
+
+template <int V>
+hipError_t launch_overlap(int groups, int iters, float* out, long long* cycles, hipStream_t stream) {
+  hipLaunchKernelGGL((overlap_kernel<V>), dim3(unsigned(groups)), dim3(256), 0, stream, iters, out, cycles);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +160,25 @@ int32_t idx_peak_mfma(int32_t kind, int32_t groups, int32_t iters, int32_t zero,
     case IDX_PEAK_FP8_16X16X128: e = launch<IDX_PEAK_FP8_16X16X128>(groups, iters, zero, out, s); break;
     case IDX_PEAK_FP4_32X32X64: e = launch<IDX_PEAK_FP4_32X32X64>(groups, iters, zero, out, s); break;
     case IDX_PEAK_FP4_16X16X128: e = launch<IDX_PEAK_FP4_16X16X128>(groups, iters, zero, out, s); break;
+    default: return 2;
+  }
+  return e == hipSuccess ? 0 : 4;
+}
+
+int32_t idx_peak_mfma_valu(int32_t valu, int32_t groups, int32_t iters, float* out, int64_t* wave_cycles,
+                           void* stream) {
+  if (groups <= 0 || iters <= 0 || out == nullptr || wave_cycles == nullptr) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  long long* cyc = reinterpret_cast<long long*>(wave_cycles);
+  hipError_t e;
+  switch (valu) {
+    case 0: e = launch_overlap<0>(groups, iters, out, cyc, s); break;
+    case 2: e = launch_overlap<2>(groups, iters, out, cyc, s); break;
+    case 3: e = launch_overlap<3>(groups, iters, out, cyc, s); break;
+    case 4: e = launch_overlap<4>(groups, iters, out, cyc, s); break;
+    case 5: e = launch_overlap<5>(groups, iters, out, cyc, s); break;
+    case 6: e = launch_overlap<6>(groups, iters, out, cyc, s); break;
+    case 8: e = launch_overlap<8>(groups, iters, out, cyc, s); break;
     default: return 2;
   }
   return e == hipSuccess ? 0 : 4;

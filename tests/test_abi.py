@@ -244,13 +244,15 @@ def _peak_lib():
     L.idx_peak_mfma.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     L.idx_peak_flop_per_mfma.restype = ctypes.c_double
     L.idx_peak_flop_per_mfma.argtypes = [ctypes.c_int32]
+    L.idx_peak_mfma_valu.restype = ctypes.c_int32
+    L.idx_peak_mfma_valu.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 3
     return L
 
 
 def test_peak_probe_exports_and_checks():
     text = re.sub(r"/\*.*?\*/", "", open(PEAK_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text)))
-    assert names == ["idx_peak_flop_per_mfma", "idx_peak_mfma"], names
+    assert names == ["idx_peak_flop_per_mfma", "idx_peak_mfma", "idx_peak_mfma_valu"], names
     L = _peak_lib()
     assert [L.idx_peak_flop_per_mfma(k) for k in range(5)] == [32768.0, 131072.0, 65536.0, 131072.0, 65536.0]
     assert L.idx_peak_flop_per_mfma(9) == 0.0
@@ -259,6 +261,11 @@ def test_peak_probe_exports_and_checks():
     assert L.idx_peak_mfma(1, 4, 0, 0, 16, None) == 1
     assert L.idx_peak_mfma(1, 4, 10, 0, None, None) == 1
     assert L.idx_peak_mfma(9, 4, 10, 0, 16, None) == 2
+    assert L.idx_peak_mfma_valu(4, 0, 10, 16, 16, None) == 1
+    assert L.idx_peak_mfma_valu(4, 4, 0, 16, 16, None) == 1
+    assert L.idx_peak_mfma_valu(4, 4, 10, None, 16, None) == 1
+    assert L.idx_peak_mfma_valu(4, 4, 10, 16, None, None) == 1
+    assert L.idx_peak_mfma_valu(7, 4, 10, 16, 16, None) == 2
 
 
 @pytest.mark.gpu
@@ -278,3 +285,20 @@ def test_peak_probe_runs_every_shape():
                 # 8 accumulators starting at 1..8, every element summed
                 per = 16 if kind in (0, 1, 3) else 4
                 assert bool((out == float(per * 36)).all()), (kind, out[:4])
+
+
+@pytest.mark.gpu
+def test_peak_overlap_probe_runs():
+    import torch
+    L = _peak_lib()
+    groups, iters = 8, 3
+    out = torch.zeros(groups * 256, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(groups * 4, dtype=torch.int64, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    for valu in (0, 2, 3, 4, 5, 6, 8):
+        cyc.zero_()
+        assert L.idx_peak_mfma_valu(valu, groups, iters, out.data_ptr(), cyc.data_ptr(), s) == 0
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all()), valu
+        # every wave ran 24 MFMAs of at least 16 cycles each
+        assert int(cyc.min()) >= 24 * 16, (valu, cyc[:4])
