@@ -749,6 +749,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       }
     }
   }
+  // sm_scale / 2 rides on the weights, so a block's fold needs no multiply
+  // for it: the |S| sums come out scaled, the linear term is scaled as it
+  // is added
+  const float half_scale = 0.5f * a.sm_scale;
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wv[t][mb][e] *= half_scale;
   // pieces: A row n is piece n%4 of row n/8, in the first column half's
   // operand (le) when n%8 < 4, else in the second's (lo); zero elsewhere
   i32x8 le, lo;
@@ -869,16 +879,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
-  const float half_scale = 0.5f * a.sm_scale;
-  // p[row][half]: weighted |S| of the lane's heads; fold the lane groups
+  // p[row][half]: weighted |S| of the lane's heads (weights carry
+  // sm_scale / 2); fold the lane groups
   auto combine = [&](const float (&p)[TW][2], float lin, float ks) {
     const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][0]), __float_as_uint(p[1][0]), false, false);
     const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0][1]), __float_as_uint(p[1][1]), false, false);
     const float x = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
     const float y = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
     const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    const float tot = (__uint_as_float(s2[0]) + __uint_as_float(s2[1])) + lin;
-    return tot * (MX ? half_scale : half_scale * ks);
+    const float tot = __builtin_fmaf(lin, half_scale, __uint_as_float(s2[0]) + __uint_as_float(s2[1]));
+    return MX ? tot : tot * ks;
   };
 
   // Software pipeline over steps: per 32-column block 18 MFMAs, column half
