@@ -845,7 +845,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   };
 
   // stores: as in score_kernel (one buffer resource per row, drops instead of
-  // branches, -inf picked byte-wise)
+  // branches), -inf by one select
   constexpr int ES = OBF ? 2 : 4;
   constexpr uint32_t kDrop = 0x80000000u;
   __amdgpu_buffer_rsrc_t ors[TW];
@@ -866,9 +866,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
       o1 = inwin ? o1 : kDrop;
     }
     float val = v;
-    if constexpr (CLEAN)
-      val = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(v), 0xFF800000u,
-                                                  inwin ? 0x07060504u : 0x03020100u));
+    if constexpr (CLEAN) val = inwin ? v : -__builtin_inff();  // one select
     if constexpr (OBF) {
       const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
       __builtin_amdgcn_raw_buffer_store_b16(hv, ors[0], int(o0), 0, kNonTemporal);
@@ -930,6 +928,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
   kload(0, bfs[0], sbs[0], kss[0]);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // The loop carries block 0's scale bytes from one iteration to the next.
+  // Hiding the prologue's values from the optimiser keeps their zero
+  // extension ahead of the loop-carried merge, where the loads already did
+  // it; otherwise a mask per byte lands at the top of every iteration.
+  if constexpr (MX) asm volatile("" : "+v"(sbs[0][0]), "+v"(sbs[0][1]));
   const int n_iter = n_pairs;  // two blocks per iteration
   for (int s = 0; s < n_iter; ++s) {
 #pragma unroll
