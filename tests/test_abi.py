@@ -245,7 +245,7 @@ def _peak_lib():
     L.idx_peak_flop_per_mfma.restype = ctypes.c_double
     L.idx_peak_flop_per_mfma.argtypes = [ctypes.c_int32]
     L.idx_peak_mfma_valu.restype = ctypes.c_int32
-    L.idx_peak_mfma_valu.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 3
+    L.idx_peak_mfma_valu.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
     return L
 
 
@@ -261,11 +261,12 @@ def test_peak_probe_exports_and_checks():
     assert L.idx_peak_mfma(1, 4, 0, 0, 16, None) == 1
     assert L.idx_peak_mfma(1, 4, 10, 0, None, None) == 1
     assert L.idx_peak_mfma(9, 4, 10, 0, 16, None) == 2
-    assert L.idx_peak_mfma_valu(4, 0, 10, 16, 16, None) == 1
-    assert L.idx_peak_mfma_valu(4, 4, 0, 16, 16, None) == 1
-    assert L.idx_peak_mfma_valu(4, 4, 10, None, 16, None) == 1
-    assert L.idx_peak_mfma_valu(4, 4, 10, 16, None, None) == 1
-    assert L.idx_peak_mfma_valu(7, 4, 10, 16, 16, None) == 2
+    assert L.idx_peak_mfma_valu(2, 4, 0, 10, 16, 16, None) == 1
+    assert L.idx_peak_mfma_valu(2, 4, 4, 0, 16, 16, None) == 1
+    assert L.idx_peak_mfma_valu(2, 4, 4, 10, None, 16, None) == 1
+    assert L.idx_peak_mfma_valu(2, 4, 4, 10, 16, None, None) == 1
+    assert L.idx_peak_mfma_valu(2, 7, 4, 10, 16, 16, None) == 2  # unsupported VALU count
+    assert L.idx_peak_mfma_valu(0, 4, 4, 10, 16, 16, None) == 2  # shape without an overlap variant
 
 
 @pytest.mark.gpu
@@ -295,10 +296,11 @@ def test_peak_overlap_probe_runs():
     out = torch.zeros(groups * 256, dtype=torch.float32, device="cuda")
     cyc = torch.zeros(groups * 4, dtype=torch.int64, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
-    for valu in (0, 2, 3, 4, 5, 6, 8):
-        cyc.zero_()
-        assert L.idx_peak_mfma_valu(valu, groups, iters, out.data_ptr(), cyc.data_ptr(), s) == 0
-        torch.cuda.synchronize()
-        assert bool(torch.isfinite(out).all()), valu
-        # every wave ran 24 MFMAs of at least 16 cycles each
-        assert int(cyc.min()) >= 24 * 16, (valu, cyc[:4])
+    for kind in (2, 3, 4):
+        for valu in (0, 2, 3, 4, 5, 6, 8, 12, 16):
+            cyc.zero_()
+            assert L.idx_peak_mfma_valu(kind, valu, groups, iters, out.data_ptr(), cyc.data_ptr(), s) == 0
+            torch.cuda.synchronize()
+            assert bool(torch.isfinite(out).all()), (kind, valu)
+            # every wave ran 24 MFMAs of at least 8 cycles each
+            assert int(cyc.min()) >= 24 * 8, (kind, valu, cyc[:4])
