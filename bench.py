@@ -289,57 +289,6 @@ def measure_peaks(dev, settle_s: float = 0.3) -> dict | None:
                     "copy: 1 GiB device-to-device, read + write bytes"}
 
 
-def measure_overlap(dev) -> dict | None:
-    """Shader cycles per scaled MFMA (fp8 16x16x128, fp4 16x16x128, fp4
-    32x32x64) when each MFMA is followed by V dependent fp32 FMAs on an
-    earlier accumulator (the scoring kernels' issue pattern, libidx_peak.so),
-    two waves per SIMD: how many VALU instructions per MFMA the matrix pipe
-    hides.  Counted in cycles, so the clock the power limit sets does not
-    enter."""
-    import ctypes
-    import torch
-    path = os.path.join(ROOT, "mqa_logits_scoring_amd", "libidx_peak.so")
-    if not os.path.exists(path):
-        return None
-    L = ctypes.CDLL(path)
-    L.idx_peak_mfma_valu.restype = ctypes.c_int32
-    L.idx_peak_mfma_valu.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
-    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    # four 4-wave workgroups per CU: two rounds of two waves per SIMD (the
-    # implied clock below, two wave lifetimes per launch, checks that)
-    groups, iters = 4 * n_cu, 2000
-    out = torch.empty(groups * 256, dtype=torch.float32, device=dev)
-    cyc = torch.empty(groups * 4, dtype=torch.int64, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    # shape: (kind, cycles one MFMA occupies the matrix pipe at the
-    # published peak, VALU counts to try)
-    shapes = {"fp8_16x16x128": (2, 32, (0, 2, 3, 4, 5, 6, 8)),
-              "fp4_16x16x128": (4, 16, (0, 2, 3, 4, 5, 6, 8)),
-              "fp4_32x32x64": (3, 32, (0, 2, 4, 6, 8, 12, 16))}
-    res = {}
-    for name, (kind, pipe, valus) in shapes.items():
-        res[name] = {}
-        for valu in valus:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            for rep in range(2):  # the second launch is the one read
-                if rep:
-                    e0.record(stream)
-                st = L.idx_peak_mfma_valu(kind, valu, groups, iters, out.data_ptr(), cyc.data_ptr(),
-                                          stream.cuda_stream)
-                if st != 0:
-                    raise RuntimeError(f"idx_peak_mfma_valu({kind}, {valu}) failed with status {st}")
-            e1.record(stream)
-            e1.synchronize()
-            med = float(cyc.cpu().median())
-            per_mfma = med / (iters * 8 * 2)  # two waves share each SIMD's matrix pipe
-            res[name][str(valu)] = {"cycles_per_mfma": round(per_mfma, 2), "mfma_busy": round(pipe / per_mfma, 3),
-                                    "implied_clock_ghz": round(2 * med / (e0.elapsed_time(e1) * 1e6), 2)}
-    return {"valu_per_mfma": res, "groups": groups, "cu_count": n_cu,
-            "note": "median over waves of shader cycles per MFMA per SIMD; mfma_busy against the cycles one MFMA "
-                    "occupies the pipe at the published peak (fp8 16x16x128 and fp4 32x32x64: 32, fp4 16x16x128: 16)"}
-
-
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -370,8 +319,6 @@ def main():
                     help="also time top-k selection (this k, by column) over the call's scores")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the MFMA throughput per shape and a device copy (libidx_peak.so)")
-    ap.add_argument("--overlap", action="store_true",
-                    help="only measure how many VALU FMAs per scaled MFMA the matrix pipe hides (libidx_peak.so)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes `steps` times (counter calibration)")
     args = ap.parse_args()
@@ -389,10 +336,6 @@ def main():
 
     if args.peaks:
         print(json.dumps(measure_peaks(dev, settle_s=1.0)), flush=True)
-        return
-
-    if args.overlap:
-        print(json.dumps(measure_overlap(dev)), flush=True)
         return
 
     if args.copy_bytes:

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define IDX_ABI_VERSION 1
+#define IDX_ABI_VERSION 2
 
 typedef enum {
   IDX_OK = 0,
@@ -67,6 +67,31 @@ typedef enum {
 typedef enum { IDX_F32 = 0, IDX_BF16 = 1 } idx_fp_t;
 
 /*
+ * How the dot products q[h,:] . k[j,:] are accumulated.
+ *
+ *  IDX_ACCUM_NATIVE  the matrix core of the input format.  BF16 and MXFP4
+ *                    products are summed with fp32 precision.  The e4m3
+ *                    matrix core (FP8, MXFP8) sums each group of 8
+ *                    consecutive products of d in fixed point, aligned to
+ *                    the group's largest product with 13 fraction bits and
+ *                    truncated, then adds the group sums in fp32: the error
+ *                    of one dot stays below 7 * 2^-13 of sum_d |q_d k_d|
+ *                    (measured on MI355X; random inputs stay near 1e-6 of
+ *                    the bound, inputs built against it reach about 8e-4).
+ *  IDX_ACCUM_FP32    every product exact and every sum in fp32, for all
+ *                    inputs within the 1e-4 * bound tolerance: FP8 and MXFP8
+ *                    operands are converted exactly to bf16 (MX block scales
+ *                    folded in; exact while every E8M0 exponent byte lies in
+ *                    [10, 246]) and scored on the bf16 matrix core, at about
+ *                    half the e4m3 rate.  BF16 and MXFP4 calls are unchanged.
+ *
+ * The bound of a cell is sm_scale * |k_j| * sum_h |w_h| |q_h| (Euclidean
+ * norms), the per-cell tolerance basis of the lightning-indexer parity
+ * contract.
+ */
+typedef enum { IDX_ACCUM_NATIVE = 0, IDX_ACCUM_FP32 = 1 } idx_accum_t;
+
+/*
  * One scoring call.  Layouts are dense row-major with the last index fastest.
  *
  *  q        [B, S_q, H, D] elements; MXFP4: [B, S_q, H, D/2] bytes, the low
@@ -83,6 +108,7 @@ typedef enum { IDX_F32 = 0, IDX_BF16 = 1 } idx_fp_t;
  *  clean_logits  1: every column outside the row's window is written -inf.
  *                0: those columns are left untouched; in-window values are
  *                bitwise identical to the clean_logits=1 call.
+ *  accumulate    an idx_accum_t (IDX_ACCUM_NATIVE when zero-initialised).
  *
  * H must be 8, 16, 32 or 64 and D 128 (else IDX_E_UNSUPPORTED); a plan is
  * built for one H (its tiles hold 512 / H rows).  q, k, w, out and the
@@ -104,6 +130,7 @@ typedef struct {
   idx_fp_t out_dtype;
   int64_t out_row_stride;
   int32_t clean_logits;
+  int32_t accumulate;
 } idx_logits_args_t;
 
 /* ABI version of the loaded library (IDX_ABI_VERSION of its build). */
@@ -165,29 +192,47 @@ idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, con
                                  size_t plan_bytes, void* stream);
 
 /*
- * Device workspace bytes a call to idx_logits_run needs; 0 for invalid
- * arguments.  It covers the plan when the call builds it (plan == NULL) and,
- * for FP8, MXFP8 and MXFP4 inputs, the per-call weighted-query pieces: those
- * formats use ReLU(x) = (x + |x|) / 2, so sum_h w_h ReLU(S_h) is half of
- * sum_h w_h |S_h| (one FMA per head in the epilogue) plus qt . k with
- * qt = sum_h w_h q_h, taken by extra MFMA blocks from qt written as pieces
- * with E8M0 block scales, each the exact residual of the ones before it
- * (four e4m3 pieces for FP8 / MXFP8, within 2^-16 of qt's block maxima;
- * eight e2m1 pieces for MXFP4, also within 2^-16).
+ * Device workspace bytes a call to idx_logits_run without a plan needs (the
+ * most any call with these arguments needs); 0 for invalid arguments.  Every
+ * call holds in its workspace:
+ *  - K reordered into matrix-core fragment order (and, for every format but
+ *    BF16, the per-key scales in block order);
+ *  - for 64-head calls of FP8, MXFP8 and MXFP4 with IDX_ACCUM_NATIVE, the
+ *    weighted-query pieces: those formats use ReLU(x) = (x + |x|) / 2, so
+ *    sum_h w_h ReLU(S_h) is half of sum_h w_h |S_h| (one FMA per head in the
+ *    epilogue) plus qt . k with qt = sum_h w_h q_h, taken by extra MFMA blocks
+ *    from qt written as pieces with E8M0 block scales, each the exact residual
+ *    of the ones before it (four e4m3 pieces for FP8 / MXFP8, within 2^-16 of
+ *    qt's block maxima; eight e2m1 pieces for MXFP4, also within 2^-16);
+ *  - for FP8 and MXFP8 with IDX_ACCUM_FP32, Q converted to bf16;
+ *  - and, only when the call builds its plan (plan == NULL), the plan.
+ * All of it depends on the call's K, Q and W, so idx_logits_run prepares it
+ * anew on every call; idx_logits_prepare / idx_logits_score let a caller
+ * prepare once and score several times.
  */
 size_t idx_logits_workspace_bytes(const idx_logits_args_t* a);
 
 /*
+ * Device workspace bytes of a call given a precomputed plan (idx_logits_run,
+ * idx_logits_run_paged with plan != NULL, and idx_logits_prepare,
+ * idx_logits_prepare_paged, idx_logits_score, idx_logits_score_paged): the
+ * sections above without the plan; never more than
+ * idx_logits_workspace_bytes.  0 for invalid arguments.
+ */
+size_t idx_logits_workspace_bytes_planned(const idx_logits_args_t* a);
+
+/*
  * Score one batch of queries on `stream`.
  *
+ * The workspace (256-byte aligned, owned by the caller, not read after the
+ * stream passes the call) must hold idx_logits_workspace_bytes_planned(a)
+ * bytes when a plan is given, idx_logits_workspace_bytes(a) otherwise; a
+ * missing or smaller one returns IDX_E_WORKSPACE.
  * plan != NULL: a plan built by idx_logits_plan for the same (B, S_q, S_k,
- *   H, D); the window arguments are then ignored.  BF16 calls need no
- *   workspace; FP8 and MX calls still need idx_logits_workspace_bytes(a).
- *   A plan whose recorded dimensions differ from `a` is detected on the
- *   device: the call then writes quiet NaN to columns [0, S_k) of every row.
- * plan == NULL: the plan is first built into `workspace` (at least
- *   idx_logits_workspace_bytes(a) bytes, 256-byte aligned, owned by the
- *   caller and not read after the stream passes the call) from
+ *   H, D); the window arguments are then ignored.  A plan whose recorded
+ *   dimensions differ from `a` is detected on the device: the call then
+ *   writes quiet NaN to columns [0, S_k) of every row.
+ * plan == NULL: the plan is first built into the workspace from
  *   q_causal_offsets / row_starts / row_ends exactly as idx_logits_plan
  *   would, then used; the result is bitwise identical to the planned call.
  */
@@ -201,11 +246,12 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
  * plan is exactly idx_logits_prepare(a, ws) followed by
  * idx_logits_score(a, plan, ws), and gives bitwise the same output.
  *
- * idx_logits_prepare writes into `workspace` (idx_logits_workspace_bytes(a)
- * bytes, 256-byte aligned) what the scoring reads besides the inputs: K
- * reordered into matrix-core fragment order and, for FP8 / MX inputs, the
- * weighted-query pieces.  It reads k (and q, q_scale, w for FP8 / MX) and
- * nothing else of `a`.
+ * idx_logits_prepare writes into `workspace`
+ * (idx_logits_workspace_bytes_planned(a) bytes, 256-byte aligned) what the
+ * scoring reads besides the inputs: K reordered into matrix-core fragment
+ * order, and the weighted-query pieces or the converted Q where the call has
+ * them.  It reads k, k_scale, q, q_scale and w, and nothing else of `a`
+ * besides dimensions, formats and `accumulate`.
  *
  * idx_logits_score scores with a plan (required, as in idx_logits_run) and a
  * workspace that idx_logits_prepare filled from the same k (and q, q_scale,
@@ -327,7 +373,10 @@ idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S
 
 /*
  * Copy the windows stored in a plan into caller device arrays
- * win_start / win_end ([B, S_q] int32) on `stream` (for inspection and tests).
+ * win_start / win_end ([B, S_q] int32, 4-byte aligned) on `stream` (for
+ * inspection and tests).  `plan` must be 256-byte aligned.  A plan recorded
+ * for other dimensions is detected on the device: every window is then
+ * reported as [-1, -1).
  */
 idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H,
                                      int32_t D, int32_t* win_start, int32_t* win_end, void* stream);

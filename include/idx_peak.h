@@ -38,24 +38,6 @@ double idx_peak_flop_per_mfma(int32_t kind);
  */
 int32_t idx_peak_mfma(int32_t kind, int32_t groups, int32_t iters, int32_t zero, float* out, void* stream);
 
-/*
- * The scoring kernels' issue pattern at its own rate: `groups` workgroups of 4
- * waves (4 x the CU count gives two passes of two waves per SIMD, the scoring
- * kernels' occupancy); every wave runs iters x 8 steps of one scaled MFMA of
- * `kind` (IDX_PEAK_FP8_16X16X128, IDX_PEAK_FP4_16X16X128 or
- * IDX_PEAK_FP4_32X32X64, pseudo-random codes) followed by `valu` dependent
- * fp32 FMAs on the absolute values of the accumulator of three MFMAs earlier.
- * Writes one float per thread to `out` (groups * 256 floats) and, per wave w
- * of workgroup g, the shader-clock cycles of its loop to wave_cycles[4 g + w]
- * (groups * 4 entries); both device memory owned by the caller.  With two
- * waves per SIMD the cycles per MFMA per SIMD are wave_cycles / (16 iters).
- * `valu` is one of 0, 2, 3, 4, 5, 6, 8, 12, 16.  Returns 0, 1 for invalid
- * arguments (nothing enqueued), 2 for an unsupported `kind` or `valu`, 4 for
- * a launch failure.
- */
-int32_t idx_peak_mfma_valu(int32_t kind, int32_t valu, int32_t groups, int32_t iters, float* out,
-                           int64_t* wave_cycles, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -21,11 +21,15 @@ LIB_PATH = os.path.join(_PKG, "libidx_logits.so")
 
 IDX_OK, IDX_E_INVALID, IDX_E_UNSUPPORTED, IDX_E_WORKSPACE, IDX_E_HIP = range(5)
 IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
+# idx_accum_t: "native" (the input format's matrix core) or "fp32" (exact
+# products, fp32 sums, for every input)
+ACCUM = {"native": 0, "fp32": 1}
+ABI_VERSION = 2
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
             "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_score_paged",
             "idx_logits_topk",
-            "idx_logits_workspace_bytes",
+            "idx_logits_workspace_bytes", "idx_logits_workspace_bytes_planned",
             "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
@@ -36,7 +40,7 @@ class IdxLogitsArgs(ctypes.Structure):
                 ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
                 ("w", ctypes.c_void_p), ("w_dtype", ctypes.c_int), ("sm_scale", ctypes.c_float),
                 ("out", ctypes.c_void_p), ("out_dtype", ctypes.c_int), ("out_row_stride", ctypes.c_int64),
-                ("clean_logits", ctypes.c_int32)]
+                ("clean_logits", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
 
 
 class IdxPagedK(ctypes.Structure):
@@ -65,6 +69,8 @@ def lib() -> ctypes.CDLL:
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.idx_abi_version.restype = I32
         L.idx_abi_version.argtypes = []
+        if L.idx_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.idx_abi_version()}, this binding {ABI_VERSION}: rebuild")
         L.idx_last_error.restype = ctypes.c_char_p
         L.idx_last_error.argtypes = []
         L.idx_logits_plan_bytes.restype = SZ
@@ -85,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, ctypes.c_int, P, P, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
+        L.idx_logits_workspace_bytes_planned.restype = SZ
+        L.idx_logits_workspace_bytes_planned.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
         L.idx_logits_run.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, P, SZ, P]
         L.idx_logits_prepare.restype = ctypes.c_int
@@ -192,7 +200,8 @@ def _shape_info(q: torch.Tensor, k: torch.Tensor, in_dtype: str):
 
 
 def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, in_dtype: str,
-              q_scale=None, k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True) -> IdxLogitsArgs:
+              q_scale=None, k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
+              accumulate: str = "native") -> IdxLogitsArgs:
     """Fill an idx_logits_args_t from tensors (no copies, no checks beyond shapes)."""
     q4, k3, B, S_q, S_k, H, D = _shape_info(q, k, in_dtype)
     if out.dtype not in FP_DTYPES or w.dtype not in FP_DTYPES:
@@ -207,6 +216,7 @@ def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tens
     a.sm_scale = float(sm_scale)
     a.out_row_stride = out.stride(-2) if out.dim() >= 2 else S_k
     a.clean_logits = 1 if clean_logits else 0
+    a.accumulate = ACCUM[accumulate]
     return a
 
 
@@ -214,11 +224,16 @@ def idx_logits_workspace_bytes(args: IdxLogitsArgs) -> int:
     return int(lib().idx_logits_workspace_bytes(ctypes.byref(args)))
 
 
+def idx_logits_workspace_bytes_planned(args: IdxLogitsArgs) -> int:
+    return int(lib().idx_logits_workspace_bytes_planned(ctypes.byref(args)))
+
+
 def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtype: str, q_scale=None,
                    k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
                    out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
                    plan: Optional[torch.Tensor] = None, q_causal_offsets=None, row_starts=None, row_ends=None,
-                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                   workspace: Optional[torch.Tensor] = None, accumulate: str = "native",
+                   stream=None) -> torch.Tensor:
     """Score q against k on the stream; returns `out` ([B,S_q,S_k] or the caller's buffer).
 
     Tensors are passed as raw device buffers: q/k of any 1- or 2-byte dtype
@@ -234,25 +249,27 @@ def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtyp
         shape = (B, S_q, S_k) if q.dim() == 4 else (S_q, S_k)
         out = torch.empty(shape, dtype=out_dtype, device=device)
     args = make_args(q, k, w, out, in_dtype=in_dtype, q_scale=q_scale, k_scale=k_scale, sm_scale=sm_scale,
-                     clean_logits=clean_logits)
+                     clean_logits=clean_logits, accumulate=accumulate)
     offs = st = en = None
     if plan is None:
         offs = _dev_i32(q_causal_offsets, device)
         st = _dev_i32(row_starts, device)
         en = _dev_i32(row_ends, device)
-    # the workspace holds the in-call plan and, for FP8 / MX inputs, the
-    # weighted-query pieces; idx_logits_workspace_bytes gives its size
+    # the workspace holds the reordered K, the weighted-query pieces or the
+    # converted Q, and the plan of a call that builds it
     if workspace is None:
-        workspace = torch.empty(max(idx_logits_workspace_bytes(args), 1), dtype=torch.uint8, device=device)
+        nbytes = idx_logits_workspace_bytes(args) if plan is None else idx_logits_workspace_bytes_planned(args)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("idx_logits_run", lib().idx_logits_run(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en),
                                                     _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out
 
 
-def _workspace_for(args: IdxLogitsArgs, workspace: Optional[torch.Tensor], device) -> torch.Tensor:
+def _workspace_for(args: IdxLogitsArgs, workspace: Optional[torch.Tensor], device, planned: bool = True):
     if workspace is None:
-        workspace = torch.empty(max(idx_logits_workspace_bytes(args), 1), dtype=torch.uint8, device=device)
+        nbytes = idx_logits_workspace_bytes_planned(args) if planned else idx_logits_workspace_bytes(args)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     return workspace
 
 
@@ -311,7 +328,7 @@ def idx_logits_plan_paged(B: int, S_q: int, S_k: int, context_lens: torch.Tensor
 
 
 def make_paged_args(q: torch.Tensor, w: torch.Tensor, out: torch.Tensor, S_k: int, *, in_dtype: str, q_scale=None,
-                    sm_scale: float = 1.0, clean_logits: bool = True) -> IdxLogitsArgs:
+                    sm_scale: float = 1.0, clean_logits: bool = True, accumulate: str = "native") -> IdxLogitsArgs:
     """idx_logits_args_t of a paged call: q [B, S_q, H, D'], out [B, S_q, >= S_k];
     k and k_scale stay NULL (the keys come from an IdxPagedK)."""
     if q.dim() != 4:
@@ -332,6 +349,7 @@ def make_paged_args(q: torch.Tensor, w: torch.Tensor, out: torch.Tensor, S_k: in
     a.sm_scale = float(sm_scale)
     a.out_row_stride = out.stride(-2)
     a.clean_logits = 1 if clean_logits else 0
+    a.accumulate = ACCUM[accumulate]
     return a
 
 
@@ -351,7 +369,7 @@ def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: i
                          q_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
                          out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
                          plan: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> torch.Tensor:
+                         accumulate: str = "native", stream=None) -> torch.Tensor:
     """One paged call: q [B, S_q, H, D'] (the S_q newest tokens of each request),
     keys from `kv` (make_paged_k), output [B, S_q, S_k]."""
     if q.dim() != 4:
@@ -360,8 +378,8 @@ def idx_logits_run_paged(q: torch.Tensor, w: torch.Tensor, kv: IdxPagedK, S_k: i
     if out is None:
         out = torch.empty((q.shape[0], q.shape[1], S_k), dtype=out_dtype, device=device)
     a = make_paged_args(q, w, out, S_k, in_dtype=in_dtype, q_scale=q_scale, sm_scale=sm_scale,
-                        clean_logits=clean_logits)
-    workspace = _workspace_for(a, workspace, device)
+                        clean_logits=clean_logits, accumulate=accumulate)
+    workspace = _workspace_for(a, workspace, device, planned=plan is not None)
     _check("idx_logits_run_paged", lib().idx_logits_run_paged(ctypes.byref(a), ctypes.byref(kv), _ptr(plan),
                                                                 _ptr(workspace),
                                                                 workspace.numel() * workspace.element_size(),

@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libidx_logits.so")
 PEAK_LIB = os.path.join(PKG, "libidx_peak.so")
 PEAK_SOURCES = ["peak.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "topk.hip", "score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
+SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "topk.hip", "score_bf16.hip", "score_bf16rs.hip", "score_fp8.hip",
+           "score_mxfp8.hip", "score_mxfp4.hip"]
 HEADERS = ["internal.h", "score_kernel.h", "score_kernel_gh.h", "plan_segment.h", os.path.join("..", "..", "include", "idx_logits.h")]
 ARCH = "gfx950"
 
@@ -43,7 +44,8 @@ def compile_flags() -> list[str]:
 # accumulators in AGPRs, and every epilogue read of them costs a copy to a
 # VGPR.  Forcing the accumulators into VGPRs moves other values (MFMA operands,
 # which can be read from AGPRs) there instead.
-EXTRA_FLAGS = {"score_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"score_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "score_bf16rs.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def flags_for(src: str) -> list[str]:

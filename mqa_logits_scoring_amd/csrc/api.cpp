@@ -120,12 +120,17 @@ idx_status_t idx_logits_plan_thd(int32_t n_seg, const int32_t* cu_seqlens_q, con
   return IDX_OK;
 }
 
-size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) {
-  if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return 0;
+static idx::WorkspaceLayout layout_of(const idx_logits_args_t* a) {
+  if (a == nullptr || a->B <= 0 || a->S_q <= 0 || a->S_k <= 0 || a->H <= 0 || a->D <= 0) return {};
   const idx_in_t f = a->in_dtype;
-  if (f != IDX_IN_BF16 && f != IDX_IN_FP8_E4M3 && f != IDX_IN_MXFP8_E4M3 && f != IDX_IN_MXFP4_E2M1) return 0;
-  return idx::workspace_layout(f, a->B, a->S_q, a->S_k, a->H).total;
+  if (f != IDX_IN_BF16 && f != IDX_IN_FP8_E4M3 && f != IDX_IN_MXFP8_E4M3 && f != IDX_IN_MXFP4_E2M1) return {};
+  if (a->accumulate != IDX_ACCUM_NATIVE && a->accumulate != IDX_ACCUM_FP32) return {};
+  return idx::workspace_layout(idx::exec_of(f, a->accumulate), a->B, a->S_q, a->S_k, a->H);
 }
+
+size_t idx_logits_workspace_bytes(const idx_logits_args_t* a) { return layout_of(a).total; }
+
+size_t idx_logits_workspace_bytes_planned(const idx_logits_args_t* a) { return layout_of(a).planned; }
 
 idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
                                      int32_t* win_start, int32_t* win_end, void* stream) {
@@ -133,7 +138,10 @@ idx_status_t idx_logits_plan_windows(const void* plan, int32_t B, int32_t S_q, i
   if (st != IDX_OK) return st;
   if (plan == nullptr || win_start == nullptr || win_end == nullptr)
     return fail(IDX_E_INVALID, "plan, win_start and win_end must be non-NULL");
-  hipError_t e = idx::launch_copy_windows(plan, int64_t(B) * S_q, win_start, win_end,
+  if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(win_start) & 3u) != 0 || (reinterpret_cast<uintptr_t>(win_end) & 3u) != 0)
+    return fail(IDX_E_INVALID, "win_start and win_end must be 4-byte aligned");
+  hipError_t e = idx::launch_copy_windows(plan, B, S_q, S_k, H, D, win_start, win_end,
                                           static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(IDX_E_HIP, "window copy launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
@@ -156,6 +164,8 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
     return fail(IDX_E_INVALID, "unknown in_dtype %d", int(f));
   if ((a->w_dtype != IDX_F32 && a->w_dtype != IDX_BF16) || (a->out_dtype != IDX_F32 && a->out_dtype != IDX_BF16))
     return fail(IDX_E_INVALID, "w_dtype and out_dtype must be IDX_F32 or IDX_BF16");
+  if (a->accumulate != IDX_ACCUM_NATIVE && a->accumulate != IDX_ACCUM_FP32)
+    return fail(IDX_E_INVALID, "accumulate must be IDX_ACCUM_NATIVE or IDX_ACCUM_FP32 (got %d)", int(a->accumulate));
   const bool mx = f == IDX_IN_MXFP8_E4M3 || f == IDX_IN_MXFP4_E2M1;
   if (a->q == nullptr || (!keys_elsewhere && a->k == nullptr) || a->w == nullptr || a->out == nullptr)
     return fail(IDX_E_INVALID, "q, k, w and out must be non-NULL");
@@ -172,7 +182,8 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
     return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
                 (long long)a->out_row_stride);
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
-  if ((int64_t(a->S_k) + 31) / 32 * 32 * idx::row_bytes_of(f) > (int64_t(1) << 31) - 1)
+  const idx::Exec x = idx::exec_of(f, a->accumulate);
+  if ((int64_t(a->S_k) + 31) / 32 * 32 * idx::row_bytes_of(x.kf) > (int64_t(1) << 31) - 1)
     return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
@@ -208,33 +219,43 @@ idx::PagedK paged_k(const idx_paged_k_t* kv) {
 // 64-head kernel, pages of 32 * 2^j keys (whole 32-key blocks, found with a
 // shift), and a cache (and scale cache) addressable with 31-bit offsets.
 // Other calls gather K first.
+// Calls that convert their operands to bf16 read the converted keys.
 bool direct_paged(const idx_logits_args_t* a, const idx_paged_k_t* kv) {
   const int64_t rows = int64_t(kv->num_pages) * kv->page_size;
   const int32_t bpp = kv->page_size / 32;
-  return a->H == 64 && kv->page_size % 32 == 0 && (bpp & (bpp - 1)) == 0 &&
+  return a->H == 64 && !idx::exec_of(a->in_dtype, a->accumulate).convert && kv->page_size % 32 == 0 &&
+         (bpp & (bpp - 1)) == 0 &&
          rows * idx::row_bytes_of(a->in_dtype) < (int64_t(1) << 31) && rows * 4 < (int64_t(1) << 31);
 }
 
-idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, size_t ws_bytes) {
+// with_plan: the call builds its plan in the workspace.
+idx_status_t check_workspace(const idx::WorkspaceLayout& WL, const void* ws, size_t ws_bytes, bool with_plan) {
   if (WL.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
+  const size_t need = with_plan ? WL.total : WL.planned;
   if (ws == nullptr)
-    return fail(IDX_E_WORKSPACE, "this call needs a workspace of %zu bytes (idx_logits_workspace_bytes)", WL.total);
+    return fail(IDX_E_WORKSPACE, "this call needs a workspace of %zu bytes (%s)", need,
+                with_plan ? "idx_logits_workspace_bytes" : "idx_logits_workspace_bytes_planned");
   if (!aligned256(ws)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
-  if (ws_bytes < WL.total) return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, WL.total);
+  if (ws_bytes < need) return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
   return IDX_OK;
 }
 
-// Per-call preparation: K in MFMA fragment order and, for FP8 / MX inputs,
-// the weighted-query pieces.
+idx::WorkspaceLayout layout_checked(const idx_logits_args_t* a) {
+  return idx::workspace_layout(idx::exec_of(a->in_dtype, a->accumulate), a->B, a->S_q, a->S_k, a->H);
+}
+
+// Per-call preparation: K in MFMA fragment order and, where the call has
+// them, the weighted-query pieces or Q converted to bf16.
 idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL, unsigned char* ws,
                      const idx::PlanBuild* build, const idx::PagedK* paged, hipStream_t s) {
-  const idx_in_t f = a->in_dtype;
-  const bool scaled = idx::has_kscale(f), pieces = idx::uses_pieces(f, a->H);
+  const idx::Exec x = idx::exec_of(a->in_dtype, a->accumulate);
+  const bool scaled = idx::has_kscale(x.kf), pieces = idx::uses_pieces(x.kf, a->H);
   hipError_t e = idx::launch_prepare(
-      f, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
+      a->in_dtype, x.convert, a->H, a->w_dtype, a->k, a->k_scale, a->B, a->S_k, ws + WL.off_kfrag,
       scaled ? reinterpret_cast<uint32_t*>(ws + WL.off_kscale) : nullptr, a->q, a->q_scale, a->w,
       int64_t(a->B) * a->S_q, pieces ? ws + WL.off_pieces : nullptr,
-      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr, build, paged, s);
+      pieces ? reinterpret_cast<uint32_t*>(ws + WL.off_pscales) : nullptr,
+      x.convert ? reinterpret_cast<uint16_t*>(ws + WL.off_qconv) : nullptr, build, paged, s);
   if (e != hipSuccess) return fail(IDX_E_HIP, "preparation launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
 }
@@ -243,11 +264,11 @@ idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL,
 // direct_paged), else NULL.
 idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
                    unsigned char* ws, hipStream_t s, const idx::PagedK* direct = nullptr) {
-  const idx_in_t f = a->in_dtype;
+  const idx::Exec x = idx::exec_of(a->in_dtype, a->accumulate);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   idx::ScoreArgs k{};
-  k.q = a->q;
-  k.q_scale = a->q_scale;
+  k.q = x.convert ? static_cast<const void*>(ws + WL.off_qconv) : a->q;
+  k.q_scale = x.convert ? nullptr : a->q_scale;
   k.w = a->w;
   k.out = a->out;
   k.plan = p;
@@ -270,10 +291,10 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.off_slot = uint32_t(L.off_slot);
   k.off_lo = uint32_t(L.off_lo);
   k.off_hi = uint32_t(L.off_hi);
-  k.pieces = idx::uses_pieces(f, a->H) ? ws + WL.off_pieces : nullptr;
-  k.pscales = idx::uses_pieces(f, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
+  k.pieces = idx::uses_pieces(x.kf, a->H) ? ws + WL.off_pieces : nullptr;
+  k.pscales = idx::uses_pieces(x.kf, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
-  k.kscale = idx::has_kscale(f) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
+  k.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
   if (direct != nullptr) {
     k.kcache = direct->k_cache;
     k.kscache = direct->k_scale_cache;
@@ -286,11 +307,13 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
 
   const bool clean = a->clean_logits != 0;
   hipError_t e = hipSuccess;
-  switch (f) {
+  switch (x.kf) {
     case IDX_IN_BF16: e = idx::launch_score_bf16(a->w_dtype, a->out_dtype, clean, k, s); break;
     case IDX_IN_FP8_E4M3: e = idx::launch_score_fp8(a->w_dtype, a->out_dtype, clean, k, s); break;
     case IDX_IN_MXFP8_E4M3: e = idx::launch_score_mxfp8(a->w_dtype, a->out_dtype, clean, k, s); break;
     case IDX_IN_MXFP4_E2M1: e = idx::launch_score_mxfp4(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case idx::kInBF16RowScale: e = idx::launch_score_bf16rs(a->w_dtype, a->out_dtype, clean, k, s); break;
+    default: return fail(IDX_E_INVALID, "unknown kernel format %d", x.kf);
   }
   if (e != hipSuccess) return fail(IDX_E_HIP, "scoring launch failed: %s", hipGetErrorString(e));
   return IDX_OK;
@@ -309,9 +332,9 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
     return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
   if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, p == nullptr)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   // a plan built here shares the preparation launch
   idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends, nullptr,
@@ -325,9 +348,9 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
 idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
   idx_status_t st = check_args(a);
   if (st != IDX_OK) return st;
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, false)) != IDX_OK) return st;
   return prepare(a, WL, ws, nullptr, nullptr, static_cast<hipStream_t>(stream));
 }
 
@@ -350,9 +373,9 @@ idx_status_t idx_logits_prepare_paged(const idx_logits_args_t* a, const idx_page
   idx_status_t st = check_args(a, true);
   if (st != IDX_OK) return st;
   if ((st = check_paged(a, kv)) != IDX_OK) return st;
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, false)) != IDX_OK) return st;
   const idx::PagedK pk = paged_k(kv);
   return prepare(a, WL, ws, nullptr, &pk, static_cast<hipStream_t>(stream));
 }
@@ -364,9 +387,9 @@ idx_status_t idx_logits_run_paged(const idx_logits_args_t* a, const idx_paged_k_
   if ((st = check_paged(a, kv)) != IDX_OK) return st;
   const unsigned char* p = static_cast<const unsigned char*>(plan);
   if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, p == nullptr)) != IDX_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, nullptr, nullptr, nullptr, kv->context_lens,
                        ws + WL.off_plan};
@@ -385,9 +408,9 @@ idx_status_t idx_logits_score_paged(const idx_logits_args_t* a, const idx_paged_
   if ((st = check_paged(a, kv)) != IDX_OK) return st;
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score_paged needs a plan");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, false)) != IDX_OK) return st;
   idx::PagedK pk = paged_k(kv);
   pk.skip_gather = direct_paged(a, kv);
   return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream),
@@ -428,9 +451,9 @@ idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void
   if (st != IDX_OK) return st;
   if (plan == nullptr) return fail(IDX_E_WORKSPACE, "idx_logits_score needs a plan");
   if (!aligned256(plan)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
-  const idx::WorkspaceLayout WL = idx::workspace_layout(a->in_dtype, a->B, a->S_q, a->S_k, a->H);
+  const idx::WorkspaceLayout WL = layout_checked(a);
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if ((st = check_workspace(WL, ws, workspace_bytes)) != IDX_OK) return st;
+  if ((st = check_workspace(WL, ws, workspace_bytes, false)) != IDX_OK) return st;
   return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream));
 }
 

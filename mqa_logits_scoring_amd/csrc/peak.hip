@@ -83,86 +83,6 @@ hipError_t launch(int groups, int iters, int zero, float* out, hipStream_t strea
   return hipGetLastError();
 }
 
-// The scoring kernels' issue pattern: each scaled MFMA (16x16x128 or
-// 32x32x64, e4m3 or e2m1 codes) followed by V dependent FMAs on the absolute
-// values of the accumulator written three MFMAs earlier (one chain per MFMA,
-// as the ReLU-weighted head sum runs), two waves per SIMD.  Each wave records
-// the shader cycles its loop took, so the cost of the VALU work beside the
-// matrix pipe reads off in cycles per MFMA, independent of the clock.
-template <int KIND, int V>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-    overlap_kernel(int iters, float* out, long long* cycles) {
-  constexpr bool BIG = KIND == IDX_PEAK_FP8_32X32X64 || KIND == IDX_PEAK_FP4_32X32X64;
-  constexpr int CODE = (KIND == IDX_PEAK_FP4_32X32X64 || KIND == IDX_PEAK_FP4_16X16X128) ? 4 : 0;
-  typedef typename std::conditional<BIG, f32x16, f32x4>::type acc_t;
-  constexpr int NR = int(sizeof(acc_t) / 4);
-  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
-  i32x8 a[8], b;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a[i][e] = int(mix(gid * 64u + uint32_t(8 * i + e) + 1u) & 0x77777777u);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = int(mix(gid * 64u + 100u + uint32_t(e)) & 0x77777777u);
-  acc_t acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = acc_t{} + float(i + 1);
-  float w[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) w[v] = float(mix(gid + 7u * uint32_t(v)) & 255u) * 1e-3f;
-  float sum = 0.f;
-  const long long t0 = clock64();
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // accumulating into acc[i] keeps the MFMA inside the loop; eight
-      // accumulators leave it independent of the previous seven
-      if constexpr (BIG)
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b, acc[i], CODE, CODE, 0, 127, 0, 127);
-      else
-        acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b, acc[i], CODE, CODE, 0, 127, 0, 127);
-      const acc_t r = acc[(i + 5) & 7];
-#pragma unroll
-      for (int v = 0; v < V; ++v) sum = __builtin_fmaf(w[v & 15], __builtin_fabsf(r[v % NR]), sum);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  const long long t1 = clock64();
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < NR; ++e) sum += acc[i][e];
-  out[gid] = sum;
-  if ((threadIdx.x & 63) == 0) cycles[blockIdx.x * 4 + (threadIdx.x >> 6)] = t1 - t0;
-}
-
-template <int KIND, int V>
-hipError_t launch_overlap(int groups, int iters, float* out, long long* cycles, hipStream_t stream) {
-  hipLaunchKernelGGL((overlap_kernel<KIND, V>), dim3(unsigned(groups)), dim3(256), 0, stream, iters, out, cycles);
-  return hipGetLastError();
-}
-
-template <int KIND>
-hipError_t launch_overlap_v(int valu, int groups, int iters, float* out, long long* cycles, hipStream_t stream,
-                            bool& ok) {
-  ok = true;
-  switch (valu) {
-    case 0: return launch_overlap<KIND, 0>(groups, iters, out, cycles, stream);
-    case 2: return launch_overlap<KIND, 2>(groups, iters, out, cycles, stream);
-    case 3: return launch_overlap<KIND, 3>(groups, iters, out, cycles, stream);
-    case 4: return launch_overlap<KIND, 4>(groups, iters, out, cycles, stream);
-    case 5: return launch_overlap<KIND, 5>(groups, iters, out, cycles, stream);
-    case 6: return launch_overlap<KIND, 6>(groups, iters, out, cycles, stream);
-    case 8: return launch_overlap<KIND, 8>(groups, iters, out, cycles, stream);
-    case 12: return launch_overlap<KIND, 12>(groups, iters, out, cycles, stream);
-    case 16: return launch_overlap<KIND, 16>(groups, iters, out, cycles, stream);
-  }
-  ok = false;
-  return hipSuccess;
-}
-
 }  // namespace
 
 extern "C" {
@@ -190,29 +110,6 @@ int32_t idx_peak_mfma(int32_t kind, int32_t groups, int32_t iters, int32_t zero,
     case IDX_PEAK_FP4_16X16X128: e = launch<IDX_PEAK_FP4_16X16X128>(groups, iters, zero, out, s); break;
     default: return 2;
   }
-  return e == hipSuccess ? 0 : 4;
-}
-
-int32_t idx_peak_mfma_valu(int32_t kind, int32_t valu, int32_t groups, int32_t iters, float* out,
-                           int64_t* wave_cycles, void* stream) {
-  if (groups <= 0 || iters <= 0 || out == nullptr || wave_cycles == nullptr) return 1;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  long long* cyc = reinterpret_cast<long long*>(wave_cycles);
-  bool ok = false;
-  hipError_t e = hipSuccess;
-  switch (kind) {
-    case IDX_PEAK_FP8_16X16X128:
-      e = launch_overlap_v<IDX_PEAK_FP8_16X16X128>(valu, groups, iters, out, cyc, s, ok);
-      break;
-    case IDX_PEAK_FP4_16X16X128:
-      e = launch_overlap_v<IDX_PEAK_FP4_16X16X128>(valu, groups, iters, out, cyc, s, ok);
-      break;
-    case IDX_PEAK_FP4_32X32X64:
-      e = launch_overlap_v<IDX_PEAK_FP4_32X32X64>(valu, groups, iters, out, cyc, s, ok);
-      break;
-    default: return 2;
-  }
-  if (!ok) return 2;
   return e == hipSuccess ? 0 : 4;
 }
 

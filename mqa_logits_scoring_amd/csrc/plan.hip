@@ -11,12 +11,18 @@ __global__ void __launch_bounds__(kSortThreads) plan_kernel(const PlanParams P) 
   plan_segment(P, blockIdx.x, sm);
 }
 
-__global__ void copy_windows_kernel(const unsigned char* plan, int64_t n_rows, size_t off_start, size_t off_end,
-                                    int32_t* ws, int32_t* we) {
+// A plan recorded for other dimensions is not read past its header: every
+// window is then reported as [-1, -1).
+__global__ void copy_windows_kernel(const unsigned char* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H,
+                                    int32_t D, size_t off_start, size_t off_end, int32_t* ws, int32_t* we) {
+  const int64_t n_rows = int64_t(B) * S_q;
   const int64_t r = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (r >= n_rows) return;
-  ws[r] = reinterpret_cast<const int32_t*>(plan + off_start)[r];
-  we[r] = reinterpret_cast<const int32_t*>(plan + off_end)[r];
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
+  const bool ok = hdr->magic == kPlanMagic && hdr->B == B && hdr->S_q == S_q && hdr->S_k == S_k && hdr->H == H &&
+                  hdr->D == D;
+  ws[r] = ok ? reinterpret_cast<const int32_t*>(plan + off_start)[r] : -1;
+  we[r] = ok ? reinterpret_cast<const int32_t*>(plan + off_end)[r] : -1;
 }
 
 }  // namespace
@@ -71,12 +77,13 @@ hipError_t launch_plan_thd(int32_t n_seg, const int32_t* cu_q, const int32_t* cu
   return hipGetLastError();
 }
 
-hipError_t launch_copy_windows(const void* plan, int64_t n_rows, int32_t* ws, int32_t* we, hipStream_t stream) {
-  const PlanLayout L = plan_layout(1, n_rows, 64);  // the window arrays do not depend on H
+hipError_t launch_copy_windows(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
+                               int32_t* ws, int32_t* we, hipStream_t stream) {
+  const PlanLayout L = plan_layout(B, S_q, H);
   const int threads = 256;
-  const int64_t blocks = (n_rows + threads - 1) / threads;
+  const int64_t blocks = (L.n_rows + threads - 1) / threads;
   hipLaunchKernelGGL(copy_windows_kernel, dim3(unsigned(blocks)), dim3(threads), 0, stream,
-                     static_cast<const unsigned char*>(plan), n_rows, L.off_start, L.off_end, ws, we);
+                     static_cast<const unsigned char*>(plan), B, S_q, S_k, H, D, L.off_start, L.off_end, ws, we);
   return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
 // Per-call preparation, one launch: the plan when the call builds it
 // (plan_segment.h), K in MFMA fragment order, the per-row K scales in block
-// order, and the weighted-query pieces (all laid out in internal.h).  The jobs
-// are independent, so their workgroups share one grid and overlap: the
-// latency-bound plan and pieces workgroups come first, the bandwidth-bound
-// copies fill the machine behind them.
+// order, and the weighted-query pieces, or for calls that accumulate FP8 /
+// MXFP8 products exactly, Q and K converted to bf16 (all laid out in
+// internal.h).  The jobs are independent, so their workgroups share one grid
+// and overlap: the latency-bound plan and pieces workgroups come first, the
+// bandwidth-bound copies fill the machine behind them.
 //
 // Element decoding follows the OCP 8-bit float and OCP Microscaling v1.0
 // definitions; the e4m3 encoder of the pieces rounds to nearest even.
@@ -80,9 +81,12 @@ struct PrepArgs {
   PagedK pk;
   // the plan, when built here
   PlanParams plan;
-  // workgroups of each job, in grid order: plan segments, pieces, K chunks,
-  // K scales
-  int64_t n_plan, n_pieces, n_kfrag, n_kscale;
+  // Q converted to bf16 ([n_rows, H, 128]), for calls that convert
+  uint16_t* qconv;
+  int32_t H;
+  // workgroups of each job, in grid order: plan segments, pieces or Q
+  // conversion, K chunks, K scales
+  int64_t n_plan, n_pieces, n_qconv, n_kfrag, n_kscale;
 };
 
 // Row of the key source holding key `row` of batch (request) b, or -1 for
@@ -147,6 +151,79 @@ __device__ void kfrag_group(const PrepArgs& a, int64_t wg) {
 #pragma unroll
   for (int j = 0; j < kMaxGroup; ++j)
     if (at[j] >= 0) reinterpret_cast<uint4*>(a.kfrag)[at[j]] = x[j];
+}
+
+// bf16 bits of a finite float, rounded to nearest even (exact for the
+// converted e4m3 values: four significant bits, within bf16's range)
+__device__ __forceinline__ uint32_t bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eight e4m3 codes (little-endian in `c`) times an E8M0 scale as eight bf16
+// values, in order: the hardware decode at scale 1 is exact, the scale a
+// multiply by a power of two.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 c, float scale) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.f, false);
+  const f2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.x, 1.f, true);
+  const f2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.f, false);
+  const f2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c.y, 1.f, true);
+  auto pack = [&](f2 v) { return bf16_rne(v.x * scale) | (bf16_rne(v.y * scale) << 16); };
+  return make_uint4(pack(a), pack(b), pack(d), pack(e));
+}
+
+// Q converted to bf16: one thread per 8 elements of one (row, head), its
+// MX block scale folded in (FP8 Q has none).
+template <int F>
+__device__ void qconv_rows(const PrepArgs& a, int64_t wg) {
+  const int64_t i = wg * 256 + threadIdx.x;
+  if (i >= a.n_rows * a.H * 16) return;
+  const int64_t qh = i >> 4;
+  const int t = int(i & 15);
+  const uint2 c = *reinterpret_cast<const uint2*>(static_cast<const unsigned char*>(a.q) + qh * 128 + 8 * t);
+  float scale = 1.f;
+  if constexpr (F == IDX_IN_MXFP8_E4M3)
+    scale = e8m0_value((static_cast<const uint32_t*>(a.q_scale)[qh] >> (8 * (t >> 2))) & 0xFFu);
+  reinterpret_cast<uint4*>(a.qconv)[i] = e4m3x8_to_bf16(c, scale);
+}
+
+// K converted to bf16 in the bf16 fragment order (KLayout<IDX_IN_BF16>): one
+// thread per 16-byte chunk (kgroup of them per thread, as kfrag_group), that
+// is 8 elements [64 g + 8 v, +8) of key row 32 u + c, MX block scale folded in.
+template <int F>
+__device__ void kconv_group(const PrepArgs& a, int64_t wg) {
+  constexpr int NV = 8;  // 16-byte chunks per lane per block (256-byte bf16 rows)
+  const int64_t n = a.B * a.nblk * NV * 64;
+  const unsigned char* base = a.paged ? a.pk.k_cache : a.k;
+  const uint32_t* sbase = a.paged ? a.pk.k_scale_cache : a.k_scale;
+  uint2 x[kMaxGroup];
+  float sc[kMaxGroup];
+  int64_t at[kMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j) {
+    at[j] = -1;
+    x[j] = make_uint2(0, 0);
+    sc[j] = 1.f;
+    const int64_t i = (wg * a.kgroup + j) * 256 + threadIdx.x;
+    if (j >= a.kgroup || i >= n) continue;
+    const int lane = int(i & 63);
+    const int v = int((i >> 6) % NV);
+    const uint32_t bu = uint32_t((i >> 6) / NV);
+    const uint32_t b32 = a.by_nblk.div(bu);
+    const int64_t b = b32, u = bu - b32 * uint32_t(a.nblk);
+    if (block_unused(a, b, u)) continue;
+    at[j] = i;
+    const int c = lane & 31, g = lane >> 5, e0 = 64 * g + 8 * v;
+    const int64_t src = key_source_row(a, b, u * 32 + c);
+    if (src >= 0) {
+      x[j] = *reinterpret_cast<const uint2*>(base + src * 128 + e0);
+      if constexpr (F == IDX_IN_MXFP8_E4M3) sc[j] = e8m0_value((sbase[src] >> (8 * (e0 >> 5))) & 0xFFu);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxGroup; ++j)
+    if (at[j] >= 0) reinterpret_cast<uint4*>(a.kfrag)[at[j]] = e4m3x8_to_bf16(x[j], sc[j]);
 }
 
 // One thread per word of the K scales in block order (kgroup per thread, as
@@ -358,7 +435,9 @@ __device__ void pieces_rows(const PrepArgs& a, int64_t wg) {
   }
 }
 
-template <int F, bool WBF>
+// CONV: Q and K of an FP8 / MXFP8 call converted to bf16 (no pieces; the
+// FP8 row scales still go to block order).
+template <int F, bool WBF, bool CONV>
 __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
   using L = KLayout<F>;
   __shared__ union {
@@ -370,35 +449,50 @@ __global__ void __launch_bounds__(256) prepare_kernel(const PrepArgs a) {
     return;
   }
   bid -= a.n_plan;
-  if constexpr (F != IDX_IN_BF16) {
-    if (bid < a.n_pieces) {
-      pieces_rows<F, WBF>(a, bid);
+  if constexpr (CONV) {
+    if (bid < a.n_qconv) {
+      qconv_rows<F>(a, bid);
       return;
     }
-    bid -= a.n_pieces;
+    bid -= a.n_qconv;
+    if (bid < a.n_kfrag) {
+      kconv_group<F>(a, bid);
+      return;
+    }
+    bid -= a.n_kfrag;
+    if constexpr (F == IDX_IN_FP8_E4M3) kscale_group<0>(a, bid);
+  } else {
+    if constexpr (F != IDX_IN_BF16) {
+      if (bid < a.n_pieces) {
+        pieces_rows<F, WBF>(a, bid);
+        return;
+      }
+      bid -= a.n_pieces;
+    }
+    if (bid < a.n_kfrag) {
+      kfrag_group<L::ROWB, L::CBASE, L::CSTRIDE>(a, bid);
+      return;
+    }
+    bid -= a.n_kfrag;
+    if constexpr (F != IDX_IN_BF16) kscale_group<L::SHIFT>(a, bid);
   }
-  if (bid < a.n_kfrag) {
-    kfrag_group<L::ROWB, L::CBASE, L::CSTRIDE>(a, bid);
-    return;
-  }
-  bid -= a.n_kfrag;
-  if constexpr (F != IDX_IN_BF16) kscale_group<L::SHIFT>(a, bid);
 }
 
-template <int F, bool WBF>
+template <int F, bool WBF, bool CONV = false>
 hipError_t launch(const PrepArgs& a, hipStream_t stream) {
-  const int64_t grid = a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale;
+  const int64_t grid = a.n_plan + a.n_pieces + a.n_qconv + a.n_kfrag + a.n_kscale;
   if (grid == 0) return hipSuccess;  // e.g. BF16 keys read from a paged cache, plan given
-  hipLaunchKernelGGL((prepare_kernel<F, WBF>), dim3(unsigned(grid)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prepare_kernel<F, WBF, CONV>), dim3(unsigned(grid)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const void* k_scale, int64_t B,
-                          int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q, const void* q_scale,
-                          const void* w, int64_t n_rows, unsigned char* pieces, uint32_t* pscales,
-                          const PlanBuild* build, const PagedK* paged, hipStream_t stream) {
+hipError_t launch_prepare(idx_in_t fmt, bool convert, int H, idx_fp_t w_dtype, const void* k, const void* k_scale,
+                          int64_t B, int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q,
+                          const void* q_scale, const void* w, int64_t n_rows, unsigned char* pieces,
+                          uint32_t* pscales, uint16_t* qconv, const PlanBuild* build, const PagedK* paged,
+                          hipStream_t stream) {
   PrepArgs a{};
   if (paged != nullptr) {
     a.paged = true;
@@ -435,19 +529,28 @@ hipError_t launch_prepare(idx_in_t fmt, idx_fp_t w_dtype, const void* k, const v
   a.n_rows = n_rows;
   a.pieces = pieces;
   a.pscales = pscales;
-  const bool scaled = has_kscale(fmt);
+  a.qconv = qconv;
+  a.H = H;
+  const Exec x{convert ? (fmt == IDX_IN_FP8_E4M3 ? kInBF16RowScale : int(IDX_IN_BF16)) : int(fmt), convert};
+  if (convert && fmt != IDX_IN_FP8_E4M3 && fmt != IDX_IN_MXFP8_E4M3) return hipErrorInvalidValue;
+  const bool scaled = has_kscale(x.kf);
   a.n_pieces = pieces != nullptr ? (n_rows + 3) / 4 : 0;  // only 64-head calls of the formats with pieces
+  a.n_qconv = convert ? (n_rows * H * 16 + 255) / 256 : 0;
   // several chunks per thread only when that still leaves at least 2048
   // workgroups of K copy
   const bool copy_k = paged == nullptr || !paged->skip_gather;
-  const int64_t n_chunks = copy_k ? B * a.nblk * (row_bytes_of(fmt) / 32) * 64 : 0;
+  const int64_t n_chunks = copy_k ? B * a.nblk * (row_bytes_of(x.kf) / 32) * 64 : 0;
   const int64_t per_wg = 256 * 2048;
   a.kgroup = int32_t(n_chunks / per_wg < 1 ? 1 : (n_chunks / per_wg > kMaxGroup ? kMaxGroup : n_chunks / per_wg));
   const int64_t span = 256 * int64_t(a.kgroup);
   a.n_kfrag = (n_chunks + span - 1) / span;
   a.n_kscale = scaled && copy_k ? (B * a.nblk * 64 + span - 1) / span : 0;
-  if (a.n_plan + a.n_pieces + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1) return hipErrorInvalidValue;
+  if (a.n_plan + a.n_pieces + a.n_qconv + a.n_kfrag + a.n_kscale > (int64_t(1) << 31) - 1)
+    return hipErrorInvalidValue;
   const bool wb = w_dtype == IDX_BF16;
+  if (convert)  // the weights are not read
+    return fmt == IDX_IN_FP8_E4M3 ? launch<IDX_IN_FP8_E4M3, false, true>(a, stream)
+                                  : launch<IDX_IN_MXFP8_E4M3, false, true>(a, stream);
   switch (fmt) {
     case IDX_IN_BF16: return launch<IDX_IN_BF16, false>(a, stream);
     case IDX_IN_FP8_E4M3: return wb ? launch<IDX_IN_FP8_E4M3, true>(a, stream) : launch<IDX_IN_FP8_E4M3, false>(a, stream);

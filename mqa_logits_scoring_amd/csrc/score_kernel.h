@@ -83,6 +83,13 @@ struct Fmt<IDX_IN_BF16> {
   static constexpr int ROWB = 256, LB = 128, KSTEPS = 8, KB = 16, CBASE = 128, CSTRIDE = 16;
   static constexpr bool MX = false, ROWSCALE = false;
 };
+// FP8 inputs converted exactly to bf16 (exact accumulation): the BF16 kernel,
+// with the per-row K scale multiplying after the head-sum as for FP8
+template <>
+struct Fmt<kInBF16RowScale> {
+  static constexpr int ROWB = 256, LB = 128, KSTEPS = 8, KB = 16, CBASE = 128, CSTRIDE = 16;
+  static constexpr bool MX = false, ROWSCALE = true;
+};
 // e4m3 in the 32x32x64 f8f6f4 MFMA: bytes 0-15 of both lane halves form one
 // 32-element block (scaled by lane half 0's scale), bytes 16-31 the other
 // (lane half 1's scale).  Lane half g therefore holds 16-byte chunks at
@@ -118,7 +125,8 @@ constexpr bool placement_matches() {
          Fmt<F>::CSTRIDE == KLayout<F>::CSTRIDE;
 }
 static_assert(placement_matches<IDX_IN_BF16>() && placement_matches<IDX_IN_FP8_E4M3>() &&
-                  placement_matches<IDX_IN_MXFP8_E4M3>() && placement_matches<IDX_IN_MXFP4_E2M1>(),
+                  placement_matches<IDX_IN_MXFP8_E4M3>() && placement_matches<IDX_IN_MXFP4_E2M1>() &&
+                  placement_matches<kInBF16RowScale>(),
               "K is reordered in the placement the MFMA operands use");
 static_assert(Fmt<IDX_IN_MXFP8_E4M3>::SCALE_SHIFT == KLayout<IDX_IN_MXFP8_E4M3>::SHIFT &&
                   Fmt<IDX_IN_MXFP4_E2M1>::SCALE_SHIFT == KLayout<IDX_IN_MXFP4_E2M1>::SHIFT,
@@ -201,7 +209,7 @@ __device__ __forceinline__ bool unit_columns(const ScoreArgs& a, int bid, int& t
 // the other's MFMAs; the BF16 kernel holds twice the Q bytes and runs one.
 template <int F>
 constexpr int waves_per_eu() {
-  return F == IDX_IN_BF16 ? 1 : 2;
+  return bf16_operands(F) ? 1 : 2;
 }
 
 // K fragment buffers per wave (even): the load of a block is issued
@@ -386,7 +394,7 @@ __global__ void __launch_bounds__(kThreads)
     f32x16 d = {};
 #pragma unroll
     for (int s = 0; s < T::KSTEPS; ++s) {
-      if constexpr (F == IDX_IN_BF16) {
+      if constexpr (bf16_operands(F)) {
         bf16x8 av, bv;
         __builtin_memcpy(&av, &q[s * KD], 16);
         __builtin_memcpy(&bv, &bf[s * KD], 16);
@@ -474,7 +482,7 @@ __global__ void __launch_bounds__(kThreads)
   f32x16 accA = {}, accB = {};
   float p0 = 0.f, p1 = 0.f;
 
-  if constexpr (F != IDX_IN_BF16) {
+  if constexpr (!bf16_operands(F)) {
     // MXFP4 (FP8 and MXFP8 run score_kernel_x16).  Blocks per 32-column
     // block u: L (linear term of both rows from the weighted-query pieces),
     // then (row 0 | row 1) x (heads 0-31 | 32-63).  The pieces are e2m1 rows
@@ -590,15 +598,21 @@ __global__ void __launch_bounds__(kThreads)
       for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[r], __int_as_float(max(__float_as_int(acc[r]), 0)), p);
       return p;
     };
-    auto combine = [&](float q0, float q1) {
+    // ks: the FP8 row scale of the lane's column (converted FP8 inputs)
+    auto combine = [&](float q0, float q1, float ks) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
-      return (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * a.sm_scale;
+      const float v = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * a.sm_scale;
+      return T::ROWSCALE ? v * ks : v;
     };
-    // (row, heads) blocks (0,0) (0,1) (1,0) (1,1), alternating accA / accB
-    auto block_relu = [&](const uint32_t (&bf)[QD], int u) {
+    // (row, heads) blocks (0,0) (0,1) (1,0) (1,1), alternating accA / accB;
+    // kprev: the row scale word of block u-1, kept past its ring buffer's
+    // reuse
+    float kprev = 1.f;
+    auto block_relu = [&](const uint32_t (&bf)[QD], uint32_t kword, int u) {
       mfma_block(accA, qf[0][0], 0, bf, 0);  // (row 0, heads 0-31) of u  ||
       p1 = epi_relu(accB, wv[1][1], p1);     //   (row 1, heads 32-63) of u-1, completing u-1
-      const float v = combine(p0, p1);
+      const float v = combine(p0, p1, kprev);
+      kprev = __uint_as_float(kword);
       __builtin_amdgcn_sched_barrier(0);
       mfma_block(accB, qf[0][1], 0, bf, 0);  // (row 0, heads 32-63)      ||
       p0 = epi_relu(accA, wv[0][0], 0.f);    //   (row 0, heads 0-31)
@@ -626,12 +640,12 @@ __global__ void __launch_bounds__(kThreads)
       for (int i = 0; i < NB; ++i) {
         const int u = NB * s + i;
         kload(u + NB - 1, bfs[(i + NB - 1) % NB], kws[(i + NB - 1) % NB]);
-        block_relu(bfs[i], u);
+        block_relu(bfs[i], kws[i], u);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     p1 = epi_relu(accB, wv[1][1], p1);
-    store(combine(p0, p1), NB * n_iter - 1);
+    store(combine(p0, p1, kprev), NB * n_iter - 1);
   }
 }
 
@@ -982,7 +996,10 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((score_kernel_x16<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0,
                          stream, a);
   } else if (pd) {
-    hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+    if constexpr (F == kInBF16RowScale) return hipErrorInvalidValue;  // converted keys are never read from a cache
+    else
+      hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
+                         a);
   } else {
     hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
   }

@@ -160,7 +160,7 @@ __global__ void __launch_bounds__(kThreads)
     f32x16 d = {};
 #pragma unroll
     for (int s = 0; s < T::KSTEPS; ++s) {
-      if constexpr (F == IDX_IN_BF16) {
+      if constexpr (bf16_operands(F)) {
         bf16x8 av, bv;
         __builtin_memcpy(&av, &q[s * KD], 16);
         __builtin_memcpy(&bv, &bf[s * KD], 16);

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     L = lib.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert lib.idx_abi_version() == 1
+    assert lib.idx_abi_version() == lib.ABI_VERSION == 2
 
 
 def test_plan_bytes():
@@ -244,15 +244,13 @@ def _peak_lib():
     L.idx_peak_mfma.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p, ctypes.c_void_p]
     L.idx_peak_flop_per_mfma.restype = ctypes.c_double
     L.idx_peak_flop_per_mfma.argtypes = [ctypes.c_int32]
-    L.idx_peak_mfma_valu.restype = ctypes.c_int32
-    L.idx_peak_mfma_valu.argtypes = [ctypes.c_int32] * 4 + [ctypes.c_void_p] * 3
     return L
 
 
 def test_peak_probe_exports_and_checks():
     text = re.sub(r"/\*.*?\*/", "", open(PEAK_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text)))
-    assert names == ["idx_peak_flop_per_mfma", "idx_peak_mfma", "idx_peak_mfma_valu"], names
+    assert names == ["idx_peak_flop_per_mfma", "idx_peak_mfma"], names
     L = _peak_lib()
     assert [L.idx_peak_flop_per_mfma(k) for k in range(5)] == [32768.0, 131072.0, 65536.0, 131072.0, 65536.0]
     assert L.idx_peak_flop_per_mfma(9) == 0.0
@@ -261,12 +259,6 @@ def test_peak_probe_exports_and_checks():
     assert L.idx_peak_mfma(1, 4, 0, 0, 16, None) == 1
     assert L.idx_peak_mfma(1, 4, 10, 0, None, None) == 1
     assert L.idx_peak_mfma(9, 4, 10, 0, 16, None) == 2
-    assert L.idx_peak_mfma_valu(2, 4, 0, 10, 16, 16, None) == 1
-    assert L.idx_peak_mfma_valu(2, 4, 4, 0, 16, 16, None) == 1
-    assert L.idx_peak_mfma_valu(2, 4, 4, 10, None, 16, None) == 1
-    assert L.idx_peak_mfma_valu(2, 4, 4, 10, 16, None, None) == 1
-    assert L.idx_peak_mfma_valu(2, 7, 4, 10, 16, 16, None) == 2  # unsupported VALU count
-    assert L.idx_peak_mfma_valu(0, 4, 4, 10, 16, 16, None) == 2  # shape without an overlap variant
 
 
 @pytest.mark.gpu
@@ -288,19 +280,58 @@ def test_peak_probe_runs_every_shape():
                 assert bool((out == float(per * 36)).all()), (kind, out[:4])
 
 
-@pytest.mark.gpu
-def test_peak_overlap_probe_runs():
-    import torch
-    L = _peak_lib()
-    groups, iters = 8, 3
-    out = torch.zeros(groups * 256, dtype=torch.float32, device="cuda")
-    cyc = torch.zeros(groups * 4, dtype=torch.int64, device="cuda")
-    s = torch.cuda.current_stream().cuda_stream
-    for kind in (2, 3, 4):
-        for valu in (0, 2, 3, 4, 5, 6, 8, 12, 16):
-            cyc.zero_()
-            assert L.idx_peak_mfma_valu(kind, valu, groups, iters, out.data_ptr(), cyc.data_ptr(), s) == 0
-            torch.cuda.synchronize()
-            assert bool(torch.isfinite(out).all()), (kind, valu)
-            # every wave ran 24 MFMAs of at least 8 cycles each
-            assert int(cyc.min()) >= 24 * 8, (kind, valu, cyc[:4])
+# ---------------------------------------------------------------------------
+# workspace sizes: a call given a plan needs no plan bytes; the accumulate
+# field is checked like the others
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+@pytest.mark.parametrize("accum", [0, 1])
+def test_workspace_sizes_and_checks(fmt, accum):
+    L = lib.lib()
+    a = _args(in_dtype=fmt, accumulate=accum, **({"q_scale": None, "k_scale": None} if fmt == 0 else {}))
+    total = lib.idx_logits_workspace_bytes(a)
+    planned = lib.idx_logits_workspace_bytes_planned(a)
+    plan_bytes = lib.idx_logits_plan_bytes(a.B, a.S_q, a.S_k, a.H, a.D)
+    assert 0 < planned < total and total - planned == plan_bytes
+    # K in fragment order is always there: 32-key blocks of 256 (bf16
+    # operands), 128 (e4m3) or 64 (e2m1) bytes per key
+    conv = accum == 1 and fmt in (1, 2)
+    row = 256 if (fmt == 0 or conv) else (64 if fmt == 3 else 128)
+    assert planned >= 64 * row
+    if conv:  # Q converted to bf16: rows x H x 256 bytes
+        assert planned >= a.B * a.S_q * a.H * 256
+    # a planned call is checked against the planned size, an unplanned one
+    # against the total (both fail before any launch here)
+    assert _run(a, plan=FAKE, ws=FAKE, ws_bytes=planned - 1) == lib.IDX_E_WORKSPACE
+    assert _run(a, plan=None, ws=FAKE, ws_bytes=total - 1) == lib.IDX_E_WORKSPACE
+    assert str(total) in lib.idx_last_error()
+    assert L.idx_logits_prepare(ctypes.byref(a), FAKE, planned - 1, None) == lib.IDX_E_WORKSPACE
+    assert L.idx_logits_score(ctypes.byref(a), FAKE, FAKE, planned - 1, None) == lib.IDX_E_WORKSPACE
+    assert str(planned) in lib.idx_last_error()
+
+
+def test_accumulate_mode_is_checked():
+    for bad in (2, -1, 7):
+        a = _args(accumulate=bad)
+        assert _run(a, plan=FAKE, ws=FAKE, ws_bytes=1 << 30) == lib.IDX_E_INVALID
+        assert "accumulate" in lib.idx_last_error()
+        assert lib.idx_logits_workspace_bytes(a) == 0 and lib.idx_logits_workspace_bytes_planned(a) == 0
+
+
+def test_exact_accumulation_only_changes_the_e4m3_formats():
+    for fmt, changes in ((0, False), (1, True), (2, True), (3, False)):
+        kw = {"q_scale": None, "k_scale": None} if fmt == 0 else {}
+        a0 = _args(in_dtype=fmt, accumulate=0, **kw)
+        a1 = _args(in_dtype=fmt, accumulate=1, **kw)
+        same = lib.idx_logits_workspace_bytes(a0) == lib.idx_logits_workspace_bytes(a1)
+        assert same != changes, fmt
+
+
+def test_plan_windows_rejects():
+    L = lib.lib()
+    assert L.idx_logits_plan_windows(FAKE + 64, 1, 16, 64, 64, 128, FAKE, FAKE, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_windows(FAKE, 1, 16, 64, 64, 128, FAKE + 2, FAKE, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_windows(FAKE, 1, 16, 64, 64, 128, FAKE, FAKE + 1, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_windows(None, 1, 16, 64, 64, 128, FAKE, FAKE, None) == lib.IDX_E_INVALID
+    assert L.idx_logits_plan_windows(FAKE, 1, 16, 64, 24, 128, FAKE, FAKE, None) == lib.IDX_E_UNSUPPORTED

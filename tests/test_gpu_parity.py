@@ -13,7 +13,8 @@ import torch
 import mqa_logits_scoring_amd as lib
 import oracle
 import workloads as W
-from gpu_util import (compare_rows, dev_inputs, make_plan, mask_check_all_rows, run, sample_rows, to_f64)
+from gpu_util import (compare_all_rows, compare_rows, dev_inputs, inside_check_all_rows, make_plan,
+                      mask_check_all_rows, run, sample_rows, to_f64)
 import oracle_pins as P
 
 pytestmark = pytest.mark.gpu
@@ -262,20 +263,52 @@ def test_named_full_size(name):
     wl = W.make(name)
     d = dev_inputs(wl)
     plan = make_plan(wl, d)
-    # an unclean call leaves the cells outside the windows as they were
+    # the output starts as NaN: a cell that no unit writes stays NaN, which the
+    # checks of every row below catch (an unclean call leaves the cells
+    # outside the windows as they were)
     odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-    out = run(wl, d, plan=plan, out=torch.zeros((wl.B, wl.S_q, wl.S_k), dtype=odt, device="cuda"))
-    out2 = run(wl, d, out=torch.zeros_like(out))
+    out = run(wl, d, plan=plan, out=torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), dtype=odt, device="cuda"))
+    out2 = run(wl, d, out=torch.full_like(out, float("nan")))
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32),
                        out2.view(torch.int16 if out.dtype == torch.bfloat16 else torch.int32))
     if wl.clean:
         mask_check_all_rows(wl, out)
+    inside_check_all_rows(wl, out)
     rows = sample_rows(wl)
     ref, bound = oracle.logits(wl, rows=rows)
     got = to_f64(out.reshape(wl.B * wl.S_q, -1)[torch.from_numpy(rows).cuda()])
     ratio, rel = compare_rows(wl, got, ref, bound, clean=wl.clean, what=name)
     print(f"{name}: {len(rows)} rows, max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+
+
+@pytest.mark.parametrize("name", ["c3", "c4_mxfp8", "c4_mxfp4"])
+def test_named_every_cell(name):
+    """Every cell of the Q2048 / KV32768 workloads against the oracle (values
+    within tolerance, -inf placement exact), not only sampled rows."""
+    wl = W.make(name)
+    d = dev_inputs(wl)
+    out = run(wl, d, out=torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    ratio, rel = compare_all_rows(wl, out, what=name)
+    print(f"{name}: every cell, max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+
+
+# Long key ranges with several tiles take the XCD-owned chunk mapping (chunk c
+# of every tile on XCD c % 8, 128 chunks per tile here): every cell of it.
+XCD_CASES = [(f, win) for f in W.FORMATS for win in ("offsets", "irregular")]
+
+
+@pytest.mark.parametrize("fmt,windows", XCD_CASES, ids=[f"{f}-{w}" for f, w in XCD_CASES])
+def test_xcd_chunk_mapping_every_cell(fmt, windows):
+    wl = W.make_random(fmt, 1, 64, 65536, seed=70, windows=windows, offsets=[0] if windows == "offsets" else None,
+                       w_dtype="bf16" if fmt == "mxfp4" else "f32", out_dtype="bf16" if fmt == "mxfp4" else "f32")
+    d = dev_inputs(wl)
+    out = run(wl, d, out=torch.full((1, wl.S_q, wl.S_k), float("nan"), device="cuda",
+                                    dtype=torch.bfloat16 if fmt == "mxfp4" else torch.float32))
+    torch.cuda.synchronize()
+    ratio, rel = compare_all_rows(wl, out, what=f"xcd {fmt} {windows}")
+    print(f"xcd {fmt} {windows}: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "bf16"])

@@ -30,7 +30,7 @@ import pytest
 
 from mqa_logits_scoring_amd import build as hip_build
 
-SCORE_SOURCES = ["score_bf16.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
+SCORE_SOURCES = ["score_bf16.hip", "score_bf16rs.hip", "score_fp8.hip", "score_mxfp8.hip", "score_mxfp4.hip"]
 
 
 def device_asm(src: str, out_dir: str) -> str:

@@ -314,6 +314,68 @@ def make_paged(fmt: str, B: int, next_n: int, ctx_lens, page_size: int, *, S_k: 
 
 
 # --------------------------------------------------------------------------
+# inputs that maximise the matrix core's own accumulation error
+# --------------------------------------------------------------------------
+
+# small magnitudes of the adversarial inputs, per format, for a large
+# element of 1.0 (6.0 for e2m1): every e4m3 subnormal m * 2^-9, a few
+# normals, and for bf16 powers of two far below one
+_ADV_SMALL = {
+    "fp8": [m * 2.0 ** -9 for m in range(1, 8)] + [2.0 ** -6 * (1 + m / 8) for m in (0, 2, 4, 7)] + [2.0 ** -5,
+                                                                                                  2.0 ** -4],
+    "mxfp8": None,  # as fp8
+    "bf16": [2.0 ** -e for e in (4, 6, 7, 8, 9, 12, 16, 20)],
+    "mxfp4": [0.5, 1.0],
+}
+
+
+def make_adversarial(fmt: str, S_q: int, S_k: int, H: int = 64, D: int = 128, *, w_dtype: str = "f32",
+                     out_dtype: str = "f32", seed: int = 0, sm_scale: float = 1.0,
+                     name: str = "adversarial") -> Workload:
+    """Inputs shaped against the accumulation of a matrix core that sums each
+    group of 8 consecutive products of a dot in fixed point aligned to the
+    group's largest product: in Q and K alike, element d of every group
+    (d % 8 == 0) is large and the seven others are small, so Q and K are
+    proportional in magnitude up to the small values (sum |q_d k_d| is then
+    within a hair of |q| |k|, the tolerance's basis) and the small products
+    fall just below or across the alignment's last kept bit.  Row i's small
+    value is the (i mod n)-th of a list, column j's the (j mod n)-th, so
+    every pair meets; the same q serves all H heads and the weights share one
+    sign, so the per-head errors add.  Every fourth row is negated (its
+    scores are then exactly 0 after the ReLU).  Windows: causal, offset 0.
+    MX scales are random per block (the groups lie inside the blocks)."""
+    assert fmt in FORMATS and D == 128
+    small = _ADV_SMALL["fp8" if fmt == "mxfp8" else fmt]
+    big = 6.0 if fmt == "mxfp4" else 1.0
+    n = len(small)
+    rng = np.random.default_rng(seed)
+    g = torch.Generator().manual_seed(seed)
+    grp = (np.arange(D) % 8) == 0
+    qrow = np.where(grp[None, :], big, np.asarray([small[i % n] for i in range(S_q)])[:, None])
+    qrow = qrow * np.where(np.arange(S_q) % 4 == 3, -1.0, 1.0)[:, None]
+    krow = np.where(grp[None, :], big, np.asarray([small[j % n] for j in range(S_k)])[:, None])
+    qv = torch.from_numpy(np.broadcast_to(qrow[:, None, :], (S_q, H, D)).copy()).float().reshape(1, S_q, H, D)
+    kv = torch.from_numpy(krow).float().reshape(1, S_k, D)
+    q_scale = k_scale = None
+    if fmt == "bf16":
+        q, k = bf16_bits(qv), bf16_bits(kv)
+    elif fmt in ("fp8", "mxfp8"):
+        q, k = e4m3_codes(qv), e4m3_codes(kv)
+    else:
+        q, k = pack_nibbles(e2m1_codes(qv.numpy())), pack_nibbles(e2m1_codes(kv.numpy()))
+    if fmt == "fp8":
+        k_scale = (torch.rand((1, S_k), generator=g, dtype=torch.float32) * 1.5 + 0.5).numpy()
+    elif fmt in ("mxfp8", "mxfp4"):
+        q_scale = e8m0_words(rng, (1, S_q, H))
+        k_scale = e8m0_words(rng, (1, S_k))
+    wf = (torch.rand((1, S_q, H), generator=g, dtype=torch.float32) + 0.5) / 8.0
+    w = bf16_bits(wf) if w_dtype == "bf16" else wf.numpy().copy()
+    return Workload(name=name, B=1, S_q=S_q, S_k=S_k, H=H, D=D, fmt=fmt, w_dtype=w_dtype, out_dtype=out_dtype,
+                    sm_scale=float(sm_scale), clean=True, q=q, q_scale=q_scale, k=k, k_scale=k_scale, w=w,
+                    offsets=np.zeros(1, np.int32), starts=None, ends=None, seed=seed)
+
+
+# --------------------------------------------------------------------------
 # the named workloads
 # --------------------------------------------------------------------------
 
