@@ -241,6 +241,27 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
                             size_t workspace_bytes, void* stream);
 
 /*
+ * idx_logits_run for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same call, bitwise the same result, with the workspace taken from a
+ * scratch array the library holds on each device
+ * (idx_logits_noalloc_scratch_bytes() bytes, set aside with the library's
+ * code object on every device it runs on, until the process ends).  The call
+ * allocates nothing.  `stream` must belong to the current device (NULL: its
+ * default stream).  A call needing more workspace than the scratch holds
+ * (idx_logits_workspace_bytes, or idx_logits_workspace_bytes_planned with a
+ * plan) returns IDX_E_WORKSPACE before anything is enqueued.  Every call on
+ * one device shares that device's scratch, which keeps the last call's
+ * contents: calls that overlap on one device (other streams, other threads)
+ * race and give wrong results; serialise them.
+ */
+idx_status_t idx_logits_run_noalloc(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                                    const int32_t* row_starts, const int32_t* row_ends, void* stream);
+
+/* Bytes of the per-device scratch of idx_logits_run_noalloc. */
+size_t idx_logits_noalloc_scratch_bytes(void);
+
+/*
  * The two phases of idx_logits_run, for callers that reuse a prepared
  * workspace or time the scoring alone.  idx_logits_run(a, plan, ...) with a
  * plan is exactly idx_logits_prepare(a, ws) followed by

@@ -30,7 +30,7 @@ EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_
             "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_score_paged",
             "idx_logits_topk",
             "idx_logits_workspace_bytes", "idx_logits_workspace_bytes_planned",
-            "idx_logits_run", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
+            "idx_logits_run", "idx_logits_run_noalloc", "idx_logits_noalloc_scratch_bytes", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
 
 class IdxLogitsArgs(ctypes.Structure):
@@ -95,6 +95,10 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_workspace_bytes_planned.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_run.restype = ctypes.c_int
         L.idx_logits_run.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, P, SZ, P]
+        L.idx_logits_run_noalloc.restype = ctypes.c_int
+        L.idx_logits_run_noalloc.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, P]
+        L.idx_logits_noalloc_scratch_bytes.restype = SZ
+        L.idx_logits_noalloc_scratch_bytes.argtypes = []
         L.idx_logits_prepare.restype = ctypes.c_int
         L.idx_logits_prepare.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, SZ, P]
         L.idx_logits_score.restype = ctypes.c_int
@@ -263,6 +267,31 @@ def idx_logits_run(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, *, in_dtyp
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("idx_logits_run", lib().idx_logits_run(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en),
                                                     _ptr(workspace), ws_bytes, _stream(stream, device)))
+    return out
+
+
+def idx_logits_noalloc_scratch_bytes() -> int:
+    return int(lib().idx_logits_noalloc_scratch_bytes())
+
+
+def idx_logits_run_noalloc(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, in_dtype: str,
+                           q_scale=None, k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
+                           plan: Optional[torch.Tensor] = None, q_causal_offsets: Optional[torch.Tensor] = None,
+                           row_starts: Optional[torch.Tensor] = None, row_ends: Optional[torch.Tensor] = None,
+                           accumulate: str = "native", stream=None) -> torch.Tensor:
+    """idx_logits_run on the library's per-device scratch: allocates nothing,
+    so `out` and the window arrays (int32 device tensors) must be given."""
+    for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("q_causal_offsets", q_causal_offsets), ("row_starts", row_starts), ("row_ends", row_ends)):
+        if t is not None and (t.dtype != torch.int32 or t.device != q.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
+    args = make_args(q, k, w, out, in_dtype=in_dtype, q_scale=q_scale, k_scale=k_scale, sm_scale=sm_scale,
+                     clean_logits=clean_logits, accumulate=accumulate)
+    _check("idx_logits_run_noalloc",
+           lib().idx_logits_run_noalloc(ctypes.byref(args), _ptr(plan), _ptr(q_causal_offsets), _ptr(row_starts),
+                                        _ptr(row_ends), _stream(stream, q.device)))
     return out
 
 

@@ -4,7 +4,17 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "internal.h"
+
+// Workspace of idx_logits_run_noalloc: one array per device, allocated with
+// the library's code object on each device it runs on and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, never a
+// device address: the device address comes from hipGetSymbolAddress, once per
+// device (scratch_on_device below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -344,6 +354,61 @@ idx_status_t idx_logits_run(const idx_logits_args_t* a, const void* plan, const 
   if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, nullptr, s)) != IDX_OK) return st;
   return score(a, p, WL, ws, s);
 }
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+unsigned char* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The device address of this device's `scratch`: the stream's device, which
+// must be the current one (the symbol is looked up with it current).
+idx_status_t scratch_on_device(void* stream, unsigned char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return fail(IDX_E_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (int(sdev) != dev)
+      return fail(IDX_E_INVALID, "the stream belongs to device %d, the current device is %d", int(sdev), dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(IDX_E_UNSUPPORTED, "device %d is beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(IDX_E_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = static_cast<unsigned char*>(p);
+  }
+  *out = g_scratch[dev];
+  return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+idx_status_t idx_logits_run_noalloc(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                                    const int32_t* row_starts, const int32_t* row_ends, void* stream) {
+  idx_status_t st = check_args(a);
+  if (st != IDX_OK) return st;
+  const idx::WorkspaceLayout WL = layout_checked(a);
+  const size_t need = plan != nullptr ? WL.planned : WL.total;
+  if (WL.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
+  if (need > kScratchBytes)
+    return fail(IDX_E_WORKSPACE, "this call needs %zu bytes of workspace; idx_logits_run_noalloc holds %zu",
+                need, kScratchBytes);
+  unsigned char* ws = nullptr;
+  if ((st = scratch_on_device(stream, &ws)) != IDX_OK) return st;
+  return idx_logits_run(a, plan, q_causal_offsets, row_starts, row_ends, ws, kScratchBytes, stream);
+}
+
+size_t idx_logits_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 idx_status_t idx_logits_prepare(const idx_logits_args_t* a, void* workspace, size_t workspace_bytes, void* stream) {
   idx_status_t st = check_args(a);
