@@ -2,27 +2,32 @@
 """Benchmark of the lightning-indexer scoring path on one MI355X.
 
 A step is one complete call of the path on inputs already resident in device
-memory: idx_logits_run without a precomputed plan, which builds the plan
-(windows + schedule) and the per-call preparation (K in fragment order,
-weighted-query pieces) in one launch, then runs the scoring kernel with its
--inf cleanup.  The default workload is
-the MXFP8 Q2048 / KV32768, H64 / D128, clean_logits=True call with FP32
-weights and output and rows seeing [0, KV-Q+row) -- the configuration
-DeepGEMM pull request 435 times (Performance section) -- on seeded random
-inputs.
+memory: idx_logits_run, which builds the per-call preparation (K in fragment
+order, weighted-query pieces) and, without a precomputed plan, the plan
+(windows + schedule) in one launch, then runs the scoring kernel with its
+-inf cleanup.  The default workload is the MXFP8 Q2048 / KV32768, H64 / D128,
+clean_logits=True call with FP32 weights and output and rows seeing
+[0, KV-Q+row) -- the configuration DeepGEMM pull request 435 times
+(Performance section) -- on seeded random inputs, with its all-zero variant
+beside it.
 
-Before the W warm-up steps, untimed calls run for --prewarm-s seconds (1 by
-default): the GPU clock ramps up over the first milliseconds of sustained
-work, and calls timed right after a short warm-up run up to 20 % slower.
+Timing follows that page's protocol, on HIP graphs: every variant is warmed,
+then captured as a graph of 5 calls into 5 distinct retained outputs and
+replayed 5 times; after a pre-warm that lets the clock settle, each of
+`steps` samples replays every variant twice (the second replay is timed with
+events on the stream the library launches on, divided by 5), the variants'
+order rotating and reversing from sample to sample so that they share one
+clock state.  Reported: median / p10 / p90 per variant.  The variants are the
+call without a plan ("metadata no", the headline `value`), the call with a
+plan built outside timing ("metadata yes"), the scoring kernel alone on a
+prepared workspace (the roofline's kernel time), the same for the all-zero
+inputs, and for FP8 / MXFP8 the call with exact accumulation.  Every graph's
+outputs are checked bitwise against eager calls.
 
-Prints one JSON line.  Alongside the whole-call time it reports the roofline
-of the scoring kernel alone, timed over `steps` back-to-back launches on the
-prepared workspace, bracketed by events on the stream they run on (events
-around every launch of the timed calls would add their own gaps to them).  HBM traffic comes from the
-rocprofv3 FETCH_SIZE / WRITE_SIZE counts kept under profiles/ (calibrated
-against a plain copy), and only while the kernel sources are the ones they
-were taken on.  The fp64 CPU oracle is timed on a bounded sample of the same
-workload.
+HBM traffic comes from the rocprofv3 FETCH_SIZE / WRITE_SIZE counts kept under
+profiles/ (calibrated against a plain copy), and only while the kernel sources
+are the ones they were taken on.  The fp64 CPU oracle is timed on a bounded
+sample of the same workload.
 
     python bench.py --write-traffic WORKLOAD FETCH.csv WRITE.csv COPY_FETCH.csv COPY_WRITE.csv COPY_BYTES [COPY_RE]
 turns rocprofv3 --pmc counter files into that traffic record (the copy runs
@@ -173,14 +178,6 @@ def build_plan(lib, wl, d, plan, stream):
                                row_starts=d["starts"], row_ends=d["ends"], plan=plan, stream=stream)
 
 
-def call(lib, wl, d, out, plan=None):
-    """One scoring call through the C ABI (plan None: built inside the call)."""
-    return lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"],
-                              k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean, out=out,
-                              plan=plan, q_causal_offsets=d["offsets"], row_starts=d["starts"],
-                              row_ends=d["ends"], workspace=d.get("workspace"))
-
-
 def visible_cells(lib, wl, plan) -> int:
     """Visible cells from the windows the library's plan holds."""
     ws, we = lib.idx_logits_plan_windows(plan, wl.B, wl.S_q, wl.S_k)
@@ -299,26 +296,72 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def gpu_clock_state() -> dict:
+    """amd-smi's view of GPU 0's clocks and power (best effort: a missing tool
+    or an unknown output layout is reported, not raised)."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception as e:  # noqa: BLE001 - a diagnostic, never fatal
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    found = {}
+
+    def walk(x, path):
+        if isinstance(x, dict):
+            for k, v in x.items():
+                walk(v, path + [str(k)])
+        elif isinstance(x, list):
+            for i, v in enumerate(x):
+                walk(v, path + [str(i)])
+        else:
+            key = ".".join(path).lower()
+            if (("gfx" in key and "clk" in key) or "power" in key) and len(found) < 24:
+                found[".".join(path)] = x
+    walk(data, [])
+    return found or {"raw": r.stdout[:400]}
+
+
+class Variant:
+    """One timed variant: `launch(i)` enqueues one call into output i of 5 on
+    torch's current stream (the graph's capture stream while capturing)."""
+
+    def __init__(self, name, launch, outs, ref_group):
+        self.name, self.launch, self.outs, self.ref_group = name, launch, outs, ref_group
+        self.graph = None
+        self.samples = []
+
+
+def _pct(xs, q):
+    return float(np.percentile(np.asarray(xs, np.float64), q))
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--write-traffic":
         write_traffic(sys.argv[2:])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=40, help="timed samples (each replays every variant's graph)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed graph replays of every variant after capture")
     ap.add_argument("--workload", default="c4_mxfp8",
                     help="named workload (c1, c2, c3, c3_noclean, c4_mxfp8, c4_mxfp4, *_zero, c5, c5_nonaligned, "
-                         "thd_bf16_r4, paged_mxfp8_decode)")
+                         "thd_bf16_r4, paged_mxfp8_decode, screen_h8/h32/h64)")
     ap.add_argument("--prewarm-s", type=float, default=1.0,
-                    help="seconds of untimed calls before the warm-up steps (lets the GPU clock ramp up)")
+                    help="seconds of untimed replays before the samples (lets the GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-zero-variant", action="store_true")
+    ap.add_argument("--no-exact-variant", action="store_true",
+                    help="skip the FP8 / MXFP8 call with exact (fp32) accumulation")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-shape and copy peak measurement")
     ap.add_argument("--topk", type=int, default=0,
                     help="also time top-k selection (this k, by column) over the call's scores")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the MFMA throughput per shape and a device copy (libidx_peak.so)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the 5 calls of a sample directly instead of replaying a captured graph "
+                         "(for profilers that follow plain kernel launches)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes `steps` times (counter calibration)")
     args = ap.parse_args()
@@ -347,127 +390,205 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "steps": args.steps}), flush=True)
         return
 
-    def measure(name: str):
-        wl = W.make(name)
-        d = device_inputs(wl, dev)
-        stream = torch.cuda.current_stream(dev)
-        odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
-        outs = [torch.empty((wl.B, wl.S_q, wl.S_k), dtype=odt, device=dev) for _ in range(2)]
-        paged = getattr(wl, "paged", None) is not None
-        if paged:
-            cargs = [lib.make_paged_args(d["q"], d["w"], o, wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
-                                         sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
-        else:
-            cargs = [lib.make_args(d["q"], d["k"], d["w"], o, in_dtype=wl.fmt, q_scale=d["q_scale"],
-                                   k_scale=d["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean) for o in outs]
-        ws = torch.empty(lib.idx_logits_workspace_bytes(cargs[0]), dtype=torch.uint8, device=dev)
-        plan = torch.empty(lib.idx_logits_plan_bytes(wl.B, wl.S_q, wl.S_k), dtype=torch.uint8, device=dev)
+    wl = W.make(args.workload)
+    paged = getattr(wl, "paged", None) is not None
+    thd = getattr(wl, "thd", None) is not None
+    odt = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    iv = torch.int16 if odt == torch.bfloat16 else torch.int32
+    variants = []
+    keep = []  # tensors the graphs read or write
 
-        thd = getattr(wl, "thd", None) is not None
+    def add_workload(w, tag, with_plan_variants):
+        d = device_inputs(w, dev)
+        keep.append(d)
+        plan = torch.empty(lib.idx_logits_plan_bytes(w.B, w.S_q, w.S_k, w.H, w.D), dtype=torch.uint8, device=dev)
+        build_plan(lib, w, d, plan, None)
+        keep.append(plan)
 
-        def step(i):
-            # one whole call through the C ABI: the plan (windows + schedule),
-            # the K reorder and the weighted-query pieces share one launch,
-            # then the scoring kernel.  Packed variable-length rows build
-            # their plan with idx_logits_plan_thd first.
-            # Paged calls read their keys straight from the cache where the
-            # library can (64 heads, pages of 32 * 2^j keys), else gather them
-            # through the block table in the same preparation launch.
-            call_plan = build_plan(lib, wl, d, plan, stream) if thd else None
+        def outs5():
+            o = [torch.empty((w.B, w.S_q, w.S_k), dtype=odt, device=dev) for _ in range(5)]
+            keep.extend(o)
+            return o
+
+        def args_for(o, accumulate="native"):
             if paged:
-                lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=d["q_scale"],
-                                         sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], workspace=ws,
-                                         stream=stream)
-                return
-            lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=wl.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
-                               sm_scale=wl.sm_scale, clean_logits=wl.clean, out=outs[i % 2], plan=call_plan,
-                               q_causal_offsets=d["offsets"], row_starts=d["starts"], row_ends=d["ends"],
-                               workspace=ws, stream=stream)
+                return lib.make_paged_args(d["q"], d["w"], o, w.S_k, in_dtype=w.fmt, q_scale=d["q_scale"],
+                                           sm_scale=w.sm_scale, clean_logits=w.clean, accumulate=accumulate)
+            return lib.make_args(d["q"], d["k"], d["w"], o, in_dtype=w.fmt, q_scale=d["q_scale"], k_scale=d["k_scale"],
+                                 sm_scale=w.sm_scale, clean_logits=w.clean, accumulate=accumulate)
 
-        # the GPU's clock ramps up over the first milliseconds of sustained
-        # work: run untimed calls for a second before the warm-up steps
-        t_warm = time.perf_counter()
-        i = 0
-        while time.perf_counter() - t_warm < args.prewarm_s:
-            step(i)
-            i += 1
-            if i % 8 == 0:
-                torch.cuda.synchronize()
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-        # whole calls: exactly `steps` of them between two synchronisations
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        us_call = wall / args.steps * 1e6
-        # the scoring kernel alone: a plan and a prepared workspace, then
-        # `steps` launches back to back on the stream the library launches on,
-        # between two events (paged: the paged scoring phase, which reads the
-        # cache directly where the one-call form does).
-        build_plan(lib, wl, d, plan, stream)
-        if paged:
-            lib.idx_logits_prepare_paged(cargs[0], d["kv"], ws, stream=stream)
-        else:
-            lib.idx_logits_prepare(cargs[0], ws, stream=stream)
+        def call_variant(name, use_plan, accumulate="native"):
+            o = outs5()
+            a0 = args_for(o[0], accumulate)
+            ws = torch.empty(lib.idx_logits_workspace_bytes(a0), dtype=torch.uint8, device=dev)
+            keep.append(ws)
+            tplan = None
+            if thd and not use_plan:  # packed rows build their plan with idx_logits_plan_thd in the call
+                tplan = torch.empty_like(plan)
+                keep.append(tplan)
 
-        def timed(i):
+            def launch(i):
+                if paged:
+                    lib.idx_logits_run_paged(d["q"], d["w"], d["kv"], w.S_k, in_dtype=w.fmt, q_scale=d["q_scale"],
+                                             sm_scale=w.sm_scale, clean_logits=w.clean, out=o[i], workspace=ws,
+                                             plan=plan if use_plan else None, accumulate=accumulate)
+                    return
+                p = plan if use_plan else (build_plan(lib, w, d, tplan, None) if thd else None)
+                lib.idx_logits_run(d["q"], d["k"], d["w"], in_dtype=w.fmt, q_scale=d["q_scale"],
+                                   k_scale=d["k_scale"], sm_scale=w.sm_scale, clean_logits=w.clean, out=o[i],
+                                   plan=p, q_causal_offsets=d["offsets"], row_starts=d["starts"], row_ends=d["ends"],
+                                   workspace=ws, accumulate=accumulate)
+            variants.append(Variant(name, launch, o, f"{tag}:{accumulate}"))
+
+        def score_variant(name):
+            o = outs5()
+            cargs = [args_for(x) for x in o]
+            ws = torch.empty(lib.idx_logits_workspace_bytes_planned(cargs[0]), dtype=torch.uint8, device=dev)
+            keep.append(ws)
             if paged:
-                lib.idx_logits_score_paged(cargs[i % 2], d["kv"], plan, ws, stream=stream)
+                lib.idx_logits_prepare_paged(cargs[0], d["kv"], ws)
             else:
-                lib.idx_logits_score(cargs[i % 2], plan, ws, stream=stream)
+                lib.idx_logits_prepare(cargs[0], ws)
 
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for i in range(args.steps):
-            timed(i)
-        ev1.record(stream)
-        ev1.synchronize()
-        kern_us = ev0.elapsed_time(ev1) * 1000 / args.steps
-        V = visible_cells(lib, wl, plan)
-        # the separately planned (and prepared) scoring gives the timed calls' output
-        ref = torch.empty_like(outs[0])
-        step(0)
-        ref.copy_(outs[0])
-        timed(0)
-        iv = torch.int16 if odt == torch.bfloat16 else torch.int32
-        if not bool(torch.equal(ref.view(iv), outs[0].view(iv))):
-            raise RuntimeError("the phased call and idx_logits_run disagree")
-        topk = None
-        if args.topk:
-            # top-k over the scores the timed calls wrote: `steps` launches
-            # back to back between two events, after a few untimed ones
-            k = args.topk
-            tidx = torch.empty((wl.B, wl.S_q, k), dtype=torch.int32, device=dev)
-            tval = torch.empty((wl.B, wl.S_q, k), dtype=torch.float32, device=dev)
-            sel = lambda: lib.idx_logits_topk(plan, outs[0], k, order="column", B=wl.B, H=wl.H, D=wl.D, S_k=wl.S_k,
-                                              out_idx=tidx, out_val=tval, stream=stream)
-            for _ in range(3):
-                sel()
-            ev0.record(stream)
-            for _ in range(args.steps):
-                sel()
-            ev1.record(stream)
-            ev1.synchronize()
-            t_us = ev0.elapsed_time(ev1) * 1000 / args.steps
-            # algorithmic bytes: every window score read once, k (index, score) pairs written per row
-            read = (2 if odt == torch.bfloat16 else 4) * V
-            written = 8 * wl.B * wl.S_q * k
-            gbs = (read + written) / (t_us * 1e-6) / 1e9
-            rec = counted_traffic(f"topk{k}:{wl.name}", "topk")
-            topk = {"k": k, "order": "column", "kernel": "topk_kernel", "kernel_us": round(t_us, 2),
-                    "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                 "traffic": None if rec is None else rec["fetch_bytes"] + rec["write_bytes"],
-                                 "algorithmic_bytes_per_launch": read + written}}
-        return wl, V, us_call, kern_us, topk
+            def launch(i):
+                if paged:
+                    lib.idx_logits_score_paged(cargs[i], d["kv"], plan, ws)
+                else:
+                    lib.idx_logits_score(cargs[i], plan, ws)
+            variants.append(Variant(name, launch, o, f"{tag}:native"))
 
-    wl, V, us_call, kern_us, topk = measure(args.workload)
+        call_variant(f"{tag}call", False)
+        if with_plan_variants:
+            call_variant(f"{tag}call_planned", True)
+            score_variant(f"{tag}kernel")
+        return d, plan
+
+    d, plan = add_workload(wl, "", True)
+    zero_name = args.workload + "_zero"
+    zwl = None
+    if not args.no_zero_variant and zero_name in W.NAMED:
+        zwl = W.make(zero_name)
+        add_workload(zwl, "zero_", True)
+    exact = wl.fmt in ("fp8", "mxfp8") and not args.no_exact_variant
+    if exact:
+        # the same call with exact accumulation (bf16 matrix core on converted operands)
+        dd = d
+        o = [torch.empty((wl.B, wl.S_q, wl.S_k), dtype=odt, device=dev) for _ in range(5)]
+        keep.extend(o)
+        if paged:
+            a0 = lib.make_paged_args(dd["q"], dd["w"], o[0], wl.S_k, in_dtype=wl.fmt, q_scale=dd["q_scale"],
+                                     sm_scale=wl.sm_scale, clean_logits=wl.clean, accumulate="fp32")
+        else:
+            a0 = lib.make_args(dd["q"], dd["k"], dd["w"], o[0], in_dtype=wl.fmt, q_scale=dd["q_scale"],
+                               k_scale=dd["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean,
+                               accumulate="fp32")
+        ws_x = torch.empty(lib.idx_logits_workspace_bytes(a0), dtype=torch.uint8, device=dev)
+        keep.append(ws_x)
+
+        def launch_exact(i):
+            if paged:
+                lib.idx_logits_run_paged(dd["q"], dd["w"], dd["kv"], wl.S_k, in_dtype=wl.fmt, q_scale=dd["q_scale"],
+                                         sm_scale=wl.sm_scale, clean_logits=wl.clean, out=o[i], workspace=ws_x,
+                                         accumulate="fp32")
+                return
+            lib.idx_logits_run(dd["q"], dd["k"], dd["w"], in_dtype=wl.fmt, q_scale=dd["q_scale"],
+                               k_scale=dd["k_scale"], sm_scale=wl.sm_scale, clean_logits=wl.clean, out=o[i],
+                               q_causal_offsets=dd["offsets"], row_starts=dd["starts"], row_ends=dd["ends"],
+                               workspace=ws_x, accumulate="fp32")
+        variants.append(Variant("call_exact_accumulation", launch_exact, o, ":fp32"))
+    if args.topk:
+        k = args.topk
+        src = variants[0].outs[0]
+        tidx = [torch.empty((wl.B, wl.S_q, k), dtype=torch.int32, device=dev) for _ in range(5)]
+        tval = [torch.empty((wl.B, wl.S_q, k), dtype=torch.float32, device=dev) for _ in range(5)]
+        keep.extend(tidx + tval)
+
+        def launch_topk(i):
+            lib.idx_logits_topk(plan, src, k, order="column", B=wl.B, H=wl.H, D=wl.D, S_k=wl.S_k, out_idx=tidx[i],
+                                out_val=tval[i])
+        variants.append(Variant(f"topk{k}", launch_topk, tidx, None))
+
+    # eager reference of every group of variants that must agree bitwise
+    refs = {}
+    for v in variants:
+        for i in range(3):
+            v.launch(i)
+    torch.cuda.synchronize()
+    for v in variants:
+        if v.ref_group is not None and v.ref_group not in refs:
+            refs[v.ref_group] = v.outs[0].clone()
+    # capture: 5 calls into 5 distinct outputs per graph, then warm replays
+    # (--eager: the 5 calls are launched directly every time)
+    class _Eager:
+        def __init__(self, v):
+            self.v = v
+
+        def replay(self):
+            for i in range(5):
+                self.v.launch(i)
+
+    for v in variants:
+        if args.eager:
+            v.graph = _Eager(v)
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(5):
+                v.launch(i)
+        v.graph = g
+    for _ in range(args.warmup):
+        for v in variants:
+            v.graph.replay()
+    torch.cuda.synchronize()
+    # the clock ramps up over the first milliseconds of sustained work
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.prewarm_s:
+        for v in variants:
+            v.graph.replay()
+        torch.cuda.synchronize()
+    clock_before = gpu_clock_state()
+    stream = torch.cuda.current_stream(dev)
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = len(variants)
+    for s in range(args.steps):
+        order = variants[s % n:] + variants[:s % n]
+        if s % 2:
+            order = order[::-1]
+        for v in order:
+            v.graph.replay()  # warm-up replay of the sample
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            v.graph.replay()
+            e1.record(stream)
+            events.append((v, s, e0, e1))
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    clock_after = gpu_clock_state()
+    per_sample = {}
+    for v, s, e0, e1 in events:
+        us = e0.elapsed_time(e1) * 1000.0 / 5
+        v.samples.append(us)
+        per_sample[(v.name, s)] = us
+    # every graph replay wrote what the eager calls wrote
+    for v in variants:
+        if v.ref_group is None:
+            continue
+        for i in range(5):
+            if not torch.equal(v.outs[i].view(iv), refs[v.ref_group].view(iv)):
+                raise RuntimeError(f"graph replay of {v.name} (output {i}) differs from the eager call")
+    stats = {v.name: {"median_us": round(statistics.median(v.samples), 2), "p10_us": round(_pct(v.samples, 10), 2),
+                      "p90_us": round(_pct(v.samples, 90), 2), "samples": len(v.samples)} for v in variants}
+    kernel_above_call = sum(1 for s in range(args.steps)
+                            if per_sample[("kernel", s)] > per_sample[("call_planned", s)])
+
+    V = visible_cells(lib, wl, plan)
     flops = 2.0 * wl.H * wl.D * V  # 2 H D per visible cell
     peak = PEAK_TFLOPS[wl.fmt]
+    us_call = stats["call"]["median_us"]
+    kern_us = stats["kernel"]["median_us"]
     rec = counted_traffic(wl.name, wl.fmt)
     traffic = None if rec is None else rec["fetch_bytes"] + rec["write_bytes"]
     achieved = flops / (kern_us * 1e-6) / 1e12
@@ -476,9 +597,10 @@ def main():
     # below the machine balance (peak FLOP/s per HBM byte/s), else the MFMA peak
     hbm_bound = flops / alg_bytes < peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     gbs = alg_bytes / (kern_us * 1e-6) / 1e9
+    tflops = lambda us: round(flops / (us * 1e-6) / 1e12, 1)
     res = {
         "metric": METRIC,
-        "value": round(us_call, 2),
+        "value": us_call,
         "unit": "µs/call",
         "n_gpus": 1,
         "steps": args.steps,
@@ -491,9 +613,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "S_q": wl.S_q, "S_k": wl.S_k, "H": wl.H, "D": wl.D,
                    "in_dtype": wl.fmt, "w_dtype": wl.w_dtype, "out_dtype": wl.out_dtype,
-                   "clean_logits": wl.clean, "visible_cells": V, "plan": "built in every step",
+                   "clean_logits": wl.clean, "visible_cells": V, "plan": "built inside the call (metadata no)",
                    "inputs": f"seeded random (seed {wl.seed})"},
-        "eff_tflops": round(flops / (us_call * 1e-6) / 1e12, 1),
+        "timing": {"protocol": ("5 eager calls" if args.eager else "HIP graph of 5 calls") +
+                               " into 5 distinct outputs per variant; per sample one warm and "
+                               "one event-timed replay of every variant, order rotating and reversing; /5",
+                   "variants": stats, "kernel_above_planned_call_samples": kernel_above_call,
+                   "wall_s_of_samples": round(wall_s, 3), "clock_before": clock_before, "clock_after": clock_after},
+        "eff_tflops": tflops(us_call),
+        "eff_tflops_planned": tflops(stats["call_planned"]["median_us"]),
         "out_gbs": round(out_bytes(wl, V) / (us_call * 1e-6) / 1e9, 1),
         "roofline": dict(
             ({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -501,28 +629,46 @@ def main():
               "mfma_frac": round(achieved / peak, 4)} if hbm_bound else
              {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
               "frac": round(achieved / peak, 4)}),
-            traffic=traffic, kernel="score_kernel", kernel_us=round(kern_us, 2), flop_per_launch=flops,
-            algorithmic_bytes_per_launch=alg_bytes),
+            traffic=traffic, kernel="score_kernel", kernel_us=kern_us, flop_per_launch=flops,
+            algorithmic_bytes_per_launch=alg_bytes,
+            call_frac=round(flops / (us_call * 1e-6) / 1e12 / peak, 4)),
     }
-    if getattr(wl, "thd", None) is not None:
+    if thd:
         cq = [int(x) for x in wl.thd["cu_q"]]
         res["config"]["thd"] = {"segments": len(cq) - 1, "seg_lens": [b - a for a, b in zip(cq, cq[1:])],
                                 "ratio": wl.thd["ratio"], "m_total": wl.S_k}
-        res["config"]["plan"] = "idx_logits_plan_thd in every step"
-    if getattr(wl, "paged", None) is not None:
+        res["config"]["plan"] = "idx_logits_plan_thd inside the timed call"
+    if paged:
         pg = wl.paged
         res["config"]["paged"] = {"page_size": pg["page_size"], "num_pages": int(pg["k_cache"].shape[0]),
                                   "max_pages": int(np.asarray(pg["block_table"]).shape[1]),
                                   "context_keys": int(np.clip(np.asarray(pg["ctx"], np.int64), 0, wl.S_k).sum())}
-        res["config"]["plan"] = "built in every step from the context lengths"
-    zero_name = args.workload + "_zero"
-    if not args.no_zero_variant and zero_name in W.NAMED:
-        zwl, zV, zus, zk, _ = measure(zero_name)
-        res["zero_inputs"] = {"workload": zwl.name, "us_per_call": round(zus, 2), "kernel_us": round(zk, 2),
+        res["config"]["plan"] = "built inside the call from the context lengths"
+    if zwl is not None:
+        zus = stats["zero_call"]["median_us"]
+        res["zero_inputs"] = {"workload": zwl.name, "call_us": zus, "call_planned_us": stats["zero_call_planned"]["median_us"],
+                              "kernel_us": stats["zero_kernel"]["median_us"],
                               "pages_us_gb200": PAGES_US.get(zero_name),
                               "ratio_to_pages": round(zus / PAGES_US[zero_name], 3) if zero_name in PAGES_US else None}
-    if topk is not None:
-        res["topk"] = topk
+    if exact:
+        xus = stats["call_exact_accumulation"]["median_us"]
+        res["exact_accumulation"] = {"call_us": xus, "eff_tflops": tflops(xus),
+                                     "frac_of_bf16_peak": round(flops / (xus * 1e-6) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+    if args.topk:
+        k = args.topk
+        t_us = stats[f"topk{k}"]["median_us"]
+        # algorithmic bytes: every window score read once, k (index, score) pairs written per row
+        read = (2 if odt == torch.bfloat16 else 4) * V
+        written = 8 * wl.B * wl.S_q * k
+        tg = (read + written) / (t_us * 1e-6) / 1e9
+        trec = counted_traffic(f"topk{k}:{wl.name}", "topk")
+        res["topk"] = {"k": k, "order": "column", "kernel": "topk_kernel", "kernel_us": t_us,
+                       "roofline": {"bound": "hbm", "achieved": round(tg, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(tg / HBM_PEAK_GBS, 4),
+                                    "traffic": None if trec is None else trec["fetch_bytes"] + trec["write_bytes"],
+                                    "algorithmic_bytes_per_launch": read + written}}
+    del variants, keep
+    torch.cuda.empty_cache()
     if not args.no_peaks:
         pk = measure_peaks(dev)
         if pk is not None and res["roofline"]["bound"] == "mfma" and wl.H == 64:

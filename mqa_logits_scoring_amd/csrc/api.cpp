@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "internal.h"
@@ -41,43 +42,51 @@ idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t 
   return IDX_OK;
 }
 
-// Work split: every tile's coverage is cut on the device into n_chunks equal
-// chunks of at least kMinChunk columns, one compute unit each.  Each unit
-// loads its rows' whole Q before its first MFMA, so units should be long; but
-// the chip needs enough of them (kTargetUnits) to stay fed, and tiles of very
-// different coverage (irregular windows) balance only when no unit is much
-// longer than kChunkCols.  When a tile has 8 or more chunks of a long key
-// range, their count is a multiple of 8 and chunk c of every tile runs on XCD
-// c % 8, so each XCD keeps its slice of K in its own L2.  A tile with 4 to 7
-// chunks keeps that count (the Q2048 / KV32768 calls: 4 chunks of about 8k
-// columns ran 0.8 % faster than 8 XCD-owned ones, half as many Q loads).
-struct Split {
-  int32_t min_chunk, n_chunks, xcd;
-};
-constexpr int64_t kTargetUnits = 1024;  // 4 per CU
+// Work split (ScoreArgs): every tile's coverage is cut on the device into
+// n_chunk equal chunks of at least kMinChunk columns, one unit each.  Each
+// unit loads its rows' whole Q before its first MFMA, so units should be
+// long; but the resident workgroups need enough of them (about four per CU)
+// to stay fed, and tiles of very different coverage (irregular windows)
+// balance only when no unit is much longer than kChunkCols.
+constexpr int64_t kUnitsPerCu = 4;
 constexpr int64_t kChunkCols = 8192;
 constexpr int64_t kMinChunk = 256;
+// CUs the split is sized against in host-side bounds (more than any device has).
+constexpr int64_t kMaxCus = 4096;
+
+int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
+
 // S_q and tile_rows: when a batch has fewer query rows than a tile, the waves
-// holding only padding rows leave at once, so more units keep the CUs fed.
-Split pick_split(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows) {
+// holding only padding rows idle, so more units keep the CUs fed.
+int32_t pick_chunks(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows, int64_t cus) {
   const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
-  Split sp{};
   const int64_t rows_per_wave = tile_rows / 4;
   const int64_t rows = S_q < tile_rows ? S_q : tile_rows;
-  const int64_t active = (rows + rows_per_wave - 1) / rows_per_wave;  // waves of a tile with a real row
-  const int64_t target = kTargetUnits * 4 / active;
-  int64_t want = (target + n_tiles - 1) / n_tiles;  // chunks per tile
-  const int64_t by_len = (span + kChunkCols - 1) / kChunkCols;
-  want = want > by_len ? want : by_len;
-  const int64_t most = (span + kMinChunk - 1) / kMinChunk;
-  want = want > most ? most : want;
-  if (span >= 8 * 1024 && want >= 8) {
-    want = (want + 7) / 8 * 8;
-    sp.xcd = 1;
+  const int64_t active = cdiv(rows, rows_per_wave);  // waves of a tile with a real row
+  const int64_t target = kUnitsPerCu * cus * 4 / active;
+  int64_t want = std::max(cdiv(target, n_tiles), cdiv(span, kChunkCols));
+  want = std::min(want, cdiv(span, kMinChunk));
+  return int32_t(std::max<int64_t>(want, 1));
+}
+
+// Work positions: every chunk of every tile, then one cleanup unit per tile.
+int64_t positions_of(const idx::PlanLayout& L, int64_t n_chunk) { return L.n_tiles * (n_chunk + 1); }
+
+// CUs of the current device, looked up once per device.
+hipError_t device_cus(int& cus) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  if (cache[dev] == 0) {
+    int c = 0;
+    if ((e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    cache[dev] = c > 0 ? c : 1;
   }
-  sp.n_chunks = int32_t(want);
-  sp.min_chunk = int32_t(kMinChunk);
-  return sp;
+  cus = cache[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -197,8 +206,8 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
     return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
-  const int64_t n_compute = int64_t(pick_split(a->S_k, L.n_tiles, a->S_q, L.tile_rows).n_chunks) * L.n_tiles;
-  if (n_compute + L.n_tiles > (int64_t(1) << 31) - 1) return fail(IDX_E_INVALID, "problem too large for one grid");
+  if (positions_of(L, pick_chunks(a->S_k, L.n_tiles, a->S_q, L.tile_rows, kMaxCus)) > (int64_t(1) << 31) - 1)
+    return fail(IDX_E_INVALID, "problem too large for one grid");
   return IDX_OK;
 }
 
@@ -291,16 +300,22 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.H = a->H;
   k.tile_rows = L.tile_rows;
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q, L.tile_rows));
-  const Split sp = pick_split(a->S_k, L.n_tiles, a->S_q, L.tile_rows);
-  k.min_chunk = sp.min_chunk;
-  k.n_chunks = sp.n_chunks;
-  k.xcd_chunks = sp.xcd;
-  k.n_compute = int32_t(int64_t(k.n_chunks) * L.n_tiles);  // bounded by check_args
+  int cus = 0;
+  hipError_t he = device_cus(cus);
+  if (he != hipSuccess) return fail(IDX_E_HIP, "device query failed: %s", hipGetErrorString(he));
+  k.min_chunk = int32_t(kMinChunk);
+  k.n_chunk = pick_chunks(a->S_k, L.n_tiles, a->S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus));
+  k.seg_per_batch = int32_t(L.n_seg / a->B);
+  k.tiles_per_seg = L.tiles_per_seg;
+  k.last_seg_tiles = int32_t(k.tiles_per_batch - (k.seg_per_batch - 1) * int64_t(L.tiles_per_seg));
+  k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
+  k.n_positions = int32_t(positions_of(L, k.n_chunk));
   k.off_start = uint32_t(L.off_start);
   k.off_end = uint32_t(L.off_end);
   k.off_slot = uint32_t(L.off_slot);
   k.off_lo = uint32_t(L.off_lo);
   k.off_hi = uint32_t(L.off_hi);
+  k.off_order = uint32_t(L.off_order);
   k.pieces = idx::uses_pieces(x.kf, a->H) ? ws + WL.off_pieces : nullptr;
   k.pscales = idx::uses_pieces(x.kf, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;

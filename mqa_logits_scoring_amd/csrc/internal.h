@@ -23,6 +23,11 @@ namespace idx {
 //                                   rows with alike windows share tiles
 //   int32 tile_lo[n_tiles]          first column computed for the tile
 //   int32 tile_hi[n_tiles]          one past the last column computed
+//   int32 tile_order[n_seg*tps]     per sort segment g (tps = kSortRows /
+//                                   tile_rows slots each), the segment's
+//                                   tiles by descending cost (covered columns
+//                                   x rows), then -1 for the missing tiles of
+//                                   a batch's last, partial segment
 //
 // A tile is tile_rows consecutive slots of one batch.  [tile_lo,
 // tile_hi) is the union of its rows' windows widened to kColAlign columns
@@ -50,9 +55,9 @@ struct PlanHeader {
 static_assert(sizeof(PlanHeader) == 256, "plan header is one 256-byte section");
 
 struct PlanLayout {
-  size_t off_start, off_end, off_slot, off_lo, off_hi, total;
-  int64_t n_rows, n_tiles;
-  int32_t tile_rows;
+  size_t off_start, off_end, off_slot, off_lo, off_hi, off_order, total;
+  int64_t n_rows, n_tiles, n_seg;
+  int32_t tile_rows, tiles_per_seg;
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -86,6 +91,10 @@ inline PlanLayout plan_layout(int64_t B, int64_t S_q, int H) {
   off += align256(size_t(L.n_tiles) * 4);
   L.off_hi = off;
   off += align256(size_t(L.n_tiles) * 4);
+  L.n_seg = plan_segments(B, S_q);
+  L.tiles_per_seg = kSortRows / L.tile_rows;
+  L.off_order = off;
+  off += align256(size_t(L.n_seg) * L.tiles_per_seg * 4);
   L.total = off;
   return L;
 }
@@ -263,12 +272,22 @@ struct ScoreArgs {
   float sm_scale;
   int32_t B, S_q, S_k, H;
   int32_t n_tiles, tiles_per_batch, tile_rows;
-  int32_t min_chunk;     // fewest columns per compute unit (multiple of 64)
-  int32_t n_chunks;      // compute units per tile: its coverage in n_chunks equal
-                         // parts of at least min_chunk columns (upper bound)
-  int32_t n_compute;     // n_tiles * n_chunks
-  int32_t xcd_chunks;    // 1: n_chunks % 8 == 0 and chunk c runs on XCD c % 8
-  uint32_t off_start, off_end, off_slot, off_lo, off_hi;
+  // Work positions, one per workgroup (blockIdx.x), which the hardware
+  // deals out in order:
+  //   [0, n_pos_compute)          chunk p % n_chunk of slot p / n_chunk
+  //   [n_pos_compute, n_positions) cleanup of tile p - n_pos_compute
+  // Slots walk the plan's tiles from the last batch to the first, each
+  // batch's sort segments from its last to its first (its last segment
+  // holds last_seg_tiles tiles, the others tiles_per_seg), and each segment's
+  // tiles in the plan's cost order: costliest first globally under causal
+  // windows (later rows see more keys), and in every segment otherwise, so
+  // the work dealt out last is short.  A tile's coverage [lo, hi)
+  // is cut into n_chunk equal chunks, multiples of 64 columns and at least
+  // min_chunk wide.
+  int32_t min_chunk, n_chunk;
+  int32_t seg_per_batch, tiles_per_seg, last_seg_tiles;
+  int32_t n_pos_compute, n_positions;
+  uint32_t off_start, off_end, off_slot, off_lo, off_hi, off_order;
   const unsigned char* pieces;   // per row PieceFmt<F>::N pieces of PieceFmt<F>::BYTES (formats with pieces)
   const uint32_t* pscales;       // per row PieceFmt<F>::SLOTS E8M0 words
   const unsigned char* kfrag;    // K in fragment order, [B][ceil(S_k/32)][32 * ROWB]
@@ -323,8 +342,8 @@ struct PagedK {
 hipError_t launch_prepare(idx_in_t fmt, bool convert, int H, idx_fp_t w_dtype, const void* k, const void* k_scale,
                           int64_t B, int64_t S_k, unsigned char* kfrag, uint32_t* kscale, const void* q,
                           const void* q_scale, const void* w, int64_t n_rows, unsigned char* pieces,
-                          uint32_t* pscales, uint16_t* qconv, const PlanBuild* build, const PagedK* paged,
-                          hipStream_t stream);
+                          uint32_t* pscales, uint16_t* qconv, const PlanBuild* build,
+                          const PagedK* paged, hipStream_t stream);
 // Top-k selection over the scores a call wrote (topk.hip): for each of the
 // plan's rows, the k <= kMaxTopK best columns of its window, by column or in
 // rank order.

@@ -69,16 +69,37 @@ __device__ inline void thd_window(const PlanParams& P, int64_t i, int64_t& s, in
 // Shared memory one segment needs (8-byte aligned).
 struct PlanSmem {
   uint64_t key[kSortRows];
+  uint64_t tkey[kSortRows / 8];  // tiles of the segment by cost (tiles hold at least 8 rows)
   int32_t win_s[kSortRows], win_e[kSortRows];
   int unsorted;
 };
+
+// Ascending bitonic sort of n = 2^k keys in LDS by a whole workgroup.
+__device__ inline void bitonic_sort(uint64_t* key, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < n / 2; t += kSortThreads) {
+        const int lo = 2 * stride * (t / stride) + (t % stride);  // bit `stride` of lo is clear
+        const int hi = lo + stride;
+        const bool ascending = (lo & size) == 0;
+        const uint64_t x = key[lo], y = key[hi];
+        if ((x > y) == ascending) {
+          key[lo] = y;
+          key[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
 
 // One segment of the plan, by one workgroup of kSortThreads threads: the
 // segment's kSortRows consecutive rows of a batch (segments hold whole tiles).
 // It computes the rows' windows, orders the rows (with explicit windows: a
 // bitonic sort by (order_key, row) in LDS), writes the slot rows and then the
-// coverage of the segment's tiles from the windows it keeps in LDS.  Segment
-// 0 also writes the header.
+// coverage of the segment's tiles from the windows it keeps in LDS, and
+// last the segment's tiles ordered by cost (covered columns x rows,
+// descending; ties by tile).  Segment 0 also writes the header.
 __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSmem& sm) {
   const int32_t B = P.B, S_q = P.S_q, S_k = P.S_k, H = P.H, D = P.D;
   const int32_t *offsets = P.offsets, *starts = P.starts, *ends = P.ends;
@@ -161,23 +182,7 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
     for (int r = threadIdx.x + 1; r < n; r += kSortThreads)
       if (key[r - 1] > key[r]) unsorted = 1;
     __syncthreads();
-    if (unsorted) {
-      for (int size = 2; size <= np2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          for (int t = threadIdx.x; t < np2 / 2; t += kSortThreads) {
-            const int lo = 2 * stride * (t / stride) + (t % stride);  // bit `stride` of lo is clear
-            const int hi = lo + stride;
-            const bool ascending = (lo & size) == 0;
-            const uint64_t x = key[lo], y = key[hi];
-            if ((x > y) == ascending) {
-              key[lo] = y;
-              key[hi] = x;
-            }
-          }
-          __syncthreads();
-        }
-      }
-    }
+    if (unsorted) bitonic_sort(key, np2);
   }
   // slot rows (the key's low word is the row's index in the segment; padding
   // keys are all ones and sort last)
@@ -191,8 +196,12 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
   // coverage of the segment's tiles: the union of their rows' windows
   // widened to kColAlign columns (0, 0 when every row is empty)
   const int n_tiles_seg = (n + TR - 1) / TR;
+  const int tps = kSortRows / TR;  // tile slots of a full segment, a power of two
+  for (int t = threadIdx.x; t < tps; t += kSortThreads) sm.tkey[t] = ~uint64_t(0);
+  __syncthreads();
   for (int t = threadIdx.x; t < n_tiles_seg; t += kSortThreads) {
     int64_t lo = S_k, hi = 0;
+    const int rows = min(TR, n - t * TR);
     for (int r = t * TR; r < t * TR + TR && r < n; ++r) {
       const int local = explicit_windows ? int(uint32_t(key[r])) : r;
       const int64_t s = win_s[local], e = win_e[local];
@@ -212,7 +221,16 @@ __device__ inline void plan_segment(const PlanParams& P, int64_t segment, PlanSm
     const int64_t tile = b * tpb + i0 / TR + t;
     tile_lo[tile] = int32_t(lo);
     tile_hi[tile] = int32_t(hi);
+    // cost below 2^37 (2^31 columns x 64 rows): the key's top bits order by
+    // descending cost, its low bits by tile
+    const uint64_t cost = uint64_t(hi - lo) * uint64_t(rows);
+    sm.tkey[t] = ((uint64_t(1) << 37) - 1 - cost) << 16 | uint64_t(t);
   }
+  __syncthreads();
+  bitonic_sort(sm.tkey, tps);
+  int32_t* order = reinterpret_cast<int32_t*>(plan + L.off_order) + segment * tps;
+  for (int r = threadIdx.x; r < tps; r += kSortThreads)
+    order[r] = r < n_tiles_seg ? int32_t(b * tpb + i0 / TR + int64_t(sm.tkey[r] & 0xFFFFu)) : -1;
 }
 
 }  // namespace idx

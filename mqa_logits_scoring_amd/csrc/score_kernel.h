@@ -178,30 +178,40 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
   }
 }
 
-// The tile and key columns [c0, c1) of compute unit `bid`; false when the
-// unit has no columns.  Workgroups are dealt to the 8 XCDs round-robin
-// (bid % 8).  When the chunk count is a multiple of 8, XCD x only ever gets
-// chunks x, x+8, ... so its slice of K stays in its own L2; consecutive units
-// of one XCD share a tile so that tile's Q is fetched once per XCD.  Longest
-// tiles go first: under causal windows the last rows see the most keys.  The
-// tile's coverage is cut in n_chunks equal parts (multiples of 64 columns, at
-// least min_chunk), so every unit of a tile gets the same amount of work.
-__device__ __forceinline__ bool unit_columns(const ScoreArgs& a, int bid, int& tile, int& c0, int& c1) {
-  int chunk;
-  if (a.xcd_chunks) {
-    const int x = bid & 7, i = bid >> 3, cpx = a.n_chunks >> 3;
-    tile = a.n_tiles - 1 - i / cpx;
-    chunk = x + 8 * (i % cpx);
+// A unit of work: compute (a tile's columns [c0, c1)), cleanup (a tile's
+// cells outside its coverage) or nothing (a missing tile of a partial
+// segment, or a chunk past the tile's coverage).
+enum { kUnitNone = 0, kUnitCompute = 1, kUnitCleanup = 2 };
+struct Unit {
+  int kind, tile, c0, c1;
+};
+
+// Work position p (ScoreArgs) -> unit.
+__device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
+  if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0};
+  const int slot = p / a.n_chunk, chunk = p - slot * a.n_chunk;
+  // slot -> (batch, segment, rank): batches and segments from the last
+  const int tpb = a.tiles_per_batch, spb = a.seg_per_batch, tps = a.tiles_per_seg, last = a.last_seg_tiles;
+  const int j = slot / tpb, r = slot - j * tpb;
+  const int b = a.B - 1 - j;
+  int seg, rank;
+  if (r < last) {
+    seg = spb - 1;
+    rank = r;
   } else {
-    tile = a.n_tiles - 1 - bid / a.n_chunks;
-    chunk = bid % a.n_chunks;
+    const int r2 = r - last;
+    seg = spb - 2 - r2 / tps;
+    rank = r2 - (r2 / tps) * tps;
   }
+  const int tile =
+      reinterpret_cast<const int32_t*>(a.plan + a.off_order)[(int64_t(b) * spb + seg) * tps + rank];
+  if (tile < 0) return Unit{kUnitNone, 0, 0, 0};
   const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
   const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
-  const int ccols = max(a.min_chunk, ((hi - lo + a.n_chunks - 1) / a.n_chunks + 63) & ~63);
-  c0 = lo + chunk * ccols;
-  c1 = min(hi, c0 + ccols);
-  return c0 < hi;
+  const int w = max(a.min_chunk, ((hi - lo + a.n_chunk - 1) / a.n_chunk + 63) & ~63);
+  const int c0 = lo + chunk * w, c1 = min(hi, c0 + w);
+  if (c0 >= c1) return Unit{kUnitNone, 0, 0, 0};
+  return Unit{kUnitCompute, tile, c0, c1};
 }
 
 // Waves per SIMD the kernel is built for: the FP8-family and FP4 kernels fit in
@@ -240,15 +250,16 @@ __global__ void __launch_bounds__(kThreads)
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
                        hdr->H == 64 && hdr->D == 128 && hdr->tile_rows == kTileRows && hdr->n_tiles == a.n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= a.n_compute) {
-    cleanup_unit<OBF, CLEAN, kTileRows>(a, bid - a.n_compute, plan_ok);
+  // one work position per workgroup, dealt in order by the hardware
+  const int pos = int(blockIdx.x);
+  if (pos >= a.n_pos_compute) {
+    cleanup_unit<OBF, CLEAN, kTileRows>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
   if (!plan_ok) return;
-
-  int tile, c0, c1;
-  if (!unit_columns(a, bid, tile, c0, c1)) return;  // columns [c0, c1) of the tile are this unit's
+  const Unit u = decode_unit(a, pos);
+  if (u.kind != kUnitCompute) return;
+  const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
 
@@ -264,7 +275,7 @@ __global__ void __launch_bounds__(kThreads)
     rows[t] = r >= 0 ? r : first_row;
   }
   // a wave with padding rows only (short tiles, e.g. two-token decode) has
-  // nothing to store; the kernel has no barrier, so it can leave
+  // nothing to store in this unit
   if (!rvalid[0] && !rvalid[1]) return;
 
   // Q fragments of head 32*mb + c for both rows, and their MX scale words
@@ -701,15 +712,16 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
                        hdr->H == 64 && hdr->D == 128 && hdr->tile_rows == kTileRows && hdr->n_tiles == a.n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= a.n_compute) {
-    cleanup_unit<OBF, CLEAN, kTileRows>(a, bid - a.n_compute, plan_ok);
+  // one work position per workgroup, dealt in order by the hardware
+  const int pos = int(blockIdx.x);
+  if (pos >= a.n_pos_compute) {
+    cleanup_unit<OBF, CLEAN, kTileRows>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
   if (!plan_ok) return;
-
-  int tile, c0, c1;
-  if (!unit_columns(a, bid, tile, c0, c1)) return;
+  const Unit u = decode_unit(a, pos);
+  if (u.kind != kUnitCompute) return;
+  const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;
   const int b = tile / a.tiles_per_batch;
 
@@ -984,26 +996,26 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   store(combine(p[1], lin[1], kblk[1]), 2 * n_iter - 1);
 }
 
+// One launch of `kernel`: a workgroup per work position.
+template <typename K>
+hipError_t launch_units(K kernel, const ScoreArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(kernel, dim3(unsigned(a.n_positions)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int F, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
-  const int64_t grid = int64_t(a.n_compute) + a.n_tiles;
   const bool pd = a.kcache != nullptr;
   if constexpr (F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3) {
-    if (pd)
-      hipLaunchKernelGGL((score_kernel_x16<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                         a);
-    else
-      hipLaunchKernelGGL((score_kernel_x16<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0,
-                         stream, a);
+    if (pd) return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, true>, a, stream);
+    return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, false>, a, stream);
   } else if (pd) {
     if constexpr (F == kInBF16RowScale) return hipErrorInvalidValue;  // converted keys are never read from a cache
     else
-      hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, true>), dim3(unsigned(grid)), dim3(kThreads), 0, stream,
-                         a);
+      return launch_units(score_kernel<F, WBF, OBF, CLEAN, true>, a, stream);
   } else {
-    hipLaunchKernelGGL((score_kernel<F, WBF, OBF, CLEAN, false>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+    return launch_units(score_kernel<F, WBF, OBF, CLEAN, false>, a, stream);
   }
-  return hipGetLastError();
 }
 
 }  // namespace idx

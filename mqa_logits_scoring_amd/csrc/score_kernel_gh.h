@@ -52,14 +52,16 @@ __global__ void __launch_bounds__(kThreads)
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
   const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
                        hdr->H == H && hdr->D == 128 && hdr->tile_rows == TR && hdr->n_tiles == a.n_tiles;
-  const int bid = blockIdx.x;
-  if (bid >= a.n_compute) {
-    cleanup_unit<OBF, CLEAN, TR>(a, bid - a.n_compute, plan_ok);
+  // one work position per workgroup, dealt in order by the hardware
+  const int pos = int(blockIdx.x);
+  if (pos >= a.n_pos_compute) {
+    cleanup_unit<OBF, CLEAN, TR>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
   if (!plan_ok) return;
-  int tile, c0, c1;
-  if (!unit_columns(a, bid, tile, c0, c1)) return;  // columns [c0, c1) of the tile are this unit's
+  const Unit u = decode_unit(a, pos);
+  if (u.kind != kUnitCompute) return;
+  const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;
   const int b = tile / a.tiles_per_batch;
 
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(kThreads)
   bool any_row = false;
 #pragma unroll
   for (int t = 0; t < WR; ++t) any_row = any_row || rvalid[t];
-  if (!any_row) return;  // padding rows only: nothing to store, and no barrier to meet
+  if (!any_row) return;  // padding rows only: nothing to store in this unit
 
   // Q fragments: block j, M row c = (query row j*RPB + c/H, head c%H); the
   // row differs between lanes when H < 32, so its index is read per lane
@@ -308,9 +310,7 @@ __global__ void __launch_bounds__(kThreads)
 
 template <int F, int H, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_gh_t(const ScoreArgs& a, hipStream_t stream) {
-  const int64_t grid = int64_t(a.n_compute) + a.n_tiles;
-  hipLaunchKernelGGL((score_kernel_gh<F, H, WBF, OBF, CLEAN>), dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_units(score_kernel_gh<F, H, WBF, OBF, CLEAN>, a, stream);
 }
 
 // Every weight type x output type x clean flag of one format and head count.
