@@ -300,6 +300,9 @@ def gpu_clock_state() -> dict:
     """amd-smi's view of GPU 0's clocks and power (best effort: a missing tool
     or an unknown output layout is reported, not raised)."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        # under a profiler the tool's preload would start with the child
+        return {"skipped": "running under a profiler"}
     try:
         r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"], capture_output=True,
                            text=True, timeout=30)
