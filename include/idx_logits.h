@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define IDX_ABI_VERSION 2
+#define IDX_ABI_VERSION 3
 
 typedef enum {
   IDX_OK = 0,
@@ -391,6 +391,44 @@ typedef enum { IDX_TOPK_BY_COLUMN = 0, IDX_TOPK_BY_SCORE = 1 } idx_topk_order_t;
 idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
                              const void* logits, idx_fp_t logits_dtype, int64_t ld, int32_t k, idx_topk_order_t order,
                              int32_t* topk_idx, float* topk_val, void* stream);
+
+/*
+ * Scoring and top-k selection in one call, without the S_q x S_k score
+ * matrix: the per-query key list of the sparse-attention page (FlashInfer
+ * SM120 sparse MLA, Summary) straight from Q, K and W, where the DeepGEMM
+ * pull request 435 page (Performance section) times the "uncompressed"
+ * logits a separate selection would read.  The result is exactly that of
+ * idx_logits_run (same a, plan or windows) followed by idx_logits_topk on its
+ * scores with the same k and order: the scores are ranked as a->out_dtype
+ * stores them (IDX_BF16: rounded to bf16), ties and NaN as idx_logits_topk
+ * ranks them.  a->out, a->out_row_stride and a->clean_logits are not used
+ * (out may be NULL); plan / q_causal_offsets / row_starts / row_ends as for
+ * idx_logits_run.
+ *
+ * How (the pages give no selection algorithm; this one is the library's):
+ * the call first scores a sample, every 16th block of 32 keys, and takes
+ * per row a threshold just below the scores the selection is likely to
+ * need; scoring then keeps, per row, only the window's cells at or above it
+ * (about 1.5 k of them) in the workspace, and the selection runs over those.
+ * A row left with fewer than min(k, window) cells, which the sample can make
+ * happen but never changes the result, is scored again keeping its whole
+ * window.
+ *  k, order, topk_idx, topk_val as for idx_logits_topk (topk_val may be NULL).
+ *  n_redo       device int32 or NULL: receives the number of rows scored
+ *               twice.
+ *  workspace    device memory of idx_logits_topk_workspace_bytes(a) bytes,
+ *               256-byte aligned (it holds the call's candidates: about
+ *               8 * B * S_q * S_k bytes, reserved but mostly untouched).
+ * Errors as for idx_logits_run, plus IDX_E_UNSUPPORTED for k outside
+ * [1, 2048].  Calls on one stream may share a workspace; calls that overlap
+ * must not.
+ */
+size_t idx_logits_topk_workspace_bytes(const idx_logits_args_t* a);
+
+idx_status_t idx_logits_run_topk(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                                 const int32_t* row_starts, const int32_t* row_ends, int32_t k,
+                                 idx_topk_order_t order, int32_t* topk_idx, float* topk_val, int32_t* n_redo,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Copy the windows stored in a plan into caller device arrays

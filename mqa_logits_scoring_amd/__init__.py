@@ -24,11 +24,11 @@ IN_DTYPES = {"bf16": 0, "fp8": 1, "mxfp8": 2, "mxfp4": 3}
 # idx_accum_t: "native" (the input format's matrix core) or "fp32" (exact
 # products, fp32 sums, for every input)
 ACCUM = {"native": 0, "fp32": 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 FP_DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 EXPORTED = ("idx_abi_version", "idx_logits_plan_bytes", "idx_logits_plan", "idx_logits_plan_thd",
             "idx_logits_plan_paged", "idx_logits_prepare_paged", "idx_logits_run_paged", "idx_logits_score_paged",
-            "idx_logits_topk",
+            "idx_logits_topk", "idx_logits_topk_workspace_bytes", "idx_logits_run_topk",
             "idx_logits_workspace_bytes", "idx_logits_workspace_bytes_planned",
             "idx_logits_run", "idx_logits_run_noalloc", "idx_logits_noalloc_scratch_bytes", "idx_logits_prepare", "idx_logits_score", "idx_logits_plan_windows", "idx_last_error")
 
@@ -89,6 +89,11 @@ def lib() -> ctypes.CDLL:
         L.idx_logits_score_paged.argtypes = [ctypes.POINTER(IdxLogitsArgs), ctypes.POINTER(IdxPagedK), P, P, SZ, P]
         L.idx_logits_topk.restype = ctypes.c_int
         L.idx_logits_topk.argtypes = [P] + [I32] * 5 + [P, ctypes.c_int, ctypes.c_int64, I32, ctypes.c_int, P, P, P]
+        L.idx_logits_topk_workspace_bytes.restype = SZ
+        L.idx_logits_topk_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
+        L.idx_logits_run_topk.restype = ctypes.c_int
+        L.idx_logits_run_topk.argtypes = [ctypes.POINTER(IdxLogitsArgs), P, P, P, P, I32, ctypes.c_int, P, P, P, P,
+                                          SZ, P]
         L.idx_logits_workspace_bytes.restype = SZ
         L.idx_logits_workspace_bytes.argtypes = [ctypes.POINTER(IdxLogitsArgs)]
         L.idx_logits_workspace_bytes_planned.restype = SZ
@@ -203,12 +208,16 @@ def _shape_info(q: torch.Tensor, k: torch.Tensor, in_dtype: str):
     return q, k, B, S_q, k.shape[1], H, D
 
 
-def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, in_dtype: str,
+def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor], *, in_dtype: str,
               q_scale=None, k_scale=None, sm_scale: float = 1.0, clean_logits: bool = True,
-              accumulate: str = "native") -> IdxLogitsArgs:
-    """Fill an idx_logits_args_t from tensors (no copies, no checks beyond shapes)."""
+              accumulate: str = "native", out_dtype: Optional[torch.dtype] = None) -> IdxLogitsArgs:
+    """Fill an idx_logits_args_t from tensors (no copies, no checks beyond
+    shapes).  out may be None (fused top-k calls): out_dtype then gives the
+    precision the scores are ranked in."""
     q4, k3, B, S_q, S_k, H, D = _shape_info(q, k, in_dtype)
-    if out.dtype not in FP_DTYPES or w.dtype not in FP_DTYPES:
+    if out is not None:
+        out_dtype = out.dtype
+    if out_dtype not in FP_DTYPES or w.dtype not in FP_DTYPES:
         raise ValueError("w and out must be float32 or bfloat16")
     a = IdxLogitsArgs()
     a.B, a.S_q, a.S_k, a.H, a.D = B, S_q, S_k, H, D
@@ -216,9 +225,9 @@ def make_args(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, out: torch.Tens
     a.q, a.k, a.w, a.out = _ptr(q), _ptr(k), _ptr(w), _ptr(out)
     a.q_scale, a.k_scale = _ptr(q_scale), _ptr(k_scale)
     a.w_dtype = FP_DTYPES[w.dtype]
-    a.out_dtype = FP_DTYPES[out.dtype]
+    a.out_dtype = FP_DTYPES[out_dtype]
     a.sm_scale = float(sm_scale)
-    a.out_row_stride = out.stride(-2) if out.dim() >= 2 else S_k
+    a.out_row_stride = S_k if out is None else (out.stride(-2) if out.dim() >= 2 else S_k)
     a.clean_logits = 1 if clean_logits else 0
     a.accumulate = ACCUM[accumulate]
     return a
@@ -462,4 +471,46 @@ def idx_logits_topk(plan: torch.Tensor, logits: torch.Tensor, k: int, *, order: 
                                                       TOPK_ORDERS[order], _ptr(out_idx),
                                                       _ptr(out_val) if with_values else None,
                                                       _stream(stream, device)))
+    return out_idx, (out_val if with_values else None)
+
+
+def idx_logits_topk_workspace_bytes(args: IdxLogitsArgs) -> int:
+    return int(lib().idx_logits_topk_workspace_bytes(ctypes.byref(args)))
+
+
+def idx_logits_run_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, topk: int, *, in_dtype: str,
+                        q_scale=None, k_scale=None, sm_scale: float = 1.0, out_dtype: torch.dtype = torch.float32,
+                        order: str = "column", plan: Optional[torch.Tensor] = None, q_causal_offsets=None,
+                        row_starts=None, row_ends=None, workspace: Optional[torch.Tensor] = None,
+                        accumulate: str = "native", with_values: bool = True, out_idx: Optional[torch.Tensor] = None,
+                        out_val: Optional[torch.Tensor] = None, n_redo: Optional[torch.Tensor] = None, stream=None):
+    """Scoring and top-`topk` selection in one call, without the score
+    matrix: the result of idx_logits_run (scores in out_dtype) followed by
+    idx_logits_topk.  Returns (idx int32 [..., S_q, topk], val float32 or
+    None); n_redo, an int32 device tensor of one element, receives the number
+    of rows scored twice."""
+    for name, t in (("q", q), ("k", k), ("w", w), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    q4, k3, B, S_q, S_k, H, D = _shape_info(q, k, in_dtype)
+    device = q.device
+    args = make_args(q, k, w, None, in_dtype=in_dtype, q_scale=q_scale, k_scale=k_scale, sm_scale=sm_scale,
+                     clean_logits=False, accumulate=accumulate, out_dtype=out_dtype)
+    lead = (B, S_q) if q.dim() == 4 else (S_q,)
+    if out_idx is None:
+        out_idx = torch.empty(lead + (topk,), dtype=torch.int32, device=device)
+    if with_values and out_val is None:
+        out_val = torch.empty(lead + (topk,), dtype=torch.float32, device=device)
+    offs = st = en = None
+    if plan is None:
+        offs = _dev_i32(q_causal_offsets, device)
+        st = _dev_i32(row_starts, device)
+        en = _dev_i32(row_ends, device)
+    if workspace is None:
+        workspace = torch.empty(max(idx_logits_topk_workspace_bytes(args), 1), dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("idx_logits_run_topk",
+           lib().idx_logits_run_topk(ctypes.byref(args), _ptr(plan), _ptr(offs), _ptr(st), _ptr(en), int(topk),
+                                     TOPK_ORDERS[order], _ptr(out_idx), _ptr(out_val) if with_values else None,
+                                     _ptr(n_redo), _ptr(workspace), ws_bytes, _stream(stream, device)))
     return out_idx, (out_val if with_values else None)

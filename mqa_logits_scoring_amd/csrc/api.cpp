@@ -174,7 +174,9 @@ namespace {
 // With keys_elsewhere (paged calls, which take their keys from an
 // idx_paged_k_t, and scoring from a prepared workspace) a->k and a->k_scale
 // are not used.
-idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false) {
+// With no_out (fused top-k calls) a->out, out_row_stride and clean_logits
+// are not used.
+idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false, bool no_out = false) {
   if (a == nullptr) return fail(IDX_E_INVALID, "args is NULL");
   idx_status_t st = check_dims(a->B, a->S_q, a->S_k, a->H, a->D);
   if (st != IDX_OK) return st;
@@ -186,20 +188,25 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false)
   if (a->accumulate != IDX_ACCUM_NATIVE && a->accumulate != IDX_ACCUM_FP32)
     return fail(IDX_E_INVALID, "accumulate must be IDX_ACCUM_NATIVE or IDX_ACCUM_FP32 (got %d)", int(a->accumulate));
   const bool mx = f == IDX_IN_MXFP8_E4M3 || f == IDX_IN_MXFP4_E2M1;
-  if (a->q == nullptr || (!keys_elsewhere && a->k == nullptr) || a->w == nullptr || a->out == nullptr)
-    return fail(IDX_E_INVALID, "q, k, w and out must be non-NULL");
+  if (a->q == nullptr || (!keys_elsewhere && a->k == nullptr) || a->w == nullptr || (!no_out && a->out == nullptr))
+    return fail(IDX_E_INVALID, no_out ? "q, k and w must be non-NULL" : "q, k, w and out must be non-NULL");
   if (mx && a->q_scale == nullptr) return fail(IDX_E_INVALID, "MX formats need q_scale");
   if (!keys_elsewhere && (mx || f == IDX_IN_FP8_E4M3) && a->k_scale == nullptr)
     return fail(IDX_E_INVALID, "FP8 and MX formats need k_scale");
-  if (!aligned16(a->q) || (!keys_elsewhere && !aligned16(a->k)) || !aligned16(a->w) || !aligned16(a->out) ||
+  if (!aligned16(a->q) || (!keys_elsewhere && !aligned16(a->k)) || !aligned16(a->w) || (!no_out && !aligned16(a->out)) ||
       (mx && !aligned16(a->q_scale)) || (!keys_elsewhere && (mx || f == IDX_IN_FP8_E4M3) && !aligned16(a->k_scale)))
     return fail(IDX_E_INVALID, "q, k, w, out and scale pointers must be 16-byte aligned");
-  if (a->out_row_stride < a->S_k)
-    return fail(IDX_E_INVALID, "out_row_stride %lld < S_k %d", (long long)a->out_row_stride, a->S_k);
   const int64_t rows = int64_t(a->B) * a->S_q;
-  if (a->out_row_stride > (int64_t(1) << 40) || rows * a->out_row_stride > (int64_t(1) << 40))
-    return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
-                (long long)a->out_row_stride);
+  if (no_out) {
+    if (rows * a->S_k > (int64_t(1) << 40))
+      return fail(IDX_E_INVALID, "%lld rows x %d keys is too large", (long long)rows, a->S_k);
+  } else {
+    if (a->out_row_stride < a->S_k)
+      return fail(IDX_E_INVALID, "out_row_stride %lld < S_k %d", (long long)a->out_row_stride, a->S_k);
+    if (a->out_row_stride > (int64_t(1) << 40) || rows * a->out_row_stride > (int64_t(1) << 40))
+      return fail(IDX_E_INVALID, "output of %lld rows x stride %lld elements is too large", (long long)rows,
+                  (long long)a->out_row_stride);
+  }
   if (!isfinite(a->sm_scale)) return fail(IDX_E_INVALID, "sm_scale must be finite");
   const idx::Exec x = idx::exec_of(f, a->accumulate);
   if ((int64_t(a->S_k) + 31) / 32 * 32 * idx::row_bytes_of(x.kf) > (int64_t(1) << 31) - 1)
@@ -279,10 +286,21 @@ idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL,
   return IDX_OK;
 }
 
-// direct: a paged call whose scoring kernel reads the cache itself (see
-// direct_paged), else NULL.
-idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
-                   unsigned char* ws, hipStream_t s, const idx::PagedK* direct = nullptr) {
+// The unit grid of a scoring launch over S_k columns (ScoreArgs).
+idx_status_t set_units(idx::ScoreArgs& k, const idx::PlanLayout& L, int64_t S_k, bool cleanup) {
+  int cus = 0;
+  hipError_t he = device_cus(cus);
+  if (he != hipSuccess) return fail(IDX_E_HIP, "device query failed: %s", hipGetErrorString(he));
+  k.min_chunk = int32_t(kMinChunk);
+  k.n_chunk = pick_chunks(S_k, L.n_tiles, k.S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus));
+  k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
+  k.n_positions = cleanup ? int32_t(positions_of(L, k.n_chunk)) : k.n_pos_compute;
+  return IDX_OK;
+}
+
+// Arguments of a scoring launch of call a with plan p (units set by set_units).
+idx::ScoreArgs score_args(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
+                          unsigned char* ws) {
   const idx::Exec x = idx::exec_of(a->in_dtype, a->accumulate);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   idx::ScoreArgs k{};
@@ -300,16 +318,9 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.H = a->H;
   k.tile_rows = L.tile_rows;
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q, L.tile_rows));
-  int cus = 0;
-  hipError_t he = device_cus(cus);
-  if (he != hipSuccess) return fail(IDX_E_HIP, "device query failed: %s", hipGetErrorString(he));
-  k.min_chunk = int32_t(kMinChunk);
-  k.n_chunk = pick_chunks(a->S_k, L.n_tiles, a->S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus));
   k.seg_per_batch = int32_t(L.n_seg / a->B);
   k.tiles_per_seg = L.tiles_per_seg;
   k.last_seg_tiles = int32_t(k.tiles_per_batch - (k.seg_per_batch - 1) * int64_t(L.tiles_per_seg));
-  k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
-  k.n_positions = int32_t(positions_of(L, k.n_chunk));
   k.off_start = uint32_t(L.off_start);
   k.off_end = uint32_t(L.off_end);
   k.off_slot = uint32_t(L.off_slot);
@@ -320,6 +331,30 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
   k.pscales = idx::uses_pieces(x.kf, a->H) ? reinterpret_cast<const uint32_t*>(ws + WL.off_pscales) : nullptr;
   k.kfrag = ws + WL.off_kfrag;
   k.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + WL.off_kscale) : nullptr;
+  return k;
+}
+
+idx_status_t launch_scoring(int kf, const idx_logits_args_t* a, bool clean, const idx::ScoreArgs& k, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  switch (kf) {
+    case IDX_IN_BF16: e = idx::launch_score_bf16(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_FP8_E4M3: e = idx::launch_score_fp8(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_MXFP8_E4M3: e = idx::launch_score_mxfp8(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case IDX_IN_MXFP4_E2M1: e = idx::launch_score_mxfp4(a->w_dtype, a->out_dtype, clean, k, s); break;
+    case idx::kInBF16RowScale: e = idx::launch_score_bf16rs(a->w_dtype, a->out_dtype, clean, k, s); break;
+    default: return fail(IDX_E_INVALID, "unknown kernel format %d", kf);
+  }
+  if (e != hipSuccess) return fail(IDX_E_HIP, "scoring launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
+}
+
+// direct: a paged call whose scoring kernel reads the cache itself (see
+// direct_paged), else NULL.
+idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx::WorkspaceLayout& WL,
+                   unsigned char* ws, hipStream_t s, const idx::PagedK* direct = nullptr) {
+  idx::ScoreArgs k = score_args(a, p, WL, ws);
+  idx_status_t st = set_units(k, idx::plan_layout(a->B, a->S_q, a->H), a->S_k, true);
+  if (st != IDX_OK) return st;
   if (direct != nullptr) {
     k.kcache = direct->k_cache;
     k.kscache = direct->k_scale_cache;
@@ -329,19 +364,7 @@ idx_status_t score(const idx_logits_args_t* a, const unsigned char* p, const idx
     k.max_pages = direct->max_pages;
     while ((32 << k.bpp_shift) < direct->page_size) ++k.bpp_shift;
   }
-
-  const bool clean = a->clean_logits != 0;
-  hipError_t e = hipSuccess;
-  switch (x.kf) {
-    case IDX_IN_BF16: e = idx::launch_score_bf16(a->w_dtype, a->out_dtype, clean, k, s); break;
-    case IDX_IN_FP8_E4M3: e = idx::launch_score_fp8(a->w_dtype, a->out_dtype, clean, k, s); break;
-    case IDX_IN_MXFP8_E4M3: e = idx::launch_score_mxfp8(a->w_dtype, a->out_dtype, clean, k, s); break;
-    case IDX_IN_MXFP4_E2M1: e = idx::launch_score_mxfp4(a->w_dtype, a->out_dtype, clean, k, s); break;
-    case idx::kInBF16RowScale: e = idx::launch_score_bf16rs(a->w_dtype, a->out_dtype, clean, k, s); break;
-    default: return fail(IDX_E_INVALID, "unknown kernel format %d", x.kf);
-  }
-  if (e != hipSuccess) return fail(IDX_E_HIP, "scoring launch failed: %s", hipGetErrorString(e));
-  return IDX_OK;
+  return launch_scoring(idx::exec_of(a->in_dtype, a->accumulate).kf, a, a->clean_logits != 0, k, s);
 }
 
 }  // namespace
@@ -535,6 +558,127 @@ idx_status_t idx_logits_score(const idx_logits_args_t* a, const void* plan, void
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   if ((st = check_workspace(WL, ws, workspace_bytes, false)) != IDX_OK) return st;
   return score(a, static_cast<const unsigned char*>(plan), WL, ws, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of a fused top-k call (internal.h, TopkLayout); total == 0 when
+// the call's arguments are out of range.
+idx::TopkLayout topk_layout_of(const idx_logits_args_t* a) {
+  idx::TopkLayout T{};
+  T.base = layout_of(a);
+  if (T.base.total == 0) return T;
+  const idx::Exec x = idx::exec_of(a->in_dtype, a->accumulate);
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
+  const int64_t rows = L.n_rows, S_k = a->S_k;
+  if (rows * S_k > (int64_t(1) << 40)) return T;
+  T.S_ks = idx::sample_col(S_k);
+  T.nblk_s = cdiv(cdiv(S_k, 32), idx::kSampleStride);
+  T.n_chunk_max = pick_chunks(S_k, L.n_tiles, a->S_q, L.tile_rows, kMaxCus);
+  size_t off = T.base.total;
+  T.off_skfrag = off;
+  off += idx::align256(size_t(a->B) * size_t(T.nblk_s) * 32 * idx::row_bytes_of(x.kf));
+  T.off_skscale = off;
+  if (idx::has_kscale(x.kf)) off += idx::align256(size_t(a->B) * size_t(T.nblk_s) * 256);
+  T.off_splan = off;
+  off += L.total;
+  T.off_sscore = off;
+  off += idx::align256(size_t(rows) * size_t(T.S_ks) * 4);
+  T.off_tau = off;
+  off += idx::align256(size_t(rows) * 4);
+  T.off_redo = off;
+  off += idx::align256(size_t(rows) * 4);
+  T.off_gate = off;
+  off += 256;
+  T.off_meta = off;
+  off += idx::align256(size_t(rows) * size_t(T.n_chunk_max) * 8);
+  T.off_cand = off;
+  off += idx::align256(size_t(rows) * size_t(S_k) * 8);
+  T.total = off;
+  return T;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t idx_logits_topk_workspace_bytes(const idx_logits_args_t* a) { return topk_layout_of(a).total; }
+
+idx_status_t idx_logits_run_topk(const idx_logits_args_t* a, const void* plan, const int32_t* q_causal_offsets,
+                                 const int32_t* row_starts, const int32_t* row_ends, int32_t k,
+                                 idx_topk_order_t order, int32_t* topk_idx, float* topk_val, int32_t* n_redo,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  idx_status_t st = check_args(a, false, true);
+  if (st != IDX_OK) return st;
+  const unsigned char* p = static_cast<const unsigned char*>(plan);
+  if (p == nullptr && (row_starts == nullptr) != (row_ends == nullptr))
+    return fail(IDX_E_INVALID, "row_starts and row_ends must be given together");
+  if (p != nullptr && !aligned256(p)) return fail(IDX_E_INVALID, "plan must be 256-byte aligned");
+  if (k < 1 || k > idx::kMaxTopK) return fail(IDX_E_UNSUPPORTED, "k=%d outside [1, %d]", k, idx::kMaxTopK);
+  if (order != IDX_TOPK_BY_COLUMN && order != IDX_TOPK_BY_SCORE)
+    return fail(IDX_E_INVALID, "order must be IDX_TOPK_BY_COLUMN or IDX_TOPK_BY_SCORE");
+  if (topk_idx == nullptr) return fail(IDX_E_INVALID, "topk_idx must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(topk_idx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(topk_val) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(n_redo) & 3u) != 0)
+    return fail(IDX_E_INVALID, "topk_idx, topk_val and n_redo must be 4-byte aligned");
+  const idx::TopkLayout T = topk_layout_of(a);
+  if (T.total == 0) return fail(IDX_E_INVALID, "workspace size overflows");
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (ws == nullptr)
+    return fail(IDX_E_WORKSPACE, "this call needs a workspace of %zu bytes (idx_logits_topk_workspace_bytes)",
+                T.total);
+  if (!aligned256(ws)) return fail(IDX_E_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < T.total)
+    return fail(IDX_E_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, T.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const idx::Exec x = idx::exec_of(a->in_dtype, a->accumulate);
+  const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
+  const idx::WorkspaceLayout& WL = T.base;
+
+  // plan (unless given) and preparation, as for idx_logits_run
+  idx::PlanBuild build{a->B, a->S_q, a->S_k, a->H, a->D, q_causal_offsets, row_starts, row_ends, nullptr,
+                       ws + WL.off_plan};
+  const bool build_plan = p == nullptr;
+  if (build_plan) p = ws + WL.off_plan;
+  if ((st = prepare(a, WL, ws, build_plan ? &build : nullptr, nullptr, s)) != IDX_OK) return st;
+  hipError_t e = idx::launch_fused_setup(T, x.kf, a->B, a->S_q, a->S_k, a->H, p, ws, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "top-k setup launch failed: %s", hipGetErrorString(e));
+
+  // the sample: every kSampleStride-th key block, scores stored unclean
+  idx::ScoreArgs ks = score_args(a, ws + T.off_splan, WL, ws);
+  ks.S_k = int32_t(T.S_ks);
+  ks.kfrag = ws + T.off_skfrag;
+  ks.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + T.off_skscale) : nullptr;
+  ks.out = ws + T.off_sscore;
+  ks.ld = T.S_ks;
+  if ((st = set_units(ks, L, T.S_ks, false)) != IDX_OK) return st;
+  if ((st = launch_scoring(x.kf, a, false, ks, s)) != IDX_OK) return st;
+
+  // thresholds, then every cell in select mode
+  idx::ScoreArgs kc = score_args(a, p, WL, ws);
+  kc.out = nullptr;
+  kc.cand = ws + T.off_cand;
+  kc.meta = reinterpret_cast<int32_t*>(ws + T.off_meta);
+  kc.tau = reinterpret_cast<const uint32_t*>(ws + T.off_tau);
+  if ((st = set_units(kc, L, a->S_k, false)) != IDX_OK) return st;
+  if (kc.n_chunk > T.n_chunk_max) return fail(IDX_E_HIP, "chunk count %d above the workspace's", kc.n_chunk);
+  e = idx::launch_threshold(T, a->B, a->S_q, a->S_k, a->H, k, a->out_dtype == IDX_BF16, kc.n_chunk, p, ws, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "threshold launch failed: %s", hipGetErrorString(e));
+  if ((st = launch_scoring(x.kf, a, false, kc, s)) != IDX_OK) return st;
+  const bool by_score = order == IDX_TOPK_BY_SCORE;
+  e = idx::launch_select(T, a->B, a->S_q, a->S_k, a->H, a->D, k, by_score, kc.n_chunk, 1, p, ws, topk_idx, topk_val,
+                         n_redo, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "selection launch failed: %s", hipGetErrorString(e));
+
+  // rows the sample misjudged, if any, again with every cell of their window
+  kc.gate = reinterpret_cast<const int32_t*>(ws + T.off_gate);
+  if ((st = launch_scoring(x.kf, a, false, kc, s)) != IDX_OK) return st;
+  e = idx::launch_select(T, a->B, a->S_q, a->S_k, a->H, a->D, k, by_score, kc.n_chunk, 2, p, ws, topk_idx, topk_val,
+                         n_redo, s);
+  if (e != hipSuccess) return fail(IDX_E_HIP, "selection launch failed: %s", hipGetErrorString(e));
+  return IDX_OK;
 }
 
 }  // extern "C"

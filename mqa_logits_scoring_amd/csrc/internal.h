@@ -261,6 +261,64 @@ struct FastDiv {
   __device__ __forceinline__ uint32_t div(uint32_t n) const { return d > 1 ? uint32_t(__umul64hi(M, n)) : n; }
 };
 
+// ---------------------------------------------------------------------------
+// Fused top-k selection (idx_logits_run_topk)
+//
+// Scores become 32-bit rank keys whose unsigned order is the ranking of the
+// selection: larger scores first, +0 and -0 equal, NaN below every number.
+// A call then
+//  1. scores a sample first: every kSampleStride-th block of 32 keys (blocks
+//     0, R, 2R, ...), as sample columns j' = 32 (j / 32R) + min(j % 32R, 32)
+//     of key j (sample_col), so a window [s, e) of keys is the window
+//     [sample_col(s), sample_col(e)) of the sample;
+//  2. takes a threshold per row, the key of the m-th best sampled score in
+//     its window, m about 1.5 k / R plus a margin (0, every cell, when the
+//     window holds at most k keys or the sample is too small to say);
+//  3. scores every cell in select mode: a cell of a row's window whose key
+//     is at least the row's threshold is appended, as (score bits, column),
+//     to the row's candidate area; the unit of columns [c0, c1) writes its
+//     candidates in column order from slot c0 of the row on, and (c0, count)
+//     to the row's entry for its chunk;
+//  4. selects the top k of every row from its candidates, which are exactly
+//     the cells ranked above the threshold; a row with fewer candidates than
+//     min(k, window) gets threshold 0 and goes through 3 and 4 once more, so
+//     the result never depends on the sample.
+// ---------------------------------------------------------------------------
+constexpr int kSampleStride = 16;
+constexpr uint32_t kTauNone = 0xFFFFFFFFu;  // threshold no key reaches: the row keeps nothing
+
+__host__ __device__ inline int64_t sample_col(int64_t j) {
+  const int64_t span = 32 * int64_t(kSampleStride);
+  const int64_t r = j % span;
+  return (j / span) * 32 + (r < 32 ? r : 32);
+}
+
+// Rank key of a score's fp32 bits (bf16 scores widened): negative scores map
+// to -bits as an unsigned (so -0 lands on +0's key 0x80000000), others get the
+// top bit set, NaN gets 0.
+__device__ __forceinline__ uint32_t rank_key(uint32_t u) {
+  const uint32_t neg = uint32_t(int32_t(u) >> 31);
+  const uint32_t k = ((u ^ neg) - neg) ^ (~neg & 0x80000000u);
+  return __builtin_isnan(__uint_as_float(u)) ? 0u : k;
+}
+
+// Extra workspace of a fused top-k call, after the sections of the scoring
+// call itself (WorkspaceLayout, plan included), 256-byte aligned:
+//   [sampled K in fragment order]   B x ceil(nblk / R) blocks
+//   [sampled K scales]              (not BF16)
+//   [sample plan]                   plan_layout(B, S_q, H).total
+//   [sample scores]                 n_rows x S_ks, fp32 or bf16
+//   [thresholds, redo flags]        n_rows x 4 each
+//   [gate]                          256 B: rows sent through the second pass
+//   [chunk entries]                 n_rows x n_chunk_max x (c0, count)
+//   [candidates]                    n_rows x S_k x (score bits, column)
+struct TopkLayout {
+  WorkspaceLayout base;
+  size_t off_skfrag, off_skscale, off_splan, off_sscore, off_tau, off_redo, off_gate, off_meta, off_cand, total;
+  int64_t S_ks, nblk_s;
+  int32_t n_chunk_max;
+};
+
 // Everything a scoring kernel needs, passed by value.
 struct ScoreArgs {
   const void* q;
@@ -299,6 +357,15 @@ struct ScoreArgs {
   const uint32_t* kscache;       // [num_pages][page_size] (not BF16)
   const int32_t* btable;         // [B][max_pages]
   int32_t num_pages, page_size, max_pages, bpp_shift;
+  // Select mode (fused top-k) when cand is set: no score is stored (out is
+  // unused, no cleanup positions); row r keeps the cells of its window whose
+  // rank key is at least tau[r] as (score bits, column) pairs at
+  // cand + 8 (r S_k + c0 + i), and writes (c0, count) to meta[2 (r n_chunk +
+  // chunk)].  With gate set, the launch does nothing while *gate is 0.
+  unsigned char* cand;
+  int32_t* meta;
+  const uint32_t* tau;
+  const int32_t* gate;
 };
 
 // Launchers (return the hipError_t of the launch).
@@ -351,6 +418,23 @@ constexpr int kMaxTopK = 2048;
 hipError_t launch_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
                        const void* logits, bool logits_bf16, int64_t ld, int32_t k, bool by_score,
                        int32_t* out_idx, float* out_val, hipStream_t stream);
+
+// Fused top-k steps (topk_fused.hip), in launch order around the scoring
+// launches.  The sample plan, sampled K, thresholds and the rest live in the
+// call's workspace at the offsets of T (ws is its base).
+// Sample plan from plan, sampled K blocks, gate = 0.
+hipError_t launch_fused_setup(const TopkLayout& T, int kf, int32_t B, int32_t S_q, int32_t S_k, int32_t H,
+                              const unsigned char* plan, unsigned char* ws, hipStream_t stream);
+// Per row: threshold from the sample scores, redo flag 0, chunk entries 0.
+hipError_t launch_threshold(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t k,
+                            bool scores_bf16, int32_t n_chunk, const unsigned char* plan, unsigned char* ws,
+                            hipStream_t stream);
+// Per row: the top k of the candidates (pass 1: every row; rows short of
+// candidates get threshold 0, redo 1 and a count in the gate; pass 2: the
+// rows with redo 1, and *n_redo = gate when n_redo is set).
+hipError_t launch_select(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, int32_t k,
+                         bool by_score, int32_t n_chunk, int pass, const unsigned char* plan, unsigned char* ws,
+                         int32_t* out_idx, float* out_val, int32_t* n_redo, hipStream_t stream);
 
 hipError_t launch_score_bf16(idx_fp_t w_dtype, idx_fp_t out_dtype, bool clean, const ScoreArgs& a,
                              hipStream_t stream);

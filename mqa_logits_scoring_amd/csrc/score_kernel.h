@@ -134,6 +134,53 @@ static_assert(Fmt<IDX_IN_MXFP8_E4M3>::SCALE_SHIFT == KLayout<IDX_IN_MXFP8_E4M3>:
 
 constexpr int kThreads = 256;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Select mode (fused top-k, ScoreArgs::cand): a lane keeps its cell as a
+// candidate instead of storing it.  One 32-column block u of a row pair:
+// lane half g holds row g's cell at column c0 + 32u + c.  A cell is kept
+// when it lies in the unit's ncols columns and in its row's window (s_rel =
+// window start - c0, w_len = window width) and the rank key of its score, as
+// the call would store it (bf16 rounded to nearest even with OBF), is at
+// least its row's threshold (tau0, tau1).  Row g's kept cells go, in column
+// order, to slots cnt_g, cnt_g + 1, ... of its candidate area (rs0 / rs1,
+// based at column c0); the other half's lanes and the lanes not kept write
+// at an offset with the top bit set, which the buffer drops.  Thresholds
+// and counts are the same in every lane, so they stay in scalar registers.
+template <bool OBF>
+__device__ __forceinline__ void sel_emit(float v, int u, int c, int g, uint32_t c0, uint32_t ncols, uint32_t s_rel,
+                                         uint32_t w_len, uint32_t tau0, uint32_t tau1, uint32_t& cnt0,
+                                         uint32_t& cnt1, __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1) {
+  constexpr uint32_t kDrop = 0x80000000u;
+  const uint32_t col = uint32_t(32 * u + c);  // u = -1 wraps past ncols
+  uint32_t bits = __float_as_uint(v);
+  if constexpr (OBF) bits = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v))) << 16;
+  const bool keep = col < ncols && col - s_rel < w_len && rank_key(bits) >= (g ? tau1 : tau0);
+  const uint64_t m = __ballot(keep);
+  const uint32_t n0 = uint32_t(__builtin_popcount(uint32_t(m))), n1 = uint32_t(__builtin_popcount(uint32_t(m >> 32)));
+  const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+  const uint32_t off = keep ? ((g ? cnt1 - n0 : cnt0) + below) * 8u : kDrop;
+  const u32x2 pair = {bits, c0 + col};
+  __builtin_amdgcn_raw_buffer_store_b64(pair, rs0, int(off | (g ? kDrop : 0u)), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(pair, rs1, int(off | (g ? 0u : kDrop)), 0, 0);
+  cnt0 += n0;
+  cnt1 += n1;
+}
+
+// A row's candidate area from column c0 on, ncols pairs (none for a padding row).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sel_rsrc(const ScoreArgs& a, int row, bool valid, int c0,
+                                                          int ncols) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.cand + (int64_t(row) * a.S_k + c0) * 8, 0, valid ? ncols * 8 : 0,
+                                           0x00020000);
+}
+
+// The unit's entry of a row: (first column, candidates kept).
+__device__ __forceinline__ void sel_finish(const ScoreArgs& a, int row, int chunk, int c0, uint32_t cnt) {
+  int32_t* e = a.meta + 2 * (int64_t(row) * a.n_chunk + chunk);
+  e[0] = c0;
+  e[1] = int32_t(cnt);
+}
+
 template <bool OBF>
 __device__ __forceinline__ void store_out(void* out, int64_t idx, float v) {
   if constexpr (OBF) {
@@ -183,12 +230,12 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
 // segment, or a chunk past the tile's coverage).
 enum { kUnitNone = 0, kUnitCompute = 1, kUnitCleanup = 2 };
 struct Unit {
-  int kind, tile, c0, c1;
+  int kind, tile, c0, c1, chunk;
 };
 
 // Work position p (ScoreArgs) -> unit.
 __device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
-  if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0};
+  if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0, 0};
   const int slot = p / a.n_chunk, chunk = p - slot * a.n_chunk;
   // slot -> (batch, segment, rank): batches and segments from the last
   const int tpb = a.tiles_per_batch, spb = a.seg_per_batch, tps = a.tiles_per_seg, last = a.last_seg_tiles;
@@ -205,13 +252,13 @@ __device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
   }
   const int tile =
       reinterpret_cast<const int32_t*>(a.plan + a.off_order)[(int64_t(b) * spb + seg) * tps + rank];
-  if (tile < 0) return Unit{kUnitNone, 0, 0, 0};
+  if (tile < 0) return Unit{kUnitNone, 0, 0, 0, 0};
   const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
   const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
   const int w = max(a.min_chunk, ((hi - lo + a.n_chunk - 1) / a.n_chunk + 63) & ~63);
   const int c0 = lo + chunk * w, c1 = min(hi, c0 + w);
-  if (c0 >= c1) return Unit{kUnitNone, 0, 0, 0};
-  return Unit{kUnitCompute, tile, c0, c1};
+  if (c0 >= c1) return Unit{kUnitNone, 0, 0, 0, 0};
+  return Unit{kUnitCompute, tile, c0, c1, chunk};
 }
 
 // Waves per SIMD the kernel is built for: the FP8-family and FP4 kernels fit in
@@ -231,10 +278,14 @@ constexpr int kfrag_ring() {
 }
 
 // PD: keys straight from a paged cache (ScoreArgs::kcache) instead of the
-// fragment-order copy.
-template <int F, bool WBF, bool OBF, bool CLEAN, bool PD = false>
+// fragment-order copy.  SEL: select mode (ScoreArgs::cand).
+template <int F, bool WBF, bool OBF, bool CLEAN, bool PD = false, bool SEL = false>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(waves_per_eu<F>(), waves_per_eu<F>()))) score_kernel(const ScoreArgs a) {
+  static_assert(!SEL || (!CLEAN && !PD), "select mode stores no scores and reads contiguous keys");
+  if constexpr (SEL) {
+    if (a.gate != nullptr && *a.gate == 0) return;  // a second pass with no row to redo
+  }
   using T = Fmt<F>;
   constexpr int TW = 2;  // query rows per wave
   static_assert(4 * TW == kTileRows, "four waves cover one tile");
@@ -277,6 +328,13 @@ __global__ void __launch_bounds__(kThreads)
   // a wave with padding rows only (short tiles, e.g. two-token decode) has
   // nothing to store in this unit
   if (!rvalid[0] && !rvalid[1]) return;
+  // select mode: the rows' thresholds; a wave whose rows keep nothing is done
+  uint32_t tau_r[TW] = {kTauNone, kTauNone};
+  if constexpr (SEL) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) tau_r[t] = rvalid[t] ? a.tau[rows[t]] : kTauNone;
+    if (tau_r[0] == kTauNone && tau_r[1] == kTauNone) return;
+  }
 
   // Q fragments of head 32*mb + c for both rows, and their MX scale words
   uint32_t qf[TW][2][QD];
@@ -454,7 +512,19 @@ __global__ void __launch_bounds__(kThreads)
   const uint32_t half0 = g ? kDrop : 0u, half1 = g ? 0u : kDrop;
   const uint32_t s_rel = uint32_t(my_s - c0) * ES;                       // window start, bytes past c0
   const uint32_t w_len = uint32_t(max(my_e - my_s, 0)) * ES;             // window width in bytes
+  // select mode: the rows' candidate areas, the lane's row's threshold and count
+  __amdgpu_buffer_rsrc_t crs[TW];
+  if constexpr (SEL) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) crs[t] = sel_rsrc(a, rows[t], rvalid[t], c0, c1 - c0);
+  }
+  uint32_t sel_cnt[TW] = {0u, 0u};
   auto store = [&](float v, int u) {
+    if constexpr (SEL) {
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), uint32_t(my_s - c0), uint32_t(max(my_e - my_s, 0)),
+                    tau_r[0], tau_r[1], sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
+      return;
+    }
     const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
     const bool inwin = off - s_rel < w_len;
     uint32_t o0 = off | half0, o1 = off | half1;
@@ -658,6 +728,9 @@ __global__ void __launch_bounds__(kThreads)
     p1 = epi_relu(accB, wv[1][1], p1);
     store(combine(p0, p1, kprev), NB * n_iter - 1);
   }
+  if constexpr (SEL) {
+    if (c == 0 && (g ? rvalid[1] : rvalid[0])) sel_finish(a, my_row, u.chunk, c0, g ? sel_cnt[1] : sel_cnt[0]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -693,10 +766,14 @@ __global__ void __launch_bounds__(kThreads)
 // Four weighted-query pieces leave a residual below 2^-16 of each d-block
 // maximum of qt; by Cauchy-Schwarz its share of a score is at most
 // 2^-16 sqrt(32) / 2 < 4.4e-5 of sm_scale * sum_h |w_h| |q_h| |k|.
-template <int F, bool WBF, bool OBF, bool CLEAN, bool PD>
+template <int F, bool WBF, bool OBF, bool CLEAN, bool PD, bool SEL = false>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
     score_kernel_x16(const ScoreArgs a) {
   static_assert(F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3, "e4m3 formats only");
+  static_assert(!SEL || (!CLEAN && !PD), "select mode stores no scores and reads contiguous keys");
+  if constexpr (SEL) {
+    if (a.gate != nullptr && *a.gate == 0) return;  // a second pass with no row to redo
+  }
   using T = Fmt<F>;
   static_assert(T::ROWB == 128 && T::CBASE == 16 && T::CSTRIDE == 32, "K fragment placement of the e4m3 formats");
   constexpr bool MX = T::MX;
@@ -736,6 +813,13 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     rows[t] = r >= 0 ? r : first_row;
   }
   if (!rvalid[0] && !rvalid[1]) return;
+  // select mode: the rows' thresholds; a wave whose rows keep nothing is done
+  uint32_t tau_r[TW] = {kTauNone, kTauNone};
+  if constexpr (SEL) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) tau_r[t] = rvalid[t] ? a.tau[rows[t]] : kTauNone;
+    if (tau_r[0] == kTauNone && tau_r[1] == kTauNone) return;
+  }
 
   // Q: head 16 mb + n of row t, d-chunks q and q + 4, scale byte q
   i32x8 qf[TW][4];
@@ -883,7 +967,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const uint32_t half0 = g ? kDrop : 0u, half1 = g ? 0u : kDrop;
   const uint32_t s_rel = uint32_t(my_s - c0) * ES;
   const uint32_t w_len = uint32_t(max(my_e - my_s, 0)) * ES;
+  // select mode: the rows' candidate areas, the lane's row's threshold and count
+  __amdgpu_buffer_rsrc_t crs[TW];
+  if constexpr (SEL) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) crs[t] = sel_rsrc(a, rows[t], rvalid[t], c0, c1 - c0);
+  }
+  uint32_t sel_cnt[TW] = {0u, 0u};
   auto store = [&](float v, int u) {
+    if constexpr (SEL) {
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), uint32_t(my_s - c0), uint32_t(max(my_e - my_s, 0)),
+                    tau_r[0], tau_r[1], sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
+      return;
+    }
     const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
     const bool inwin = off - s_rel < w_len;
     uint32_t o0 = off | half0, o1 = off | half1;
@@ -994,6 +1090,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
   for (int j = 2 * kSteps - kLag; j < 2 * kSteps; ++j) epilogue(j);
   store(combine(p[1], lin[1], kblk[1]), 2 * n_iter - 1);
+  if constexpr (SEL) {
+    if (c == 0 && (g ? rvalid[1] : rvalid[0])) sel_finish(a, my_row, u.chunk, c0, g ? sel_cnt[1] : sel_cnt[0]);
+  }
 }
 
 // One launch of `kernel`: a workgroup per work position.
@@ -1006,6 +1105,17 @@ hipError_t launch_units(K kernel, const ScoreArgs& a, hipStream_t stream) {
 template <int F, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
   const bool pd = a.kcache != nullptr;
+  if (a.cand != nullptr) {  // select mode: launched without cleaning, on contiguous keys
+    if constexpr (CLEAN) {
+      return hipErrorInvalidValue;
+    } else {
+      if (pd) return hipErrorInvalidValue;
+      if constexpr (F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3)
+        return launch_units(score_kernel_x16<F, WBF, OBF, false, false, true>, a, stream);
+      else
+        return launch_units(score_kernel<F, WBF, OBF, false, false, true>, a, stream);
+    }
+  }
   if constexpr (F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3) {
     if (pd) return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, true>, a, stream);
     return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, false>, a, stream);

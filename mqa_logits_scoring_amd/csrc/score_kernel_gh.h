@@ -36,9 +36,22 @@ struct HeadTiling {
   static_assert(TR == 512 / H, "a tile holds 512 (row, head) pairs");
 };
 
-template <int F, int H, bool WBF, bool OBF, bool CLEAN>
+// SEL: select mode (ScoreArgs::cand), as in the 64-head kernels.  At 8 heads
+// a wave's 16 rows each carry a threshold and a count besides their windows,
+// more than fits beside two waves per SIMD: that variant runs one.
+template <int F, int H, bool SEL>
+constexpr int gh_waves_per_eu() {
+  return SEL && H == 8 ? 1 : waves_per_eu<F>();
+}
+
+template <int F, int H, bool WBF, bool OBF, bool CLEAN, bool SEL = false>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(waves_per_eu<F>(), waves_per_eu<F>()))) score_kernel_gh(const ScoreArgs a) {
+    __attribute__((amdgpu_waves_per_eu(gh_waves_per_eu<F, H, SEL>(), gh_waves_per_eu<F, H, SEL>())))
+    score_kernel_gh(const ScoreArgs a) {
+  static_assert(!SEL || !CLEAN, "select mode stores no scores");
+  if constexpr (SEL) {
+    if (a.gate != nullptr && *a.gate == 0) return;  // a second pass with no row to redo
+  }
   using T = Fmt<F>;
   using HT = HeadTiling<H>;
   constexpr int WR = HT::WR, TR = HT::TR, RPB = HT::RPB, REGS = HT::REGS, NBLK = HT::NBLK;
@@ -81,6 +94,19 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
   for (int t = 0; t < WR; ++t) any_row = any_row || rvalid[t];
   if (!any_row) return;  // padding rows only: nothing to store in this unit
+  // select mode: the rows' thresholds; a wave whose rows keep nothing is done
+  uint32_t tau_r[WR];
+#pragma unroll
+  for (int t = 0; t < WR; ++t) tau_r[t] = kTauNone;
+  if constexpr (SEL) {
+    bool any_sel = false;
+#pragma unroll
+    for (int t = 0; t < WR; ++t) {
+      tau_r[t] = rvalid[t] ? a.tau[rows[t]] : kTauNone;
+      any_sel = any_sel || tau_r[t] != kTauNone;
+    }
+    if (!any_sel) return;
+  }
 
   // Q fragments: block j, M row c = (query row j*RPB + c/H, head c%H); the
   // row differs between lanes when H < 32, so its index is read per lane
@@ -193,23 +219,33 @@ __global__ void __launch_bounds__(kThreads)
   // unit's width, 0 for a padding row), the other half's lanes dropped by an
   // offset with the top bit set; -inf picked byte-wise by v_perm_b32, never by
   // a branch (see the 64-head kernel for why).
+  // (select mode: in columns, with the pair's threshold and candidate count)
   constexpr int ES = OBF ? 2 : 4;
+  constexpr int EW = SEL ? 1 : ES;
   constexpr uint32_t kDrop = 0x80000000u;
   const uint32_t half0 = g ? kDrop : 0u, half1 = g ? 0u : kDrop;
-  uint32_t s_rel[WR / 2], w_len[WR / 2];
+  uint32_t s_rel[WR / 2], w_len[WR / 2], sel_cnt[WR];
 #pragma unroll
   for (int i = 0; i < WR / 2; ++i) {
     const int my_row = g ? rows[2 * i + 1] : rows[2 * i];
     const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
     const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
-    s_rel[i] = uint32_t(my_s - c0) * ES;
-    w_len[i] = uint32_t(max(my_e - my_s, 0)) * ES;
+    s_rel[i] = uint32_t(my_s - c0) * EW;
+    w_len[i] = uint32_t(max(my_e - my_s, 0)) * EW;
   }
+#pragma unroll
+  for (int t = 0; t < WR; ++t) sel_cnt[t] = 0;
   auto out_rsrc = [&](int t) {
     return __builtin_amdgcn_make_buffer_rsrc(static_cast<unsigned char*>(a.out) + (int64_t(rows[t]) * a.ld + c0) * ES,
                                              0, rvalid[t] ? (c1 - c0) * ES : 0, kBufWord3);
   };
   auto store_pair = [&](float v, int u, int i) {
+    if constexpr (SEL) {
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), s_rel[i], w_len[i], tau_r[2 * i], tau_r[2 * i + 1],
+                    sel_cnt[2 * i], sel_cnt[2 * i + 1], sel_rsrc(a, rows[2 * i], rvalid[2 * i], c0, c1 - c0),
+                    sel_rsrc(a, rows[2 * i + 1], rvalid[2 * i + 1], c0, c1 - c0));
+      return;
+    }
     const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
     const bool inwin = off - s_rel[i] < w_len[i];
     uint32_t o0 = off | half0, o1 = off | half1;
@@ -306,10 +342,22 @@ __global__ void __launch_bounds__(kThreads)
   }
   epi(accB, wv[3], 3);
   finish(3, NB * n_iter - 1, kprev);
+  if constexpr (SEL) {
+#pragma unroll
+    for (int i = 0; i < WR / 2; ++i)
+      if (c == 0 && (g ? rvalid[2 * i + 1] : rvalid[2 * i]))
+        sel_finish(a, g ? rows[2 * i + 1] : rows[2 * i], u.chunk, c0, g ? sel_cnt[2 * i + 1] : sel_cnt[2 * i]);
+  }
 }
 
 template <int F, int H, bool WBF, bool OBF, bool CLEAN>
 hipError_t launch_score_gh_t(const ScoreArgs& a, hipStream_t stream) {
+  if (a.cand != nullptr) {  // select mode: launched without cleaning
+    if constexpr (CLEAN)
+      return hipErrorInvalidValue;
+    else
+      return launch_units(score_kernel_gh<F, H, WBF, OBF, false, true>, a, stream);
+  }
   return launch_units(score_kernel_gh<F, H, WBF, OBF, CLEAN>, a, stream);
 }
 

@@ -52,15 +52,6 @@ constexpr int kCounts = kPerThread * kTopkWaves;  // (register, wave) counts of 
 static_assert(kCounts <= kTopkThreads, "one (register, wave) count per thread at most");
 static_assert(kPerThread <= 32, "a thread's registers fit one 32-bit mask");
 
-// Unsigned order of the result = the ranking of the scores (NaN lowest).
-__device__ __forceinline__ uint32_t rank_key(uint32_t u) {
-  // negative: -u as an unsigned (so -0 lands on +0's key 0x80000000),
-  // positive: u with the top bit set; NaN: 0
-  const uint32_t neg = uint32_t(int32_t(u) >> 31);
-  const uint32_t k = ((u ^ neg) - neg) ^ (~neg & 0x80000000u);
-  return __builtin_isnan(__uint_as_float(u)) ? 0u : k;
-}
-
 template <bool BF>
 __device__ __forceinline__ uint32_t score_bits(const void* logits, int64_t i) {
   if constexpr (BF)

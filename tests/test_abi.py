@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     L = lib.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert lib.idx_abi_version() == lib.ABI_VERSION == 2
+    assert lib.idx_abi_version() == lib.ABI_VERSION == 3
 
 
 def test_plan_bytes():
@@ -335,3 +335,48 @@ def test_plan_windows_rejects():
     assert L.idx_logits_plan_windows(FAKE, 1, 16, 64, 64, 128, FAKE, FAKE + 1, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_windows(None, 1, 16, 64, 64, 128, FAKE, FAKE, None) == lib.IDX_E_INVALID
     assert L.idx_logits_plan_windows(FAKE, 1, 16, 64, 24, 128, FAKE, FAKE, None) == lib.IDX_E_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------
+# fused scoring + top-k (idx_logits_run_topk): host-side checks only
+# ---------------------------------------------------------------------------
+
+def _run_topk(a, k=8, order=0, idx=FAKE, val=FAKE, n_redo=None, plan=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.lib().idx_logits_run_topk(ctypes.byref(a), plan, None, None, None, k, order, idx, val, n_redo, ws,
+                                         ws_bytes, None)
+
+
+def test_run_topk_rejects():
+    # out is not used: NULL or misaligned out passes the checks that fail here
+    a = _args(out=None, out_row_stride=0)
+    assert _run_topk(a, k=0) == lib.IDX_E_UNSUPPORTED
+    assert _run_topk(a, k=lib.MAX_TOPK + 1) == lib.IDX_E_UNSUPPORTED
+    assert _run_topk(a, order=2) == lib.IDX_E_INVALID
+    assert _run_topk(a, idx=None) == lib.IDX_E_INVALID
+    assert _run_topk(a, idx=FAKE + 2) == lib.IDX_E_INVALID
+    assert _run_topk(a, val=FAKE + 1) == lib.IDX_E_INVALID
+    assert _run_topk(a, n_redo=FAKE + 1) == lib.IDX_E_INVALID
+    assert _run_topk(a, plan=FAKE + 64) == lib.IDX_E_INVALID
+    assert _run_topk(a, ws=None) == lib.IDX_E_WORKSPACE
+    assert "idx_logits_topk_workspace_bytes" in lib.idx_last_error()
+    assert _run_topk(a, ws=FAKE + 16) == lib.IDX_E_INVALID
+    need = lib.idx_logits_topk_workspace_bytes(a)
+    assert _run_topk(a, ws_bytes=need - 1) == lib.IDX_E_WORKSPACE
+    assert str(need) in lib.idx_last_error()
+    for kw, st in ((dict(H=24), lib.IDX_E_UNSUPPORTED), (dict(q=None), lib.IDX_E_INVALID),
+                   (dict(k_scale=None), lib.IDX_E_INVALID), (dict(in_dtype=9), lib.IDX_E_INVALID),
+                   (dict(accumulate=3), lib.IDX_E_INVALID), (dict(sm_scale=float("nan")), lib.IDX_E_INVALID)):
+        assert _run_topk(_args(out=None, **kw)) == st, kw
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
+def test_topk_workspace_holds_the_candidates(fmt):
+    kw = {"q_scale": None, "k_scale": None} if fmt == 0 else {}
+    for B, S_q, S_k in ((1, 16, 64), (2, 300, 5000), (1, 2048, 32768)):
+        a = _args(in_dtype=fmt, B=B, S_q=S_q, S_k=S_k, out=None, **kw)
+        total = lib.idx_logits_topk_workspace_bytes(a)
+        base = lib.idx_logits_workspace_bytes(_args(in_dtype=fmt, B=B, S_q=S_q, S_k=S_k, out_row_stride=S_k, **kw))
+        # the scoring call's own sections, then at least one (score, column)
+        # pair per cell and the sample's scores (S_k / 16 columns per row)
+        assert total >= base + 8 * B * S_q * S_k + 4 * B * S_q * (S_k // 16)
+    assert lib.idx_logits_topk_workspace_bytes(_args(H=24)) == 0
