@@ -358,8 +358,9 @@ def main():
     ap.add_argument("--no-exact-variant", action="store_true",
                     help="skip the FP8 / MXFP8 call with exact (fp32) accumulation")
     ap.add_argument("--no-peaks", action="store_true", help="skip the MFMA-shape and copy peak measurement")
-    ap.add_argument("--topk", type=int, default=0,
-                    help="also time top-k selection (this k, by column) over the call's scores")
+    ap.add_argument("--topk", type=int, default=2048,
+                    help="also time top-k selection (this k, by column): over the call's scores, and fused with "
+                         "the scoring (idx_logits_run_topk); 0 skips both")
     ap.add_argument("--peaks", action="store_true",
                     help="only measure the MFMA throughput per shape and a device copy (libidx_peak.so)")
     ap.add_argument("--eager", action="store_true",
@@ -509,7 +510,28 @@ def main():
         def launch_topk(i):
             lib.idx_logits_topk(plan, src, k, order="column", B=wl.B, H=wl.H, D=wl.D, S_k=wl.S_k, out_idx=tidx[i],
                                 out_val=tval[i])
-        variants.append(Variant(f"topk{k}", launch_topk, tidx, None))
+        variants.append(Variant(f"topk{k}", launch_topk, tidx, f"topk{k}"))
+        if not paged:
+            # scoring and selection in one call, plan built inside as for "call";
+            # its indices must equal the two-phase ones bit for bit
+            fidx = [torch.empty((wl.B, wl.S_q, k), dtype=torch.int32, device=dev) for _ in range(5)]
+            fval = [torch.empty((wl.B, wl.S_q, k), dtype=torch.float32, device=dev) for _ in range(5)]
+            n_redo = torch.zeros(1, dtype=torch.int32, device=dev)
+            keep.extend(fidx + fval + [n_redo])
+            fa = lib.make_args(d["q"], d["k"], d["w"], None, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                               k_scale=d["k_scale"], sm_scale=wl.sm_scale, out_dtype=odt)
+            fws = torch.empty(lib.idx_logits_topk_workspace_bytes(fa), dtype=torch.uint8, device=dev)
+            keep.append(fws)
+            tplan_f = torch.empty_like(plan) if thd else None
+
+            def launch_fused(i):
+                p = build_plan(lib, wl, d, tplan_f, None) if thd else None
+                lib.idx_logits_run_topk(d["q"], d["k"], d["w"], k, in_dtype=wl.fmt, q_scale=d["q_scale"],
+                                        k_scale=d["k_scale"], sm_scale=wl.sm_scale, out_dtype=odt, order="column",
+                                        plan=p, q_causal_offsets=d["offsets"], row_starts=d["starts"],
+                                        row_ends=d["ends"], workspace=fws, out_idx=fidx[i], out_val=fval[i],
+                                        n_redo=n_redo)
+            variants.append(Variant(f"fused_topk{k}", launch_fused, fidx, f"topk{k}"))
 
     # eager reference of every group of variants that must agree bitwise
     refs = {}
@@ -670,6 +692,13 @@ def main():
                                     "frac": round(tg / HBM_PEAK_GBS, 4),
                                     "traffic": None if trec is None else trec["fetch_bytes"] + trec["write_bytes"],
                                     "algorithmic_bytes_per_launch": read + written}}
+        if f"fused_topk{k}" in stats:
+            f_us = stats[f"fused_topk{k}"]["median_us"]
+            two = us_call + t_us
+            res["topk"]["fused"] = {"call_us": f_us, "two_phase_us": round(two, 2),
+                                    "speedup_vs_two_phase": round(two / f_us, 3), "eff_tflops": tflops(f_us),
+                                    "rows_scored_twice": int(n_redo.item()),
+                                    "indices_equal_two_phase": True}
     del variants, keep
     torch.cuda.empty_cache()
     if not args.no_peaks:

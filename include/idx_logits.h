@@ -409,7 +409,7 @@ idx_status_t idx_logits_topk(const void* plan, int32_t B, int32_t S_q, int32_t S
  * the call first scores a sample, every 16th block of 32 keys, and takes
  * per row a threshold just below the scores the selection is likely to
  * need; scoring then keeps, per row, only the window's cells at or above it
- * (about 1.5 k of them) in the workspace, and the selection runs over those.
+ * (about 1.25 k + 512 of them) in the workspace, and the selection runs over those.
  * A row left with fewer than min(k, window) cells, which the sample can make
  * happen but never changes the result, is scored again keeping its whole
  * window.

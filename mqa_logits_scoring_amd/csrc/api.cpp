@@ -58,12 +58,15 @@ int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 // S_q and tile_rows: when a batch has fewer query rows than a tile, the waves
 // holding only padding rows idle, so more units keep the CUs fed.
-int32_t pick_chunks(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows, int64_t cus) {
+// units_per_cu: a sample scoring launch (fused top-k), whose units are short
+// anyway, takes one round of units (two workgroups per CU).
+int32_t pick_chunks(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows, int64_t cus,
+                    int64_t units_per_cu = kUnitsPerCu) {
   const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
   const int64_t rows_per_wave = tile_rows / 4;
   const int64_t rows = S_q < tile_rows ? S_q : tile_rows;
   const int64_t active = cdiv(rows, rows_per_wave);  // waves of a tile with a real row
-  const int64_t target = kUnitsPerCu * cus * 4 / active;
+  const int64_t target = units_per_cu * cus * 4 / active;
   int64_t want = std::max(cdiv(target, n_tiles), cdiv(span, kChunkCols));
   want = std::min(want, cdiv(span, kMinChunk));
   return int32_t(std::max<int64_t>(want, 1));
@@ -287,12 +290,13 @@ idx_status_t prepare(const idx_logits_args_t* a, const idx::WorkspaceLayout& WL,
 }
 
 // The unit grid of a scoring launch over S_k columns (ScoreArgs).
-idx_status_t set_units(idx::ScoreArgs& k, const idx::PlanLayout& L, int64_t S_k, bool cleanup) {
+idx_status_t set_units(idx::ScoreArgs& k, const idx::PlanLayout& L, int64_t S_k, bool cleanup,
+                       int64_t units_per_cu = kUnitsPerCu) {
   int cus = 0;
   hipError_t he = device_cus(cus);
   if (he != hipSuccess) return fail(IDX_E_HIP, "device query failed: %s", hipGetErrorString(he));
   k.min_chunk = int32_t(kMinChunk);
-  k.n_chunk = pick_chunks(S_k, L.n_tiles, k.S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus));
+  k.n_chunk = pick_chunks(S_k, L.n_tiles, k.S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus), units_per_cu);
   k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
   k.n_positions = cleanup ? int32_t(positions_of(L, k.n_chunk)) : k.n_pos_compute;
   return IDX_OK;
@@ -590,6 +594,8 @@ idx::TopkLayout topk_layout_of(const idx_logits_args_t* a) {
   off += idx::align256(size_t(rows) * 4);
   T.off_redo = off;
   off += idx::align256(size_t(rows) * 4);
+  T.off_big = off;
+  off += idx::align256(size_t(rows) * 4);
   T.off_gate = off;
   off += 256;
   T.off_meta = off;
@@ -653,7 +659,7 @@ idx_status_t idx_logits_run_topk(const idx_logits_args_t* a, const void* plan, c
   ks.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + T.off_skscale) : nullptr;
   ks.out = ws + T.off_sscore;
   ks.ld = T.S_ks;
-  if ((st = set_units(ks, L, T.S_ks, false)) != IDX_OK) return st;
+  if ((st = set_units(ks, L, T.S_ks, false, 2)) != IDX_OK) return st;
   if ((st = launch_scoring(x.kf, a, false, ks, s)) != IDX_OK) return st;
 
   // thresholds, then every cell in select mode

@@ -272,8 +272,9 @@ struct FastDiv {
 //     of key j (sample_col), so a window [s, e) of keys is the window
 //     [sample_col(s), sample_col(e)) of the sample;
 //  2. takes a threshold per row, the key of the m-th best sampled score in
-//     its window, m about 1.5 k / R plus a margin (0, every cell, when the
-//     window holds at most k keys or the sample is too small to say);
+//     its window with its low 16 bits cleared, m about 1.25 k / R plus a
+//     margin (0, every cell, when the window holds at most k keys or the
+//     sample is too small to say);
 //  3. scores every cell in select mode: a cell of a row's window whose key
 //     is at least the row's threshold is appended, as (score bits, column),
 //     to the row's candidate area; the unit of columns [c0, c1) writes its
@@ -308,13 +309,13 @@ __device__ __forceinline__ uint32_t rank_key(uint32_t u) {
 //   [sampled K scales]              (not BF16)
 //   [sample plan]                   plan_layout(B, S_q, H).total
 //   [sample scores]                 n_rows x S_ks, fp32 or bf16
-//   [thresholds, redo flags]        n_rows x 4 each
-//   [gate]                          256 B: rows sent through the second pass
+//   [thresholds, redo list, big-row list]  n_rows x 4 each
+//   [gate]                          256 B: counts of the two lists
 //   [chunk entries]                 n_rows x n_chunk_max x (c0, count)
 //   [candidates]                    n_rows x S_k x (score bits, column)
 struct TopkLayout {
   WorkspaceLayout base;
-  size_t off_skfrag, off_skscale, off_splan, off_sscore, off_tau, off_redo, off_gate, off_meta, off_cand, total;
+  size_t off_skfrag, off_skscale, off_splan, off_sscore, off_tau, off_redo, off_big, off_gate, off_meta, off_cand, total;
   int64_t S_ks, nblk_s;
   int32_t n_chunk_max;
 };
@@ -425,13 +426,14 @@ hipError_t launch_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, in
 // Sample plan from plan, sampled K blocks, gate = 0.
 hipError_t launch_fused_setup(const TopkLayout& T, int kf, int32_t B, int32_t S_q, int32_t S_k, int32_t H,
                               const unsigned char* plan, unsigned char* ws, hipStream_t stream);
-// Per row: threshold from the sample scores, redo flag 0, chunk entries 0.
+// Per row: threshold from the sample scores, chunk entries 0.
 hipError_t launch_threshold(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t k,
                             bool scores_bf16, int32_t n_chunk, const unsigned char* plan, unsigned char* ws,
                             hipStream_t stream);
 // Per row: the top k of the candidates (pass 1: every row; rows short of
-// candidates get threshold 0, redo 1 and a count in the gate; pass 2: the
-// rows with redo 1, and *n_redo = gate when n_redo is set).
+// candidates get threshold 0 and join the redo list, whose length gate[0]
+// gates the second scoring launch; pass 2: the rows of the redo list, and
+// *n_redo = gate[0] when n_redo is set).
 hipError_t launch_select(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D, int32_t k,
                          bool by_score, int32_t n_chunk, int pass, const unsigned char* plan, unsigned char* ws,
                          int32_t* out_idx, float* out_val, int32_t* n_redo, hipStream_t stream);

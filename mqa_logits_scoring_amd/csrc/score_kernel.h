@@ -137,25 +137,48 @@ constexpr int kThreads = 256;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Select mode (fused top-k, ScoreArgs::cand): a lane keeps its cell as a
-// candidate instead of storing it.  One 32-column block u of a row pair:
-// lane half g holds row g's cell at column c0 + 32u + c.  A cell is kept
-// when it lies in the unit's ncols columns and in its row's window (s_rel =
-// window start - c0, w_len = window width) and the rank key of its score, as
-// the call would store it (bf16 rounded to nearest even with OBF), is at
-// least its row's threshold (tau0, tau1).  Row g's kept cells go, in column
-// order, to slots cnt_g, cnt_g + 1, ... of its candidate area (rs0 / rs1,
-// based at column c0); the other half's lanes and the lanes not kept write
-// at an offset with the top bit set, which the buffer drops.  Thresholds
-// and counts are the same in every lane, so they stay in scalar registers.
+// candidate instead of storing it.
+//
+// A row's threshold key (internal.h, rank_key order) as a float compare: a
+// score reaches key tau exactly when it is a number >= tau_value(tau)
+// (rank keys of numbers order like the numbers, +0 and -0 alike), or when
+// tau is 0, which keeps NaN too (keep_all); kTauNone gives NaN, which no
+// score reaches.
+__device__ __forceinline__ float tau_value(uint32_t tau) {
+  if (tau == kTauNone) return __builtin_nanf("");
+  if (tau == 0u) return -__builtin_inff();
+  return __uint_as_float((tau >> 31) ? (tau & 0x7FFFFFFFu) : (0u - tau));
+}
+
+// Thresholds of a row pair, as the select-mode epilogue uses them (the same
+// in every lane, so they stay in scalar registers).
+struct SelTau {
+  float v0, v1;
+  bool all0, all1;
+};
+__device__ __forceinline__ SelTau sel_tau(uint32_t tau0, uint32_t tau1) {
+  return SelTau{tau_value(tau0), tau_value(tau1), tau0 == 0u, tau1 == 0u};
+}
+
+// One 32-column block u of a row pair: lane half g holds row g's cell at
+// column c0 + 32u + c.  A cell is kept when its column lies in [lo, lo + len)
+// past c0 (its row's window cut to the unit's columns) and its score, as the
+// call would store it (bf16 rounded to nearest even with OBF), reaches its
+// row's threshold.  Row g's kept cells go, in column order, to slots cnt_g,
+// cnt_g + 1, ... of its candidate area (rs0 / rs1, based at column c0); the
+// other half's lanes and the lanes not kept write at an offset with the top
+// bit set, which the buffer drops.  Counts, like thresholds, are the same in
+// every lane.
 template <bool OBF>
-__device__ __forceinline__ void sel_emit(float v, int u, int c, int g, uint32_t c0, uint32_t ncols, uint32_t s_rel,
-                                         uint32_t w_len, uint32_t tau0, uint32_t tau1, uint32_t& cnt0,
-                                         uint32_t& cnt1, __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1) {
+__device__ __forceinline__ void sel_emit(float v, int u, int c, int g, uint32_t c0, uint32_t lo, uint32_t len,
+                                         const SelTau& tau, uint32_t& cnt0, uint32_t& cnt1,
+                                         __amdgpu_buffer_rsrc_t rs0, __amdgpu_buffer_rsrc_t rs1) {
   constexpr uint32_t kDrop = 0x80000000u;
-  const uint32_t col = uint32_t(32 * u + c);  // u = -1 wraps past ncols
+  const uint32_t col = uint32_t(32 * u + c);  // u = -1 wraps far past every window
   uint32_t bits = __float_as_uint(v);
   if constexpr (OBF) bits = uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v))) << 16;
-  const bool keep = col < ncols && col - s_rel < w_len && rank_key(bits) >= (g ? tau1 : tau0);
+  const bool reach = __uint_as_float(bits) >= (g ? tau.v1 : tau.v0) || (g ? tau.all1 : tau.all0);
+  const bool keep = col - lo < len && reach;
   const uint64_t m = __ballot(keep);
   const uint32_t n0 = uint32_t(__builtin_popcount(uint32_t(m))), n1 = uint32_t(__builtin_popcount(uint32_t(m >> 32)));
   const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
@@ -165,6 +188,14 @@ __device__ __forceinline__ void sel_emit(float v, int u, int c, int g, uint32_t 
   __builtin_amdgcn_raw_buffer_store_b64(pair, rs1, int(off | (g ? 0u : kDrop)), 0, 0);
   cnt0 += n0;
   cnt1 += n1;
+}
+
+// A row's window cut to the unit's columns [c0, c1), relative to c0: start
+// and width (0 when they do not meet).
+__device__ __forceinline__ void sel_window(int s, int e, int c0, int c1, uint32_t& lo, uint32_t& len) {
+  const int a = max(s, c0), b = min(e, c1);
+  lo = uint32_t(a - c0);
+  len = uint32_t(max(b - a, 0));
 }
 
 // A row's candidate area from column c0 on, ncols pairs (none for a padding row).
@@ -519,10 +550,12 @@ __global__ void __launch_bounds__(kThreads)
     for (int t = 0; t < TW; ++t) crs[t] = sel_rsrc(a, rows[t], rvalid[t], c0, c1 - c0);
   }
   uint32_t sel_cnt[TW] = {0u, 0u};
+  const SelTau stau = sel_tau(tau_r[0], tau_r[1]);
+  uint32_t sel_lo = 0, sel_len = 0;
+  if constexpr (SEL) sel_window(my_s, my_e, c0, c1, sel_lo, sel_len);
   auto store = [&](float v, int u) {
     if constexpr (SEL) {
-      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), uint32_t(my_s - c0), uint32_t(max(my_e - my_s, 0)),
-                    tau_r[0], tau_r[1], sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), sel_lo, sel_len, stau, sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
       return;
     }
     const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
@@ -974,10 +1007,12 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     for (int t = 0; t < TW; ++t) crs[t] = sel_rsrc(a, rows[t], rvalid[t], c0, c1 - c0);
   }
   uint32_t sel_cnt[TW] = {0u, 0u};
+  const SelTau stau = sel_tau(tau_r[0], tau_r[1]);
+  uint32_t sel_lo = 0, sel_len = 0;
+  if constexpr (SEL) sel_window(my_s, my_e, c0, c1, sel_lo, sel_len);
   auto store = [&](float v, int u) {
     if constexpr (SEL) {
-      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), uint32_t(my_s - c0), uint32_t(max(my_e - my_s, 0)),
-                    tau_r[0], tau_r[1], sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), sel_lo, sel_len, stau, sel_cnt[0], sel_cnt[1], crs[0], crs[1]);
       return;
     }
     const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped

@@ -230,8 +230,12 @@ __global__ void __launch_bounds__(kThreads)
     const int my_row = g ? rows[2 * i + 1] : rows[2 * i];
     const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[my_row];
     const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[my_row];
-    s_rel[i] = uint32_t(my_s - c0) * EW;
-    w_len[i] = uint32_t(max(my_e - my_s, 0)) * EW;
+    if constexpr (SEL) {
+      sel_window(my_s, my_e, c0, c1, s_rel[i], w_len[i]);
+    } else {
+      s_rel[i] = uint32_t(my_s - c0) * EW;
+      w_len[i] = uint32_t(max(my_e - my_s, 0)) * EW;
+    }
   }
 #pragma unroll
   for (int t = 0; t < WR; ++t) sel_cnt[t] = 0;
@@ -241,7 +245,7 @@ __global__ void __launch_bounds__(kThreads)
   };
   auto store_pair = [&](float v, int u, int i) {
     if constexpr (SEL) {
-      sel_emit<OBF>(v, u, c, g, uint32_t(c0), uint32_t(c1 - c0), s_rel[i], w_len[i], tau_r[2 * i], tau_r[2 * i + 1],
+      sel_emit<OBF>(v, u, c, g, uint32_t(c0), s_rel[i], w_len[i], sel_tau(tau_r[2 * i], tau_r[2 * i + 1]),
                     sel_cnt[2 * i], sel_cnt[2 * i + 1], sel_rsrc(a, rows[2 * i], rvalid[2 * i], c0, c1 - c0),
                     sel_rsrc(a, rows[2 * i + 1], rvalid[2 * i + 1], c0, c1 - c0));
       return;

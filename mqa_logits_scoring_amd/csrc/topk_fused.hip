@@ -27,7 +27,12 @@ namespace {
 constexpr int kFThreads = 256;
 constexpr int kFWaves = kFThreads / 64;
 constexpr int kThrStage = 4096;   // sample keys a threshold workgroup keeps in LDS
-constexpr int kSelStage = 8192;   // candidate keys a selection workgroup keeps in LDS
+constexpr int kSelStage = 8192;   // candidates a selection workgroup keeps in LDS
+// A selection workgroup works on one row at a time: 16 waves (two
+// workgroups per CU fit their LDS) keep its serial steps short.
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kPieceGroup = 256;  // chunk entries a selection workgroup reads at a time
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
@@ -40,8 +45,9 @@ __device__ __forceinline__ bool plan_matches(const unsigned char* plan, int32_t 
          h->n_tiles == int32_t(L.n_tiles) && h->tile_rows == L.tile_rows;
 }
 
-// Inclusive prefix sum of v over the workgroup (thread order); `total`
-// receives the sum.  Contains barriers.
+// Inclusive prefix sum of v over a workgroup of NW waves (thread order);
+// `total` receives the sum.  Contains barriers.
+template <int NW = kFWaves>
 __device__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
@@ -54,7 +60,7 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kFWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const uint32_t s = wsum[w];
     before += w < wave ? s : 0u;
     all += s;
@@ -68,13 +74,64 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
 // the want-th largest counted key (1 <= want <= keys counted), the keys in
 // higher bins and the keys in its bin, into res[0..2].  Lane l reads bins
 // 4l..4l+3; a suffix sum over the lanes gives each lane the count above it.
+// Minimum and maximum of per-thread values over a workgroup of NW waves
+// (mm[0..2 NW) is scratch).  Contains barriers.
+template <int NW = kFWaves>
+__device__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32_t* mm) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    lo = min(lo, uint32_t(__shfl_xor(lo, d, 64)));
+    hi = max(hi, uint32_t(__shfl_xor(hi, d, 64)));
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    mm[wave] = lo;
+    mm[NW + wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, mm[w]);
+    hi = max(hi, mm[NW + w]);
+  }
+  __syncthreads();
+}
+
+// Bits a radix select must look at when every key lies in [lo, hi]: those
+// below the highest bit where lo and hi differ (keys that share their top
+// bits would all land in one histogram bin, and LDS atomics on one address
+// serialize).
+__device__ __forceinline__ int varying_bits(uint32_t lo, uint32_t hi) {
+  return lo == hi ? 8 : 32 - __builtin_clz(lo ^ hi);
+}
+
+// Radix-select histograms: 256 bins in kHistCopies copies, lane l counting
+// into copy l % kHistCopies, so that the lanes of one instruction that count
+// the same digit mostly hit different words (LDS atomics on one word
+// serialize).  Copy c of bin b is word c * kHistStride + b, which also puts a
+// bin's copies in different banks.
+constexpr int kHistCopies = 8;
+constexpr int kHistStride = 257;
+constexpr int kHistWords = kHistCopies * kHistStride;
+
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin) {
+  atomicAdd(&hist[(threadIdx.x & (kHistCopies - 1)) * kHistStride + bin], 1u);
+}
+
+// Wave 0 over the histogram (bin = digit): the digit whose bin holds the
+// want-th largest counted key (1 <= want <= keys counted), the keys in higher
+// bins and the keys in its bin, into res[0..2].  Lane l reads bins 4l..4l+3;
+// a suffix sum over the lanes gives each lane the count above it.
 __device__ void find_bin256(const uint32_t* hist, uint32_t want, uint32_t* res) {
   const int lane = threadIdx.x;
   uint32_t h[4], own = 0;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    h[b] = hist[4 * lane + b];
-    own += h[b];
+    uint32_t x = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) x += hist[c * kHistStride + 4 * lane + b];
+    h[b] = x;
+    own += x;
   }
   uint32_t x = own;  // keys in the bins of lanes >= lane
 #pragma unroll
@@ -99,21 +156,25 @@ __device__ void find_bin256(const uint32_t* hist, uint32_t want, uint32_t* res) 
   }
 }
 
-// Radix select over keys, 8 bits per pass from the top: the want-th largest
-// key (want >= 1) of those `for_each` visits, with how many keys equal it and
-// how many of those the want-th still takes (want_left).  for_each(fn) calls
-// fn(key) for every key, from every thread, and may contain barriers.
-template <typename ForEach>
+// Radix select over keys, 8 bits per pass from bit hi_bit down to bit
+// stop_bit: the want-th largest key (want >= 1) of those `for_each` visits,
+// its bits below stop_bit cleared, with how many keys share its bits above
+// and how many of those the want-th still takes (want_left).  for_each(fn)
+// calls fn(key) for every key, from every thread, and may contain barriers.
+// Bits above hi_bit are taken as given (prefix0, the same for every key).
+// NT: threads of the workgroup.
+template <int NT, typename ForEach>
 __device__ uint32_t radix_select(ForEach for_each, uint32_t want, uint32_t* hist, uint32_t* res, uint32_t& count_eq,
-                                 uint32_t& want_left, int hi_bit = 32) {
-  uint32_t prefix = 0, pmask = 0;
-  for (int hi = hi_bit; hi > 0; hi -= 8) {
-    const int lo = hi > 8 ? hi - 8 : 0;
+                                 uint32_t& want_left, int hi_bit = 32, int stop_bit = 0, uint32_t prefix0 = 0) {
+  uint32_t prefix = hi_bit >= 32 ? 0u : prefix0 & ~((1u << hi_bit) - 1u);
+  uint32_t pmask = hi_bit >= 32 ? 0u : ~((1u << hi_bit) - 1u);
+  for (int hi = hi_bit; hi > stop_bit; hi -= 8) {
+    const int lo = hi - 8 > stop_bit ? hi - 8 : stop_bit;
     const uint32_t dm = (1u << (hi - lo)) - 1u;
-    for (int i = threadIdx.x; i < 256; i += kFThreads) hist[i] = 0;
+    for (int i = threadIdx.x; i < kHistWords; i += NT) hist[i] = 0;
     __syncthreads();
     for_each([&](uint32_t key) {
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> lo) & dm], 1u);
+      if ((key & pmask) == prefix) hist_add(hist, (key >> lo) & dm);
     });
     __syncthreads();
     if (threadIdx.x < 64) find_bin256(hist, want, res);
@@ -161,7 +222,8 @@ __global__ void __launch_bounds__(kFThreads) fused_setup_kernel(const SetupArgs 
     sh->D = 128;
     sh->n_tiles = int32_t(L.n_tiles);
     sh->tile_rows = L.tile_rows;
-    *a.gate = 0;
+    a.gate[0] = 0;  // rows to score again
+    a.gate[1] = 0;  // rows left to the workgroup selection
   }
   if (ok) {
     const int32_t* ws = reinterpret_cast<const int32_t*>(a.plan + L.off_start);
@@ -210,35 +272,136 @@ __global__ void __launch_bounds__(kFThreads) fused_setup_kernel(const SetupArgs 
 // ---------------------------------------------------------------------------
 // threshold
 
+// ---------------------------------------------------------------------------
+// one row per wave
+//
+// The selection of most rows runs one wave per row, four rows per
+// workgroup, each wave with its own LDS area and no workgroup barrier: a
+// row's steps are short, so what bounds them is latency, and a CU then works
+// on up to eight rows at once.
+
+// LDS written by some lanes of a wave and read by others: a wave's LDS
+// accesses complete in order; the fence keeps the compiler from moving them
+// across and waits for those outstanding.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+constexpr int kRowWaves = 4;                    // rows (waves) per workgroup
+constexpr int kWaveHistWords = 2 * kHistStride;  // two lane-interleaved copies
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x = min(x, uint32_t(__shfl_xor(x, d, 64)));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) x = max(x, uint32_t(__shfl_xor(x, d, 64)));
+  return x;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// A wave's radix select (as radix_select, over the wave's own histogram):
+// for_each(fn) calls fn(key) for every key, from every lane.
+template <typename ForEach>
+__device__ uint32_t wave_radix_select(ForEach for_each, uint32_t want, uint32_t* hist, uint32_t& count_eq,
+                                      uint32_t& want_left, int hi_bit, int stop_bit, uint32_t prefix0) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = hi_bit >= 32 ? 0u : prefix0 & ~((1u << hi_bit) - 1u);
+  uint32_t pmask = hi_bit >= 32 ? 0u : ~((1u << hi_bit) - 1u);
+  for (int hi = hi_bit; hi > stop_bit; hi -= 8) {
+    const int lo = hi - 8 > stop_bit ? hi - 8 : stop_bit;
+    const uint32_t dm = (1u << (hi - lo)) - 1u;
+    for (int i = lane; i < kWaveHistWords; i += 64) hist[i] = 0;
+    wave_sync();
+    for_each([&](uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(lane & 1) * kHistStride + ((key >> lo) & dm)], 1u);
+    });
+    wave_sync();
+    // lane l: bins 4l..4l+3; the lane whose bins hold the want-th key reports
+    uint32_t h[4], own = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      h[b] = hist[4 * lane + b] + hist[kHistStride + 4 * lane + b];
+      own += h[b];
+    }
+    uint32_t x = own;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_down(x, d, 64);
+      if (lane + d < 64) x += y;
+    }
+    const uint32_t above = x - own;
+    const bool here = above < want && want <= x;
+    uint32_t dig = 0, abv = 0, cnt = 0, cum = above;
+    bool found = false;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+      if (!found && cum + h[b] >= want) {
+        dig = uint32_t(4 * lane + b);
+        abv = cum;
+        cnt = h[b];
+        found = true;
+      }
+      cum += h[b];
+    }
+    const uint64_t who = __ballot(here);
+    const int src = __builtin_ctzll(who);  // exactly one lane holds it
+    const uint32_t d = __builtin_amdgcn_readlane(dig, src);
+    want -= __builtin_amdgcn_readlane(abv, src);
+    count_eq = __builtin_amdgcn_readlane(cnt, src);
+    prefix |= d << lo;
+    pmask |= dm << lo;
+    wave_sync();  // the next pass clears the bins read here
+  }
+  want_left = want;
+  return prefix;
+}
+
+// ---------------------------------------------------------------------------
+// threshold
+
 struct ThrArgs {
   const unsigned char* plan;
   PlanLayout L;
   int32_t B, S_q, S_k, H, S_ks, k, n_chunk;
   const void* sscore;  // [n_rows, S_ks] sample scores
   uint32_t* tau;
-  int32_t* redo;
   int32_t* meta;
 };
 
-// Sampled cells a row's threshold ranks: about 1.5 times the share of the
-// sample that the selection takes, plus 32.  With the sample's cells spread
-// like the window's, the window then holds about 1.5 k + 32 R cells at or
-// above the threshold, and fewer than k only when the sample misjudges the
-// k-th score's rank by about a third; such a row is scored again.
+// Sampled cells a row's threshold ranks: 1.25 times the share of the sample
+// that the selection takes, plus 32.  With the sample's cells spread like the
+// window's, the window then holds about 1.25 k + 32 R cells at or above the
+// threshold (3072 for k = 2048, R = 16), with a spread of about R sqrt(m): it
+// holds fewer than k (the row is scored again) or more than one wave keeps
+// in LDS (the workgroup selection takes it) each about 4.6 spreads away.
 __device__ __forceinline__ int64_t sample_rank(int64_t n_out, int64_t n, int64_t ns) {
-  return (3 * n_out * ns + 2 * n - 1) / (2 * n) + 32;
+  return (5 * n_out * ns + 4 * n - 1) / (4 * n) + 32;
 }
 
 template <bool BF>
 __global__ void __launch_bounds__(kFThreads) threshold_kernel(const ThrArgs a) {
   __shared__ uint32_t stage[kThrStage];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[kHistWords];
   __shared__ uint32_t res[4];
+  __shared__ uint32_t mm[2 * kFWaves];
   const int t = threadIdx.x;
   const int64_t r = blockIdx.x;
   int32_t* me = a.meta + 2 * r * a.n_chunk;
   for (int j = t; j < 2 * a.n_chunk; j += kFThreads) me[j] = 0;
-  if (t == 0) a.redo[r] = 0;
   const PlanLayout& L = a.L;
   if (!plan_matches(a.plan, a.B, a.S_q, a.S_k, a.H, 128, L)) {
     if (t == 0) a.tau[r] = kTauNone;
@@ -262,9 +425,28 @@ __global__ void __launch_bounds__(kFThreads) threshold_kernel(const ThrArgs a) {
       return rank_key(static_cast<const uint32_t*>(a.sscore)[base + i]);
   };
   const bool staged = ns <= kThrStage;
+  int hi_bit = 32;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   if (staged) {
-    for (int64_t i = t; i < ns; i += kFThreads) stage[i] = key_at(i);
-    __syncthreads();
+    // every load of a thread issued before the first store: their latencies overlap
+    constexpr int U = kThrStage / kFThreads;
+    uint32_t kv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = int64_t(u) * kFThreads + t;
+      kv[u] = key_at(i < ns ? i : ns - 1);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = int64_t(u) * kFThreads + t;
+      if (i < ns) {
+        stage[i] = kv[u];
+        kmin = min(kmin, kv[u]);
+        kmax = max(kmax, kv[u]);
+      }
+    }
+    block_min_max(kmin, kmax, mm);
+    hi_bit = varying_bits(kmin, kmax);
   }
   auto for_each = [&](auto fn) {
     if (staged) {
@@ -273,8 +455,12 @@ __global__ void __launch_bounds__(kFThreads) threshold_kernel(const ThrArgs a) {
       for (int64_t i = t; i < ns; i += kFThreads) fn(key_at(i));
     }
   };
+  // the top 16 key bits of the m-th best sampled score, lower bits 0: at
+  // least m sampled cells reach it (a threshold a little below the m-th
+  // score takes a few more candidates, in two passes instead of four)
   uint32_t count_eq, left;
-  const uint32_t T = radix_select(for_each, uint32_t(m), hist, res, count_eq, left);
+  const uint32_t T = radix_select<kFThreads>(for_each, uint32_t(m), hist, res, count_eq, left,
+                                             hi_bit > 16 ? hi_bit : 16, 16, kmin);
   if (t == 0) a.tau[r] = T;
 }
 
@@ -285,54 +471,294 @@ struct SelArgs {
   const unsigned char* plan;
   PlanLayout L;
   int32_t B, S_q, S_k, H, D, k, n_chunk, pass;
-  const uint2* cand;  // [n_rows, S_k] (score bits, column)
+  const uint2* cand;   // [n_rows, S_k] (score bits, column)
   int32_t* meta;
   uint32_t* tau;
-  int32_t* redo;
+  int32_t* redo;       // rows scored again, gate[0] of them
+  int32_t* big;        // rows left to the workgroup kernel, gate[1] of them
   int32_t* gate;
+  const int32_t* list; // workgroup kernel: its rows (redo or big), list_count of them; NULL: row = workgroup
+  const int32_t* list_count;
   int32_t* out_idx;
   float* out_val;
   int32_t* n_redo;
 };
 
-struct SelSmem {
-  union {
-    uint32_t key[kSelStage];     // the candidates' keys, by position
-    uint64_t pair[kMaxTopK];     // rank order: (key, ~slot) of the selection
-  };
-  uint32_t out_bits[kMaxTopK];   // the selection in column order: score bits
-  int32_t out_col[kMaxTopK];     // and columns
-  uint32_t hist[256];
-  int32_t pc0[kFThreads];        // a group's chunk entries: first column,
-  uint32_t pbase[kFThreads];     // first position
-  uint32_t wsum[kFWaves];
-  uint32_t res[4];
+// Pass 1, a row short of candidates: it is scored again keeping its whole
+// window (threshold 0, chunk entries cleared, on the redo list).
+__device__ void send_to_redo(const SelArgs& a, int64_t r, int lane_in_group, int group_size) {
+  int32_t* mw = a.meta + 2 * r * a.n_chunk;
+  for (int j = lane_in_group; j < 2 * a.n_chunk; j += group_size) mw[j] = 0;
+  if (lane_in_group == 0) {
+    a.tau[r] = 0u;
+    a.redo[atomicAdd(&a.gate[0], 1)] = int32_t(r);
+  }
+}
+
+// ---- one wave per row (pass 1, by column) ---------------------------------
+
+constexpr int kRowStage = 4096;   // candidates a wave keeps in LDS
+constexpr int kRowChunks = 128;   // chunk entries a wave keeps
+
+struct RowWave {
+  uint32_t key[kRowStage];        // keys by position; then the selection's positions
+  uint32_t hist[kWaveHistWords];
+  int32_t pc0[kRowChunks];        // chunk entries: first column, first position
+  uint32_t pbase[kRowChunks];
 };
 
-// Every candidate position of row r in column order, 256 at a time: calls
-// fn(valid, position, candidate index) from every thread the same number of
-// times (fn may contain barriers).  The row's chunks are read kFThreads at a
-// time; a chunk's candidates are consecutive positions, in column order, and
-// the chunks' columns ascend.
-template <typename Fn>
-__device__ void walk(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
+// Slots in the row's candidate area of ascending candidate positions: each
+// lane keeps the chunk of its last position and moves forward from there
+// (the last chunk starting at or before p; chunks with no candidate share
+// their base with the next one), so a wave walking positions in order does
+// a step or two per position instead of a search.
+struct SlotCursor {
+  int j = 0;
+  __device__ __forceinline__ uint32_t slot(const RowWave& w, int n_chunk, uint32_t p) {
+    while (j + 1 < n_chunk && w.pbase[j + 1] <= p) ++j;
+    return uint32_t(w.pc0[j]) + (p - w.pbase[j]);
+  }
+};
+
+__global__ void __launch_bounds__(64 * kRowWaves) select_rows_kernel(const SelArgs a) {
+  __shared__ RowWave sm[kRowWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r = int64_t(blockIdx.x) * kRowWaves + wave;
+  const PlanLayout& L = a.L;
+  if (r >= L.n_rows) return;
+  RowWave& w = sm[wave];
+  const int k = a.k;
+  int32_t* oi = a.out_idx + r * k;
+  float* ov = a.out_val != nullptr ? a.out_val + r * k : nullptr;
+  if (!plan_matches(a.plan, a.B, a.S_q, a.S_k, a.H, a.D, L)) {  // loud, not plausible
+    for (int i = lane; i < k; i += 64) {
+      oi[i] = -1;
+      if (ov) ov[i] = __int_as_float(0x7FC00000);
+    }
+    if (lane == 0) a.tau[r] = kTauNone;
+    return;
+  }
+  auto to_big = [&]() {
+    if (lane == 0) a.big[atomicAdd(&a.gate[1], 1)] = int32_t(r);
+  };
+  if (a.n_chunk > kRowChunks) {
+    to_big();
+    return;
+  }
+  const int64_t s = reinterpret_cast<const int32_t*>(a.plan + L.off_start)[r];
+  const int64_t e = reinterpret_cast<const int32_t*>(a.plan + L.off_end)[r];
+  const int64_t n = e > s ? e - s : 0;
+  const uint32_t n_out = uint32_t(n < k ? n : k);
+  // chunk entries (lane l: chunks l and l + 64) and their first positions
+  const int32_t* me = a.meta + 2 * r * a.n_chunk;
+  const int j0 = lane, j1 = lane + 64;
+  const int32_t c00 = j0 < a.n_chunk ? me[2 * j0] : 0, c01 = j1 < a.n_chunk ? me[2 * j1] : 0;
+  const uint32_t n0 = j0 < a.n_chunk ? uint32_t(me[2 * j0 + 1]) : 0u;
+  const uint32_t n1 = j1 < a.n_chunk ? uint32_t(me[2 * j1 + 1]) : 0u;
+  const uint32_t i0 = wave_scan(n0), i1 = wave_scan(n1);
+  const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
+  const uint32_t C = t0 + __builtin_amdgcn_readlane(i1, 63);
+  if (C < n_out) {
+    send_to_redo(a, r, lane, 64);
+    return;
+  }
+  if (lane == 0) a.tau[r] = kTauNone;  // done: a second pass keeps nothing of it
+  if (C > uint32_t(kRowStage)) {
+    to_big();
+    return;
+  }
+  for (int i = int(n_out) + lane; i < k; i += 64) {
+    oi[i] = -1;
+    if (ov) ov[i] = -__builtin_inff();
+  }
+  if (n_out == 0) return;
+  if (j0 < kRowChunks) {
+    w.pc0[j0] = c00;
+    w.pbase[j0] = i0 - n0;
+  }
+  if (j1 < kRowChunks) {
+    w.pc0[j1] = c01;
+    w.pbase[j1] = t0 + i1 - n1;
+  }
+  wave_sync();
+
+  // ---- stage the keys by position (loads issued eight at a time) ----------
+  const uint2* row = a.cand + r * int64_t(a.S_k);
+  const int nc = a.n_chunk;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  constexpr int U = 8;
+  SlotCursor cur;
+  for (uint32_t p0 = 0; p0 < C; p0 += 64 * U) {
+    uint32_t bits[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t p = p0 + uint32_t(64 * u + lane);
+      bits[u] = row[p < C ? cur.slot(w, nc, p) : 0u].x;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t p = p0 + uint32_t(64 * u + lane);
+      if (p < C) {
+        const uint32_t key = rank_key(bits[u]);
+        w.key[p] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+  }
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  wave_sync();
+
+  // ---- threshold: key T, and for keys equal to T the positions up to P2 ---
+  const bool all = C == n_out;
+  uint32_t T = 0, P2 = 0xFFFFFFFFu;
+  if (!all) {
+    uint32_t count_eq, want;
+    T = wave_radix_select(
+        [&](auto fn) {
+          for (uint32_t p = lane; p < C; p += 64) fn(w.key[p]);
+        },
+        n_out, w.hist, count_eq, want, varying_bits(kmin, kmax), 0, kmin);
+    if (want < count_eq) {  // ties at T: the want smallest positions among them
+      int nbits = 1;
+      while ((uint32_t(1) << nbits) < C) ++nbits;
+      const uint32_t top = (1u << nbits) - 1u;
+      uint32_t ce2, left2;
+      const uint32_t V = wave_radix_select(
+          [&](auto fn) {
+            for (uint32_t p = lane; p < C; p += 64)
+              if (w.key[p] == T) fn(top - p);
+          },
+          want, w.hist, ce2, left2, nbits, 0, 0u);
+      P2 = top - V;
+    }
+  }
+
+  // ---- the selection's positions in column order, in place ----------------
+  // (a step writes only places below the positions it read)
+  uint32_t done = 0;
+  for (uint32_t p0 = 0; p0 < C; p0 += 64) {
+    const uint32_t p = p0 + uint32_t(lane);
+    bool in = false;
+    if (p < C) {
+      const uint32_t key = w.key[p];
+      in = all || key > T || (key == T && p <= P2);
+    }
+    const uint64_t b = __ballot(in);
+    wave_sync();
+    if (in) w.key[done + lanes_below(b)] = p;
+    done += uint32_t(__popcll(b));
+  }
+  wave_sync();
+
+  // ---- output: scores and columns read back by slot ---------------------------
+  SlotCursor oc;
+  for (uint32_t i0 = 0; i0 < n_out; i0 += 64 * U) {
+    uint2 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + uint32_t(64 * u + lane);
+      v[u] = row[i < n_out ? oc.slot(w, nc, w.key[i]) : 0u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = i0 + uint32_t(64 * u + lane);
+      if (i < n_out) {
+        oi[i] = int32_t(v[u].y);
+        if (ov) ov[i] = __uint_as_float(v[u].x);
+      }
+    }
+  }
+}
+
+// ---- one workgroup per row ---------------------------------------------------
+struct SelSmem {
+  // the candidates as (rank key, slot) by position, slot = index in the
+  // row's candidate area; compacted in place to the selection in column
+  // order; rank order sorts (key, ~place) pairs held past the selection's
+  // kMaxTopK entries
+  uint2 cand[kSelStage];
+  uint32_t hist[kHistWords];
+  int32_t pc0[kPieceGroup];      // a group's chunk entries: first column,
+  uint32_t pcnt[kPieceGroup];    // candidates,
+  uint32_t pbase[kPieceGroup];   // first position
+  uint32_t wsum[kSelWaves];
+  uint32_t res[4];
+  uint32_t mm[2 * kSelWaves];
+};
+static_assert(2 * kMaxTopK <= kSelStage, "rank order sorts behind the selection");
+
+// Loads per lane issued before any is used (their latencies overlap).
+constexpr int kSelUnroll = 4;
+
+// Reads the row's chunk entries kPieceGroup at a time and, for each group,
+// runs body(gsize, gbase) with pc0 / pcnt / pbase filled (pbase relative to
+// gbase, the positions of the earlier groups).  Contains barriers.
+template <typename Body>
+__device__ void for_groups(const SelArgs& a, int64_t r, SelSmem& sm, Body body) {
   const int t = threadIdx.x;
   const int32_t* me = a.meta + 2 * r * a.n_chunk;
   uint32_t gbase = 0;
-  for (int g0 = 0; g0 < a.n_chunk; g0 += kFThreads) {
+  for (int g0 = 0; g0 < a.n_chunk; g0 += kPieceGroup) {
     const int j = g0 + t;
-    const int32_t c0 = j < a.n_chunk ? me[2 * j] : 0;
-    const uint32_t cnt = j < a.n_chunk ? uint32_t(me[2 * j + 1]) : 0u;
+    const bool own = t < kPieceGroup && j < a.n_chunk;
+    const int32_t c0 = own ? me[2 * j] : 0;
+    const uint32_t cnt = own ? uint32_t(me[2 * j + 1]) : 0u;
     uint32_t total;
-    const uint32_t incl = block_scan(cnt, sm.wsum, total);
-    sm.pc0[t] = c0;
-    sm.pbase[t] = incl - cnt;
-    const int gsize = a.n_chunk - g0 < kFThreads ? a.n_chunk - g0 : kFThreads;
+    const uint32_t incl = block_scan<kSelWaves>(cnt, sm.wsum, total);
+    if (t < kPieceGroup) {
+      sm.pc0[t] = c0;
+      sm.pcnt[t] = cnt;
+      sm.pbase[t] = incl - cnt;
+    }
+    const int gsize = a.n_chunk - g0 < kPieceGroup ? a.n_chunk - g0 : kPieceGroup;
     __syncthreads();
-    for (uint32_t q0 = 0; q0 < total; q0 += kFThreads) {
+    body(gsize, gbase, total);
+    gbase += total;
+    __syncthreads();  // the next group rewrites the entries
+  }
+}
+
+// Every candidate of row r, chunk by chunk (a wave per chunk, its lanes over
+// the chunk's candidates): fn(position, slot, score bits) -- positions follow
+// the columns, slots index the row's candidate area.  fn must not contain
+// barriers (the waves' shares differ).
+template <typename Fn>
+__device__ void for_candidates(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint2* row = a.cand + r * int64_t(a.S_k);
+  for_groups(a, r, sm, [&](int gsize, uint32_t gbase, uint32_t) {
+    for (int jj = wave; jj < gsize; jj += kSelWaves) {
+      const uint32_t c0 = uint32_t(sm.pc0[jj]), cnt = sm.pcnt[jj], base = gbase + sm.pbase[jj];
+      for (uint32_t i0 = 0; i0 < cnt; i0 += 64 * kSelUnroll) {
+        uint32_t bits[kSelUnroll];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+          const uint32_t i = i0 + uint32_t(64 * u + lane);
+          bits[u] = row[c0 + (i < cnt ? i : cnt - 1)].x;
+        }
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+          const uint32_t i = i0 + uint32_t(64 * u + lane);
+          if (i < cnt) fn(base + i, c0 + i, bits[u]);
+        }
+      }
+    }
+  });
+}
+
+// Every candidate position in order, kSelThreads at a time: fn(valid,
+// position, (key, slot)) from every thread the same number of times (fn may
+// contain barriers).  For rows whose candidates do not fit in LDS; the
+// position's chunk is found by a binary search over the group's entries.
+template <typename Fn>
+__device__ void walk(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
+  const int t = threadIdx.x;
+  const uint2* row = a.cand + r * int64_t(a.S_k);
+  for_groups(a, r, sm, [&](int gsize, uint32_t gbase, uint32_t total) {
+    for (uint32_t q0 = 0; q0 < total; q0 += kSelThreads) {
       const uint32_t q = q0 + uint32_t(t);
-      // the last chunk of the group starting at or before q (chunks with no
-      // candidate share their base with the next one)
       int lo = 0, hi = gsize - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -341,28 +767,24 @@ __device__ void walk(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
         else
           hi = mid - 1;
       }
-      fn(q < total, gbase + q, r * int64_t(a.S_k) + sm.pc0[lo] + int64_t(q - sm.pbase[lo]));
+      const uint32_t slot = q < total ? uint32_t(sm.pc0[lo]) + (q - sm.pbase[lo]) : 0u;
+      fn(q < total, gbase + q, make_uint2(rank_key(row[slot].x), slot));
     }
-    gbase += total;
-    __syncthreads();  // the next group rewrites pc0 and pbase
-  }
+  });
 }
 
+// The selection of row r by the whole workgroup: rows whose candidates do
+// not fit one wave's LDS (or whose chunk entries do not), pass 1 by score,
+// and pass 2.
 template <bool BY_SCORE>
-__global__ void __launch_bounds__(kFThreads) select_kernel(const SelArgs a) {
-  __shared__ SelSmem sm;
+__device__ void select_row(const SelArgs& a, int64_t r, SelSmem& sm) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t r = blockIdx.x;
-  if (a.pass == 2) {
-    if (r == 0 && t == 0 && a.n_redo != nullptr) *a.n_redo = *a.gate;
-    if (a.redo[r] == 0) return;
-  }
   const int k = a.k;
   int32_t* oi = a.out_idx + r * k;
   float* ov = a.out_val != nullptr ? a.out_val + r * k : nullptr;
   const PlanLayout& L = a.L;
   if (!plan_matches(a.plan, a.B, a.S_q, a.S_k, a.H, a.D, L)) {  // loud, not plausible
-    for (int i = t; i < k; i += kFThreads) {
+    for (int i = t; i < k; i += kSelThreads) {
       oi[i] = -1;
       if (ov) ov[i] = __int_as_float(0x7FC00000);
     }
@@ -373,29 +795,23 @@ __global__ void __launch_bounds__(kFThreads) select_kernel(const SelArgs a) {
   const int64_t e = reinterpret_cast<const int32_t*>(a.plan + L.off_end)[r];
   const int64_t n = e > s ? e - s : 0;
   const uint32_t n_out = uint32_t(n < k ? n : k);
-  for (int i = int(n_out) + t; i < k; i += kFThreads) {
+  for (int i = int(n_out) + t; i < k; i += kSelThreads) {
     oi[i] = -1;
     if (ov) ov[i] = -__builtin_inff();
   }
   // candidates of the row
   const int32_t* me = a.meta + 2 * r * a.n_chunk;
   uint32_t mine = 0;
-  for (int j = t; j < a.n_chunk; j += kFThreads) mine += uint32_t(me[2 * j + 1]);
+  for (int j = t; j < a.n_chunk; j += kSelThreads) mine += uint32_t(me[2 * j + 1]);
   uint32_t C;
-  block_scan(mine, sm.wsum, C);
+  block_scan<kSelWaves>(mine, sm.wsum, C);
   if (C < n_out) {
     // fewer than the selection takes: the threshold was too high for this
     // row (pass 1), which is scored again keeping every cell of its window
     if (a.pass == 1) {
-      int32_t* mw = a.meta + 2 * r * a.n_chunk;
-      for (int j = t; j < 2 * a.n_chunk; j += kFThreads) mw[j] = 0;
-      if (t == 0) {
-        a.tau[r] = 0u;
-        a.redo[r] = 1;
-        atomicAdd(a.gate, 1);
-      }
+      send_to_redo(a, r, t, kSelThreads);
     } else {  // cannot happen: threshold 0 keeps the whole window
-      for (int i = t; i < int(n_out); i += kFThreads) {
+      for (int i = t; i < int(n_out); i += kSelThreads) {
         oi[i] = -1;
         if (ov) ov[i] = __int_as_float(0x7FC00000);
       }
@@ -405,31 +821,40 @@ __global__ void __launch_bounds__(kFThreads) select_kernel(const SelArgs a) {
   if (a.pass == 1 && t == 0) a.tau[r] = kTauNone;  // done: a second pass keeps nothing of it
   if (n_out == 0) return;
 
-  // ---- the threshold among the candidates: key T, and for keys equal to T
-  // the positions up to P2 (positions follow the columns) ----------------------
+  // ---- stage (key, slot) by position when it fits; keys' range -------------
   const bool all = C == n_out;
   const bool staged = C <= uint32_t(kSelStage);
+  int hi_bit = 32;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (staged) {
+    for_candidates(a, r, sm, [&](uint32_t p, uint32_t slot, uint32_t bits) {
+      const uint32_t key = rank_key(bits);
+      sm.cand[p] = make_uint2(key, slot);
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+    });
+    block_min_max<kSelWaves>(kmin, kmax, sm.mm);  // its barriers also complete the staging
+    hi_bit = varying_bits(kmin, kmax);
+  }
+
+  // ---- the threshold among the candidates: key T, and for keys equal to T
+  // the positions up to P2 (positions follow the columns) ----------------------
   uint32_t T = 0, P2 = 0xFFFFFFFFu;
   if (!all) {
-    if (staged) {
-      walk(a, r, sm, [&](bool valid, uint32_t p, int64_t ci) {
-        if (valid) sm.key[p] = rank_key(a.cand[ci].x);
-      });
-      __syncthreads();
-    }
-    // fn(key, position) over every candidate
+    // fn(key, position) over every candidate (no barrier in fn)
     auto visit = [&](auto fn) {
       if (staged) {
-        for (uint32_t p = t; p < C; p += kFThreads) fn(sm.key[p], p);
+        for (uint32_t p = t; p < C; p += kSelThreads) {
+          const uint2 v = sm.cand[p];
+          fn(v.x, p);
+        }
       } else {
-        walk(a, r, sm, [&](bool valid, uint32_t p, int64_t ci) {
-          if (valid) fn(rank_key(a.cand[ci].x), p);
-        });
+        for_candidates(a, r, sm, [&](uint32_t p, uint32_t, uint32_t bits) { fn(rank_key(bits), p); });
       }
     };
     uint32_t count_eq, want;
-    T = radix_select([&](auto fn) { visit([&](uint32_t key, uint32_t) { fn(key); }); }, n_out, sm.hist, sm.res,
-                     count_eq, want);
+    T = radix_select<kSelThreads>([&](auto fn) { visit([&](uint32_t key, uint32_t) { fn(key); }); }, n_out,
+                                  sm.hist, sm.res, count_eq, want, hi_bit, 0, kmin);
     if (want < count_eq) {
       // ties at T: the want smallest positions among them, as the want
       // largest of top - position
@@ -437,7 +862,7 @@ __global__ void __launch_bounds__(kFThreads) select_kernel(const SelArgs a) {
       while ((uint64_t(1) << nbits) < uint64_t(C)) ++nbits;
       const uint32_t top = nbits >= 32 ? 0xFFFFFFFFu : (1u << nbits) - 1u;
       uint32_t ce2, left2;
-      const uint32_t V = radix_select(
+      const uint32_t V = radix_select<kSelThreads>(
           [&](auto fn) {
             visit([&](uint32_t key, uint32_t p) {
               if (key == T) fn(top - p);
@@ -447,73 +872,99 @@ __global__ void __launch_bounds__(kFThreads) select_kernel(const SelArgs a) {
       P2 = top - V;
     }
   }
-  auto selected = [&](uint32_t key, uint32_t p) { return all || key > T || (key == T && p <= P2); };
 
-  // ---- the selection in column order, staged in LDS --------------------------
-  uint32_t done = 0;
-  walk(a, r, sm, [&](bool valid, uint32_t p, int64_t ci) {
-    bool in = false;
-    if (valid) {
-      const uint32_t key = all ? 0u : (staged ? sm.key[p] : rank_key(a.cand[ci].x));
-      in = selected(key, p);
-    }
-    const uint64_t b = __ballot(in);
-    if (lane == 0) sm.wsum[wave] = uint32_t(__popcll(b));
-    __syncthreads();
-    uint32_t before = 0, total = 0;
+  // ---- the selection in column order, compacted to the front of sm.cand ---
+  // (in place when staged: a round writes only places below its positions,
+  // after every thread has read them)
+  if (!all || !staged) {
+    uint32_t done = 0;
+    auto compact = [&](bool valid, uint32_t p, uint2 v) {
+      const bool in = valid && (all || v.x > T || (v.x == T && p <= P2));
+      const uint64_t b = __ballot(in);
+      if (lane == 0) sm.wsum[wave] = uint32_t(__popcll(b));
+      __syncthreads();
+      uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < kFWaves; ++w) {
-      before += w < wave ? sm.wsum[w] : 0u;
-      total += sm.wsum[w];
-    }
-    if (in) {
-      const uint32_t at = done + before + lanes_below(b);
-      if (at < n_out) {  // exactly n_out are selected
-        const uint2 v = a.cand[ci];
-        sm.out_bits[at] = v.x;
-        sm.out_col[at] = int32_t(v.y);
+      for (int w = 0; w < kSelWaves; ++w) {
+        before += w < wave ? sm.wsum[w] : 0u;
+        total += sm.wsum[w];
       }
+      if (in) {
+        const uint32_t at = done + before + lanes_below(b);
+        if (at < n_out) sm.cand[at] = v;  // exactly n_out are selected
+      }
+      done += total;
+      __syncthreads();  // wsum is rewritten by the next round
+    };
+    if (staged) {
+      for (uint32_t p0 = 0; p0 < C; p0 += kSelThreads) {
+        const uint32_t p = p0 + uint32_t(t);
+        const uint2 v = p < C ? sm.cand[p] : make_uint2(0u, 0u);
+        compact(p < C, p, v);
+      }
+    } else {
+      walk(a, r, sm, compact);
     }
-    done += total;
-    __syncthreads();  // wsum is rewritten by the next round
-  });
+  }
   __syncthreads();
 
+  // ---- output: scores and columns read back by slot ---------------------------
+  const uint2* row = a.cand + r * int64_t(a.S_k);
   if constexpr (!BY_SCORE) {
-    for (int i = t; i < int(n_out); i += kFThreads) {
-      oi[i] = sm.out_col[i];
-      if (ov) ov[i] = __uint_as_float(sm.out_bits[i]);
+    for (int i = t; i < int(n_out); i += kSelThreads) {
+      const uint2 v = row[sm.cand[i].y];
+      oi[i] = int32_t(v.y);
+      if (ov) ov[i] = __uint_as_float(v.x);
     }
   } else {
-    // rank order: (key, ~slot) pairs sorted descending, slot = place in the
-    // column order (so equal keys keep the smaller column first); padding 0
-    // sorts below every real pair
+    // rank order: (key, ~place) pairs sorted descending, place = index in
+    // the column order (so equal keys keep the smaller column first); padding
+    // 0 sorts below every real pair
+    uint64_t* pair = reinterpret_cast<uint64_t*>(&sm.cand[kMaxTopK]);
     int P = 1;
     while (P < int(n_out)) P <<= 1;
-    for (int i = t; i < P; i += kFThreads)
-      sm.pair[i] = i < int(n_out) ? (uint64_t(rank_key(sm.out_bits[i])) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(i))
-                                  : 0ull;
+    for (int i = t; i < P; i += kSelThreads)
+      pair[i] = i < int(n_out) ? (uint64_t(sm.cand[i].x) << 32) | uint64_t(0xFFFFFFFFu - uint32_t(i)) : 0ull;
     __syncthreads();
     for (int size = 2; size <= P; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = t; i < P / 2; i += kFThreads) {
+        for (int i = t; i < P / 2; i += kSelThreads) {
           const int lo = 2 * stride * (i / stride) + (i % stride);
           const int hi = lo + stride;
           const bool descending = (lo & size) == 0;
-          const uint64_t x = sm.pair[lo], y = sm.pair[hi];
+          const uint64_t x = pair[lo], y = pair[hi];
           if ((x < y) == descending) {
-            sm.pair[lo] = y;
-            sm.pair[hi] = x;
+            pair[lo] = y;
+            pair[hi] = x;
           }
         }
         __syncthreads();
       }
     }
-    for (int i = t; i < int(n_out); i += kFThreads) {
-      const uint32_t slot = 0xFFFFFFFFu - uint32_t(sm.pair[i]);
-      oi[i] = sm.out_col[slot];
-      if (ov) ov[i] = __uint_as_float(sm.out_bits[slot]);
+    for (int i = t; i < int(n_out); i += kSelThreads) {
+      const uint2 v = row[sm.cand[0xFFFFFFFFu - uint32_t(pair[i])].y];
+      oi[i] = int32_t(v.y);
+      if (ov) ov[i] = __uint_as_float(v.x);
     }
+  }
+}
+
+// LIST: the rows of a.list (a.list_count of them), walked by a fixed grid
+// (one workgroup per CU: a row of such a list is long); else one workgroup
+// per row, two per CU.
+template <bool BY_SCORE, bool LIST>
+__global__ void __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(LIST ? 4 : 8, LIST ? 4 : 8)))
+select_kernel(const SelArgs a) {
+  __shared__ SelSmem sm;
+  if constexpr (!LIST) {
+    select_row<BY_SCORE>(a, blockIdx.x, sm);
+  } else {
+    const int32_t count = *a.list_count;
+    for (int32_t i = blockIdx.x; i < count; i += int32_t(gridDim.x)) {
+      select_row<BY_SCORE>(a, a.list[i], sm);
+      __syncthreads();  // the next row reuses sm
+    }
+    if (a.pass == 2 && blockIdx.x == 0 && threadIdx.x == 0 && a.n_redo != nullptr) *a.n_redo = a.gate[0];
   }
 }
 
@@ -559,7 +1010,6 @@ hipError_t launch_threshold(const TopkLayout& T, int32_t B, int32_t S_q, int32_t
   a.n_chunk = n_chunk;
   a.sscore = ws + T.off_sscore;
   a.tau = reinterpret_cast<uint32_t*>(ws + T.off_tau);
-  a.redo = reinterpret_cast<int32_t*>(ws + T.off_redo);
   a.meta = reinterpret_cast<int32_t*>(ws + T.off_meta);
   const dim3 grid(unsigned(a.L.n_rows));
   if (scores_bf16)
@@ -587,15 +1037,34 @@ hipError_t launch_select(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_
   a.meta = reinterpret_cast<int32_t*>(ws + T.off_meta);
   a.tau = reinterpret_cast<uint32_t*>(ws + T.off_tau);
   a.redo = reinterpret_cast<int32_t*>(ws + T.off_redo);
+  a.big = reinterpret_cast<int32_t*>(ws + T.off_big);
   a.gate = reinterpret_cast<int32_t*>(ws + T.off_gate);
   a.out_idx = out_idx;
   a.out_val = out_val;
   a.n_redo = n_redo;
-  const dim3 grid(unsigned(a.L.n_rows));
-  if (by_score)
-    hipLaunchKernelGGL(select_kernel<true>, grid, dim3(kFThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(select_kernel<false>, grid, dim3(kFThreads), 0, stream, a);
+  // rows walked from a list: one workgroup per CU of a 256-CU device at most
+  const unsigned list_grid = unsigned(std::min<int64_t>(a.L.n_rows, 256));
+  if (pass == 2) {
+    a.list = a.redo;
+    a.list_count = a.gate;
+    if (by_score)
+      hipLaunchKernelGGL((select_kernel<true, true>), dim3(list_grid), dim3(kSelThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((select_kernel<false, true>), dim3(list_grid), dim3(kSelThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (by_score) {
+    hipLaunchKernelGGL((select_kernel<true, false>), dim3(unsigned(a.L.n_rows)), dim3(kSelThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  // by column: a wave per row, then the rows it leaves to the workgroup kernel
+  hipLaunchKernelGGL(select_rows_kernel, dim3(unsigned((a.L.n_rows + kRowWaves - 1) / kRowWaves)),
+                     dim3(64 * kRowWaves), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.list = a.big;
+  a.list_count = a.gate + 1;
+  hipLaunchKernelGGL((select_kernel<false, true>), dim3(list_grid), dim3(kSelThreads), 0, stream, a);
   return hipGetLastError();
 }
 
