@@ -13,7 +13,7 @@ import torch
 import mqa_logits_scoring_amd as lib
 import oracle
 import workloads as W
-from gpu_util import (compare_all_rows, compare_rows, dev_inputs, inside_check_all_rows, make_plan,
+from gpu_util import (out_dtype, compare_all_rows, compare_rows, dev_inputs, inside_check_all_rows, make_plan,
                       mask_check_all_rows, run, sample_rows, to_f64)
 import oracle_pins as P
 
@@ -430,6 +430,28 @@ def test_mx_block_layout_probes():
         out = run(wl, dev_inputs(wl))
         torch.cuda.synchronize()
         _full_compare(wl, out, what=f"layout probe {wl.fmt}")
+
+
+# ---------------------------------------------------------------------------
+# decode-sized batches: at most two query rows per batch, where every wave of
+# a unit scores the tile's two rows over its own share of the columns
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S_q", [1, 2])
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_decode_rows_every_cell(fmt, S_q):
+    """Every cell of B = 5 batches of one or two query rows, causal offsets of
+    every size (an empty window, a window of one key, the whole of K) and
+    S_k long enough to span several chunks per tile, output pre-filled with
+    NaN so a cell no wave wrote is caught."""
+    wl = W.make_random(fmt, 5, S_q, 20000, seed=80 + S_q, offsets=[0, -19999, -19998 - S_q, -7000, -12345],
+                       w_dtype="bf16" if fmt == "mxfp4" else "f32")
+    d = dev_inputs(wl)
+    out = torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), dtype=out_dtype(wl), device="cuda")
+    run(wl, d, out=out)
+    torch.cuda.synchronize()
+    inside_check_all_rows(wl, out)
+    _full_compare(wl, out, what=f"decode {fmt} S_q={S_q}")
 
 
 # ---------------------------------------------------------------------------
