@@ -216,7 +216,12 @@ idx_status_t check_args(const idx_logits_args_t* a, bool keys_elsewhere = false,
     return fail(IDX_E_UNSUPPORTED, "S_k=%d is too long: one batch's K must stay under 2 GiB", a->S_k);
   const idx::PlanLayout L = idx::plan_layout(a->B, a->S_q, a->H);
   if (L.total > 0xFFFFFFFFull) return fail(IDX_E_INVALID, "plan too large");
-  if (positions_of(L, pick_chunks(a->S_k, L.n_tiles, a->S_q, L.tile_rows, kMaxCus)) > (int64_t(1) << 31) - 1)
+  // decode-sized calls (at most two rows per batch at 64 heads) cut units of
+  // at least kMinChunk columns; the others as pick_chunks
+  const int64_t max_chunks = a->H == 64 && a->S_q <= idx::kTileRows / 4
+                                 ? cdiv(int64_t(a->S_k) + idx::kColAlign - 1, kMinChunk)
+                                 : pick_chunks(a->S_k, L.n_tiles, a->S_q, L.tile_rows, kMaxCus);
+  if (positions_of(L, max_chunks) > (int64_t(1) << 31) - 1)
     return fail(IDX_E_INVALID, "problem too large for one grid");
   return IDX_OK;
 }
@@ -296,7 +301,13 @@ idx_status_t set_units(idx::ScoreArgs& k, const idx::PlanLayout& L, int64_t S_k,
   hipError_t he = device_cus(cus);
   if (he != hipSuccess) return fail(IDX_E_HIP, "device query failed: %s", hipGetErrorString(he));
   k.min_chunk = int32_t(kMinChunk);
-  k.n_chunk = pick_chunks(S_k, L.n_tiles, k.S_q, L.tile_rows, std::min<int64_t>(cus, kMaxCus), units_per_cu);
+  // Decode-sized tiles split a unit over all four waves: few, long units
+  // then (one round, two per CU; measured against two rounds and against
+  // units of one width for every tile), since each wave's start (its rows'
+  // Q, weights and windows) costs about as much as streaming 500 keys.
+  const int64_t rows = k.wave_split ? L.tile_rows : k.S_q;
+  if (k.wave_split) units_per_cu = std::min<int64_t>(units_per_cu, 2);
+  k.n_chunk = pick_chunks(S_k, L.n_tiles, rows, L.tile_rows, std::min<int64_t>(cus, kMaxCus), units_per_cu);
   k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
   k.n_positions = cleanup ? int32_t(positions_of(L, k.n_chunk)) : k.n_pos_compute;
   return IDX_OK;
@@ -322,6 +333,7 @@ idx::ScoreArgs score_args(const idx_logits_args_t* a, const unsigned char* p, co
   k.H = a->H;
   k.tile_rows = L.tile_rows;
   k.tiles_per_batch = int32_t(idx::tiles_per_batch(a->S_q, L.tile_rows));
+  k.wave_split = a->H == 64 && a->S_q <= idx::kTileRows / 4 ? 1 : 0;
   k.seg_per_batch = int32_t(L.n_seg / a->B);
   k.tiles_per_seg = L.tiles_per_seg;
   k.last_seg_tiles = int32_t(k.tiles_per_batch - (k.seg_per_batch - 1) * int64_t(L.tiles_per_seg));
@@ -668,6 +680,7 @@ idx_status_t idx_logits_run_topk(const idx_logits_args_t* a, const void* plan, c
   kc.cand = ws + T.off_cand;
   kc.meta = reinterpret_cast<int32_t*>(ws + T.off_meta);
   kc.tau = reinterpret_cast<const uint32_t*>(ws + T.off_tau);
+  kc.wave_split = 0;  // select mode keeps one unit per (row, chunk) entry
   if ((st = set_units(kc, L, a->S_k, false)) != IDX_OK) return st;
   if (kc.n_chunk > T.n_chunk_max) return fail(IDX_E_HIP, "chunk count %d above the workspace's", kc.n_chunk);
   e = idx::launch_threshold(T, a->B, a->S_q, a->S_k, a->H, k, a->out_dtype == IDX_BF16, kc.n_chunk, p, ws, s);

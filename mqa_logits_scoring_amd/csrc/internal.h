@@ -345,6 +345,10 @@ struct ScoreArgs {
   // min_chunk wide.
   int32_t min_chunk, n_chunk;
   int32_t seg_per_batch, tiles_per_seg, last_seg_tiles;
+  // 64-head calls with at most two query rows per batch (decode): every
+  // wave of a unit scores the tile's two rows over a quarter of its columns,
+  // instead of three of its four waves holding padding rows only
+  int32_t wave_split;
   int32_t n_pos_compute, n_positions;
   uint32_t off_start, off_end, off_slot, off_lo, off_hi, off_order;
   const unsigned char* pieces;   // per row PieceFmt<F>::N pieces of PieceFmt<F>::BYTES (formats with pieces)

@@ -341,7 +341,20 @@ __global__ void __launch_bounds__(kThreads)
   if (!plan_ok) return;
   const Unit u = decode_unit(a, pos);
   if (u.kind != kUnitCompute) return;
-  const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
+  const int tile = u.tile;
+  int c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
+  // the wave whose tile slots hold this wave's rows: its own, or with
+  // decode-sized tiles (wave_split: at most two rows per batch) slots 0 and 1
+  // for every wave, each wave taking a quarter of the unit's columns
+  int slot_wave = wave;
+  if (!SEL && a.wave_split) {
+    const int per = (((c1 - c0 + 63) / 64) + 3) / 4;  // 64-column pairs per wave
+    const int w0 = c0 + 64 * per * wave;
+    c1 = min(c1, w0 + 64 * per);
+    c0 = w0;
+    if (c0 >= c1) return;
+    slot_wave = 0;
+  }
   const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
 
@@ -352,7 +365,7 @@ __global__ void __launch_bounds__(kThreads)
   bool rvalid[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
-    const int r = slot_row[int64_t(tile) * kTileRows + wave * TW + t];
+    const int r = slot_row[int64_t(tile) * kTileRows + slot_wave * TW + t];
     rvalid[t] = r >= 0;
     rows[t] = r >= 0 ? r : first_row;
   }
@@ -452,12 +465,16 @@ __global__ void __launch_bounds__(kThreads)
                                                        kBufWord3)
                    : srs;
   const int32_t* btrow = PD ? a.btable + int64_t(b) * a.max_pages : nullptr;
+  // paged: blocks are loaded in order, and the page of the next one is read
+  // from the block table one load ahead, off the path of the key loads
+  int pg_next = 0;
+  if constexpr (PD) pg_next = __builtin_amdgcn_readfirstlane(btrow[uint32_t(min(kb0, nblk - 1)) >> a.bpp_shift]);
   auto kload = [&](int u, uint32_t (&bf)[QD], uint32_t& kword) {
     const int blk = min(kb0 + u, nblk - 1);
     if constexpr (PD) {
-      const uint32_t slot = uint32_t(blk) >> a.bpp_shift;
       const uint32_t rem = uint32_t(blk) & ((1u << a.bpp_shift) - 1u);
-      int pg = __builtin_amdgcn_readfirstlane(btrow[slot]);
+      int pg = pg_next;
+      pg_next = __builtin_amdgcn_readfirstlane(btrow[uint32_t(min(blk + 1, nblk - 1)) >> a.bpp_shift]);
       pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
       const uint32_t row0 = uint32_t(pg) * uint32_t(a.page_size) + rem * 32u;
 #pragma unroll
@@ -831,7 +848,20 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if (!plan_ok) return;
   const Unit u = decode_unit(a, pos);
   if (u.kind != kUnitCompute) return;
-  const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
+  const int tile = u.tile;
+  int c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
+  // the wave whose tile slots hold this wave's rows: its own, or with
+  // decode-sized tiles (wave_split: at most two rows per batch) slots 0 and 1
+  // for every wave, each wave taking a quarter of the unit's columns
+  int slot_wave = wave;
+  if (!SEL && a.wave_split) {
+    const int per = (((c1 - c0 + 63) / 64) + 3) / 4;  // 64-column pairs per wave
+    const int w0 = c0 + 64 * per * wave;
+    c1 = min(c1, w0 + 64 * per);
+    c0 = w0;
+    if (c0 >= c1) return;
+    slot_wave = 0;
+  }
   const int n_pairs = (c1 - c0 + 63) / 64;
   const int b = tile / a.tiles_per_batch;
 
@@ -841,7 +871,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   bool rvalid[TW];
 #pragma unroll
   for (int t = 0; t < TW; ++t) {
-    const int r = slot_row[int64_t(tile) * kTileRows + wave * TW + t];
+    const int r = slot_row[int64_t(tile) * kTileRows + slot_wave * TW + t];
     rvalid[t] = r >= 0;
     rows[t] = r >= 0 ? r : first_row;
   }
@@ -947,13 +977,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
                                              int(uint32_t(a.num_pages) * uint32_t(a.page_size) * 4u), kBufWord3)
          : srs;
   const int32_t* btrow = PD ? a.btable + int64_t(b) * a.max_pages : nullptr;
+  // paged: blocks are loaded in order, and the page of the next one is read
+  // from the block table one load ahead, off the path of the key loads
+  int pg_next = 0;
+  if constexpr (PD) pg_next = __builtin_amdgcn_readfirstlane(btrow[uint32_t(min(kb0, nblk - 1)) >> a.bpp_shift]);
   const int koff = (q >> 1) * 1024 + (32 * (q & 1) + n) * 16;
   auto kload = [&](int u, i32x8 (&bf)[2], uint32_t (&sb)[2], uint32_t& ks) {
     const int blk = min(kb0 + u, nblk - 1);
     if constexpr (PD) {
-      const uint32_t slot = uint32_t(blk) >> a.bpp_shift;
       const uint32_t rem = uint32_t(blk) & ((1u << a.bpp_shift) - 1u);
-      int pg = __builtin_amdgcn_readfirstlane(btrow[slot]);
+      int pg = pg_next;
+      pg_next = __builtin_amdgcn_readfirstlane(btrow[uint32_t(min(blk + 1, nblk - 1)) >> a.bpp_shift]);
       pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
       const uint32_t row0 = uint32_t(pg) * uint32_t(a.page_size) + rem * 32u;
 #pragma unroll
