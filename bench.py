@@ -180,8 +180,11 @@ def build_plan(lib, wl, d, plan, stream):
 
 def visible_cells(lib, wl, plan) -> int:
     """Visible cells from the windows the library's plan holds."""
-    ws, we = lib.idx_logits_plan_windows(plan, wl.B, wl.S_q, wl.S_k)
-    return int((we.long() - ws.long()).clamp(min=0).sum().item())
+    ws, we = lib.idx_logits_plan_windows(plan, wl.B, wl.S_q, wl.S_k, wl.H, wl.D)
+    v = int((we.long() - ws.long()).clamp(min=0).sum().item())
+    if v == 0 and bool((ws < 0).any()):
+        raise RuntimeError("the plan does not match the workload's dimensions")
+    return v
 
 
 def input_bytes(wl) -> int:

@@ -665,14 +665,18 @@ idx_status_t idx_logits_run_topk(const idx_logits_args_t* a, const void* plan, c
   if (e != hipSuccess) return fail(IDX_E_HIP, "top-k setup launch failed: %s", hipGetErrorString(e));
 
   // the sample: every kSampleStride-th key block, scores stored unclean
-  idx::ScoreArgs ks = score_args(a, ws + T.off_splan, WL, ws);
-  ks.S_k = int32_t(T.S_ks);
-  ks.kfrag = ws + T.off_skfrag;
-  ks.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + T.off_skscale) : nullptr;
-  ks.out = ws + T.off_sscore;
-  ks.ld = T.S_ks;
-  if ((st = set_units(ks, L, T.S_ks, false, 2)) != IDX_OK) return st;
-  if ((st = launch_scoring(x.kf, a, false, ks, s)) != IDX_OK) return st;
+  // (not needed when no window can hold more than k keys: every row then
+  // keeps its whole window, and the thresholds read no sample)
+  if (a->S_k > k) {
+    idx::ScoreArgs ks = score_args(a, ws + T.off_splan, WL, ws);
+    ks.S_k = int32_t(T.S_ks);
+    ks.kfrag = ws + T.off_skfrag;
+    ks.kscale = idx::has_kscale(x.kf) ? reinterpret_cast<const uint32_t*>(ws + T.off_skscale) : nullptr;
+    ks.out = ws + T.off_sscore;
+    ks.ld = T.S_ks;
+    if ((st = set_units(ks, L, T.S_ks, false, 2)) != IDX_OK) return st;
+    if ((st = launch_scoring(x.kf, a, false, ks, s)) != IDX_OK) return st;
+  }
 
   // thresholds, then every cell in select mode
   idx::ScoreArgs kc = score_args(a, p, WL, ws);

@@ -77,6 +77,7 @@ FUSED = [
     ("mxfp4", dict(B=1, S_q=33, S_k=9000, windows="irregular", out_dtype="bf16", w_dtype="bf16"), 512),
     ("fp8", dict(B=3, S_q=17, S_k=40000, offsets=[0, -1, -39000]), 2048),
     ("fp8", dict(B=1, S_q=9, S_k=1000, windows="irregular"), 1),
+    ("mxfp8", dict(B=2, S_q=40, S_k=1500, windows="irregular"), 2048),   # no window holds more than k: no sample
 ]
 
 
