@@ -62,7 +62,7 @@ int64_t cdiv(int64_t x, int64_t y) { return (x + y - 1) / y; }
 // anyway, takes one round of units (two workgroups per CU).
 int32_t pick_chunks(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows, int64_t cus,
                     int64_t units_per_cu = kUnitsPerCu) {
-  const int64_t span = S_k + idx::kColAlign - 1;  // widest tile coverage
+  const int64_t span = cdiv(S_k, idx::kColAlign) * idx::kColAlign;  // widest tile coverage
   const int64_t rows_per_wave = tile_rows / 4;
   const int64_t rows = S_q < tile_rows ? S_q : tile_rows;
   const int64_t active = cdiv(rows, rows_per_wave);  // waves of a tile with a real row
