@@ -62,7 +62,7 @@ def kernel_source_hash(fmt: str) -> str:
     top-k kernel)."""
     import hashlib
     h = hashlib.sha256()
-    files = ("topk.hip", "internal.h") if fmt == "topk" else ("score_kernel.h", "score_kernel_gh.h", "internal.h",
+    files = ("topk.hip", "select_wave.h", "internal.h") if fmt == "topk" else ("score_kernel.h", "score_kernel_gh.h", "internal.h",
                                                               f"score_{fmt}.hip", "api.cpp")
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -110,7 +110,7 @@ def write_traffic(argv) -> None:
     fmt, workload = wl.fmt, wl.name
     kernel_re = "score_kernel"
     if topk_k:
-        fmt, workload, kernel_re = "topk", f"topk{topk_k}:{wl.name}", "topk_kernel"
+        fmt, workload, kernel_re = "topk", f"topk{topk_k}:{wl.name}", "topk_rows_kernel|topk_kernel"
     copy_bytes = int(copy_bytes)
     kib = 1024.0
     # the copy kernel reads and writes copy_bytes per dispatch
@@ -690,7 +690,7 @@ def main():
         written = 8 * wl.B * wl.S_q * k
         tg = (read + written) / (t_us * 1e-6) / 1e9
         trec = counted_traffic(f"topk{k}:{wl.name}", "topk")
-        res["topk"] = {"k": k, "order": "column", "kernel": "topk_kernel", "kernel_us": t_us,
+        res["topk"] = {"k": k, "order": "column", "kernel": "topk_rows_kernel", "kernel_us": t_us,
                        "roofline": {"bound": "hbm", "achieved": round(tg, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(tg / HBM_PEAK_GBS, 4),
                                     "traffic": None if trec is None else trec["fetch_bytes"] + trec["write_bytes"],

@@ -21,7 +21,7 @@ PEAK_SOURCES = ["peak.hip"]
 BUILD_DIR = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "plan.hip", "prepare.hip", "topk.hip", "topk_fused.hip", "score_bf16.hip", "score_bf16rs.hip", "score_fp8.hip",
            "score_mxfp8.hip", "score_mxfp4.hip"]
-HEADERS = ["internal.h", "score_kernel.h", "score_kernel_gh.h", "plan_segment.h", os.path.join("..", "..", "include", "idx_logits.h")]
+HEADERS = ["internal.h", "score_kernel.h", "score_kernel_gh.h", "plan_segment.h", "select_wave.h", os.path.join("..", "..", "include", "idx_logits.h")]
 ARCH = "gfx950"
 
 

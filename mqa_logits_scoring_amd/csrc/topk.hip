@@ -31,7 +31,7 @@
 //     counts gives every selected column its place; in rank order they go to
 //     LDS as (key, ~column) pairs and a bitonic sort orders them.
 
-#include "internal.h"
+#include "select_wave.h"
 
 namespace idx {
 
@@ -78,13 +78,9 @@ struct TopkSmem {
   uint32_t digit, above, count, n_cand, n_sel;
 };
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
-}
-
 // Inclusive prefix sum of v over the workgroup's threads (thread order);
 // `total` receives the sum over all threads.  Contains barriers.
-__device__ uint32_t block_scan(uint32_t v, TopkSmem& sm, uint32_t& total) {
+__device__ uint32_t scan_1024(uint32_t v, TopkSmem& sm, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t x = v;
 #pragma unroll
@@ -128,7 +124,7 @@ __device__ PassResult find_digit(TopkSmem& sm, uint32_t want) {
     local += x;
   }
   uint32_t total;
-  const uint32_t incl = block_scan(local, sm, total);
+  const uint32_t incl = scan_1024(local, sm, total);
   const uint32_t above = total - incl;  // keys in the bins of higher threads
   if (above < want && above + local >= want) {
     uint32_t cum = above;
@@ -306,7 +302,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
         for (int m = 0; m < kPerThread; ++m) cm |= uint32_t((key[m] & mask) == prefix) << m;
         const uint32_t mine = uint32_t(__builtin_popcount(cm));
         uint32_t total;
-        uint32_t pos = done + block_scan(mine, sm, total) - mine;
+        uint32_t pos = done + scan_1024(mine, sm, total) - mine;
 #pragma unroll
         for (int m = 0; m < kPerThread; ++m) {
           if ((cm >> m) & 1u) {
@@ -387,7 +383,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
       __syncthreads();
       uint32_t total;
       const uint32_t mine = t < kCounts ? sm.wcount[t] : 0u;
-      const uint32_t excl = block_scan(mine, sm, total) - mine;
+      const uint32_t excl = scan_1024(mine, sm, total) - mine;
       if (t < kCounts) sm.wcount[t] = excl;  // entry t = (m, wave) in column order: its first place
       __syncthreads();
       const uint32_t bases = lane < kPerThread ? sm.wcount[lane * kTopkWaves + wave] : 0u;
@@ -478,6 +474,427 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
   }
 }
 
+// ---------------------------------------------------------------------------
+// Column order, one 256-thread workgroup per row
+//
+// The kernel above holds a whole CU for one row, all of it in registers.
+// Rows selected by column run here instead, four workgroups per CU, each
+// with about 33 KB of LDS:
+//  - A window of at most kTbStage columns is staged whole: key p is column
+//    s + p.
+//  - A wider one is thresholded first, as the fused selection is: the key of
+//    the m-th best of a sample of its columns (the first 32 of every 512),
+//    its low 16 bits cleared, m = sample_rank.  The four waves then stream a
+//    quarter of the window each and append the keys that reach it, with
+//    their columns, in any order: about 1.25 k + 512 of them.
+//  - A radix select over the staged keys, then over the columns of the keys
+//    equal to its threshold, gives the selection; its columns are marked in
+//    a bitmap of the window, and a scan of the bitmap lists them in column
+//    order.
+//  - A row whose threshold keeps more keys than the stage holds (many equal
+//    scores) or fewer than it must select, or whose sample does not fit, is
+//    selected from memory by its first wave: the same radix selects, every
+//    pass streaming the window, then one more pass writing the selection in
+//    column order.
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTbThreads = 256;
+constexpr int kTbWaves = kTbThreads / 64;
+constexpr int kTbStage = 4096;                // keys a row keeps in LDS
+constexpr int kTbMaxBitmapCols = 65536;       // windows the bitmap covers (thresholded rows)
+// Rows the workgroup kernel takes: byte offsets of a row's columns fit 31 bits.
+constexpr int64_t kTkMaxCols = int64_t(1) << 28;
+
+struct TbSmem {
+  uint32_t key[kTbStage];  // keys by position; then the selection's columns in order
+  uint16_t col[kTbStage];  // window column (past s) of each position of a thresholded row
+  union {
+    uint32_t hist[kHistWords];                 // radix-select histograms
+    uint32_t bits[kTbMaxBitmapCols / 32];      // the selection's columns
+  };
+  uint32_t res[4];
+  uint32_t mm[2 * kTbWaves];
+  uint32_t wsum[kTbWaves];
+  uint32_t count;
+};
+static_assert(kTbMaxBitmapCols / 32 <= kHistWords, "the bitmap shares the histograms' words");
+static_assert(kMaxTopK <= kTbStage, "the selection's columns are listed in the key stage");
+
+// Streams a row's columns [s, e): body(key, bits, c, valid) runs for the V
+// columns c, c + 1, ... of each lane's share, lanes in order and shares in
+// column order, and returns false to stop (the same in every lane).  The
+// columns from the first 16-byte boundary at or past s to the last one at or
+// before e are read in 16-byte loads, two batches of U per lane in flight,
+// through a resource that ends at that last boundary (a load past it reads
+// zeros, none is cut by it); the few columns before and after, in lane 0,
+// one by one through rs, which covers the row's columns [0, e) from its
+// first (rowp).
+template <bool BF, typename Body>
+__device__ __forceinline__ void stream_window(__amdgpu_buffer_rsrc_t rs, const unsigned char* rowp, int64_t s,
+                                              int64_t e, Body body) {
+  constexpr int ES = BF ? 2 : 4, V = 16 / ES, U = 4;
+  constexpr int64_t kStep = 64 * V * U;
+  const int lane = threadIdx.x & 63;
+  // columns [c, c_end) in lane 0, one load each
+  auto few = [&](int64_t c, int64_t c_end) {
+    uint32_t bits[V], key[V];
+    bool valid[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      valid[j] = lane == 0 && c + j < c_end;
+      const int64_t cj = valid[j] ? c + j : c;
+      bits[j] = BF ? uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rs, int(cj * 2), 0, 0)) << 16
+                   : __builtin_amdgcn_raw_buffer_load_b32(rs, int(cj * 4), 0, 0);
+      key[j] = rank_key(bits[j]);
+    }
+    return body(key, bits, c, valid);
+  };
+  const int64_t mis = int64_t(((reinterpret_cast<uintptr_t>(rowp) + uint64_t(s) * ES) & 15u) / ES);
+  const int64_t h = mis == 0 ? s : (s + V - mis < e ? s + V - mis : e);  // first aligned column
+  const int64_t t = h + (e - h) / V * V;                                  // last aligned column
+  if (h > s && !few(s, h)) return;
+  if (t > h) {
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), 0, int(t * ES), 0x00020000);
+    u32x4 b0[U], b1[U];
+    auto issue = [&](u32x4 (&b)[U], int64_t cb) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        b[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, int((cb + int64_t(64 * u + lane) * V) * ES), 0, 0);
+    };
+    const uint32_t n = uint32_t(t - h);
+    auto consume = [&](const u32x4 (&b)[U], int64_t cb) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c0 = cb + int64_t(64 * u + lane) * V;
+        const uint32_t r0 = uint32_t(c0 - h);
+        uint32_t bits[V], key[V];
+        bool valid[V];
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+          const uint32_t d = b[u][j * ES / 4];
+          bits[j] = BF ? ((j & 1) ? (d & 0xFFFF0000u) : (d << 16)) : d;
+          key[j] = rank_key(bits[j]);
+          valid[j] = r0 + uint32_t(j) < n;
+        }
+        if (!body(key, bits, c0, valid)) return false;
+      }
+      return true;
+    };
+    int64_t cb = h;
+    issue(b0, cb);
+    for (;;) {
+      issue(b1, cb + kStep);
+      if (!consume(b0, cb)) return;
+      if (cb + kStep >= t) break;
+      issue(b0, cb + 2 * kStep);
+      if (!consume(b1, cb + kStep)) return;
+      if (cb + 2 * kStep >= t) break;
+      cb += 2 * kStep;
+    }
+  }
+  if (e > t && t >= h) few(t, e);
+}
+
+template <bool BF>
+__global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned char* plan, int32_t B, int32_t S_q,
+                                                               int32_t S_k, int32_t H, int32_t D, const void* logits,
+                                                               int64_t ld, int32_t k, int32_t* out_idx,
+                                                               float* out_val, uint32_t off_start, uint32_t off_end) {
+  __shared__ TbSmem sm;
+  constexpr int ES = BF ? 2 : 4, V = 16 / ES;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t row = blockIdx.x;
+  int32_t* oi = out_idx + row * k;
+  float* ov = out_val != nullptr ? out_val + row * k : nullptr;
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(plan);
+  if (!(hdr->magic == kPlanMagic && hdr->B == B && hdr->S_q == S_q && hdr->S_k == S_k && hdr->H == H &&
+        hdr->D == D)) {  // a plan for other dimensions: loud, not plausible
+    for (int i = t; i < k; i += kTbThreads) {
+      oi[i] = -1;
+      if (ov) ov[i] = __int_as_float(0x7FC00000);
+    }
+    return;
+  }
+  const int64_t s = reinterpret_cast<const int32_t*>(plan + off_start)[row];
+  const int64_t e = reinterpret_cast<const int32_t*>(plan + off_end)[row];
+  const int64_t n = e > s ? e - s : 0;
+  const uint32_t n_out = uint32_t(n < k ? n : k);
+  for (int i = int(n_out) + t; i < k; i += kTbThreads) {
+    oi[i] = -1;
+    if (ov) ov[i] = -__builtin_inff();
+  }
+  if (n == 0) return;
+  const unsigned char* rowp = static_cast<const unsigned char*>(logits) + row * ld * ES;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), 0, int(e * ES), 0x00020000);
+  auto bits_at = [&](int64_t c) -> uint32_t {  // score bits of column c < e
+    if constexpr (BF)
+      return uint32_t(__builtin_amdgcn_raw_buffer_load_b16(rs, int(c * 2), 0, 0)) << 16;
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(rs, int(c * 4), 0, 0);
+  };
+  constexpr int U = kTbStage / kTbThreads;  // 16 loads per thread in flight while staging
+  if (n <= int64_t(k)) {  // the whole window
+    for (int64_t i0 = 0; i0 < n; i0 += kTbThreads * U) {
+      uint32_t b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + kTbThreads * u + t;
+        b[u] = bits_at(s + (i < n ? i : n - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = i0 + kTbThreads * u + t;
+        if (i < n) {
+          oi[i] = int32_t(s + i);
+          if (ov) ov[i] = __uint_as_float(b[u]);
+        }
+      }
+    }
+    return;
+  }
+  const bool direct = n <= kTbStage;
+  bool exact = false;
+  uint32_t C = 0, kmin = 0xFFFFFFFFu, kmax = 0u;
+  if (direct) {  // every key of the window, key p = column s + p
+    uint32_t b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = kTbThreads * u + t;
+      b[u] = bits_at(s + (p < n ? p : n - 1));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = kTbThreads * u + t;
+      if (p < n) {
+        const uint32_t key = rank_key(b[u]);
+        sm.key[p] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+    C = uint32_t(n);
+  } else {
+    // the sample: the first 32 columns of every 512 of the window
+    const int64_t ns = 32 * (n / 512) + (n % 512 < 32 ? n % 512 : 32);
+    const int64_t m = sample_rank(n_out, n, ns);
+    exact = ns > kTbStage || m >= ns;
+    if (!exact) {
+      uint32_t smin = 0xFFFFFFFFu, smax = 0u;
+      uint32_t b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = kTbThreads * u + t < ns ? kTbThreads * u + t : ns - 1;
+        b[u] = bits_at(s + 512 * (i / 32) + i % 32);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = kTbThreads * u + t;
+        if (i < ns) {
+          const uint32_t key = rank_key(b[u]);
+          sm.key[i] = key;
+          smin = min(smin, key);
+          smax = max(smax, key);
+        }
+      }
+      block_min_max<kTbWaves>(smin, smax, sm.mm);  // its barriers also complete the staging
+      uint32_t ce, wl;
+      const int hb = varying_bits(smin, smax);
+      const uint32_t tau = radix_select<kTbThreads>(
+          [&](auto fn) {
+            for (int64_t i = t; i < ns; i += kTbThreads) fn(sm.key[i]);
+          },
+          uint32_t(m), sm.hist, sm.res, ce, wl, hb > 16 ? hb : 16, 16, smin);
+      if (t == 0) sm.count = 0;
+      __syncthreads();  // the sample is read; the candidates overwrite it
+      // each wave a quarter of the window's aligned columns (the first wave
+      // also the columns before them, the last the columns after), appending
+      // the keys that reach tau: a wave reserves its places with one atomic
+      auto append = [&](const uint32_t* key, const uint32_t*, int64_t c0, const bool* valid) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) keep |= uint32_t(valid[j] && key[j] >= tau) << j;
+        const uint32_t cnt = uint32_t(__builtin_popcount(keep));
+        const uint32_t incl = wave_scan(cnt);
+        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+        if (tot != 0) {
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&sm.count, tot);
+          uint32_t pos = uint32_t(__shfl(int(base), 0, 64)) + incl - cnt;
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            if ((keep >> j) & 1u) {
+              if (pos < uint32_t(kTbStage)) {
+                sm.key[pos] = key[j];
+                sm.col[pos] = uint16_t(c0 + j - s);
+              }
+              kmin = min(kmin, key[j]);
+              kmax = max(kmax, key[j]);
+              ++pos;
+            }
+          }
+        }
+        return true;
+      };
+      const int64_t mis = int64_t(((reinterpret_cast<uintptr_t>(rowp) + uint64_t(s) * ES) & 15u) / ES);
+      const int64_t h = mis == 0 ? s : (s + V - mis < e ? s + V - mis : e);  // first aligned column
+      const int64_t nv = (e - h) / V;                                         // aligned vectors
+      const int64_t q0 = h + nv * wave / kTbWaves * V, q1 = h + nv * (wave + 1) / kTbWaves * V;
+      if (wave == 0 && h > s) stream_window<BF>(rs, rowp, s, h, append);
+      if (q1 > q0) stream_window<BF>(rs, rowp, q0, q1, append);
+      if (wave == kTbWaves - 1 && h + nv * V < e) stream_window<BF>(rs, rowp, h + nv * V, e, append);
+      __syncthreads();
+      C = sm.count;
+      exact = C > uint32_t(kTbStage) || C < n_out;
+    }
+  }
+
+  int nbits = 1;
+  while ((int64_t(1) << nbits) < n) ++nbits;
+  const uint32_t top = (1u << nbits) - 1u;  // n <= 2^28
+  if (!exact) {
+    block_min_max<kTbWaves>(kmin, kmax, sm.mm);  // its barriers also complete the staging
+    auto col_of = [&](uint32_t p) -> uint32_t { return direct ? p : uint32_t(sm.col[p]); };
+    uint32_t T = 0, P2 = 0xFFFFFFFFu;  // selected: key > T, or key == T at column <= P2
+    if (C > n_out) {
+      uint32_t count_eq, want;
+      T = radix_select<kTbThreads>(
+          [&](auto fn) {
+#pragma unroll 4
+            for (uint32_t p = t; p < C; p += kTbThreads) fn(sm.key[p]);
+          },
+          n_out, sm.hist, sm.res, count_eq, want, varying_bits(kmin, kmax), 0, kmin, true);
+      if (want < count_eq) {  // ties at T: the want smallest columns among them
+        uint32_t ce2, left2;
+        const uint32_t Vs = radix_select<kTbThreads>(
+            [&](auto fn) {
+              for (uint32_t p = t; p < C; p += kTbThreads)
+                if (sm.key[p] == T) fn(top - col_of(p));
+            },
+            want, sm.hist, sm.res, ce2, left2, nbits, 0, 0u, true);
+        P2 = top - Vs;
+      }
+    }
+    // the selection's columns, marked in a bitmap of the window, then listed
+    // in column order: thread t scans words [t W, t W + W)
+    const int words = int((n + 31) / 32);
+    for (int i = t; i < words; i += kTbThreads) sm.bits[i] = 0;
+    __syncthreads();
+#pragma unroll 4
+    for (uint32_t p = t; p < C; p += kTbThreads) {
+      const uint32_t key = sm.key[p], c = col_of(p);
+      if (key > T || (key == T && c <= P2)) atomicOr(&sm.bits[c >> 5], 1u << (c & 31));
+    }
+    __syncthreads();
+    const int W = (words + kTbThreads - 1) / kTbThreads;
+    uint32_t mine = 0;
+    for (int j = 0; j < W; ++j) {
+      const int wd = t * W + j;
+      if (wd < words) mine += uint32_t(__builtin_popcount(sm.bits[wd]));
+    }
+    uint32_t total;
+    uint32_t pos = block_scan<kTbWaves>(mine, sm.wsum, total) - mine;
+    for (int j = 0; j < W; ++j) {
+      const int wd = t * W + j;
+      uint32_t bw = wd < words ? sm.bits[wd] : 0u;
+      while (bw != 0) {
+        const int b = __builtin_ctz(bw);
+        bw &= bw - 1u;
+        if (pos < n_out) sm.key[pos] = uint32_t(32 * wd + b);
+        ++pos;
+      }
+    }
+    __syncthreads();
+    constexpr int UO = kMaxTopK / kTbThreads;
+    int64_t cc[UO];
+    uint32_t bv[UO];
+#pragma unroll
+    for (int u = 0; u < UO; ++u) {
+      const uint32_t i = uint32_t(kTbThreads * u + t);
+      cc[u] = s + int64_t(i < n_out ? sm.key[i] : 0u);
+      bv[u] = ov ? bits_at(cc[u]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < UO; ++u) {
+      const uint32_t i = uint32_t(kTbThreads * u + t);
+      if (i < n_out) {
+        oi[i] = int32_t(cc[u]);
+        if (ov) ov[i] = __uint_as_float(bv[u]);
+      }
+    }
+    return;
+  }
+
+  // ---- from memory, by the first wave: every pass streams the window ---------
+  if (wave != 0) return;
+  uint32_t* hist = sm.hist;  // two copies' worth, as a wave's radix select uses
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+  stream_window<BF>(rs, rowp, s, e, [&](const uint32_t* key, const uint32_t*, int64_t, const bool* valid) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (valid[j]) {
+        kmin = min(kmin, key[j]);
+        kmax = max(kmax, key[j]);
+      }
+    }
+    return true;
+  });
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  uint32_t T, P2 = 0xFFFFFFFFu;
+  {
+    uint32_t count_eq, want;
+    T = wave_radix_select(
+        [&](auto fn) {
+          stream_window<BF>(rs, rowp, s, e, [&](const uint32_t* key, const uint32_t*, int64_t, const bool* valid) {
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+              if (valid[j]) fn(key[j]);
+            return true;
+          });
+        },
+        n_out, hist, count_eq, want, varying_bits(kmin, kmax), 0, kmin, true);
+    if (want < count_eq) {  // ties at T: the want smallest columns among them
+      uint32_t ce2, left2;
+      const uint32_t Vs = wave_radix_select(
+          [&](auto fn) {
+            stream_window<BF>(rs, rowp, s, e,
+                              [&](const uint32_t* key, const uint32_t*, int64_t c0, const bool* valid) {
+#pragma unroll
+                                for (int j = 0; j < V; ++j)
+                                  if (valid[j] && key[j] == T) fn(top - uint32_t(c0 + j - s));
+                                return true;
+                              });
+          },
+          want, hist, ce2, left2, nbits, 0, 0u, true);
+      P2 = top - Vs;
+    }
+  }
+  uint32_t done = 0;
+  stream_window<BF>(rs, rowp, s, e, [&](const uint32_t* key, const uint32_t* bits, int64_t c0, const bool* valid) {
+    uint32_t sel = 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      sel |= uint32_t(valid[j] && (key[j] > T || (key[j] == T && uint32_t(c0 + j - s) <= P2))) << j;
+    const uint32_t cnt = uint32_t(__builtin_popcount(sel));
+    const uint32_t incl = wave_scan(cnt);
+    uint32_t pos = done + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      if (((sel >> j) & 1u) && pos < n_out) {
+        oi[pos] = int32_t(c0 + j);
+        if (ov) ov[pos] = __uint_as_float(bits[j]);
+        ++pos;
+      }
+    }
+    done += __builtin_amdgcn_readlane(incl, 63);
+    return done < n_out;
+  });
+}
+
 template <bool BF, bool BY_SCORE>
 void launch_t(dim3 grid, const unsigned char* p, int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t D,
               const void* logits, int64_t ld, int32_t k, int32_t* out_idx, float* out_val, const PlanLayout& L,
@@ -497,6 +914,16 @@ hipError_t launch_topk(const void* plan, int32_t B, int32_t S_q, int32_t S_k, in
                        int32_t* out_idx, float* out_val, hipStream_t stream) {
   const PlanLayout L = plan_layout(B, S_q, H);
   const unsigned char* p = static_cast<const unsigned char*>(plan);
+  if (!by_score && int64_t(S_k) <= kTkMaxCols) {
+    const dim3 g(unsigned(L.n_rows));
+    if (logits_bf16)
+      hipLaunchKernelGGL(topk_rows_kernel<true>, g, dim3(kTbThreads), 0, stream, p, B, S_q, S_k, H, D, logits, ld,
+                         k, out_idx, out_val, uint32_t(L.off_start), uint32_t(L.off_end));
+    else
+      hipLaunchKernelGGL(topk_rows_kernel<false>, g, dim3(kTbThreads), 0, stream, p, B, S_q, S_k, H, D, logits, ld,
+                         k, out_idx, out_val, uint32_t(L.off_start), uint32_t(L.off_end));
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned(L.n_rows));
   if (logits_bf16) {
     if (by_score)

@@ -148,3 +148,28 @@ def test_topk_without_values_and_plan_mismatch():
     idx, val = lib.idx_logits_topk(other, v, 16, S_k=500)
     torch.cuda.synchronize()
     assert bool((idx == -1).all()) and bool(torch.isnan(val).all())
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_topk_window_sizes_around_the_stage(kind):
+    """Windows on both sides of the sizes where the per-row selection changes
+    method: staged whole (up to 4096 columns), thresholded from a sample (up
+    to 65536), and selected from memory (wider, or many equal scores)."""
+    rng = np.random.default_rng(17 + len(kind))
+    S_k, k = 70000, 2048
+    widths = [2049, 4095, 4096, 4097, 8192, 65535, 65536, 65537, 70000]
+    n_rows = len(widths) + 3
+    v = _crafted(rng, n_rows, S_k, kind)
+    starts = np.zeros(n_rows, np.int64)
+    ends = np.zeros(n_rows, np.int64)
+    for i, wdt in enumerate(widths):
+        starts[i] = rng.integers(0, S_k - wdt + 1)
+        ends[i] = starts[i] + wdt
+    starts[-3:], ends[-3:] = [1, 3, 0], [S_k - 2, S_k - 1, S_k]  # unaligned starts and ends
+    plan = _windows_plan(1, n_rows, S_k, starts, ends)
+    ld = S_k + 5
+    buf = np.full((n_rows, ld), np.float32(9.0))
+    buf[:, :S_k] = v
+    logits = torch.from_numpy(buf).reshape(1, n_rows, ld).cuda()
+    _check(plan, logits, k, starts, ends, f"{kind} widths", S_k=S_k, orders=("column",))
+    _check(plan, logits.to(torch.bfloat16), k, starts, ends, f"{kind} widths bf16", S_k=S_k, orders=("column",))
