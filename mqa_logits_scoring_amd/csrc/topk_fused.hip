@@ -124,19 +124,6 @@ __global__ void __launch_bounds__(kFThreads) fused_setup_kernel(const SetupArgs 
 // ---------------------------------------------------------------------------
 // threshold
 
-// ---------------------------------------------------------------------------
-// one row per wave
-//
-// The selection of most rows runs one wave per row, four rows per
-// workgroup, each wave with its own LDS area and no workgroup barrier: a
-// row's steps are short, so what bounds them is latency, and a CU then works
-// on up to eight rows at once.
-
-constexpr int kRowWaves = 4;                    // rows (waves) per workgroup
-
-// ---------------------------------------------------------------------------
-// threshold
-
 struct ThrArgs {
   const unsigned char* plan;
   PlanLayout L;
@@ -249,51 +236,62 @@ __device__ void send_to_redo(const SelArgs& a, int64_t r, int lane_in_group, int
   }
 }
 
-// ---- one wave per row (pass 1, by column) ---------------------------------
+// ---- a 256-thread workgroup per row (pass 1, by column) ----------------------
+//
+// Most rows: candidates staged by position (positions follow the columns:
+// chunks ascend, and a chunk's candidates are in column order), a radix
+// select over them and over the positions of the keys equal to its
+// threshold, the selection's positions compacted in place, and the output
+// gathered by slot.  About 25 KB of LDS, so six rows per CU are in flight.
 
-constexpr int kRowStage = 4096;   // candidates a wave keeps in LDS
-constexpr int kRowChunks = 128;   // chunk entries a wave keeps
+constexpr int kRowThreads = 256;
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kRowStage = 4096;   // candidates a row keeps in LDS
+constexpr int kRowChunks = 128;   // chunk entries a row keeps
+constexpr int kRowPer = kRowStage / kRowThreads;  // positions per thread
 
-struct RowWave {
+struct RowSmem {
   uint32_t key[kRowStage];        // keys by position; then the selection's positions
-  uint32_t hist[kWaveHistWords];
+  uint32_t hist[kHistWords];
   int32_t pc0[kRowChunks];        // chunk entries: first column, first position
   uint32_t pbase[kRowChunks];
+  uint32_t res[4];
+  uint32_t mm[2 * kRowWaves];
+  uint32_t wsum[kRowWaves];
+  uint32_t count;
 };
 
 // Slots in the row's candidate area of ascending candidate positions: each
-// lane keeps the chunk of its last position and moves forward from there
+// thread keeps the chunk of its last position and moves forward from there
 // (the last chunk starting at or before p; chunks with no candidate share
-// their base with the next one), so a wave walking positions in order does
+// their base with the next one), so a thread walking positions in order does
 // a step or two per position instead of a search.
 struct SlotCursor {
   int j = 0;
-  __device__ __forceinline__ uint32_t slot(const RowWave& w, int n_chunk, uint32_t p) {
+  __device__ __forceinline__ uint32_t slot(const RowSmem& w, int n_chunk, uint32_t p) {
     while (j + 1 < n_chunk && w.pbase[j + 1] <= p) ++j;
     return uint32_t(w.pc0[j]) + (p - w.pbase[j]);
   }
 };
 
-__global__ void __launch_bounds__(64 * kRowWaves) select_rows_kernel(const SelArgs a) {
-  __shared__ RowWave sm[kRowWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t r = int64_t(blockIdx.x) * kRowWaves + wave;
+__global__ void __launch_bounds__(kRowThreads) select_rows_kernel(const SelArgs a) {
+  __shared__ RowSmem sm;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t r = blockIdx.x;
   const PlanLayout& L = a.L;
-  if (r >= L.n_rows) return;
-  RowWave& w = sm[wave];
   const int k = a.k;
   int32_t* oi = a.out_idx + r * k;
   float* ov = a.out_val != nullptr ? a.out_val + r * k : nullptr;
   if (!plan_matches(a.plan, a.B, a.S_q, a.S_k, a.H, a.D, L)) {  // loud, not plausible
-    for (int i = lane; i < k; i += 64) {
+    for (int i = t; i < k; i += kRowThreads) {
       oi[i] = -1;
       if (ov) ov[i] = __int_as_float(0x7FC00000);
     }
-    if (lane == 0) a.tau[r] = kTauNone;
+    if (t == 0) a.tau[r] = kTauNone;
     return;
   }
   auto to_big = [&]() {
-    if (lane == 0) a.big[atomicAdd(&a.gate[1], 1)] = int32_t(r);
+    if (t == 0) a.big[atomicAdd(&a.gate[1], 1)] = int32_t(r);
   };
   if (a.n_chunk > kRowChunks) {
     to_big();
@@ -303,125 +301,128 @@ __global__ void __launch_bounds__(64 * kRowWaves) select_rows_kernel(const SelAr
   const int64_t e = reinterpret_cast<const int32_t*>(a.plan + L.off_end)[r];
   const int64_t n = e > s ? e - s : 0;
   const uint32_t n_out = uint32_t(n < k ? n : k);
-  // chunk entries (lane l: chunks l and l + 64) and their first positions
-  const int32_t* me = a.meta + 2 * r * a.n_chunk;
-  const int j0 = lane, j1 = lane + 64;
-  const int32_t c00 = j0 < a.n_chunk ? me[2 * j0] : 0, c01 = j1 < a.n_chunk ? me[2 * j1] : 0;
-  const uint32_t n0 = j0 < a.n_chunk ? uint32_t(me[2 * j0 + 1]) : 0u;
-  const uint32_t n1 = j1 < a.n_chunk ? uint32_t(me[2 * j1 + 1]) : 0u;
-  const uint32_t i0 = wave_scan(n0), i1 = wave_scan(n1);
-  const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
-  const uint32_t C = t0 + __builtin_amdgcn_readlane(i1, 63);
+  // chunk entries (the first wave, lane l: chunks l and l + 64) and their
+  // first positions
+  if (wave == 0) {
+    const int32_t* me = a.meta + 2 * r * a.n_chunk;
+    const int j0 = lane, j1 = lane + 64;
+    const int32_t c00 = j0 < a.n_chunk ? me[2 * j0] : 0, c01 = j1 < a.n_chunk ? me[2 * j1] : 0;
+    const uint32_t n0 = j0 < a.n_chunk ? uint32_t(me[2 * j0 + 1]) : 0u;
+    const uint32_t n1 = j1 < a.n_chunk ? uint32_t(me[2 * j1 + 1]) : 0u;
+    const uint32_t i0 = wave_scan(n0), i1 = wave_scan(n1);
+    const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
+    sm.pc0[j0] = c00;
+    sm.pbase[j0] = i0 - n0;
+    sm.pc0[j1] = c01;
+    sm.pbase[j1] = t0 + i1 - n1;
+    if (lane == 0) sm.count = t0 + __builtin_amdgcn_readlane(i1, 63);
+  }
+  __syncthreads();
+  const uint32_t C = sm.count;
   if (C < n_out) {
-    send_to_redo(a, r, lane, 64);
+    send_to_redo(a, r, t, kRowThreads);
     return;
   }
-  if (lane == 0) a.tau[r] = kTauNone;  // done: a second pass keeps nothing of it
+  if (t == 0) a.tau[r] = kTauNone;  // done: a second pass keeps nothing of it
   if (C > uint32_t(kRowStage)) {
     to_big();
     return;
   }
-  for (int i = int(n_out) + lane; i < k; i += 64) {
+  for (int i = int(n_out) + t; i < k; i += kRowThreads) {
     oi[i] = -1;
     if (ov) ov[i] = -__builtin_inff();
   }
   if (n_out == 0) return;
-  if (j0 < kRowChunks) {
-    w.pc0[j0] = c00;
-    w.pbase[j0] = i0 - n0;
-  }
-  if (j1 < kRowChunks) {
-    w.pc0[j1] = c01;
-    w.pbase[j1] = t0 + i1 - n1;
-  }
-  wave_sync();
 
-  // ---- stage the keys by position (loads issued eight at a time) ----------
+  // ---- stage the keys by position (every load of a thread in flight) --------
   const uint2* row = a.cand + r * int64_t(a.S_k);
   const int nc = a.n_chunk;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  constexpr int U = 8;
-  SlotCursor cur;
-  for (uint32_t p0 = 0; p0 < C; p0 += 64 * U) {
-    uint32_t bits[U];
+  {
+    SlotCursor cur;
+    uint32_t bits[kRowPer];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t p = p0 + uint32_t(64 * u + lane);
-      bits[u] = row[p < C ? cur.slot(w, nc, p) : 0u].x;
+    for (int u = 0; u < kRowPer; ++u) {
+      const uint32_t p = uint32_t(kRowThreads * u + t);
+      bits[u] = row[p < C ? cur.slot(sm, nc, p) : 0u].x;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t p = p0 + uint32_t(64 * u + lane);
+    for (int u = 0; u < kRowPer; ++u) {
+      const uint32_t p = uint32_t(kRowThreads * u + t);
       if (p < C) {
         const uint32_t key = rank_key(bits[u]);
-        w.key[p] = key;
+        sm.key[p] = key;
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       }
     }
   }
-  kmin = wave_min(kmin);
-  kmax = wave_max(kmax);
-  wave_sync();
+  block_min_max<kRowWaves>(kmin, kmax, sm.mm);  // its barriers also complete the staging
 
   // ---- threshold: key T, and for keys equal to T the positions up to P2 ---
   const bool all = C == n_out;
   uint32_t T = 0, P2 = 0xFFFFFFFFu;
   if (!all) {
     uint32_t count_eq, want;
-    T = wave_radix_select(
+    T = radix_select<kRowThreads>(
         [&](auto fn) {
-          for (uint32_t p = lane; p < C; p += 64) fn(w.key[p]);
+#pragma unroll 4
+          for (uint32_t p = t; p < C; p += kRowThreads) fn(sm.key[p]);
         },
-        n_out, w.hist, count_eq, want, varying_bits(kmin, kmax), 0, kmin, true);
+        n_out, sm.hist, sm.res, count_eq, want, varying_bits(kmin, kmax), 0, kmin, true);
     if (want < count_eq) {  // ties at T: the want smallest positions among them
       int nbits = 1;
       while ((uint32_t(1) << nbits) < C) ++nbits;
       const uint32_t top = (1u << nbits) - 1u;
       uint32_t ce2, left2;
-      const uint32_t V = wave_radix_select(
+      const uint32_t V = radix_select<kRowThreads>(
           [&](auto fn) {
-            for (uint32_t p = lane; p < C; p += 64)
-              if (w.key[p] == T) fn(top - p);
+            for (uint32_t p = t; p < C; p += kRowThreads)
+              if (sm.key[p] == T) fn(top - p);
           },
-          want, w.hist, ce2, left2, nbits, 0, 0u, true);
+          want, sm.hist, sm.res, ce2, left2, nbits, 0, 0u, true);
       P2 = top - V;
     }
   }
 
-  // ---- the selection's positions in column order, in place ----------------
-  // (a step writes only places below the positions it read)
-  uint32_t done = 0;
-  for (uint32_t p0 = 0; p0 < C; p0 += 64) {
-    const uint32_t p = p0 + uint32_t(lane);
-    bool in = false;
-    if (p < C) {
-      const uint32_t key = w.key[p];
-      in = all || key > T || (key == T && p <= P2);
+  // ---- the selection's positions in column order, in place -----------------
+  // thread t: positions [t P, t P + P); the scan's barriers order every read
+  // before the first write
+  {
+    const uint32_t P = (C + kRowThreads - 1) / kRowThreads;  // <= kRowPer
+    uint32_t selm = 0;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const uint32_t p = uint32_t(t) * P + uint32_t(j);
+      if (uint32_t(j) < P && p < C) {
+        const uint32_t key = sm.key[p];
+        selm |= uint32_t(all || key > T || (key == T && p <= P2)) << j;
+      }
     }
-    const uint64_t b = __ballot(in);
-    wave_sync();
-    if (in) w.key[done + lanes_below(b)] = p;
-    done += uint32_t(__popcll(b));
+    const uint32_t mine = uint32_t(__builtin_popcount(selm));
+    uint32_t total;
+    uint32_t o = block_scan<kRowWaves>(mine, sm.wsum, total) - mine;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j)
+      if ((selm >> j) & 1u) sm.key[o++] = uint32_t(t) * P + uint32_t(j);
   }
-  wave_sync();
+  __syncthreads();
 
   // ---- output: scores and columns read back by slot ---------------------------
+  constexpr int UO = kMaxTopK / kRowThreads;
   SlotCursor oc;
-  for (uint32_t i0 = 0; i0 < n_out; i0 += 64 * U) {
-    uint2 v[U];
+  uint2 v[UO];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t i = i0 + uint32_t(64 * u + lane);
-      v[u] = row[i < n_out ? oc.slot(w, nc, w.key[i]) : 0u];
-    }
+  for (int u = 0; u < UO; ++u) {
+    const uint32_t i = uint32_t(kRowThreads * u + t);
+    v[u] = row[i < n_out ? oc.slot(sm, nc, sm.key[i]) : 0u];
+  }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t i = i0 + uint32_t(64 * u + lane);
-      if (i < n_out) {
-        oi[i] = int32_t(v[u].y);
-        if (ov) ov[i] = __uint_as_float(v[u].x);
-      }
+  for (int u = 0; u < UO; ++u) {
+    const uint32_t i = uint32_t(kRowThreads * u + t);
+    if (i < n_out) {
+      oi[i] = int32_t(v[u].y);
+      if (ov) ov[i] = __uint_as_float(v[u].x);
     }
   }
 }
@@ -811,9 +812,10 @@ hipError_t launch_select(const TopkLayout& T, int32_t B, int32_t S_q, int32_t S_
     hipLaunchKernelGGL((select_kernel<true, false>), dim3(unsigned(a.L.n_rows)), dim3(kSelThreads), 0, stream, a);
     return hipGetLastError();
   }
-  // by column: a wave per row, then the rows it leaves to the workgroup kernel
-  hipLaunchKernelGGL(select_rows_kernel, dim3(unsigned((a.L.n_rows + kRowWaves - 1) / kRowWaves)),
-                     dim3(64 * kRowWaves), 0, stream, a);
+  // by column: a 256-thread workgroup per row, then the rows it leaves to the
+  // 1024-thread kernel
+  hipLaunchKernelGGL(select_rows_kernel, dim3(unsigned(a.L.n_rows)),
+                     dim3(kRowThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.list = a.big;
