@@ -49,7 +49,7 @@ idx_status_t check_dims(int32_t B, int32_t S_q, int32_t S_k, int32_t H, int32_t 
 // to stay fed, and tiles of very different coverage (irregular windows)
 // balance only when no unit is much longer than kChunkCols.
 constexpr int64_t kUnitsPerCu = 4;
-constexpr int64_t kChunkCols = 8192;
+constexpr int64_t kChunkCols = 16384;
 constexpr int64_t kMinChunk = 256;
 // CUs the split is sized against in host-side bounds (more than any device has).
 constexpr int64_t kMaxCus = 4096;

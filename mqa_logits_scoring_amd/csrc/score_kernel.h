@@ -588,8 +588,11 @@ __global__ void __launch_bounds__(kThreads)
                                                   inwin ? 0x07060504u : 0x03020100u));
     if constexpr (OBF) {
       const uint16_t h = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));  // round to nearest even
-      __builtin_amdgcn_raw_buffer_store_b16(h, ors[0], int(o0), 0, kNonTemporal);
-      __builtin_amdgcn_raw_buffer_store_b16(h, ors[1], int(o1), 0, kNonTemporal);
+      // bf16: a half-wave covers half of a 128-byte line and the next block
+      // the other half, so these stores stay in L2 to meet there (non-temporal
+      // ones left as two half-line writes)
+      __builtin_amdgcn_raw_buffer_store_b16(h, ors[0], int(o0), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(h, ors[1], int(o1), 0, 0);
     } else {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[0], int(o0), 0, kNonTemporal);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[1], int(o1), 0, kNonTemporal);
@@ -1060,8 +1063,9 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     if constexpr (CLEAN) val = inwin ? v : -__builtin_inff();  // one select
     if constexpr (OBF) {
       const uint16_t hv = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));
-      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[0], int(o0), 0, kNonTemporal);
-      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[1], int(o1), 0, kNonTemporal);
+      // cached, as in score_kernel: the line's other half comes with the next block
+      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[0], int(o0), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(hv, ors[1], int(o1), 0, 0);
     } else {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[0], int(o0), 0, kNonTemporal);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors[1], int(o1), 0, kNonTemporal);

@@ -263,8 +263,9 @@ __global__ void __launch_bounds__(kThreads)
                                                   inwin ? 0x07060504u : 0x03020100u));
     if constexpr (OBF) {
       const uint16_t h = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));  // round to nearest even
-      __builtin_amdgcn_raw_buffer_store_b16(h, out_rsrc(2 * i), int(o0), 0, kNonTemporal);
-      __builtin_amdgcn_raw_buffer_store_b16(h, out_rsrc(2 * i + 1), int(o1), 0, kNonTemporal);
+      // cached, as in score_kernel: the line's other half comes with the next block
+      __builtin_amdgcn_raw_buffer_store_b16(h, out_rsrc(2 * i), int(o0), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(h, out_rsrc(2 * i + 1), int(o1), 0, 0);
     } else {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), out_rsrc(2 * i), int(o0), 0, kNonTemporal);
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), out_rsrc(2 * i + 1), int(o1), 0, kNonTemporal);
