@@ -309,7 +309,18 @@ idx_status_t set_units(idx::ScoreArgs& k, const idx::PlanLayout& L, int64_t S_k,
   if (k.wave_split) units_per_cu = std::min<int64_t>(units_per_cu, 2);
   k.n_chunk = pick_chunks(S_k, L.n_tiles, rows, L.tile_rows, std::min<int64_t>(cus, kMaxCus), units_per_cu);
   k.n_pos_compute = int32_t(L.n_tiles * k.n_chunk);  // bounded by check_args
-  k.n_positions = cleanup ? int32_t(positions_of(L, k.n_chunk)) : k.n_pos_compute;
+  // Decode-sized tiles of very different coverage (each request's context):
+  // chunks of one width, as many as there are places in one round, so the
+  // longest is no wider than that width (n equal chunks per tile left the
+  // longest requests' chunks about twice the mean)
+  k.dyn_units = 0;
+  if (k.wave_split && L.n_tiles <= idx::kDynUnitTiles && L.n_tiles == k.B &&
+      int64_t(S_k + idx::kColAlign) * L.n_tiles < (int64_t(1) << 31)) {  // the kernel sums widths in 32 bits
+    k.dyn_units = 1;
+    k.n_pos_compute =
+        int32_t(std::max<int64_t>(units_per_cu * std::min<int64_t>(cus, kMaxCus), L.n_tiles + 64));
+  }
+  k.n_positions = cleanup ? int32_t(k.n_pos_compute + L.n_tiles) : k.n_pos_compute;
   return IDX_OK;
 }
 

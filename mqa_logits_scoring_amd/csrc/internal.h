@@ -320,6 +320,8 @@ struct TopkLayout {
   int32_t n_chunk_max;
 };
 
+constexpr int kDynUnitTiles = 256;
+
 // Everything a scoring kernel needs, passed by value.
 struct ScoreArgs {
   const void* q;
@@ -349,6 +351,11 @@ struct ScoreArgs {
   // wave of a unit scores the tile's two rows over a quarter of its columns,
   // instead of three of its four waves holding padding rows only
   int32_t wave_split;
+  // Decode-sized calls of at most kDynUnitTiles tiles (one per batch): the
+  // units are not n_chunk per tile but chunks of one width for every tile,
+  // the width set in the kernel from the tiles' total coverage so that they
+  // number at most n_pos_compute; positions past them are empty
+  int32_t dyn_units;
   int32_t n_pos_compute, n_positions;
   uint32_t off_start, off_end, off_slot, off_lo, off_hi, off_order;
   const unsigned char* pieces;   // per row PieceFmt<F>::N pieces of PieceFmt<F>::BYTES (formats with pieces)

@@ -264,9 +264,64 @@ struct Unit {
   int kind, tile, c0, c1, chunk;
 };
 
+// dyn_units: compute position p -> unit.  Every wave reads every tile's
+// coverage (tiles are batches here), sums the widths, takes the chunk width
+// w that keeps the chunks (ceil(width / w) per tile) within the positions,
+// and finds the tile whose chunks hold position p by a scan over the tiles
+// in order.  All 64 lanes take part.
+__device__ __forceinline__ Unit decode_dyn_unit(const ScoreArgs& a, int p) {
+  const int lane = int(threadIdx.x & 63);
+  const int32_t* lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo);
+  const int32_t* hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi);
+  constexpr int K = kDynUnitTiles / 64;
+  int tlo[K], span[K];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int t = lane + 64 * k, tc = min(t, a.n_tiles - 1);  // loads in bounds, issued together
+    const int l = lo[tc], h = hi[tc];
+    tlo[k] = l;
+    span[k] = t < a.n_tiles ? max(h - l, 0) : 0;
+    tot += uint32_t(span[k]);
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) tot += uint32_t(__shfl_xor(int(tot), d, 64));
+  // the same in every lane: read as such, so that what follows stays scalar
+  tot = __builtin_amdgcn_readfirstlane(tot);
+  const uint32_t room = uint32_t(a.n_pos_compute - a.n_tiles);
+  const int w = max(a.min_chunk, int((((tot + room - 1) / room) + 63u) & ~63u));
+  // no branch on the result (the kernels' MFMAs must not sit under a saved
+  // exec mask): every step runs, the hit is kept by selects
+  uint32_t carry = 0;
+  int tile = -1, c0 = 0, c1 = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const uint32_t cnt = uint32_t((span[k] + w - 1) / w);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = uint32_t(__shfl_up(int(incl), d, 64));
+      incl += lane >= d ? y : 0u;
+    }
+    const uint32_t first = carry + incl - cnt;
+    const uint64_t here = __ballot(cnt != 0 && first <= uint32_t(p) && uint32_t(p) < first + cnt);
+    const int src = here != 0 ? __builtin_ctzll(here) : 0;
+    const int lo_s = __builtin_amdgcn_readlane(tlo[k], src);
+    const int end_s = __builtin_amdgcn_readlane(tlo[k] + span[k], src);
+    const int first_s = __builtin_amdgcn_readlane(int(first), src);
+    const int a0 = lo_s + (p - first_s) * w;
+    tile = here != 0 ? src + 64 * k : tile;
+    c0 = here != 0 ? a0 : c0;
+    c1 = here != 0 ? min(a0 + w, end_s) : c1;
+    carry += uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+  }
+  return Unit{tile >= 0 ? int(kUnitCompute) : int(kUnitNone), max(tile, 0), c0, c1, 0};
+}
+
 // Work position p (ScoreArgs) -> unit.
 __device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
   if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0, 0};
+  if (a.dyn_units) return decode_dyn_unit(a, p);
   const int slot = p / a.n_chunk, chunk = p - slot * a.n_chunk;
   // slot -> (batch, segment, rank): batches and segments from the last
   const int tpb = a.tiles_per_batch, spb = a.seg_per_batch, tps = a.tiles_per_seg, last = a.last_seg_tiles;
