@@ -265,8 +265,8 @@ struct Unit {
 };
 
 // dyn_units: compute position p -> unit.  Every wave reads every tile's
-// coverage (tiles are batches here), sums the widths, takes the chunk width
-// w that keeps the chunks (ceil(width / w) per tile) within the positions,
+// coverage (tiles are batches here), sums the widths, takes a chunk width w
+// that keeps the chunks (ceil(width / w) per tile) within the positions,
 // and finds the tile whose chunks hold position p by a scan over the tiles
 // in order.  All 64 lanes take part.
 __device__ __forceinline__ Unit decode_dyn_unit(const ScoreArgs& a, int p) {
@@ -288,8 +288,20 @@ __device__ __forceinline__ Unit decode_dyn_unit(const ScoreArgs& a, int p) {
   for (int d = 32; d > 0; d >>= 1) tot += uint32_t(__shfl_xor(int(tot), d, 64));
   // the same in every lane: read as such, so that what follows stays scalar
   tot = __builtin_amdgcn_readfirstlane(tot);
-  const uint32_t room = uint32_t(a.n_pos_compute - a.n_tiles);
-  const int w = max(a.min_chunk, int((((tot + room - 1) / room) + 63u) & ~63u));
+  // a width that surely fits (each tile rounds up by less than one chunk),
+  // or, when it also fits, the narrower one that counts half a chunk per tile
+  auto width_for = [&](uint32_t room) {
+    return max(a.min_chunk, int((((tot + room - 1) / room) + 63u) & ~63u));
+  };
+  const int w_sure = width_for(uint32_t(a.n_pos_compute - a.n_tiles));
+  const int w_try = width_for(uint32_t(a.n_pos_compute - (a.n_tiles + 1) / 2));
+  uint32_t need = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) need += uint32_t((span[k] + w_try - 1) / w_try);
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) need += uint32_t(__shfl_xor(int(need), d, 64));
+  need = __builtin_amdgcn_readfirstlane(need);
+  const int w = need <= uint32_t(a.n_pos_compute) ? w_try : w_sure;
   // no branch on the result (the kernels' MFMAs must not sit under a saved
   // exec mask): every step runs, the hit is kept by selects
   uint32_t carry = 0;
