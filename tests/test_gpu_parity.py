@@ -606,6 +606,33 @@ def test_other_head_counts_thd_and_paged(H):
     _full_compare(wl, run(wl, d), what=f"paged H={H}")
 
 
+@pytest.mark.parametrize("n_req", [12, 40])
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8"])
+def test_paged_decode_wave_lengths(fmt, n_req):
+    """Two-token decode over requests of random context up to 40000 keys: the
+    units' waves stream from one to seven 64-column pairs of keys, odd and
+    even counts, straight from the cache through a ring of four blocks.  The
+    result is bitwise that of the gathered two-phase call (fragment-order
+    keys, a ring of two), and sampled rows are within tolerance of the
+    oracle."""
+    rng = np.random.default_rng(43 + n_req)
+    ctx = rng.integers(1, 40000, n_req).tolist()
+    wl = W.make_paged(fmt, n_req, 2, ctx, 64, seed=44)
+    d = dev_inputs(wl)
+    plan = make_plan(wl, d)
+    one = run(wl, d, plan=plan)
+    out = torch.full_like(one, float("nan"))
+    args = lib.make_paged_args(d["q"], d["w"], out, wl.S_k, in_dtype=fmt, q_scale=d["q_scale"], sm_scale=wl.sm_scale)
+    ws = lib.idx_logits_prepare_paged(args, d["kv"])
+    lib.idx_logits_score(args, plan, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int32), out.view(torch.int32)), "paged and gathered keys differ"
+    rows = np.array([0, 1, 2 * (n_req // 2), 2 * n_req - 1])
+    ref, bound = oracle.logits(wl, rows=rows)
+    got = to_f64(one.reshape(wl.B * wl.S_q, -1)[torch.from_numpy(rows).cuda()])[:, : wl.S_k]
+    compare_rows(wl, got, ref, bound, clean=wl.clean, what=f"paged decode {fmt} r{n_req}")
+
+
 @pytest.mark.parametrize("page_size", [32, 64, 128])
 @pytest.mark.parametrize("fmt", W.FORMATS)
 def test_paged_direct_equals_gather(fmt, page_size):
