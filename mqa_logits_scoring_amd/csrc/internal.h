@@ -303,6 +303,16 @@ __device__ __forceinline__ uint32_t rank_key(uint32_t u) {
   return __builtin_isnan(__uint_as_float(u)) ? 0u : k;
 }
 
+// A threshold key (rank_key order) as a float compare: a score reaches key
+// tau exactly when it is a number >= tau_value(tau) (rank keys of numbers
+// order like the numbers, +0 and -0 alike), or when tau is 0, which keeps NaN
+// too; kTauNone gives NaN, which no score reaches.
+__device__ __forceinline__ float tau_value(uint32_t tau) {
+  if (tau == kTauNone) return __builtin_nanf("");
+  if (tau == 0u) return -__builtin_inff();
+  return __uint_as_float((tau >> 31) ? (tau & 0x7FFFFFFFu) : (0u - tau));
+}
+
 // Extra workspace of a fused top-k call, after the sections of the scoring
 // call itself (WorkspaceLayout, plan included), 256-byte aligned:
 //   [sampled K in fragment order]   B x ceil(nblk / R) blocks

@@ -139,17 +139,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Select mode (fused top-k, ScoreArgs::cand): a lane keeps its cell as a
 // candidate instead of storing it.
 //
-// A row's threshold key (internal.h, rank_key order) as a float compare: a
-// score reaches key tau exactly when it is a number >= tau_value(tau)
-// (rank keys of numbers order like the numbers, +0 and -0 alike), or when
-// tau is 0, which keeps NaN too (keep_all); kTauNone gives NaN, which no
-// score reaches.
-__device__ __forceinline__ float tau_value(uint32_t tau) {
-  if (tau == kTauNone) return __builtin_nanf("");
-  if (tau == 0u) return -__builtin_inff();
-  return __uint_as_float((tau >> 31) ? (tau & 0x7FFFFFFFu) : (0u - tau));
-}
-
 // Thresholds of a row pair, as the select-mode epilogue uses them (the same
 // in every lane, so they stay in scalar registers).
 struct SelTau {

@@ -46,14 +46,19 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return x;
 }
 
-// Inclusive prefix sum over the wave's lanes.
+// Inclusive prefix sum over the wave's lanes, in data-parallel moves between
+// lanes (no LDS): within each row of 16 lanes by shifts of 1, 2, 4 and 8,
+// then the last lane of row 0 added to row 1 and of row 2 to row 3, and the
+// last lane of row 1 (by then the sum of rows 0 and 1) to rows 2 and 3.  A
+// lane whose source is outside its row, or whose row the row mask leaves
+// out, adds the 0 it starts from.
 __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xF, 0xF, false));  // row_shr:1
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xF, 0xF, false));  // row_shr:2
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xF, 0xF, false));  // row_shr:4
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xF, 0xF, false));  // row_shr:8
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xC, 0xF, false));  // row_bcast:31
   return x;
 }
 
@@ -132,7 +137,7 @@ __device__ __forceinline__ int64_t sample_rank(int64_t n_out, int64_t n, int64_t
 // `total` receives the sum.  Contains barriers.
 template <int NW>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -166,7 +171,7 @@ __device__ __forceinline__ void block_min_max(uint32_t& lo, uint32_t& hi, uint32
     lo = min(lo, uint32_t(__shfl_xor(lo, d, 64)));
     hi = max(hi, uint32_t(__shfl_xor(hi, d, 64)));
   }
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if ((threadIdx.x & 63) == 0) {
     mm[wave] = lo;
     mm[NW + wave] = hi;

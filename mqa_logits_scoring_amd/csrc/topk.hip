@@ -81,7 +81,7 @@ struct TopkSmem {
 // Inclusive prefix sum of v over the workgroup's threads (thread order);
 // `total` receives the sum over all threads.  Contains barriers.
 __device__ uint32_t scan_1024(uint32_t v, TopkSmem& sm, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t x = v;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
                                                              int64_t ld, int32_t k, int32_t* out_idx,
                                                              float* out_val, uint32_t off_start, uint32_t off_end) {
   __shared__ TopkSmem sm;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t row = blockIdx.x;
   int32_t* oi = out_idx + row * k;
   float* ov = out_val != nullptr ? out_val + row * k : nullptr;
@@ -597,6 +597,78 @@ __device__ __forceinline__ void stream_window(__amdgpu_buffer_rsrc_t rs, const u
   if (e > t && t >= h) few(t, e);
 }
 
+// A wave's share of a thresholded row: the aligned columns [h, t) (16-byte
+// boundaries of the row), read as stream_window reads them, and every score
+// that reaches tf (a number >= tf: the rank keys of numbers order like the
+// numbers) appended to the stage with its window column, raw bits for now,
+// in any order.  Places are reserved once per batch of U loads: a prefix
+// sum of the lanes' counts and one LDS atomic.  A batch that would run past
+// the stage is counted and not written (the row is then selected from
+// memory).
+template <bool BF>
+__device__ __forceinline__ void stream_keep(const unsigned char* rowp, int64_t s, int64_t h, int64_t t, float tf,
+                                            TbSmem& sm) {
+  constexpr int ES = BF ? 2 : 4, V = 16 / ES, U = 4;
+  constexpr int64_t kStep = 64 * V * U;
+  const int lane = threadIdx.x & 63;
+  if (t <= h) return;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rowp), 0, int(t * ES), 0x00020000);
+  u32x4 b0[U], b1[U];
+  auto issue = [&](u32x4 (&b)[U], int64_t cb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      b[u] = __builtin_amdgcn_raw_buffer_load_b128(ra, int((cb + int64_t(64 * u + lane) * V) * ES), 0, 0);
+  };
+  auto consume = [&](const u32x4 (&b)[U], int64_t cb) {
+    uint32_t bits[U][V];
+    bool keep[U][V];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = cb + int64_t(64 * u + lane) * V < t;  // t is a vector boundary: whole vectors in or out
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const uint32_t d = b[u][j * ES / 4];
+        bits[u][j] = BF ? ((j & 1) ? (d & 0xFFFF0000u) : (d << 16)) : d;
+        keep[u][j] = in && __uint_as_float(bits[u][j]) >= tf;
+        cnt += keep[u][j] ? 1u : 0u;
+      }
+    }
+    const uint32_t incl = wave_scan(cnt);
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+    if (tot == 0) return;
+    uint32_t base = 0;
+    if (lane == 63) base = atomicAdd(&sm.count, tot);
+    base = __builtin_amdgcn_readlane(base, 63);
+    if (base + tot > uint32_t(kTbStage)) return;
+    uint32_t pos = base + incl - cnt;
+    const uint32_t c_lane = uint32_t(cb - s) + uint32_t(lane * V);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        if (keep[u][j]) {
+          sm.key[pos] = bits[u][j];
+          sm.col[pos] = uint16_t(c_lane + uint32_t(64 * u * V + j));
+          ++pos;
+        }
+      }
+    }
+  };
+  int64_t cb = h;
+  issue(b0, cb);
+  for (;;) {
+    issue(b1, cb + kStep);
+    consume(b0, cb);
+    if (cb + kStep >= t) break;
+    issue(b0, cb + 2 * kStep);
+    consume(b1, cb + kStep);
+    if (cb + 2 * kStep >= t) break;
+    cb += 2 * kStep;
+  }
+}
+
 template <bool BF>
 __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned char* plan, int32_t B, int32_t S_q,
                                                                int32_t S_k, int32_t H, int32_t D, const void* logits,
@@ -604,7 +676,7 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
                                                                float* out_val, uint32_t off_start, uint32_t off_end) {
   __shared__ TbSmem sm;
   constexpr int ES = BF ? 2 : 4, V = 16 / ES;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t row = blockIdx.x;
   int32_t* oi = out_idx + row * k;
   float* ov = out_val != nullptr ? out_val + row * k : nullptr;
@@ -711,43 +783,45 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
       __syncthreads();  // the sample is read; the candidates overwrite it
       // each wave a quarter of the window's aligned columns (the first wave
       // also the columns before them, the last the columns after), appending
-      // the keys that reach tau: a wave reserves its places with one atomic
-      auto append = [&](const uint32_t* key, const uint32_t*, int64_t c0, const bool* valid) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int j = 0; j < V; ++j) keep |= uint32_t(valid[j] && key[j] >= tau) << j;
-        const uint32_t cnt = uint32_t(__builtin_popcount(keep));
-        const uint32_t incl = wave_scan(cnt);
-        const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-        if (tot != 0) {
-          uint32_t base = 0;
-          if (lane == 0) base = atomicAdd(&sm.count, tot);
-          uint32_t pos = uint32_t(__shfl(int(base), 0, 64)) + incl - cnt;
-#pragma unroll
-          for (int j = 0; j < V; ++j) {
-            if ((keep >> j) & 1u) {
-              if (pos < uint32_t(kTbStage)) {
-                sm.key[pos] = key[j];
-                sm.col[pos] = uint16_t(c0 + j - s);
-              }
-              kmin = min(kmin, key[j]);
-              kmax = max(kmax, key[j]);
-              ++pos;
-            }
-          }
-        }
-        return true;
-      };
+      // the scores that reach tau.  tau = 0 keeps every score, NaN included:
+      // that row is selected from memory
+      const float tf = tau_value(tau);
       const int64_t mis = int64_t(((reinterpret_cast<uintptr_t>(rowp) + uint64_t(s) * ES) & 15u) / ES);
       const int64_t h = mis == 0 ? s : (s + V - mis < e ? s + V - mis : e);  // first aligned column
       const int64_t nv = (e - h) / V;                                         // aligned vectors
       const int64_t q0 = h + nv * wave / kTbWaves * V, q1 = h + nv * (wave + 1) / kTbWaves * V;
-      if (wave == 0 && h > s) stream_window<BF>(rs, rowp, s, h, append);
-      if (q1 > q0) stream_window<BF>(rs, rowp, q0, q1, append);
-      if (wave == kTbWaves - 1 && h + nv * V < e) stream_window<BF>(rs, rowp, h + nv * V, e, append);
+      // the unaligned columns before h and after the last vector: lane 0 of
+      // the first and last waves, one by one
+      auto few = [&](int64_t c, int64_t c_end) {
+        if (lane == 0) {
+          for (int64_t cc = c; cc < c_end; ++cc) {
+            const uint32_t b = bits_at(cc);
+            if (__uint_as_float(b) >= tf) {
+              const uint32_t p = atomicAdd(&sm.count, 1u);
+              if (p < uint32_t(kTbStage)) {
+                sm.key[p] = b;
+                sm.col[p] = uint16_t(cc - s);
+              }
+            }
+          }
+        }
+      };
+      if (tau != 0u) {
+        if (wave == 0 && h > s) few(s, h);
+        stream_keep<BF>(rowp, s, q0, q1, tf, sm);
+        if (wave == kTbWaves - 1 && h + nv * V < e) few(h + nv * V, e);
+      }
       __syncthreads();
       C = sm.count;
-      exact = C > uint32_t(kTbStage) || C < n_out;
+      exact = tau == 0u || C > uint32_t(kTbStage) || C < n_out;
+      if (!exact) {  // the staged scores' bits become rank keys
+        for (uint32_t p = uint32_t(t); p < C; p += kTbThreads) {
+          const uint32_t key = rank_key(sm.key[p]);
+          sm.key[p] = key;
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
     }
   }
 

@@ -276,7 +276,7 @@ struct SlotCursor {
 
 __global__ void __launch_bounds__(kRowThreads) select_rows_kernel(const SelArgs a) {
   __shared__ RowSmem sm;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int64_t r = blockIdx.x;
   const PlanLayout& L = a.L;
   const int k = a.k;
@@ -481,7 +481,7 @@ __device__ void for_groups(const SelArgs& a, int64_t r, SelSmem& sm, Body body) 
 // barriers (the waves' shares differ).
 template <typename Fn>
 __device__ void for_candidates(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint2* row = a.cand + r * int64_t(a.S_k);
   for_groups(a, r, sm, [&](int gsize, uint32_t gbase, uint32_t) {
     for (int jj = wave; jj < gsize; jj += kSelWaves) {
@@ -533,7 +533,7 @@ __device__ void walk(const SelArgs& a, int64_t r, SelSmem& sm, Fn fn) {
 // and pass 2.
 template <bool BY_SCORE>
 __device__ void select_row(const SelArgs& a, int64_t r, SelSmem& sm) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int k = a.k;
   int32_t* oi = a.out_idx + r * k;
   float* ov = a.out_val != nullptr ? a.out_val + r * k : nullptr;
