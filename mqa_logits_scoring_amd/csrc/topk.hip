@@ -489,8 +489,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
 //    their columns, in any order: about 1.25 k + 512 of them.
 //  - A radix select over the staged keys, then over the columns of the keys
 //    equal to its threshold, gives the selection; its columns are marked in
-//    a bitmap of the window, and a scan of the bitmap lists them in column
-//    order.
+//    a bitmap of the window, whose word counts give each selected column its
+//    place in column order, and its score is written there from the stage
+//    (no second read of the row).
 //  - A row whose threshold keeps more keys than the stage holds (many equal
 //    scores) or fewer than it must select, or whose sample does not fit, is
 //    selected from memory by its first wave: the same radix selects, every
@@ -507,19 +508,20 @@ constexpr int kTbMaxBitmapCols = 65536;       // windows the bitmap covers (thre
 constexpr int64_t kTkMaxCols = int64_t(1) << 28;
 
 struct TbSmem {
-  uint32_t key[kTbStage];  // keys by position; then the selection's columns in order
+  uint32_t key[kTbStage];  // staged scores' bits (fp32; bf16 widened), by position
   uint16_t col[kTbStage];  // window column (past s) of each position of a thresholded row
   union {
     uint32_t hist[kHistWords];                 // radix-select histograms
     uint32_t bits[kTbMaxBitmapCols / 32];      // the selection's columns
   };
+  uint16_t wpre[kTbMaxBitmapCols / 32];        // selected columns in the bitmap's words before each
   uint32_t res[4];
   uint32_t mm[2 * kTbWaves];
   uint32_t wsum[kTbWaves];
   uint32_t count;
 };
 static_assert(kTbMaxBitmapCols / 32 <= kHistWords, "the bitmap shares the histograms' words");
-static_assert(kMaxTopK <= kTbStage, "the selection's columns are listed in the key stage");
+static_assert(kMaxTopK <= 65535, "places in the output fit the 16-bit word prefixes");
 
 // Streams a row's columns [s, e): body(key, bits, c, valid) runs for the V
 // columns c, c + 1, ... of each lane's share, lanes in order and shares in
@@ -742,7 +744,7 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
       const int64_t p = kTbThreads * u + t;
       if (p < n) {
         const uint32_t key = rank_key(b[u]);
-        sm.key[p] = key;
+        sm.key[p] = b[u];
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       }
@@ -814,10 +816,9 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
       __syncthreads();
       C = sm.count;
       exact = tau == 0u || C > uint32_t(kTbStage) || C < n_out;
-      if (!exact) {  // the staged scores' bits become rank keys
+      if (!exact) {  // the staged scores' key range
         for (uint32_t p = uint32_t(t); p < C; p += kTbThreads) {
           const uint32_t key = rank_key(sm.key[p]);
-          sm.key[p] = key;
           kmin = min(kmin, key);
           kmax = max(kmax, key);
         }
@@ -837,7 +838,7 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
       T = radix_select<kTbThreads>(
           [&](auto fn) {
 #pragma unroll 4
-            for (uint32_t p = t; p < C; p += kTbThreads) fn(sm.key[p]);
+            for (uint32_t p = t; p < C; p += kTbThreads) fn(rank_key(sm.key[p]));
           },
           n_out, sm.hist, sm.res, count_eq, want, varying_bits(kmin, kmax), 0, kmin, true);
       if (want < count_eq) {  // ties at T: the want smallest columns among them
@@ -845,21 +846,30 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
         const uint32_t Vs = radix_select<kTbThreads>(
             [&](auto fn) {
               for (uint32_t p = t; p < C; p += kTbThreads)
-                if (sm.key[p] == T) fn(top - col_of(p));
+                if (rank_key(sm.key[p]) == T) fn(top - col_of(p));
             },
             want, sm.hist, sm.res, ce2, left2, nbits, 0, 0u, true);
         P2 = top - Vs;
       }
     }
-    // the selection's columns, marked in a bitmap of the window, then listed
-    // in column order: thread t scans words [t W, t W + W)
+    // the selection's columns, marked in a bitmap of the window; a column's
+    // place in the output is the number of marked columns before it: the
+    // selected columns of the words before its own (thread t sums words
+    // [t W, t W + W), a prefix sum over the threads) and those below it in
+    // its own word.  A thresholded row's selected scores are written there
+    // from the stage, each with its column; a staged window (score of column
+    // p at p) is listed in column order and written in order.
     const int words = int((n + 31) / 32);
     for (int i = t; i < words; i += kTbThreads) sm.bits[i] = 0;
     __syncthreads();
+    auto selected = [&](uint32_t raw, uint32_t c) {
+      const uint32_t key = rank_key(raw);
+      return key > T || (key == T && c <= P2);
+    };
 #pragma unroll 4
     for (uint32_t p = t; p < C; p += kTbThreads) {
-      const uint32_t key = sm.key[p], c = col_of(p);
-      if (key > T || (key == T && c <= P2)) atomicOr(&sm.bits[c >> 5], 1u << (c & 31));
+      const uint32_t c = col_of(p);
+      if (selected(sm.key[p], c)) atomicOr(&sm.bits[c >> 5], 1u << (c & 31));
     }
     __syncthreads();
     const int W = (words + kTbThreads - 1) / kTbThreads;
@@ -870,32 +880,45 @@ __global__ void __launch_bounds__(kTbThreads) topk_rows_kernel(const unsigned ch
     }
     uint32_t total;
     uint32_t pos = block_scan<kTbWaves>(mine, sm.wsum, total) - mine;
+    if (direct) {
+      // column p's score is staged at p: list the selected columns in order
+      // (in the unused column stage), then write the output in order
+      for (int j = 0; j < W; ++j) {
+        const int wd = t * W + j;
+        uint32_t bw = wd < words ? sm.bits[wd] : 0u;
+        while (bw != 0) {
+          const int b = __builtin_ctz(bw);
+          bw &= bw - 1u;
+          if (pos < n_out) sm.col[pos] = uint16_t(32 * wd + b);
+          ++pos;
+        }
+      }
+      __syncthreads();
+      for (uint32_t i = t; i < n_out; i += kTbThreads) {
+        const uint32_t c = sm.col[i];
+        oi[i] = int32_t(s + int64_t(c));
+        if (ov) ov[i] = __uint_as_float(sm.key[c]);
+      }
+      return;
+    }
     for (int j = 0; j < W; ++j) {
       const int wd = t * W + j;
-      uint32_t bw = wd < words ? sm.bits[wd] : 0u;
-      while (bw != 0) {
-        const int b = __builtin_ctz(bw);
-        bw &= bw - 1u;
-        if (pos < n_out) sm.key[pos] = uint32_t(32 * wd + b);
-        ++pos;
+      if (wd < words) {
+        sm.wpre[wd] = uint16_t(pos);
+        pos += uint32_t(__builtin_popcount(sm.bits[wd]));
       }
     }
     __syncthreads();
-    constexpr int UO = kMaxTopK / kTbThreads;
-    int64_t cc[UO];
-    uint32_t bv[UO];
-#pragma unroll
-    for (int u = 0; u < UO; ++u) {
-      const uint32_t i = uint32_t(kTbThreads * u + t);
-      cc[u] = s + int64_t(i < n_out ? sm.key[i] : 0u);
-      bv[u] = ov ? bits_at(cc[u]) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < UO; ++u) {
-      const uint32_t i = uint32_t(kTbThreads * u + t);
-      if (i < n_out) {
-        oi[i] = int32_t(cc[u]);
-        if (ov) ov[i] = __uint_as_float(bv[u]);
+#pragma unroll 4
+    for (uint32_t p = t; p < C; p += kTbThreads) {
+      const uint32_t raw = sm.key[p], c = col_of(p);
+      if (selected(raw, c)) {
+        const uint32_t w = c >> 5;
+        const uint32_t r = uint32_t(sm.wpre[w]) + uint32_t(__builtin_popcount(sm.bits[w] & ((1u << (c & 31)) - 1u)));
+        if (r < n_out) {
+          oi[r] = int32_t(s + int64_t(c));
+          if (ov) ov[r] = __uint_as_float(raw);
+        }
       }
     }
     return;
