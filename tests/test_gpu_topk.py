@@ -97,15 +97,23 @@ def _crafted(rng, n_rows, S_k, kind):
         v[rng.random(v.shape) < 0.2] = np.nan
         v[rng.random(v.shape) < 0.05] = -np.inf
         return v
+    if kind == "mostly_nan":  # the sample's threshold lands on NaN's key: those rows go to the path from memory
+        v = rng.standard_normal((n_rows, S_k)).astype(np.float32)
+        v[rng.random(v.shape) < 0.97] = np.nan
+        v[rng.random(v.shape) < 0.01] = -0.0
+        return v
     if kind == "equal":
         return np.full((n_rows, S_k), 1.5, np.float32)
     return rng.standard_normal((n_rows, S_k)).astype(np.float32) * np.float32(1e-3)
 
 
-@pytest.mark.parametrize("kind", ["ties", "nan", "equal", "normal"])
+CRAFTED = ["ties", "nan", "equal", "normal", "mostly_nan"]
+
+
+@pytest.mark.parametrize("kind", CRAFTED)
 @pytest.mark.parametrize("k", [1, 7, 300, 2048])
 def test_topk_crafted(kind, k):
-    rng = np.random.default_rng(["ties", "nan", "equal", "normal"].index(kind) * 10007 + k)
+    rng = np.random.default_rng(CRAFTED.index(kind) * 10007 + k)
     B, S_q, S_k = 2, 9, 37000
     v = _crafted(rng, B * S_q, S_k, kind)
     starts = rng.integers(0, S_k, size=B * S_q)
