@@ -9,6 +9,12 @@ parity test is sure to notice:
   condition whose operand is an MFMA result), the masked-off lanes lose what
   the compiler assumed they still hold.
 * No scratch: a spill in the main loop brings a full memory wait with it.
+* No waterfall loop (a loop that takes a buffer resource held in vector
+  registers one distinct value at a time) where the work is: between the
+  first and last matrix instruction of a scoring kernel, or anywhere in the
+  top-k kernels.  The compiler builds one when it cannot prove a resource's
+  base or size the same in every lane (a wave index taken from the thread
+  index without readfirstlane did that to every load of the top-k stream).
 
 The check compiles each score source to device assembly and walks it in text
 order: an if-region opens at s_and_saveexec / s_or_saveexec and closes at the
@@ -88,6 +94,31 @@ def private_segment_sizes(asm: str) -> dict[str, int]:
     return sizes
 
 
+def waterfall_loops(asm: str, hot_only: bool) -> list[str]:
+    """Kernels and lines of waterfall loops: a compare of a 64-bit value in
+    scalar registers with vector registers, followed within a few
+    instructions by an exec save, a buffer or global access and the exec
+    mask's flip that loops back.  hot_only: only those between the kernel's
+    first and last matrix instruction."""
+    found = []
+    for m in re.finditer(r"^(_Z\w+):", asm, re.M):
+        start = m.end()
+        end = asm.find(".Lfunc_end", start)
+        lines = [l.split(";")[0].strip() for l in asm[start:end].splitlines()]
+        mf = [i for i, l in enumerate(lines) if l.startswith("v_mfma")]
+        lo, hi = (mf[0], mf[-1]) if (hot_only and mf) else (0, len(lines))
+        if hot_only and not mf:
+            continue
+        for i in range(lo, hi):
+            l = lines[i]
+            if l.startswith("v_cmp_eq_u64") and ", s[" in l:
+                win = lines[i:i + 8]
+                if (any("saveexec" in x for x in win) and any(x.startswith(("buffer_", "global_")) for x in win)
+                        and any(x.startswith("s_xor_b64 exec") for x in win)):
+                    found.append(f"{m.group(1)}: line {i}")
+    return found
+
+
 @pytest.fixture(scope="module")
 def score_asm(tmp_path_factory):
     d = str(tmp_path_factory.mktemp("asm"))
@@ -125,3 +156,33 @@ def test_no_scratch(score_asm, src):
     assert sizes, f"{src}: no kernel descriptors found"
     spilled = {k: v for k, v in sizes.items() if v}
     assert not spilled, f"{src}: kernels use scratch: {spilled}"
+
+
+def test_checker_flags_waterfall():
+    asm = "\n".join([
+        "_Zkern:",
+        "  v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+        ".LBB0_1:",
+        "  v_readfirstlane_b32 s8, v46",
+        "  v_cmp_eq_u64_e32 vcc, s[8:9], v[46:47]",
+        "  s_and_saveexec_b64 s[4:5], vcc",
+        "  buffer_store_dword v9, v4, s[8:11], 0 offen",
+        "  s_xor_b64 exec, exec, s[4:5]",
+        "  s_cbranch_execnz .LBB0_1",
+        "  v_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], v[20:23], 0",
+        ".Lfunc_end0:",
+    ])
+    assert len(waterfall_loops(asm, hot_only=True)) == 1
+    assert not waterfall_loops(asm.replace("buffer_store_dword", "v_mov_b32"), hot_only=False)
+
+
+@pytest.mark.parametrize("src", SCORE_SOURCES)
+def test_no_waterfall_in_scoring_loops(score_asm, src):
+    bad = waterfall_loops(score_asm[src], hot_only=True)
+    assert not bad, f"{src}: {len(bad)} waterfall loops among the matrix instructions, e.g. {bad[:3]}"
+
+
+@pytest.mark.parametrize("src", ["topk.hip", "topk_fused.hip"])
+def test_no_waterfall_in_topk(src, tmp_path):
+    bad = waterfall_loops(device_asm(src, str(tmp_path)), hot_only=False)
+    assert not bad, f"{src}: {len(bad)} waterfall loops, e.g. {bad[:3]}"
