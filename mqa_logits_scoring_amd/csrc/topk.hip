@@ -479,13 +479,13 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(const unsigned char*
 //
 // The kernel above holds a whole CU for one row, all of it in registers.
 // Rows selected by column run here instead, four workgroups per CU, each
-// with about 33 KB of LDS:
-//  - A window of at most kTbStage columns is staged whole: key p is column
-//    s + p.
+// with about 37 KB of LDS:
+//  - A window of at most kTbStage columns is staged whole: the score of
+//    column s + p at p.
 //  - A wider one is thresholded first, as the fused selection is: the key of
 //    the m-th best of a sample of its columns (the first 32 of every 512),
 //    its low 16 bits cleared, m = sample_rank.  The four waves then stream a
-//    quarter of the window each and append the keys that reach it, with
+//    quarter of the window each and stage the scores that reach it, with
 //    their columns, in any order: about 1.25 k + 512 of them.
 //  - A radix select over the staged keys, then over the columns of the keys
 //    equal to its threshold, gives the selection; its columns are marked in
