@@ -51,7 +51,8 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp8": 5000.0, "mxfp4": 10100.0}
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 METRIC = "µs/call + effective TFLOP/s (visible cells) at H64/D128, MXFP8 Q2048/KV32768"
-PAGES_US = {"c4_mxfp8_zero": 412.0, "c4_mxfp4_zero": 407.9}  # GB200, no metadata, all-zero inputs
+# GB200, no metadata, all-zero inputs (DeepGEMM pull request 435, Performance section)
+PAGES_US = {"c4_mxfp8_zero": 412.0, "c4_mxfp4_zero": 407.9, "q8k_mxfp8_zero": 3022.2, "q8k_mxfp4_zero": 2968.9}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 CSRC = os.path.join(ROOT, "mqa_logits_scoring_amd", "csrc")
 

@@ -282,6 +282,31 @@ def test_named_full_size(name):
     print(f"{name}: {len(rows)} rows, max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+def test_q8192_kv65536_full_size(fmt):
+    """The page's long case, Q8192 / KV65536 with windows [0, KV - Q + row):
+    on all-zero inputs (the page's timing setup) every in-window cell is
+    exactly 0 and every other one -inf, checked over all 537 M cells; on
+    random inputs a spread of rows is within tolerance of the oracle."""
+    wl = W.make(f"q8k_{fmt}_zero")
+    d = dev_inputs(wl)
+    out = run(wl, d, out=torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    mask_check_all_rows(wl, out)
+    inside_check_all_rows(wl, out)
+    assert bool((out[torch.isfinite(out)] == 0).all()), "a zero workload scored a nonzero cell"
+    del out, d
+    wl = W.make(f"q8k_{fmt}")
+    d = dev_inputs(wl)
+    out = run(wl, d, out=torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), device="cuda"))
+    torch.cuda.synchronize()
+    mask_check_all_rows(wl, out)
+    rows = np.array([0, 1, 2047, 4096, 8190, 8191])
+    ref, bound = oracle.logits(wl, rows=rows)
+    got = to_f64(out.reshape(wl.B * wl.S_q, -1)[torch.from_numpy(rows).cuda()])
+    compare_rows(wl, got, ref, bound, what=f"q8192/kv65536 {fmt}")
+
+
 @pytest.mark.parametrize("name", ["c3", "c4_mxfp8", "c4_mxfp4"])
 def test_named_every_cell(name):
     """Every cell of the Q2048 / KV32768 workloads against the oracle (values

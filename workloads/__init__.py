@@ -425,6 +425,14 @@ def _paged_decode(**kw):
                       name="paged_mxfp8_decode", **kw)
 
 
+def _q8k(fmt, zero=False, **kw):
+    # the long case of the DeepGEMM pull request 435 page's timing table
+    # (Performance section): Q8192 / KV65536, windows [0, KV - Q + row), fp32
+    # weights and scores; the page times it on all-zero inputs with scales 1
+    return make_random(fmt, 1, 8192, 65536, w_dtype="f32", sm_scale=1.0, seed=11, offsets=[-1], zero=zero,
+                       name=f"q8192_kv65536_{fmt}{'_zero' if zero else ''}", **kw)
+
+
 def _screen(H, **kw):
     # the head-count screen of the DeepGEMM pull request 435 page (H = 8, 32,
     # 64 at Q = KV = 8192, Performance section): MXFP8, causal, fp32 weights
@@ -446,6 +454,10 @@ NAMED = {
     "c5_nonaligned": lambda **kw: _c5(S_q=129, S_k=4100, seed=6, name="c5_nonaligned", **kw),
     "thd_bf16_r4": _thd,
     "paged_mxfp8_decode": _paged_decode,
+    "q8k_mxfp8": lambda **kw: _q8k("mxfp8", **kw),
+    "q8k_mxfp4": lambda **kw: _q8k("mxfp4", **kw),
+    "q8k_mxfp8_zero": lambda **kw: _q8k("mxfp8", zero=True, **kw),
+    "q8k_mxfp4_zero": lambda **kw: _q8k("mxfp4", zero=True, **kw),
     "screen_h8": lambda **kw: _screen(8, **kw),
     "screen_h32": lambda **kw: _screen(32, **kw),
     "screen_h64": lambda **kw: _screen(64, **kw),
