@@ -843,6 +843,196 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ---------------------------------------------------------------------------
+// BF16 operands with one query row per wave (plain calls on contiguous keys,
+// tiles of more than two rows).
+//
+// Two rows of BF16 Q take 128 registers, so score_kernel runs one wave per
+// SIMD for BF16, and nothing covers a wave's own waits (the loads of its Q,
+// of its next key block).  Here a workgroup's four waves take one row each,
+// half a tile: a unit is (tile, chunk, half), two work positions per unit,
+// and the 64 Q registers of one row leave room for two waves per SIMD, so
+// two workgroups share a CU and one's loads run under the other's MFMAs.
+// Per 32-column block a wave issues the two 32x32 blocks of its row (heads
+// 0-31, 32-63) over all of d, each interleaved with the epilogue of the
+// previous one, in the order score_kernel uses for one row, so every score
+// is bitwise the one score_kernel gives.  After the head-sum swap both lane
+// halves hold the row's 32 columns; the first half stores them.
+template <int F, bool WBF, bool OBF, bool CLEAN>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+    score_kernel_bf16w(const ScoreArgs a) {
+  static_assert(bf16_operands(F), "BF16 operands only");
+  using T = Fmt<F>;
+  constexpr bool HAS_KS = T::ROWSCALE;
+  constexpr int QD = T::LB / 4;  // dwords per lane per row
+  constexpr int KD = T::KB / 4;  // dwords per lane per k-step
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), g = lane >> 5, c = lane & 31;
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(a.plan);
+  const bool plan_ok = hdr->magic == kPlanMagic && hdr->B == a.B && hdr->S_q == a.S_q && hdr->S_k == a.S_k &&
+                       hdr->H == 64 && hdr->D == 128 && hdr->tile_rows == kTileRows && hdr->n_tiles == a.n_tiles;
+  const int pos = int(blockIdx.x);
+  if (pos >= a.n_pos_compute) {
+    cleanup_unit<OBF, CLEAN, kTileRows>(a, pos - a.n_pos_compute, plan_ok);
+    return;
+  }
+  if (!plan_ok) return;
+  // positions 2j and 2j + 1: the two halves of unit j, next to each other
+  const Unit u = decode_unit(a, pos >> 1);
+  if (u.kind != kUnitCompute) return;
+  const int tile = u.tile, c0 = u.c0, c1 = u.c1;
+  const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
+  const int b = tile / a.tiles_per_batch;
+
+  const int32_t* slot_row = reinterpret_cast<const int32_t*>(a.plan + a.off_slot);
+  const int row = __builtin_amdgcn_readfirstlane(slot_row[int64_t(tile) * kTileRows + (pos & 1) * 4 + wave]);
+  if (row < 0) return;  // a padding slot: nothing to score
+
+  // Q fragments of heads 32*mb + c, weights of the lane's 16 heads per block
+  uint32_t qf[2][QD];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int64_t qrow = int64_t(row) * 64 + 32 * mb + c;
+    const unsigned char* src = static_cast<const unsigned char*>(a.q) + qrow * T::ROWB + g * T::CBASE;
+#pragma unroll
+    for (int v = 0; v < QD / 4; ++v) {
+      const uint4 x = *reinterpret_cast<const uint4*>(src + v * T::CSTRIDE);
+      qf[mb][4 * v + 0] = x.x;
+      qf[mb][4 * v + 1] = x.y;
+      qf[mb][4 * v + 2] = x.z;
+      qf[mb][4 * v + 3] = x.w;
+    }
+  }
+  float wv[2][16];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int64_t off = int64_t(row) * 64 + 32 * mb + 8 * q4 + 4 * g;
+      if constexpr (WBF) {
+        const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.w) + off);
+        wv[mb][4 * q4 + 0] = __uint_as_float(x.x << 16);
+        wv[mb][4 * q4 + 1] = __uint_as_float(x.x & 0xFFFF0000u);
+        wv[mb][4 * q4 + 2] = __uint_as_float(x.y << 16);
+        wv[mb][4 * q4 + 3] = __uint_as_float(x.y & 0xFFFF0000u);
+      } else {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(a.w) + off);
+        wv[mb][4 * q4 + 0] = x.x;
+        wv[mb][4 * q4 + 1] = x.y;
+        wv[mb][4 * q4 + 2] = x.z;
+        wv[mb][4 * q4 + 3] = x.w;
+      }
+    }
+  }
+  const int my_s = reinterpret_cast<const int32_t*>(a.plan + a.off_start)[row];
+  const int my_e = reinterpret_cast<const int32_t*>(a.plan + a.off_end)[row];
+
+  // K in fragment order (as score_kernel reads it)
+  const int nblk = (a.S_k + 31) >> 5;
+  const int kb0 = c0 >> 5;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<unsigned char*>(a.kfrag) + int64_t(b) * nblk * (32 * T::ROWB), 0, nblk * (32 * T::ROWB), kBufWord3);
+  const __amdgpu_buffer_rsrc_t srs =
+      HAS_KS ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(a.kscale) + int64_t(b) * nblk * 64, 0,
+                                                 nblk * 256, kBufWord3)
+             : krs;
+  auto kload = [&](int u, uint32_t (&bf)[QD], uint32_t& kword) {
+    const int blk = min(kb0 + u, nblk - 1);
+#pragma unroll
+    for (int v = 0; v < QD / 4; ++v) {
+      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + v * 1024, blk * (32 * T::ROWB), 0);
+      bf[4 * v + 0] = x[0];
+      bf[4 * v + 1] = x[1];
+      bf[4 * v + 2] = x[2];
+      bf[4 * v + 3] = x[3];
+    }
+    if constexpr (HAS_KS) kword = __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, blk * 256, 0);
+  };
+  auto mfma_block = [&](f32x16& acc, const uint32_t (&q)[QD], const uint32_t (&bf)[QD]) {
+    f32x16 d = {};
+#pragma unroll
+    for (int st = 0; st < T::KSTEPS; ++st) {
+      bf16x8 av, bv;
+      __builtin_memcpy(&av, &q[st * KD], 16);
+      __builtin_memcpy(&bv, &bf[st * KD], 16);
+      d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, d, 0, 0, 0);
+    }
+    acc = d;
+  };
+
+  // stores: one resource for the row, based at the unit's first column; the
+  // second lane half and, without cleaning, cells outside the window drop
+  constexpr int ES = OBF ? 2 : 4;
+  constexpr uint32_t kDrop = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+      static_cast<unsigned char*>(a.out) + (int64_t(row) * a.ld + c0) * ES, 0, (c1 - c0) * ES, kBufWord3);
+  const uint32_t half = g ? kDrop : 0u;
+  const uint32_t s_rel = uint32_t(my_s - c0) * ES;
+  const uint32_t w_len = uint32_t(max(my_e - my_s, 0)) * ES;
+  auto store = [&](float v, int u) {
+    const uint32_t off = uint32_t(32 * u + c) * ES;  // u = -1 wraps to a huge offset: dropped
+    const bool inwin = off - s_rel < w_len;
+    uint32_t o = off | half;
+    if constexpr (!CLEAN) o = inwin ? o : kDrop;
+    float val = v;
+    if constexpr (CLEAN)
+      val = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(v), 0xFF800000u,
+                                                  inwin ? 0x07060504u : 0x03020100u));
+    if constexpr (OBF) {
+      const uint16_t h = __builtin_bit_cast(uint16_t, static_cast<__bf16>(val));  // round to nearest even
+      __builtin_amdgcn_raw_buffer_store_b16(h, ors, int(o), 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ors, int(o), 0, kNonTemporal);
+    }
+  };
+
+  // ReLU as a signed-integer max of the float's bits (as in score_kernel),
+  // weighted and summed over the lane's 16 heads of one block
+  auto epi_relu = [&](const f32x16& acc, const float (&w)[16], float p) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) p = __builtin_fmaf(w[r], __int_as_float(max(__float_as_int(acc[r]), 0)), p);
+    return p;
+  };
+  // both lane halves' sums of the column, in each half
+  auto combine = [&](float p, float ks) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    const float v = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * a.sm_scale;
+    return T::ROWSCALE ? v * ks : v;
+  };
+  f32x16 accA = {}, accB = {};
+  float p = 0.f;
+  float kprev = 1.f;
+  auto block = [&](const uint32_t (&bf)[QD], uint32_t kword, int u) {
+    mfma_block(accA, qf[0], bf);        // heads 0-31 of u   ||
+    p = epi_relu(accB, wv[1], p);       //   heads 32-63 of u-1, completing u-1
+    const float v = combine(p, kprev);
+    kprev = __uint_as_float(kword);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(accB, qf[1], bf);        // heads 32-63 of u  ||
+    p = epi_relu(accA, wv[0], 0.f);     //   heads 0-31 of u
+    __builtin_amdgcn_sched_barrier(0);
+    store(v, u - 1);
+  };
+  constexpr int NB = 2;
+  uint32_t bfs[NB][QD];
+  uint32_t kws[NB] = {};
+  kload(0, bfs[0], kws[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  for (int st = 0; st < n_pairs; ++st) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int u = NB * st + i;
+      kload(u + 1, bfs[1 - i], kws[1 - i]);
+      block(bfs[i], kws[i], u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  p = epi_relu(accB, wv[1], p);
+  store(combine(p, kprev), 2 * n_pairs - 1);
+}
+
+// ---------------------------------------------------------------------------
 // 64-head kernel for FP8 and MXFP8 keys in fragment order, on 16x16x128 MFMAs
 //
 // Same units, rows per wave, windows, stores and cleanup as score_kernel; the
@@ -1253,6 +1443,16 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
     else
       return launch_units(score_kernel<F, WBF, OBF, CLEAN, true>, a, stream);
   } else {
+    if constexpr (bf16_operands(F)) {
+      // one row per wave: two positions per compute unit, cleanup after them
+      const int64_t n_clean = int64_t(a.n_positions) - a.n_pos_compute;
+      if (!a.wave_split && !a.dyn_units && 2 * int64_t(a.n_pos_compute) + n_clean < (int64_t(1) << 31)) {
+        ScoreArgs h = a;
+        h.n_pos_compute = 2 * a.n_pos_compute;
+        h.n_positions = int32_t(h.n_pos_compute + n_clean);
+        return launch_units(score_kernel_bf16w<F, WBF, OBF, CLEAN>, h, stream);
+      }
+    }
     return launch_units(score_kernel<F, WBF, OBF, CLEAN, false>, a, stream);
   }
 }
