@@ -79,6 +79,27 @@ def test_ragged_key_tails(fmt, S_k):
     _full_compare(wl, out)
 
 
+@pytest.mark.parametrize("S_q", [3, 4, 5, 9, 12, 16])
+@pytest.mark.parametrize("exact", [False, True], ids=["bf16", "fp8-exact"])
+def test_half_tile_units_every_cell(S_q, exact):
+    """BF16 operands (and FP8 converted to bf16 for exact accumulation) run
+    one query row per wave, half a tile per workgroup: tiles whose second
+    half is padding, partly padded, or full, over two batches, irregular
+    windows, every cell against the oracle, and bitwise the same with the
+    plan passed in and built inside."""
+    wl = W.make_random("fp8" if exact else "bf16", 2, S_q, 1000, seed=60 + S_q, windows="irregular",
+                       out_dtype="bf16" if S_q % 2 else "f32")
+    d = dev_inputs(wl)
+    acc = "fp32" if exact else "native"
+    out = run(wl, d, accumulate=acc, out=torch.full((wl.B, wl.S_q, wl.S_k), float("nan"), device="cuda",
+                                                     dtype=torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32))
+    out2 = run(wl, d, plan=make_plan(wl, d), accumulate=acc)
+    torch.cuda.synchronize()
+    iv = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out.view(iv), out2.view(iv))
+    _full_compare(wl, out)
+
+
 def test_c1_full():
     wl = W.make("c1")
     d = dev_inputs(wl)
