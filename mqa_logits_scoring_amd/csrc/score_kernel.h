@@ -4,10 +4,14 @@
 //   out[i, j] = sm_scale * sum_h w[i,h] * max(0, q[i,h,:] . k[j,:])
 // (the lightning-indexer score; include/idx_logits.h says where the pages
 // define it) and writes -inf to the tile's in-coverage cells outside a row's
-// window when cleaning.  Cells outside the tile's coverage are written by
-// cleanup units that run after the compute units in the same grid, so cleanup
-// never competes with the matrix work of a compute unit (the placement lesson
-// of DeepGEMM pull request 435, Investigation notes).
+// window when cleaning.  Cells outside the tile's coverage are written, in
+// this kernel, by cleanup units that run after the compute units in the same
+// grid, so cleanup never competes with the matrix work of a compute unit (the
+// placement lesson of DeepGEMM pull request 435, Investigation notes).  The
+// FP8-family kernel and the one-row BF16 kernel below instead clean each row
+// in the compute unit that scores it, after its last score store: with two
+// workgroups per CU the other's MFMAs cover those stores, and the launch has
+// no tail of cleanup units.
 //
 // Work decomposition
 //   workgroup = 4 waves = one tile of kTileRows query rows x one key chunk
@@ -245,12 +249,44 @@ __device__ void cleanup_unit(const ScoreArgs& a, int tile, bool plan_ok) {
   }
 }
 
+// -inf over [0, lo) and [hi, S_k) of one output row, by one wave (lane =
+// its lane): wave-uniform loops whose buffer ranges drop what lies past each
+// part, so no lane branches.  Compute units that clean their own rows call
+// it after their last store; nothing waits on these stores.
+template <bool OBF>
+__device__ __forceinline__ void clean_row_outside(const ScoreArgs& a, int row, int lo, int hi, int lane) {
+  constexpr int ES = OBF ? 2 : 4;
+  unsigned char* base = static_cast<unsigned char*>(a.out) + int64_t(row) * a.ld * ES;
+  const __amdgpu_buffer_rsrc_t r0 = __builtin_amdgcn_make_buffer_rsrc(base, 0, lo * ES, kBufWord3);
+  const __amdgpu_buffer_rsrc_t r1 =
+      __builtin_amdgcn_make_buffer_rsrc(base + int64_t(hi) * ES, 0, (a.S_k - hi) * ES, kBufWord3);
+  for (int j = 0; j < lo; j += 64) {
+    if constexpr (OBF) __builtin_amdgcn_raw_buffer_store_b16(uint16_t(0xFF80u), r0, (j + lane) * ES, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(0xFF800000u, r0, (j + lane) * ES, 0, kNonTemporal);
+  }
+  for (int j = 0; j < a.S_k - hi; j += 64) {
+    if constexpr (OBF) __builtin_amdgcn_raw_buffer_store_b16(uint16_t(0xFF80u), r1, (j + lane) * ES, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b32(0xFF800000u, r1, (j + lane) * ES, 0, kNonTemporal);
+  }
+}
+
+// Compute units clean their own rows when the launch has no cleanup units
+// (launch_score_t drops them for the plain, non-paged, non-decode FP8-family
+// and one-row BF16 kernels when cleaning).
+__device__ __forceinline__ bool units_clean_own_rows(const ScoreArgs& a) {
+  return a.n_positions == a.n_pos_compute && !a.wave_split && !a.dyn_units;
+}
+
 // A unit of work: compute (a tile's columns [c0, c1)), cleanup (a tile's
 // cells outside its coverage) or nothing (a missing tile of a partial
-// segment, or a chunk past the tile's coverage).
+// segment, or a chunk past the tile's coverage).  [0, cl0) and [cl1, S_k) are
+// the cells outside the coverage that the unit cleans when compute units
+// clean their own rows: the first chunk takes the cells left of the
+// coverage, the last the cells right of it; chunk 0 of a tile whose rows all
+// see nothing (kind none, tile >= 0) takes whole rows.
 enum { kUnitNone = 0, kUnitCompute = 1, kUnitCleanup = 2 };
 struct Unit {
-  int kind, tile, c0, c1, chunk;
+  int kind, tile, c0, c1, chunk, cl0, cl1;
 };
 
 // dyn_units: compute position p -> unit.  Every wave reads every tile's
@@ -316,12 +352,12 @@ __device__ __forceinline__ Unit decode_dyn_unit(const ScoreArgs& a, int p) {
     c1 = here != 0 ? min(a0 + w, end_s) : c1;
     carry += uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
   }
-  return Unit{tile >= 0 ? int(kUnitCompute) : int(kUnitNone), max(tile, 0), c0, c1, 0};
+  return Unit{tile >= 0 ? int(kUnitCompute) : int(kUnitNone), max(tile, 0), c0, c1, 0, 0, a.S_k};
 }
 
 // Work position p (ScoreArgs) -> unit.
 __device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
-  if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0, 0};
+  if (p >= a.n_pos_compute) return Unit{kUnitCleanup, p - a.n_pos_compute, 0, 0, 0, 0, a.S_k};
   if (a.dyn_units) return decode_dyn_unit(a, p);
   const int slot = p / a.n_chunk, chunk = p - slot * a.n_chunk;
   // slot -> (batch, segment, rank): batches and segments from the last
@@ -339,13 +375,13 @@ __device__ __forceinline__ Unit decode_unit(const ScoreArgs& a, int p) {
   }
   const int tile =
       reinterpret_cast<const int32_t*>(a.plan + a.off_order)[(int64_t(b) * spb + seg) * tps + rank];
-  if (tile < 0) return Unit{kUnitNone, 0, 0, 0, 0};
+  if (tile < 0) return Unit{kUnitNone, -1, 0, 0, 0, 0, a.S_k};
   const int lo = reinterpret_cast<const int32_t*>(a.plan + a.off_lo)[tile];
   const int hi = reinterpret_cast<const int32_t*>(a.plan + a.off_hi)[tile];
   const int w = max(a.min_chunk, ((hi - lo + a.n_chunk - 1) / a.n_chunk + 63) & ~63);
   const int c0 = lo + chunk * w, c1 = min(hi, c0 + w);
-  if (c0 >= c1) return Unit{kUnitNone, 0, 0, 0, 0};
-  return Unit{kUnitCompute, tile, c0, c1, chunk};
+  if (c0 >= c1) return Unit{kUnitNone, tile, c0, c0, chunk, 0, chunk == 0 ? 0 : a.S_k};
+  return Unit{kUnitCompute, tile, c0, c1, chunk, chunk == 0 ? c0 : 0, c1 == hi ? c1 : a.S_k};
 }
 
 // Waves per SIMD the kernel is built for: the FP8-family and FP4 kernels fit in
@@ -856,7 +892,11 @@ __global__ void __launch_bounds__(kThreads)
 // 0-31, 32-63) over all of d, each interleaved with the epilogue of the
 // previous one, in the order score_kernel uses for one row, so every score
 // is bitwise the one score_kernel gives.  After the head-sum swap both lane
-// halves hold the row's 32 columns; the first half stores them.
+// halves hold the row's 32 columns; the first half stores them.  When
+// cleaning, each wave then writes -inf to its row outside the tile's coverage
+// (the first chunk left of it, the last chunk right of it): on short rows
+// (packed variable-length rows see about 420 keys) a tail of cleanup units
+// had cost a tenth of the launch.
 template <int F, bool WBF, bool OBF, bool CLEAN>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
     score_kernel_bf16w(const ScoreArgs a) {
@@ -877,10 +917,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     cleanup_unit<OBF, CLEAN, kTileRows>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
-  if (!plan_ok) return;
+  const bool own_clean = CLEAN && units_clean_own_rows(a);
+  if (!plan_ok) {
+    // no cleanup units to fill the rows with NaN: the first half of each
+    // tile's first chunk does it
+    if (own_clean && (pos & 1) == 0 && (pos >> 1) % a.n_chunk == 0)
+      cleanup_unit<OBF, CLEAN, kTileRows>(a, (pos >> 1) / a.n_chunk, false);
+    return;
+  }
   // positions 2j and 2j + 1: the two halves of unit j, next to each other
   const Unit u = decode_unit(a, pos >> 1);
-  if (u.kind != kUnitCompute) return;
+  // a tile whose rows all see nothing runs with no key block when it cleans
+  // its rows: its one store falls outside the (empty) column range
+  if (u.kind != kUnitCompute && !(own_clean && u.tile >= 0 && u.cl1 < a.S_k)) return;
   const int tile = u.tile, c0 = u.c0, c1 = u.c1;
   const int n_pairs = (c1 - c0 + 63) / 64;  // pairs of 32-column blocks
   const int b = tile / a.tiles_per_batch;
@@ -1030,12 +1079,14 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
   p = epi_relu(accB, wv[1], p);
   store(combine(p, kprev), 2 * n_pairs - 1);
+  if (own_clean) clean_row_outside<OBF>(a, row, u.cl0, u.cl1, lane);
 }
 
 // ---------------------------------------------------------------------------
 // 64-head kernel for FP8 and MXFP8 keys in fragment order, on 16x16x128 MFMAs
 //
-// Same units, rows per wave, windows, stores and cleanup as score_kernel; the
+// Same units, rows per wave, windows and stores as score_kernel, but each wave
+// cleans its own rows outside the coverage (no cleanup units); the
 // contraction and the linear term are cut differently.  A 16x16x128 block
 // takes all 128 d at once: A = 16 heads of one query row, B = 16 key columns.
 // Per 32 columns a wave issues 2 rows x 4 head blocks x 2 column halves = 16
@@ -1094,9 +1145,23 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
     cleanup_unit<OBF, CLEAN, kTileRows>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
-  if (!plan_ok) return;
+  // with no cleanup units in the launch, each wave cleans its own rows
+  const bool own_clean = CLEAN && !PD && !SEL && units_clean_own_rows(a);
+  if (!plan_ok) {
+    if (own_clean && pos % a.n_chunk == 0) cleanup_unit<OBF, CLEAN, kTileRows>(a, pos / a.n_chunk, false);
+    return;
+  }
   const Unit u = decode_unit(a, pos);
-  if (u.kind != kUnitCompute) return;
+  if (u.kind != kUnitCompute) {
+    if (own_clean && u.tile >= 0 && u.cl1 < a.S_k) {  // a tile whose rows all see nothing
+      const int32_t* srow = reinterpret_cast<const int32_t*>(a.plan + a.off_slot);
+      for (int t = 0; t < 2; ++t) {
+        const int r = __builtin_amdgcn_readfirstlane(srow[int64_t(u.tile) * kTileRows + wave * 2 + t]);
+        if (r >= 0) clean_row_outside<OBF>(a, r, 0, 0, lane);
+      }
+    }
+    return;
+  }
   const int tile = u.tile;
   int c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
   // the wave whose tile slots hold this wave's rows: its own, or with
@@ -1412,6 +1477,11 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   if constexpr (SEL) {
     if (c == 0 && (g ? rvalid[1] : rvalid[0])) sel_finish(a, my_row, u.chunk, c0, g ? sel_cnt[1] : sel_cnt[0]);
   }
+  if (own_clean) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+      if (rvalid[t]) clean_row_outside<OBF>(a, rows[t], u.cl0, u.cl1, lane);
+  }
 }
 
 // One launch of `kernel`: a workgroup per work position.
@@ -1435,17 +1505,23 @@ hipError_t launch_score_t(const ScoreArgs& a, hipStream_t stream) {
         return launch_units(score_kernel<F, WBF, OBF, false, false, true>, a, stream);
     }
   }
+  // the plain FP8-family kernel cleans its own rows: no cleanup units (the
+  // MXFP4 / generic kernel keeps them: there the cleaning lengthened the last
+  // chunks of long rows, which end the launch)
+  ScoreArgs own = a;
+  if (CLEAN && !pd && !a.wave_split && !a.dyn_units) own.n_positions = a.n_pos_compute;
   if constexpr (F == IDX_IN_FP8_E4M3 || F == IDX_IN_MXFP8_E4M3) {
     if (pd) return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, true>, a, stream);
-    return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, false>, a, stream);
+    return launch_units(score_kernel_x16<F, WBF, OBF, CLEAN, false>, own, stream);
   } else if (pd) {
     if constexpr (F == kInBF16RowScale) return hipErrorInvalidValue;  // converted keys are never read from a cache
     else
       return launch_units(score_kernel<F, WBF, OBF, CLEAN, true>, a, stream);
   } else {
     if constexpr (bf16_operands(F)) {
-      // one row per wave: two positions per compute unit, cleanup after them
-      const int64_t n_clean = int64_t(a.n_positions) - a.n_pos_compute;
+      // one row per wave: two positions per compute unit; with cleaning, each
+      // wave cleans its own row (no cleanup units)
+      const int64_t n_clean = CLEAN ? 0 : int64_t(a.n_positions) - a.n_pos_compute;
       if (!a.wave_split && !a.dyn_units && 2 * int64_t(a.n_pos_compute) + n_clean < (int64_t(1) << 31)) {
         ScoreArgs h = a;
         h.n_pos_compute = 2 * a.n_pos_compute;

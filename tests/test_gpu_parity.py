@@ -261,13 +261,40 @@ def test_row_stride_guard_band():
     assert torch.equal(buf[..., :77], ref)
 
 
-def test_plan_dimension_mismatch_is_loud():
-    wl = W.make_random("fp8", 1, 16, 128, seed=14, offsets=[0])
+@pytest.mark.parametrize("fmt", W.FORMATS)
+def test_plan_dimension_mismatch_is_loud(fmt):
+    """A plan of other dimensions fills every cell with NaN, whichever kernel
+    (and whichever unit cleans a row) the call takes."""
+    wl = W.make_random(fmt, 1, 16, 128, seed=14, offsets=[0])
     d = dev_inputs(wl)
-    other = W.make_random("fp8", 1, 16, 256, seed=14, offsets=[0])
+    other = W.make_random(fmt, 1, 16, 256, seed=14, offsets=[0])
     plan = make_plan(other, dev_inputs(other))
     out = run(wl, d, plan=plan)
     assert bool(torch.isnan(out).all())
+
+
+# Tiles whose rows all see nothing (rows 8-23: two whole tiles of 8 rows, and
+# at 64 heads two halves each) between tiles with windows, keys long enough
+# for several chunks per tile: every cell against the oracle, over a buffer
+# that starts as NaN, so a cell no unit writes shows.
+@pytest.mark.parametrize("fmt", W.FORMATS)
+@pytest.mark.parametrize("S_k", [300, 9000])
+def test_empty_tiles_every_cell(fmt, S_k):
+    S_q = 40
+    rng = np.random.default_rng(71)
+    starts = rng.integers(0, S_k // 2, S_q)
+    ends = starts + rng.integers(1, S_k // 2, S_q)
+    starts[8:24] = S_k // 3
+    ends[8:24] = S_k // 3  # empty
+    wl = W.make_random(fmt, 1, S_q, S_k, seed=71, windows="explicit", starts=starts.tolist(), ends=ends.tolist(),
+                       out_dtype="bf16" if fmt == "mxfp4" else "f32")
+    d = dev_inputs(wl)
+    out = run(wl, d, out=torch.full((1, S_q, S_k), float("nan"), device="cuda",
+                                    dtype=torch.bfloat16 if fmt == "mxfp4" else torch.float32))
+    torch.cuda.synchronize()
+    assert bool(torch.isneginf(out[0, 8:24].float()).all())
+    ratio, rel = compare_all_rows(wl, out, what=f"empty tiles {fmt} S_k={S_k}")
+    print(f"empty tiles {fmt} S_k={S_k}: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
 
 
 # ---------------------------------------------------------------------------
