@@ -71,9 +71,23 @@ __global__ void __launch_bounds__(kThreads)
     cleanup_unit<OBF, CLEAN, TR>(a, pos - a.n_pos_compute, plan_ok);
     return;
   }
-  if (!plan_ok) return;
+  // with no cleanup units in the launch, each wave cleans its own rows
+  const bool own_clean = CLEAN && !SEL && units_clean_own_rows(a);
+  if (!plan_ok) {
+    if (own_clean && pos % a.n_chunk == 0) cleanup_unit<OBF, CLEAN, TR>(a, pos / a.n_chunk, false);
+    return;
+  }
   const Unit u = decode_unit(a, pos);
-  if (u.kind != kUnitCompute) return;
+  if (u.kind != kUnitCompute) {
+    if (own_clean && u.tile >= 0 && u.cl1 < a.S_k) {  // a tile whose rows all see nothing
+      const int32_t* srow = reinterpret_cast<const int32_t*>(a.plan + a.off_slot) + int64_t(u.tile) * TR;
+      for (int t = 0; t < WR; ++t) {
+        const int r = __builtin_amdgcn_readfirstlane(srow[wave * WR + t]);
+        if (r >= 0) clean_row_outside<OBF>(a, r, 0, 0, lane);
+      }
+    }
+    return;
+  }
   const int tile = u.tile, c0 = u.c0, c1 = u.c1;  // columns [c0, c1) of the tile are this unit's
   const int n_pairs = (c1 - c0 + 63) / 64;
   const int b = tile / a.tiles_per_batch;
@@ -353,6 +367,11 @@ __global__ void __launch_bounds__(kThreads)
       if (c == 0 && (g ? rvalid[2 * i + 1] : rvalid[2 * i]))
         sel_finish(a, g ? rows[2 * i + 1] : rows[2 * i], u.chunk, c0, g ? sel_cnt[2 * i + 1] : sel_cnt[2 * i]);
   }
+  if (own_clean) {
+#pragma unroll
+    for (int t = 0; t < WR; ++t)
+      if (rvalid[t]) clean_row_outside<OBF>(a, rows[t], u.cl0, u.cl1, lane);
+  }
 }
 
 template <int F, int H, bool WBF, bool OBF, bool CLEAN>
@@ -363,7 +382,10 @@ hipError_t launch_score_gh_t(const ScoreArgs& a, hipStream_t stream) {
     else
       return launch_units(score_kernel_gh<F, H, WBF, OBF, false, true>, a, stream);
   }
-  return launch_units(score_kernel_gh<F, H, WBF, OBF, CLEAN>, a, stream);
+  // each wave cleans its own rows: no cleanup units
+  ScoreArgs own = a;
+  if (CLEAN) own.n_positions = a.n_pos_compute;
+  return launch_units(score_kernel_gh<F, H, WBF, OBF, CLEAN>, own, stream);
 }
 
 // Every weight type x output type x clean flag of one format and head count.

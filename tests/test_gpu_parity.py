@@ -273,28 +273,30 @@ def test_plan_dimension_mismatch_is_loud(fmt):
     assert bool(torch.isnan(out).all())
 
 
-# Tiles whose rows all see nothing (rows 8-23: two whole tiles of 8 rows, and
-# at 64 heads two halves each) between tiles with windows, keys long enough
+# Tiles whose rows all see nothing between tiles with windows (the plan sorts
+# empty rows to the end of their segment: at 64 heads 16 empty rows of 40 fill
+# two tiles of 8, at 8 heads 80 of 200 fill one tile of 64), keys long enough
 # for several chunks per tile: every cell against the oracle, over a buffer
 # that starts as NaN, so a cell no unit writes shows.
 @pytest.mark.parametrize("fmt", W.FORMATS)
 @pytest.mark.parametrize("S_k", [300, 9000])
-def test_empty_tiles_every_cell(fmt, S_k):
-    S_q = 40
+@pytest.mark.parametrize("H", [64, 8])
+def test_empty_tiles_every_cell(fmt, S_k, H):
+    S_q, n_empty = (40, 16) if H == 64 else (200, 80)
     rng = np.random.default_rng(71)
     starts = rng.integers(0, S_k // 2, S_q)
     ends = starts + rng.integers(1, S_k // 2, S_q)
-    starts[8:24] = S_k // 3
-    ends[8:24] = S_k // 3  # empty
-    wl = W.make_random(fmt, 1, S_q, S_k, seed=71, windows="explicit", starts=starts.tolist(), ends=ends.tolist(),
-                       out_dtype="bf16" if fmt == "mxfp4" else "f32")
+    starts[8:8 + n_empty] = S_k // 3
+    ends[8:8 + n_empty] = S_k // 3  # empty
+    wl = W.make_random(fmt, 1, S_q, S_k, H=H, seed=71, windows="explicit", starts=starts.tolist(),
+                       ends=ends.tolist(), out_dtype="bf16" if fmt == "mxfp4" else "f32")
     d = dev_inputs(wl)
     out = run(wl, d, out=torch.full((1, S_q, S_k), float("nan"), device="cuda",
                                     dtype=torch.bfloat16 if fmt == "mxfp4" else torch.float32))
     torch.cuda.synchronize()
-    assert bool(torch.isneginf(out[0, 8:24].float()).all())
-    ratio, rel = compare_all_rows(wl, out, what=f"empty tiles {fmt} S_k={S_k}")
-    print(f"empty tiles {fmt} S_k={S_k}: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
+    assert bool(torch.isneginf(out[0, 8:8 + n_empty].float()).all())
+    ratio, rel = compare_all_rows(wl, out, what=f"empty tiles {fmt} H={H} S_k={S_k}")
+    print(f"empty tiles {fmt} H={H} S_k={S_k}: max err/bound {ratio:.3e}, rel-L2 {rel:.3e}")
 
 
 # ---------------------------------------------------------------------------
