@@ -73,8 +73,8 @@ int32_t pick_chunks(int64_t S_k, int64_t n_tiles, int64_t S_q, int64_t tile_rows
 }
 
 // Work positions: every chunk of every tile, then one cleanup unit per tile
-// (the most a launch takes: the FP8-family and one-row BF16 kernels clean
-// their own rows and launch no cleanup units).
+// (the most a launch takes: the FP8-family, one-row BF16 and 8-32-head
+// kernels clean their own rows and launch no cleanup units).
 int64_t positions_of(const idx::PlanLayout& L, int64_t n_chunk) { return L.n_tiles * (n_chunk + 1); }
 
 // CUs of the current device, looked up once per device.

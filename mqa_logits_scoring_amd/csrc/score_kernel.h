@@ -8,10 +8,11 @@
 // this kernel, by cleanup units that run after the compute units in the same
 // grid, so cleanup never competes with the matrix work of a compute unit (the
 // placement lesson of DeepGEMM pull request 435, Investigation notes).  The
-// FP8-family kernel and the one-row BF16 kernel below instead clean each row
-// in the compute unit that scores it, after its last score store: with two
-// workgroups per CU the other's MFMAs cover those stores, and the launch has
-// no tail of cleanup units.
+// FP8-family kernel and the one-row BF16 kernel below, and the 8-32-head
+// kernel (score_kernel_gh.h), instead clean each row in the compute unit that
+// scores it, after its last score store: with two workgroups per CU the
+// other's MFMAs cover those stores, and the launch has no tail of cleanup
+// units.
 //
 // Work decomposition
 //   workgroup = 4 waves = one tile of kTileRows query rows x one key chunk
@@ -271,8 +272,8 @@ __device__ __forceinline__ void clean_row_outside(const ScoreArgs& a, int row, i
 }
 
 // Compute units clean their own rows when the launch has no cleanup units
-// (launch_score_t drops them for the plain, non-paged, non-decode FP8-family
-// and one-row BF16 kernels when cleaning).
+// (the launchers drop them for the plain, non-paged, non-decode FP8-family,
+// one-row BF16 and 8-32-head kernels when cleaning).
 __device__ __forceinline__ bool units_clean_own_rows(const ScoreArgs& a) {
   return a.n_positions == a.n_pos_compute && !a.wave_split && !a.dyn_units;
 }

@@ -19,6 +19,11 @@
 // row r / (16 / RPB) of the block whatever g is, so each lane keeps one
 // partial sum per query row of its wave, and one permlane32 swap per pair of
 // rows joins the lane halves' head sets and leaves row 2i + g in lane half g.
+//
+// Cleaning: when the call cleans, each wave writes -inf to its rows outside
+// the tile's coverage after its last score store (the first chunk left of
+// the coverage, the last chunk right of it), and the launch has no cleanup
+// units.
 #pragma once
 
 #include "score_kernel.h"
